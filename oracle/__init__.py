@@ -1,0 +1,159 @@
+"""fp64 CPU oracle for the Mamba selective scan (S6) and its decode step.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the smoke check and the
+bench's CPU-baseline leg, never by the product path. It shares no code with
+the HIP library: the arithmetic lives in ``ssm_oracle.c`` (plain C, fp64,
+sequential recurrence; see its header for the passages each line follows) and
+this module only compiles it with gcc and marshals numpy arrays into it.
+
+Element types: ``float64``, ``float32`` and ``uint16`` arrays are accepted for
+the per-token tensors (u, delta, B, C, z); a ``uint16`` array holds bf16 bit
+patterns. A, D and h0 are widened to float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "ssm_oracle.c")
+LIBRARY = os.path.join(HERE, "libssm_oracle.so")
+
+F64, F32, BF16 = 0, 1, 2
+EULER, ZOH = 0, 1
+_TYPE_OF = {np.dtype(np.float64): F64, np.dtype(np.float32): F32, np.dtype(np.uint16): BF16}
+_DISC = {"euler": EULER, "zoh": ZOH}
+
+_lock = threading.Lock()
+_handles: dict[str, "Oracle"] = {}
+
+
+def build(source: str = SOURCE, output: str = LIBRARY, strict: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math) into ``output``."""
+    tmp = output + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall"]
+    cmd += ["-Werror"] if strict else ["-w"]
+    cmd += ["-o", tmp, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
+    return output
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes handle on one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.oracle_selective_scan.argtypes = [i64, i64, i64, i64, i32, i32,
+                                              vp, vp, vp, vp, vp, vp, vp, vp,
+                                              i64, vp, vp, vp, i32]
+        lib.oracle_selective_scan.restype = i32
+        lib.oracle_state_update.argtypes = [i64, i64, i64, i32, i32,
+                                            vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.oracle_state_update.restype = i32
+        self.lib = lib
+        self.path = path
+
+    @staticmethod
+    def _per_token(arrays):
+        types = {a.dtype for a in arrays if a is not None}
+        if len(types) != 1:
+            raise TypeError("u, delta, B, C and z must share one element type, got %s" % types)
+        t = types.pop()
+        if t not in _TYPE_OF:
+            raise TypeError("unsupported element type %s" % t)
+        return _TYPE_OF[t]
+
+    def selective_scan(self, u, delta, A, B, C, D=None, z=None, h0=None,
+                       disc="euler", channels=None, nthreads=0, want_y=True):
+        """Scan (batch, L, dim) inputs.
+
+        Returns ``(y, h_last)``. With ``channels=None`` every channel is
+        computed and ``y`` is (batch, L, dim), ``h_last`` (batch, dim, N).
+        With ``channels`` a sequence of (b, d) pairs, ``y`` is (k, L) and
+        ``h_last`` is (k, N), row i belonging to ``channels[i]``.
+        """
+        u = np.ascontiguousarray(u)
+        batch, L, dim = u.shape
+        N = A.shape[1]
+        typ = self._per_token([u, delta, B, C, z])
+        delta = np.ascontiguousarray(delta)
+        B = np.ascontiguousarray(B)
+        C = np.ascontiguousarray(C)
+        assert delta.shape == u.shape and B.shape == (batch, L, N) and C.shape == (batch, L, N)
+        A64 = np.ascontiguousarray(A, dtype=np.float64)
+        assert A64.shape == (dim, N)
+        D64 = None if D is None else np.ascontiguousarray(D, dtype=np.float64)
+        zc = None if z is None else np.ascontiguousarray(z)
+        if zc is not None:
+            assert zc.shape == u.shape
+        h064 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+        if h064 is not None:
+            assert h064.shape == (batch, dim, N)
+        if channels is None:
+            sel = None
+            nsel = batch * dim
+        else:
+            sel = np.ascontiguousarray([b * dim + d for b, d in channels], dtype=np.int64)
+            nsel = len(sel)
+        y = np.empty((nsel, L), np.float64) if want_y else None
+        hl = np.empty((nsel, N), np.float64)
+        rc = self.lib.oracle_selective_scan(batch, L, dim, N, typ, _DISC[disc],
+                                            _ptr(u), _ptr(delta), _ptr(A64), _ptr(B), _ptr(C),
+                                            _ptr(D64), _ptr(zc), _ptr(h064),
+                                            nsel, _ptr(sel), _ptr(y), _ptr(hl), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_selective_scan rejected its arguments")
+        if channels is None:
+            if y is not None:
+                y = y.reshape(batch, dim, L).transpose(0, 2, 1).copy()
+            hl = hl.reshape(batch, dim, N)
+        return y, hl
+
+    def state_update(self, x, delta, A, B, C, h, D=None, z=None, disc="euler", nthreads=0):
+        """One decode step. ``h`` (batch, dim, N) float64 is updated in place; returns y."""
+        x = np.ascontiguousarray(x)
+        batch, dim = x.shape
+        N = A.shape[1]
+        typ = self._per_token([x, delta, B, C, z])
+        assert h.dtype == np.float64 and h.flags.c_contiguous and h.shape == (batch, dim, N)
+        A64 = np.ascontiguousarray(A, dtype=np.float64)
+        D64 = None if D is None else np.ascontiguousarray(D, dtype=np.float64)
+        y = np.empty((batch, dim), np.float64)
+        rc = self.lib.oracle_state_update(batch, dim, N, typ, _DISC[disc],
+                                          _ptr(x), _ptr(np.ascontiguousarray(delta)), _ptr(A64),
+                                          _ptr(np.ascontiguousarray(B)), _ptr(np.ascontiguousarray(C)),
+                                          _ptr(D64), _ptr(None if z is None else np.ascontiguousarray(z)),
+                                          _ptr(h), _ptr(y), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_state_update rejected its arguments")
+        return y
+
+
+def load(path: str | None = None) -> Oracle:
+    """Load (building first if needed) the oracle library at ``path``."""
+    path = path or LIBRARY
+    with _lock:
+        if path not in _handles:
+            if path == LIBRARY and (not os.path.exists(path)
+                                    or os.path.getmtime(path) < os.path.getmtime(SOURCE)):
+                build()
+            _handles[path] = Oracle(path)
+        return _handles[path]
+
+
+def selective_scan(*args, **kwargs):
+    return load().selective_scan(*args, **kwargs)
+
+
+def state_update(*args, **kwargs):
+    return load().state_update(*args, **kwargs)

@@ -1,0 +1,242 @@
+"""Seeded synthetic inputs for the selective scan and the decode step.
+
+Shared by the tests, the bench and the smoke check, and by both sides of
+every parity comparison (the HIP path and the fp64 oracle). It holds none of
+the scan's arithmetic: it only draws random tensors, shapes them like a Mamba
+layer's scan inputs and rounds them to the storage type.
+
+Recipe (one workload per entry of ``CONFIGS``):
+  * u, B, C, z ~ N(0, 1); decode state h ~ N(0, 1).
+  * delta = softplus(0.5 * N(0,1) + bias[d]) with one bias per channel,
+    bias = inv_softplus(U[1e-3, 1e-1]), or inv_softplus of a log-uniform draw
+    in [1e-4, 1e-1] for the long-context workload. delta is therefore
+    positive, as after the softplus of youngju.dev SelectiveSSM.forward.
+  * A[d, n] = -(n + 1): the S4D-Real values that the pages' A_log = log(1..N)
+    initialisation produces (eommydocs §5.1 SelectiveSSM, youngju.dev
+    MambaBlock.__init__).
+  * D = 1 (tiny workload) or D ~ N(1, 0.1).
+  * bf16 tensors are produced as float32 and rounded to nearest-even; they are
+    returned as uint16 bit patterns, which both sides read.
+Streams: numpy PCG64 children of SeedSequence(seed), one per tensor in the
+fixed order [u, delta_noise, delta_bias, B, C, z, D, h0]; large tensors are
+drawn in fixed 4 Mi-element blocks, each from its own grandchild seed, so the
+values do not depend on the number of threads used to draw them.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+
+BLOCK = 1 << 22
+STREAMS = ("u", "delta_noise", "delta_bias", "B", "C", "z", "D", "h0")
+
+
+@dataclass(frozen=True)
+class ScanConfig:
+    name: str
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    dtype: str          # "f32" or "bf16": type of u, delta, B, C, z, y
+    gate: bool          # z present
+    d_skip: str         # "ones" or "normal"
+    bias: str           # "uniform" or "loguniform"
+
+    @property
+    def tokens_ch(self) -> int:
+        return self.batch * self.seqlen * self.dim
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    steps: int
+    dtype: str = "bf16"
+    gate: bool = True
+    bias: str = "uniform"
+
+
+CONFIGS = {
+    "tiny": ScanConfig("tiny", 1, 64, 16, 4, "f32", False, "ones", "uniform"),
+    "mamba130m": ScanConfig("mamba130m", 4, 2048, 1536, 16, "bf16", True, "normal", "uniform"),
+    "mamba1.4b": ScanConfig("mamba1.4b", 8, 8192, 4096, 16, "bf16", True, "normal", "uniform"),
+    "long": ScanConfig("long", 1, 131072, 5120, 16, "bf16", True, "normal", "loguniform"),
+}
+DECODE = DecodeConfig("decode", 256, 5120, 16, 1000)
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _stream(seed: int, name: str) -> np.random.SeedSequence:
+    return np.random.SeedSequence(seed).spawn(len(STREAMS))[STREAMS.index(name)]
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); returns uint16 patterns."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 patterns to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def inv_softplus(y):
+    return np.log(np.expm1(y))
+
+
+def _blocked(seed_seq, total, fill, out_dtype):
+    """Fill a flat array of ``total`` elements block by block, in parallel."""
+    out = np.empty(total, dtype=out_dtype)
+    nblocks = (total + BLOCK - 1) // BLOCK
+    children = seed_seq.spawn(nblocks) if nblocks else []
+
+    def work(i):
+        lo, hi = i * BLOCK, min(total, (i + 1) * BLOCK)
+        rng = np.random.Generator(np.random.PCG64(children[i]))
+        out[lo:hi] = fill(rng, lo, hi)
+
+    if nblocks <= 1:
+        for i in range(nblocks):
+            work(i)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nblocks)))
+    return out
+
+
+def _normal(seed, name, shape, dtype):
+    total = int(np.prod(shape))
+    if dtype == "bf16":
+        fill = lambda rng, lo, hi: to_bf16_bits(rng.standard_normal(hi - lo, dtype=np.float32))
+        return _blocked(_stream(seed, name), total, fill, np.uint16).reshape(shape)
+    fill = lambda rng, lo, hi: rng.standard_normal(hi - lo, dtype=np.float32)
+    return _blocked(_stream(seed, name), total, fill, np.float32).reshape(shape)
+
+
+def delta_bias(seed: int, dim: int, kind: str) -> np.ndarray:
+    """Per-channel pre-softplus bias of delta (float64)."""
+    rng = np.random.Generator(np.random.PCG64(_stream(seed, "delta_bias")))
+    if kind == "loguniform":
+        target = np.exp(rng.uniform(np.log(1e-4), np.log(1e-1), size=dim))
+    else:
+        target = rng.uniform(1e-3, 1e-1, size=dim)
+    return inv_softplus(target)
+
+
+def _delta(seed, shape, bias, dtype, stream="delta_noise"):
+    dim = shape[-1]
+    total = int(np.prod(shape))
+
+    def fill(rng, lo, hi):
+        noise = rng.standard_normal(hi - lo, dtype=np.float32).astype(np.float64)
+        d_idx = np.arange(lo, hi, dtype=np.int64) % dim
+        val = softplus(0.5 * noise + bias[d_idx]).astype(np.float32)
+        return to_bf16_bits(val) if dtype == "bf16" else val
+
+    out_dtype = np.uint16 if dtype == "bf16" else np.float32
+    return _blocked(_stream(seed, stream), total, fill, out_dtype).reshape(shape)
+
+
+def a_matrix(dim: int, dstate: int) -> np.ndarray:
+    """A[d, n] = -(n + 1), float32."""
+    return np.broadcast_to(-np.arange(1, dstate + 1, dtype=np.float32), (dim, dstate)).copy()
+
+
+def d_skip(seed: int, dim: int, kind: str) -> np.ndarray:
+    if kind == "ones":
+        return np.ones(dim, np.float32)
+    rng = np.random.Generator(np.random.PCG64(_stream(seed, "D")))
+    return rng.normal(1.0, 0.1, size=dim).astype(np.float32)
+
+
+def scan_inputs(cfg: ScanConfig, seed: int = 0, batch: int | None = None,
+                seqlen: int | None = None, dim: int | None = None, dstate: int | None = None):
+    """Inputs of one scan workload (sizes may be overridden for reduced tests).
+
+    Returns a dict with u, delta, A, B, C, D, z (None without a gate), h0 (None).
+    """
+    b = cfg.batch if batch is None else batch
+    L = cfg.seqlen if seqlen is None else seqlen
+    d = cfg.dim if dim is None else dim
+    N = cfg.dstate if dstate is None else dstate
+    bias = delta_bias(seed, d, cfg.bias)
+    return dict(
+        u=_normal(seed, "u", (b, L, d), cfg.dtype),
+        delta=_delta(seed, (b, L, d), bias, cfg.dtype),
+        A=a_matrix(d, N),
+        B=_normal(seed, "B", (b, L, N), cfg.dtype),
+        C=_normal(seed, "C", (b, L, N), cfg.dtype),
+        D=d_skip(seed, d, cfg.d_skip),
+        z=_normal(seed, "z", (b, L, d), cfg.dtype) if cfg.gate else None,
+        h0=None,
+    )
+
+
+def decode_static(cfg: DecodeConfig = DECODE, seed: int = 0, batch=None, dim=None, dstate=None):
+    """A, D, the initial state h (fp32 N(0,1)) and the delta bias of a decode workload."""
+    b = cfg.batch if batch is None else batch
+    d = cfg.dim if dim is None else dim
+    N = cfg.dstate if dstate is None else dstate
+    return dict(A=a_matrix(d, N), D=d_skip(seed, d, "normal"),
+                h=_normal(seed, "h0", (b, d, N), "f32"),
+                bias=delta_bias(seed, d, cfg.bias))
+
+
+def decode_step(cfg: DecodeConfig = DECODE, step_set: int = 0, seed: int = 0,
+                batch=None, dim=None, dstate=None, bias=None):
+    """Per-token inputs x, delta, z (batch, dim) and B, C (batch, N) of one step set."""
+    b = cfg.batch if batch is None else batch
+    d = cfg.dim if dim is None else dim
+    N = cfg.dstate if dstate is None else dstate
+    if bias is None:
+        bias = delta_bias(seed, d, cfg.bias)
+    s = seed + 1000003 * (step_set + 1)   # a distinct master seed per step set
+    return dict(
+        x=_normal(s, "u", (b, d), cfg.dtype),
+        delta=_delta(s, (b, d), bias, cfg.dtype),
+        B=_normal(s, "B", (b, N), cfg.dtype),
+        C=_normal(s, "C", (b, N), cfg.dtype),
+        z=_normal(s, "z", (b, d), cfg.dtype) if cfg.gate else None,
+    )
+
+
+def algorithmic_bytes(cfg: ScanConfig, h_last: bool = True, h0: bool = False) -> int:
+    """Bytes the scan must move: every input once, every output once."""
+    es = 4 if cfg.dtype == "f32" else 2
+    per_tok = 3 if not cfg.gate else 4          # u, delta, y (+ z)
+    nbytes = per_tok * cfg.tokens_ch * es
+    nbytes += 2 * cfg.batch * cfg.seqlen * cfg.dstate * es      # B, C
+    nbytes += cfg.dim * cfg.dstate * 4 + cfg.dim * 4            # A, D
+    if h_last:
+        nbytes += cfg.batch * cfg.dim * cfg.dstate * 4
+    if h0:
+        nbytes += cfg.batch * cfg.dim * cfg.dstate * 4
+    return nbytes
+
+
+def decode_bytes(cfg: DecodeConfig = DECODE) -> int:
+    """Bytes one decode step must move: h read and written, x/delta/z/y, B/C, A, D."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    bd = cfg.batch * cfg.dim
+    return (2 * bd * cfg.dstate * 4 + (4 if cfg.gate else 3) * bd * es
+            + 2 * cfg.batch * cfg.dstate * es + cfg.dim * cfg.dstate * 4 + cfg.dim * 4)

@@ -1,0 +1,362 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes an oracle handle (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees with an independent statement of the
+same quantity. They are collected by ``test_oracle_pins.py`` against the real
+oracle and by ``test_oracle_mutants.py`` against deliberately broken copies of
+it (to show that a plausible mistake anywhere in the oracle fails a pin).
+
+None of these re-types the oracle's loop. The independent statements are:
+  * the unrolled sum-of-products form in arbitrary precision (``oracle.brute``),
+  * the LTI convolution kernel K_k = sum_n C_n Abar_n^k Bbar_n with
+    Abar^k = exp(k*delta*A) in closed form (itwiki "상태 공간 모델", "순환 형태와
+    합성곱 형태"), as a direct causal convolution and through numpy.fft with
+    zero padding to 2L (youngju.dev S4Layer.forward),
+  * delta -> 0 keeps the state (itwiki "Mamba의 선택 메커니즘";
+    ricepunchb "Mamba" §3.2; doyouknow.kr §3-1),
+  * large delta forgets and focuses on the input (same passages),
+  * zero-order hold is the exact solution of x' = Ax + Bu with u held over the
+    step (eommydocs §1.2; itwiki "이산화"), checked by RK4 integration,
+  * N = 1, A = 0 reduces the scan to a prefix sum (numpy.cumsum),
+  * the affine-pair composition (a1,b1).(a2,b2) = (a2 a1, a2 b1 + b2) is
+    associative (ricepunchb "Mamba" §5.1),
+  * resuming from the last state reproduces the tail (ricepunchb §4.2:
+    only the last hidden state is needed to continue),
+  * with h0 = 0 and no gate the output is linear in u and causal,
+  * the SiLU gate and the D skip at points with a closed form.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import brute
+
+RNG_SEED = 1234
+
+
+def rel_err(got, ref):
+    """max |g - r| / max(|r|, rms(r)) over the tensor (rms floor for cancellation)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    floor = np.maximum(np.abs(ref), rms if rms > 0 else 1e-300)
+    return float(np.max(np.abs(got - ref) / floor))
+
+
+def _case(rng, batch, L, dim, N, with_d=True, with_z=False, with_h0=False, a_zero=False):
+    u = rng.standard_normal((batch, L, dim))
+    delta = np.exp(rng.uniform(np.log(1e-3), np.log(0.5), (batch, L, dim)))
+    A = -np.exp(rng.uniform(np.log(0.2), np.log(8.0), (dim, N)))
+    if a_zero:
+        A[:] = 0.0
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    D = rng.normal(1.0, 0.3, dim) if with_d else None
+    z = rng.standard_normal((batch, L, dim)) if with_z else None
+    h0 = rng.standard_normal((batch, dim, N)) if with_h0 else None
+    return dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, h0=h0)
+
+
+def pin_brute_force(o):
+    """P1: the oracle equals the 50-digit unrolled form on small random cases."""
+    rng = np.random.default_rng(RNG_SEED)
+    cases = [
+        (dict(batch=2, L=7, dim=3, N=3, with_d=True, with_z=True, with_h0=True), "euler"),
+        (dict(batch=1, L=9, dim=2, N=4, with_d=False, with_z=False, with_h0=False), "euler"),
+        (dict(batch=2, L=6, dim=2, N=2, with_d=True, with_z=True, with_h0=True), "zoh"),
+        (dict(batch=1, L=5, dim=3, N=1, with_d=True, with_z=False, with_h0=True), "zoh"),
+    ]
+    for shape, disc in cases:
+        x = _case(rng, **shape)
+        y, hl = o.selective_scan(**x, disc=disc)
+        yb, hb = brute.selective_scan(**x, disc=disc)
+        assert rel_err(y, yb) < 1e-12, ("y", shape, disc, rel_err(y, yb))
+        assert rel_err(hl, hb) < 1e-12, ("h_last", shape, disc, rel_err(hl, hb))
+
+
+def pin_brute_force_storage_types(o):
+    """P1 for float32 and bf16 inputs: the oracle widens them exactly."""
+    rng = np.random.default_rng(RNG_SEED + 1)
+    x = _case(rng, 2, 6, 3, 4, with_d=True, with_z=True, with_h0=False)
+    for name in ("u", "delta", "B", "C", "z"):
+        x[name] = x[name].astype(np.float32)
+    y32, h32 = o.selective_scan(**x)
+    yb, hb = brute.selective_scan(**x)
+    assert rel_err(y32, yb) < 1e-12 and rel_err(h32, hb) < 1e-12
+    bf = dict(x)
+    for name in ("u", "delta", "B", "C", "z"):
+        bits = x[name].view(np.uint32) >> np.uint32(16)      # truncation: any pattern will do
+        bf[name] = bits.astype(np.uint16)
+    ybf, hbf = o.selective_scan(**bf)
+    widened = {k: (v if k not in ("u", "delta", "B", "C", "z")
+                   else (bf[k].astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64))
+               for k, v in bf.items()}
+    yw, hw = brute.selective_scan(**widened)
+    assert rel_err(ybf, yw) < 1e-12 and rel_err(hbf, hw) < 1e-12
+
+
+def _lti_case(rng, batch, L, dim, N, disc, with_h0):
+    """Delta per channel, B and C held constant over t (and across batch rows)."""
+    dch = np.exp(rng.uniform(np.log(1e-2), np.log(0.3), dim))
+    A = -np.exp(rng.uniform(np.log(0.1), np.log(4.0), (dim, N)))
+    Bn = rng.standard_normal(N)
+    Cn = rng.standard_normal(N)
+    u = rng.standard_normal((batch, L, dim))
+    D = rng.normal(1.0, 0.2, dim)
+    h0 = rng.standard_normal((batch, dim, N)) if with_h0 else None
+    x = dict(u=u, delta=np.broadcast_to(dch, (batch, L, dim)).copy(), A=A,
+             B=np.broadcast_to(Bn, (batch, L, N)).copy(), C=np.broadcast_to(Cn, (batch, L, N)).copy(),
+             D=D, z=None, h0=h0)
+    dA = dch[:, None] * A                                        # (dim, N)
+    if disc == "zoh":
+        bbar = np.expm1(dA) / A * Bn[None, :]
+    else:
+        bbar = dch[:, None] * Bn[None, :]
+    k = np.arange(L)
+    # K[d, k] = sum_n C_n exp(k dA[d,n]) Bbar[d,n]: the closed-form kernel
+    K = np.einsum("n,dnk,dn->dk", Cn, np.exp(dA[:, :, None] * k[None, None, :]), bbar)
+    # initial-state response: sum_n C_n exp((t+1) dA) h0
+    if h0 is not None:
+        free = np.einsum("n,dnt,bdn->btd", Cn, np.exp(dA[:, :, None] * (k[None, None, :] + 1)), h0)
+    else:
+        free = 0.0
+    return x, K, free, D
+
+
+def pin_lti_direct(o):
+    """P2: constant delta, B, C -> y = u * K + D u, by direct causal convolution."""
+    rng = np.random.default_rng(RNG_SEED + 2)
+    for disc in ("euler", "zoh"):
+        batch, L, dim, N = 2, 160, 3, 5
+        x, K, free, D = _lti_case(rng, batch, L, dim, N, disc, with_h0=True)
+        ref = np.zeros((batch, L, dim))
+        for t in range(L):
+            # y_t = sum_{k<=t} K_k u_{t-k}
+            ref[:, t, :] = np.einsum("dk,bkd->bd", K[:, :t + 1][:, ::-1], x["u"][:, :t + 1, :])
+        ref = ref + free + D[None, None, :] * x["u"]
+        y, _ = o.selective_scan(**x, disc=disc)
+        assert rel_err(y, ref) < 1e-10, (disc, rel_err(y, ref))
+
+
+def pin_lti_fft(o):
+    """P2 at length 4096 through an FFT convolution zero-padded to 2L."""
+    rng = np.random.default_rng(RNG_SEED + 3)
+    batch, L, dim, N = 1, 4096, 2, 4
+    x, K, _, D = _lti_case(rng, batch, L, dim, N, "euler", with_h0=False)
+    uf = np.fft.rfft(x["u"].transpose(0, 2, 1), n=2 * L)
+    kf = np.fft.rfft(K, n=2 * L)
+    conv = np.fft.irfft(uf * kf[None], n=2 * L)[..., :L].transpose(0, 2, 1)
+    ref = conv + D[None, None, :] * x["u"]
+    y, _ = o.selective_scan(**x)
+    assert rel_err(y, ref) < 1e-10, rel_err(y, ref)
+
+
+def pin_delta_zero(o):
+    """P3: delta = 0 keeps h = h0 exactly and y_t = C_t . h0 + D u_t."""
+    rng = np.random.default_rng(RNG_SEED + 4)
+    for disc in ("euler", "zoh"):
+        x = _case(rng, 2, 12, 3, 4, with_d=True, with_z=False, with_h0=True)
+        x["delta"] = np.zeros_like(x["delta"])
+        y, hl = o.selective_scan(**x, disc=disc)
+        assert np.array_equal(hl, x["h0"]), disc
+        ref = np.einsum("btn,bdn->btd", x["C"], x["h0"]) + x["D"][None, None, :] * x["u"]
+        assert rel_err(y, ref) < 1e-13, disc
+
+
+def pin_large_delta(o):
+    """P4: with A < 0 and a huge delta, Abar -> 0, so h_t is the current input term only:
+    ZOH gives -B_t u_t / A, the simplified rule gives delta B_t u_t."""
+    rng = np.random.default_rng(RNG_SEED + 5)
+    x = _case(rng, 1, 6, 2, 3, with_d=False, with_z=False, with_h0=True)
+    big = 2.0e3
+    x["delta"] = np.full_like(x["delta"], big)
+    for disc in ("zoh", "euler"):
+        for L1 in range(1, 7):
+            sub = dict(x, u=x["u"][:, :L1], delta=x["delta"][:, :L1], B=x["B"][:, :L1], C=x["C"][:, :L1])
+            _, hl = o.selective_scan(**sub, disc=disc)
+            bt = x["B"][0, L1 - 1]          # (N,)
+            ut = x["u"][0, L1 - 1]          # (dim,)
+            if disc == "zoh":
+                ref = -(ut[:, None] * bt[None, :]) / x["A"]
+            else:
+                ref = big * ut[:, None] * bt[None, :]
+            assert rel_err(hl[0], ref) < 1e-12, (disc, L1)
+
+
+def _rk4_hold(a, bcoef, u, h, dt, steps=10000):
+    """Integrate h' = a h + bcoef u over [0, dt] with u held, classic RK4."""
+    f = lambda hh: a * hh + bcoef * u
+    s = dt / steps
+    for _ in range(steps):
+        k1 = f(h)
+        k2 = f(h + 0.5 * s * k1)
+        k3 = f(h + 0.5 * s * k2)
+        k4 = f(h + s * k3)
+        h = h + s / 6.0 * (k1 + 2 * k2 + 2 * k3 + k4)
+    return h
+
+
+def pin_zoh_exact_hold(o):
+    """P5: one ZOH step equals the exact continuous solution with the input held,
+    and the ZOH input term tends to the simplified one as delta -> 0."""
+    rng = np.random.default_rng(RNG_SEED + 6)
+    dim, N = 2, 3
+    A = -np.exp(rng.uniform(np.log(0.2), np.log(5.0), (dim, N)))
+    B = rng.standard_normal((1, 1, N))
+    C = rng.standard_normal((1, 1, N))
+    u = rng.standard_normal((1, 1, dim))
+    h0 = rng.standard_normal((1, dim, N))
+    delta = np.array([[[0.37, 1.3]]])
+    _, hl = o.selective_scan(u=u, delta=delta, A=A, B=B, C=C, h0=h0, disc="zoh")
+    ref = _rk4_hold(A, B[0, 0][None, :], u[0, 0][:, None], h0[0], delta[0, 0][:, None])
+    assert np.all(np.abs(hl[0] - ref) <= 1e-10 * np.maximum(1.0, np.abs(ref))), (hl[0], ref)
+    tiny = np.full((1, 1, dim), 1e-7)
+    _, hz = o.selective_scan(u=u, delta=tiny, A=A, B=B, C=C, disc="zoh")
+    _, he = o.selective_scan(u=u, delta=tiny, A=A, B=B, C=C, disc="euler")
+    assert rel_err(hz, he) < 1e-6
+
+
+def pin_prefix_sum(o):
+    """P6: N = 1 and A = 0 make Abar = 1, so h_t = cumsum(delta B u) (both rules)."""
+    rng = np.random.default_rng(RNG_SEED + 7)
+    for disc in ("euler", "zoh"):
+        x = _case(rng, 2, 300, 3, 1, with_d=False, a_zero=True)
+        y, hl = o.selective_scan(**dict(x, C=np.ones_like(x["C"])), disc=disc)
+        ref = np.cumsum(x["delta"] * x["B"][:, :, :1] * x["u"], axis=1)
+        assert rel_err(y, ref) < 1e-12, disc
+        assert rel_err(hl[:, :, 0], ref[:, -1, :]) < 1e-12, disc
+
+
+def _aggregate(o, x, disc):
+    """Segment aggregate (P, H) from the oracle: P = decay of a unit state with no input,
+    H = end state from zero."""
+    N = x["A"].shape[1]
+    batch, _, dim = x["u"].shape
+    ones = np.ones((batch, dim, N))
+    _, P = o.selective_scan(**dict(x, B=np.zeros_like(x["B"]), h0=ones, z=None), disc=disc)
+    _, H = o.selective_scan(**dict(x, h0=None, z=None), disc=disc)
+    return P, H
+
+
+def pin_affine_composition(o):
+    """P7: segments compose as affine maps h -> P h + H, and the composition is
+    associative: any bracketing over four segments gives the full scan's state."""
+    rng = np.random.default_rng(RNG_SEED + 8)
+    x = _case(rng, 2, 40, 3, 4, with_d=True, with_z=False, with_h0=True)
+    cuts = [0, 7, 19, 20, 40]
+    segs = []
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        sub = {k: (v[:, lo:hi] if k in ("u", "delta", "B", "C") else v) for k, v in x.items()}
+        segs.append(_aggregate(o, sub, "euler"))
+
+    def comp(p, q):  # apply p first, then q
+        return (q[0] * p[0], q[0] * p[1] + q[1])
+
+    left = comp(comp(comp(segs[0], segs[1]), segs[2]), segs[3])
+    right = comp(segs[0], comp(segs[1], comp(segs[2], segs[3])))
+    tree = comp(comp(segs[0], segs[1]), comp(segs[2], segs[3]))
+    _, hl = o.selective_scan(**x)
+    for P, H in (left, right, tree):
+        assert rel_err(P * x["h0"] + H, hl) < 1e-12
+
+
+def pin_resume(o):
+    """P8: scanning [0, L) equals scanning [0, L1) then [L1, L) from its last state."""
+    rng = np.random.default_rng(RNG_SEED + 9)
+    for disc in ("euler", "zoh"):
+        x = _case(rng, 2, 50, 3, 4, with_d=True, with_z=True, with_h0=True)
+        y, hl = o.selective_scan(**x, disc=disc)
+        L1 = 23
+        head = {k: (v[:, :L1] if k in ("u", "delta", "B", "C", "z") else v) for k, v in x.items()}
+        tail = {k: (v[:, L1:] if k in ("u", "delta", "B", "C", "z") else v) for k, v in x.items()}
+        y1, h1 = o.selective_scan(**head, disc=disc)
+        y2, h2 = o.selective_scan(**dict(tail, h0=h1), disc=disc)
+        assert np.array_equal(np.concatenate([y1, y2], axis=1), y), disc
+        assert np.array_equal(h2, hl), disc
+
+
+def pin_decode_is_scan(o):
+    """P9: k decode steps equal a k-token scan (state in, state out, per-token y)."""
+    rng = np.random.default_rng(RNG_SEED + 10)
+    for disc in ("euler", "zoh"):
+        x = _case(rng, 3, 5, 4, 3, with_d=True, with_z=True, with_h0=True)
+        y, hl = o.selective_scan(**x, disc=disc)
+        h = x["h0"].copy()
+        for t in range(5):
+            yt = o.state_update(x["u"][:, t], x["delta"][:, t], x["A"], x["B"][:, t], x["C"][:, t],
+                                h, D=x["D"], z=x["z"][:, t], disc=disc)
+            assert rel_err(yt, y[:, t]) < 1e-14, (disc, t)
+        assert rel_err(h, hl) < 1e-14, disc
+
+
+def pin_linear_causal(o):
+    """P10: with h0 = 0 and no gate, y is linear in u; y_s ignores u_t for t > s."""
+    rng = np.random.default_rng(RNG_SEED + 11)
+    x = _case(rng, 2, 30, 3, 4, with_d=True)
+    u1, u2 = x["u"], rng.standard_normal(x["u"].shape)
+    y1, _ = o.selective_scan(**x)
+    y2, _ = o.selective_scan(**dict(x, u=u2))
+    y3, _ = o.selective_scan(**dict(x, u=2.5 * u1 - 0.75 * u2))
+    assert rel_err(y3, 2.5 * y1 - 0.75 * y2) < 1e-12
+    up = u1.copy()
+    up[:, 17, :] += 1.0
+    y4, _ = o.selective_scan(**dict(x, u=up))
+    assert np.array_equal(y4[:, :17], y1[:, :17])
+    assert np.all(np.abs(y4[:, 17] - y1[:, 17]) > 0)
+
+
+def pin_gate_and_skip(o):
+    """SiLU gate and D skip at points with closed forms; the readout uses h_t after
+    the update (a one-token scan from zero gives C . (delta B u) + D u)."""
+    # B = 0 keeps h = 0, so y = D u silu(z); silu(1) = 1/(1+e^-1), silu(-2) = -2/(1+e^2)
+    u = np.array([[[1.0, 3.0]]])
+    z = np.array([[[1.0, -2.0]]])
+    x = dict(u=u, delta=np.full_like(u, 0.1), A=-np.ones((2, 2)), B=np.zeros((1, 1, 2)),
+             C=np.ones((1, 1, 2)), D=np.array([1.0, 0.5]), z=z, h0=None)
+    y, _ = o.selective_scan(**x)
+    ref = np.array([1.0 / (1.0 + np.exp(-1.0)), 1.5 * (-2.0) / (1.0 + np.exp(2.0))])
+    assert rel_err(y[0, 0], ref) < 1e-15
+    x["z"] = np.zeros_like(z)
+    y0, _ = o.selective_scan(**x)
+    assert np.all(y0 == 0.0)
+    # readout after update: L = 1 from zero
+    rng = np.random.default_rng(RNG_SEED + 12)
+    xr = _case(rng, 2, 1, 3, 4, with_d=True)
+    y1, _ = o.selective_scan(**xr)
+    ref1 = (np.einsum("bn,bd,bd,bn->bd", xr["C"][:, 0], xr["delta"][:, 0], xr["u"][:, 0], xr["B"][:, 0])
+            + xr["D"][None, :] * xr["u"][:, 0])
+    assert rel_err(y1[:, 0], ref1) < 1e-14
+    # C = 0 leaves only the skip, exactly
+    y2, _ = o.selective_scan(**dict(xr, C=np.zeros_like(xr["C"])))
+    assert np.array_equal(y2, xr["D"][None, None, :] * xr["u"])
+
+
+def pin_channel_selection(o):
+    """Computing a subset of channels gives exactly the rows of the full scan."""
+    rng = np.random.default_rng(RNG_SEED + 13)
+    x = _case(rng, 3, 20, 5, 3, with_d=True, with_z=True, with_h0=True)
+    y, hl = o.selective_scan(**x)
+    chans = [(2, 4), (0, 0), (1, 3), (2, 0)]
+    ys, hs = o.selective_scan(**x, channels=chans)
+    for i, (b, d) in enumerate(chans):
+        assert np.array_equal(ys[i], y[b, :, d]) and np.array_equal(hs[i], hl[b, d])
+
+
+ALL_PINS = [
+    pin_brute_force,
+    pin_brute_force_storage_types,
+    pin_lti_direct,
+    pin_lti_fft,
+    pin_delta_zero,
+    pin_large_delta,
+    pin_zoh_exact_hold,
+    pin_prefix_sum,
+    pin_affine_composition,
+    pin_resume,
+    pin_decode_is_scan,
+    pin_linear_causal,
+    pin_gate_and_skip,
+    pin_channel_selection,
+]

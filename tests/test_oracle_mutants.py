@@ -1,0 +1,70 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one of them: a dropped term, a wrong sign, a wrong index,
+a transposed operand, a wrong readout order, a broken storage-type widening.
+
+Each mutant is a textual edit of oracle/ssm_oracle.c compiled into a temporary
+directory; the real oracle is never touched.
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "decay_sign": ("exp(dt * a_dn);", "exp(-dt * a_dn);"),
+    "drop_delta_in_input": ("return delta * b_tn * u;", "return b_tn * u;"),
+    "zoh_missing_delta": ("expm1(delta * a_dn) / a_dn", "expm1(delta * a_dn) / (delta * a_dn)"),
+    "zoh_limit_wrong": (": delta;\n        return coef", ": 1.0;\n        return coef"),
+    "a_transposed": ("const double a_dn = A[d * N + n];\n            const double abar",
+                     "const double a_dn = A[n * dim + d];\n            const double abar"),
+    "b_ignores_time": ("load(B, type, row * N + n), ut)", "load(B, type, b * L * N + n), ut)"),
+    "c_from_b": ("yt += load(C, type, row * N + n) * h[n];", "yt += load(B, type, row * N + n) * h[n];"),
+    "readout_before_update": (
+        "            h[n] = abar * h[n] + bu;\n            yt += load(C, type, row * N + n) * h[n];",
+        "            yt += load(C, type, row * N + n) * h[n];\n            h[n] = abar * h[n] + bu;"),
+    "drop_skip": ("yt += dskip * ut;", "yt += 0.0 * ut;"),
+    "skip_wrong_channel": ("const double dskip = D ? D[d] : 0.0;", "const double dskip = D ? D[0] : 0.0;"),
+    "gate_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "gate_is_sigmoid": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    "h0_transposed": ("h[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;",
+                      "h[n] = h0 ? h0[(b * N + n) * dim + d] : 0.0;"),
+    "state_not_decayed": ("h[n] = abar * h[n] + bu;", "h[n] = h[n] + bu;"),
+    "bf16_shift": ("<< 16;", "<< 15;"),
+    "f32_truncated": ("return (double)((const float *)p)[i];", "return (double)(float)(int)((const float *)p)[i];"),
+    "decode_b_row": ("load(B, type, b * N + n), xt);", "load(B, type, n), xt);"),
+    "decode_c_row": ("yt += load(C, type, b * N + n) * hc[n];", "yt += load(C, type, n) * hc[n];"),
+    "decode_no_skip": ("yt += (D ? D[d] : 0.0) * xt;", "yt += 0.0 * xt;"),
+    "decode_no_gate": ("            yt *= silu(load(z, type, c));", "            yt *= 1.0;"),
+    "last_state_not_written": ("hl[n] = h[n];", "hl[n] = 0.0 * h[n];"),
+}
+
+
+def _source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+def test_mutations_apply_once():
+    src = _source()
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, name
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = _source().replace(old, new)
+    c_path = os.path.join(tmp_path, "mutant.c")
+    with open(c_path, "w") as f:
+        f.write(src)
+    lib = oracle.build(source=c_path, output=os.path.join(tmp_path, "libmutant.so"), strict=False)
+    o = oracle.Oracle(lib)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, "mutant %s survived every pin" % name
