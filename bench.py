@@ -1,0 +1,257 @@
+"""Throughput of the selective scan on one MI355X.
+
+One step = one ssm_scan_fwd over the Mamba-1.4B-shaped layer workload
+(batch 8, L 8192, d_inner 4096, d_state 16; bf16 u/delta/B/C/z/y, fp32 A/D and
+state; D skip, SiLU gate, final state written), inputs resident in HBM.
+Prints one JSON line: selective-scan Gtokens*ch/s, the dominant kernel's
+roofline position (measured with HIP events on the stream it runs on), the
+algorithmic HBM rate, the decode step measured alongside, and the fp64 CPU
+oracle timed on a bounded sample of the same workload (whose outputs are
+also compared with the GPU's timed outputs).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import ssm_inputs as si  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+# fp32 VALU issue rate without packed instructions: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+WORKLOAD = "mamba1.4b"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_scan_mamba1.4b.json")
+CSRC = os.path.join(ROOT, "selective_state_space_78_amd", "csrc")
+
+
+def valu_ops_per_token_ch(N: int, gate: bool) -> int:
+    """Minimal fp32 VALU lane-operations of the method per (b, t, d):
+    per state: delta*A, exp2, (delta*u)*B, fma(a, h, Bu), fma(C, h, y);
+    per token: delta*u, fma(D, u, y), and for the gate z*log2e, exp2, 1+e, rcp, z*r, y*s."""
+    return 5 * N + 2 + (6 if gate else 0)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def to_dev(a, torch):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms)))
+
+
+def measured_traffic(per_launch_tokens: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(x, y_dev, torch, budget_s=15.0):
+    """The fp64 oracle, as it stands, on batch row 0 of the same workload for a
+    bounded number of channels over the full sequence. Its outputs are also
+    compared with the GPU's timed outputs for those channels."""
+    import oracle
+    o = oracle.load()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    L = x["u"].shape[1]
+    # size the sample from a short probe run
+    probe = [(0, d) for d in range(threads)]
+    t0 = time.perf_counter()
+    o.selective_scan(**x, channels=probe, nthreads=threads)
+    per_ch = (time.perf_counter() - t0) / len(probe) * threads
+    k = int(max(threads, min(x["u"].shape[2], budget_s * threads / max(per_ch, 1e-9))))
+    k = (k // threads) * threads
+    chans = [(0, d) for d in range(k)]
+    t0 = time.perf_counter()
+    yr, hr = o.selective_scan(**x, channels=chans, nthreads=threads)
+    sec = time.perf_counter() - t0
+    yg = y_dev[0, :, :k].float().cpu().numpy().T          # (k, L)
+    err = rel_err(yg, yr)
+    return {
+        "value": k * L / sec / 1e9,
+        "unit": "Gtokens*ch/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "batch row 0, channels 0..%d, all %d tokens (%d token*ch), fp64, %.1f s" % (k - 1, L, k * L, sec),
+        "parity_max_rel_err_vs_gpu": err,
+    }
+
+
+def bench_decode(torch, ssm, steps=200, warmup=10, nsets=16):
+    cfg = si.DECODE
+    st = si.decode_static(cfg, seed=0)
+    sets = [{k: to_dev(v, torch) for k, v in si.decode_step(cfg, i, seed=0, bias=st["bias"]).items()}
+            for i in range(nsets)]
+    A, D, h = to_dev(st["A"], torch), to_dev(st["D"], torch), to_dev(st["h"], torch)
+    y = torch.empty((cfg.batch, cfg.dim), dtype=torch.bfloat16, device="cuda")
+    for i in range(warmup):
+        s = sets[i % nsets]
+        ssm.ssm_state_update(s["x"], s["delta"], A, s["B"], s["C"], h, D=D, z=s["z"], y=y)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        s = sets[i % nsets]
+        ssm.ssm_state_update(s["x"], s["delta"], A, s["B"], s["C"], h, D=D, z=s["z"], y=y)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    nbytes = si.decode_bytes(cfg)
+    return {
+        "workload": "decode b%d d%d N%d, %d in-place steps cycling %d input sets" % (
+            cfg.batch, cfg.dim, cfg.dstate, steps, nsets),
+        "us_per_step": us,
+        "Gtokens*ch/s": cfg.batch * cfg.dim / (us * 1e-6) / 1e9,
+        "algorithmic_bytes_per_step": nbytes,
+        "GB/s": nbytes / (us * 1e-6) / 1e9,
+        "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "note": "the 84 MB state fits the 256 MB Infinity Cache; effective rate",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--tuning", type=str, default=None, help="state_groups,segments")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every channel is independent; see the sharding note in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_78_amd as ssm
+
+    cfg = si.CONFIGS[WORKLOAD]
+    print("bench: generating %s inputs" % WORKLOAD, file=sys.stderr, flush=True)
+    x = si.scan_inputs(cfg, seed=0)
+    dev = {k: to_dev(v, torch) for k, v in x.items() if v is not None}
+    y = torch.empty((cfg.batch, cfg.seqlen, cfg.dim), dtype=torch.bfloat16, device="cuda")
+    h_last = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device="cuda")
+    tuning = tuple(int(v) for v in args.tuning.split(",")) if args.tuning else None
+    plan = tuning or ssm.ssm_scan_plan(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate)
+    need = ssm.ssm_scan_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, tuning=tuning)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
+
+    def step():
+        ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                         y=y, h_last=h_last, workspace=ws, tuning=tuning)
+
+    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch events on the stream the kernels run on (torch's current stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record()
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    t_all1.record()
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    mean_launch_ms = float(np.mean(per))
+    ms_per_step = total_ms / args.steps
+    tok = cfg.tokens_ch
+    value = tok / (ms_per_step * 1e-3) / 1e9
+    nbytes = si.algorithmic_bytes(cfg)
+    ops = valu_ops_per_token_ch(cfg.dstate, cfg.gate) * tok
+    achieved_tops = ops / (mean_launch_ms * 1e-3) / 1e12
+    gbps = nbytes / (mean_launch_ms * 1e-3) / 1e9
+    print("bench: %.3f ms/step (median launch %.3f ms)" % (ms_per_step, per[len(per) // 2]),
+          file=sys.stderr, flush=True)
+
+    out = {
+        "metric": "selective-scan Gtokens*ch/s (+ achieved HBM GB/s, % of MI355X peak)",
+        "value": value,
+        "unit": "Gtokens*ch/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Mamba-1.4B-shaped layer scan: batch 8, L 8192, d_inner 4096, d_state 16, "
+                        "bf16 u/delta/B/C/z/y, fp32 A/D/state, D skip + SiLU gate + final state",
+            "global_batch": cfg.batch, "seq_len": cfg.seqlen, "dim": cfg.dim, "dstate": cfg.dstate,
+            "io_dtype": "bf16", "parallelism": "none (1 GPU)",
+            "launch": {"state_groups": plan[0], "segments": plan[1]},
+        },
+        "roofline": {
+            "bound": "alu",
+            "kernel": "scan_kernel (main pass)" if plan[1] == 1 else "scan passes (aggregate + carry + main)",
+            "achieved": achieved_tops,
+            "peak": VALU_PEAK_TOPS,
+            "unit": "Top/s",
+            "frac": achieved_tops / VALU_PEAK_TOPS,
+            "ops_per_token_ch": valu_ops_per_token_ch(cfg.dstate, cfg.gate),
+            "mean_launch_ms": mean_launch_ms,
+            "traffic": measured_traffic(tok),
+        },
+        "hbm": {
+            "algorithmic_bytes_per_launch": nbytes,
+            "achieved_GBps": gbps,
+            "peak_GBps": HBM_PEAK_GBPS,
+            "frac": gbps / HBM_PEAK_GBPS,
+        },
+    }
+    if not args.no_decode:
+        print("bench: decode", file=sys.stderr, flush=True)
+        out["decode"] = bench_decode(torch, ssm)
+    if not args.no_cpu:
+        print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(x, y, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * ssm_scan.h — C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * The library computes the Mamba selective scan (S6) forward pass and its
+ * one-token decode step with hand-written HIP kernels. Every pointer that
+ * names tensor data is a DEVICE pointer owned by the caller; the library
+ * allocates and frees nothing. Work is enqueued asynchronously on the given
+ * HIP stream: buffers must stay alive until the stream has finished with
+ * them. No function prints, throws or exits; each returns an ssm_status.
+ *
+ * Operation (for every batch row b, channel d and state n; each channel is
+ * an independent single-input single-output SSM, itwiki "상태 공간 모델",
+ * section "제어 이론의 상태 공간 표현과의 관계"):
+ *
+ *   Abar_t = exp(delta_t * A[d,n])                 discretised decay
+ *   Bu_t   = delta_t * B_t[n] * u_t                default: simplified rule
+ *          = (exp(delta_t A) - 1)/A * B_t[n] * u_t zero-order hold (SSM_DISC_ZOH)
+ *   h_t    = Abar_t * h_{t-1} + Bu_t               h_{-1} = h0 (or 0)
+ *   y_t    = sum_n C_t[n] h_t[n] + D[d] u_t        readout after the update
+ *   y_t   *= z_t * sigmoid(z_t)                    optional SiLU gate
+ *
+ * Passages: eommydocs "State Space Models (SSM)" §3.2 "Selective Scan
+ * Algorithm" (shapes of u, delta, A, B, C and the deltaA / deltaB_u
+ * discretisation); youngju.dev "Mamba와 State Space Model 논문 심층 분석",
+ * SelectiveSSM.selective_scan and MambaBlock.forward (recurrence, readout,
+ * y + D*x skip, y * silu(z) gate); itwiki "상태 공간 모델", "동작 원리 › 이산화"
+ * (zero-order hold); doyouknow.kr "Mamba와 상태 공간 모델(SSM)의 부상 완벽
+ * 가이드" §3-1 (h_t = exp(delta_t A) h_{t-1} + delta_t B_t x_t).
+ *
+ * Numerics: state and arithmetic in fp32; bf16 inputs are widened exactly;
+ * bf16 outputs are rounded to nearest-even. NaN and Inf propagate unchecked.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. Every error is detected on the host before any work is
+ * enqueued, except SSM_ERR_HIP, which reports a failed kernel launch. */
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL = -1,        /* a required pointer is NULL */
+    SSM_ERR_SHAPE = -2,       /* a negative size, or sizes whose byte count overflows */
+    SSM_ERR_DTYPE = -3,       /* unknown element type */
+    SSM_ERR_UNSUPPORTED = -4, /* dstate outside 1..64, unknown discretisation, bad tuning */
+    SSM_ERR_ALIAS = -5,       /* an output overlaps an input or another output */
+    SSM_ERR_WORKSPACE = -6,   /* workspace missing or smaller than ssm_scan_workspace_size() */
+    SSM_ERR_HIP = -7,         /* the HIP runtime refused a launch (e.g. not a gfx950 device) */
+    SSM_ERR_ALIGN = -8        /* a pointer is not aligned to its element size */
+} ssm_status;
+
+/* Element type of the per-token tensors u, delta, z, B, C and of the output y.
+ * A, D and all states are always fp32. */
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* Discretisation of B (A is always exp(delta*A)). */
+typedef enum { SSM_DISC_EULER = 0, SSM_DISC_ZOH = 1 } ssm_disc;
+
+/* Sizes and types of one scan. */
+typedef struct {
+    int64_t batch;   /* b  >= 0 */
+    int64_t seqlen;  /* L  >= 0 */
+    int64_t dim;     /* d  >= 0 (channels, d_inner) */
+    int64_t dstate;  /* N  in 1..64 */
+    int32_t dtype;   /* ssm_dtype */
+    int32_t disc;    /* ssm_disc */
+} ssm_scan_desc;
+
+/* Optional launch shape, for tuning and for tests of every kernel variant.
+ * Zero fields are chosen by the library. state_groups: waves that share one
+ * 64-channel tile, each owning dstate/state_groups states (1,2,4,8,16);
+ * segments: independent pieces of the sequence, joined by an affine carry
+ * (1..64). */
+typedef struct {
+    int32_t state_groups;
+    int32_t segments;
+} ssm_scan_tuning;
+
+/* Bytes of device workspace ssm_scan_fwd needs for `desc` (0 when it needs
+ * none). Returns 0 for an invalid descriptor. */
+size_t ssm_scan_workspace_size(const ssm_scan_desc *desc);
+
+/*
+ * Selective scan forward (the pages' selective_scan(u, delta, A, B, C) with
+ * the D skip and SiLU gate of the Mamba block fused in).
+ *
+ *   u, delta  (batch, seqlen, dim)   dtype, row-major, channel fastest
+ *   A         (dim, dstate)          fp32 (negative for a decaying state)
+ *   B, C      (batch, seqlen, dstate) dtype, shared by all channels of a row
+ *   D         (dim) fp32, or NULL for no skip term
+ *   z         (batch, seqlen, dim)   dtype, or NULL for no gate
+ *   h0        (batch, dim, dstate)   fp32 initial state, or NULL for zeros
+ *   y         (batch, seqlen, dim)   dtype, written
+ *   h_last    (batch, dim, dstate)   fp32 final state, written; may be NULL.
+ *             h_last may equal h0 exactly (resume in place).
+ *   workspace device scratch of at least ssm_scan_workspace_size(desc) bytes
+ *             (may be NULL when that size is 0); its contents on entry do
+ *             not matter and are clobbered.
+ * delta is used as given (the caller applies softplus). Outputs must not
+ * overlap any input, each other or the workspace. Pointers must be aligned to
+ * their element size. seqlen == 0 writes h_last = h0 (or zeros) and no y.
+ */
+int ssm_scan_fwd(const ssm_scan_desc *desc,
+                 const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, void *y, float *h_last,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ssm_scan_workspace_size / ssm_scan_fwd with an explicit launch shape
+ * (tuning == NULL is the same as the plain calls). */
+size_t ssm_scan_workspace_size_tuned(const ssm_scan_desc *desc, const ssm_scan_tuning *tuning);
+int ssm_scan_fwd_tuned(const ssm_scan_desc *desc,
+                       const void *u, const void *delta, const float *A,
+                       const void *B, const void *C, const float *D, const void *z,
+                       const float *h0, void *y, float *h_last,
+                       void *workspace, size_t workspace_bytes,
+                       const ssm_scan_tuning *tuning, hipStream_t stream);
+
+/* The launch shape ssm_scan_fwd would use for `desc` (written to *out). */
+int ssm_scan_plan(const ssm_scan_desc *desc, ssm_scan_tuning *out);
+
+/*
+ * One decode step: the recurrence for a single new token per sequence, with
+ * the fixed-size state updated in place (itwiki "상태 공간 모델", "순환 형태와
+ * 합성곱 형태": generation only updates h_t; ricepunchb "Mamba" §4.2: only the
+ * last hidden state is needed to produce the next token).
+ *
+ *   x, delta, z  (batch, dim)          dtype; z may be NULL (no gate)
+ *   A            (dim, dstate)         fp32
+ *   B, C         (batch, dstate)       dtype
+ *   D            (dim) fp32 or NULL
+ *   h            (batch, dim, dstate)  fp32, read and overwritten
+ *   y            (batch, dim)          dtype, written; must not overlap h or an input
+ * Equal to ssm_scan_fwd with seqlen 1, h0 = h and h_last = h.
+ */
+int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t dtype, int32_t disc,
+                     const void *x, const void *delta, const float *A,
+                     const void *B, const void *C, const float *D, const void *z,
+                     float *h, void *y, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *ssm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,218 @@
+"""Python binding of the MI355X selective-scan library (libssm_scan.so).
+
+Argument marshalling only: every step of the scan and of the decode step runs
+in the library's HIP kernels. PyTorch supplies device memory and the current
+HIP stream; the library itself is a plain C ABI (include/ssm_scan.h) that
+links no torch. There is no fallback: if the library is missing, every call
+raises.
+
+Names follow the C ABI: ``ssm_scan_fwd``, ``ssm_scan_workspace_size``,
+``ssm_scan_plan``, ``ssm_state_update``, ``ssm_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libssm_scan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_DISC_EULER, SSM_DISC_ZOH = 0, 1
+_DISC = {"euler": SSM_DISC_EULER, "zoh": SSM_DISC_ZOH}
+
+# Every symbol include/ssm_scan.h declares.
+EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_workspace_size_tuned",
+           "ssm_scan_fwd_tuned", "ssm_scan_plan", "ssm_state_update", "ssm_status_string")
+
+
+class ScanDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32), ("disc", ctypes.c_int32)]
+
+
+class ScanTuning(ctypes.Structure):
+    _fields_ = [("state_groups", ctypes.c_int32), ("segments", ctypes.c_int32)]
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, ssm_status_string(status), status))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY):
+                raise ImportError("libssm_scan.so is not built (run __graft_entry__.build() or "
+                                  "python selective_state_space_78_amd/build.py); there is no fallback")
+            L = ctypes.CDLL(LIBRARY)
+            vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+            pdesc, ptun = ctypes.POINTER(ScanDesc), ctypes.POINTER(ScanTuning)
+            L.ssm_scan_workspace_size.argtypes = [pdesc]
+            L.ssm_scan_workspace_size.restype = sz
+            L.ssm_scan_workspace_size_tuned.argtypes = [pdesc, ptun]
+            L.ssm_scan_workspace_size_tuned.restype = sz
+            L.ssm_scan_plan.argtypes = [pdesc, ptun]
+            L.ssm_scan_plan.restype = ctypes.c_int
+            scan_args = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz]
+            L.ssm_scan_fwd.argtypes = scan_args + [vp]
+            L.ssm_scan_fwd.restype = ctypes.c_int
+            L.ssm_scan_fwd_tuned.argtypes = scan_args + [ptun, vp]
+            L.ssm_scan_fwd_tuned.restype = ctypes.c_int
+            L.ssm_state_update.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            L.ssm_state_update.restype = ctypes.c_int
+            L.ssm_status_string.argtypes = [ctypes.c_int]
+            L.ssm_status_string.restype = ctypes.c_char_p
+            _lib = L
+        return _lib
+
+
+def ssm_status_string(status: int) -> str:
+    return lib().ssm_status_string(int(status)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    if t.dtype == torch.float32:
+        return SSM_F32
+    raise TypeError("per-token tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape=None, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _tuning(tuning):
+    if tuning is None:
+        return None
+    g, s = tuning
+    return ctypes.byref(ScanTuning(int(g), int(s)))
+
+
+def make_desc(batch, seqlen, dim, dstate, dtype, disc="euler") -> ScanDesc:
+    return ScanDesc(int(batch), int(seqlen), int(dim), int(dstate), int(dtype), _DISC[disc])
+
+
+def ssm_scan_workspace_size(batch, seqlen, dim, dstate, dtype=SSM_BF16, disc="euler", tuning=None) -> int:
+    desc = make_desc(batch, seqlen, dim, dstate, dtype, disc)
+    if tuning is None:
+        return int(lib().ssm_scan_workspace_size(ctypes.byref(desc)))
+    return int(lib().ssm_scan_workspace_size_tuned(ctypes.byref(desc), _tuning(tuning)))
+
+
+def ssm_scan_plan(batch, seqlen, dim, dstate, dtype=SSM_BF16, disc="euler"):
+    """(state_groups, segments) the library picks for this shape."""
+    desc = make_desc(batch, seqlen, dim, dstate, dtype, disc)
+    out = ScanTuning()
+    rc = lib().ssm_scan_plan(ctypes.byref(desc), ctypes.byref(out))
+    if rc != 0:
+        raise SsmError(rc, "ssm_scan_plan")
+    return out.state_groups, out.segments
+
+
+def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None,
+                 disc="euler", workspace=None, tuning=None, stream=None, want_h_last=True):
+    """Selective scan forward on device tensors.
+
+    u, delta, z: (batch, L, dim); B, C: (batch, L, N) of the same dtype
+    (bfloat16 or float32); A: (dim, N) float32; D: (dim,) float32; h0:
+    (batch, dim, N) float32. Outputs y (batch, L, dim) and h_last
+    (batch, dim, N) are allocated when not given. Returns (y, h_last).
+    ``tuning`` is an optional (state_groups, segments) pair.
+    """
+    import torch
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    dev = u.device
+    dt = u.dtype
+    code = _dtype_code(u)
+    _check(u, "u", device=dev)
+    _check(delta, "delta", (batch, L, dim), dt, dev)
+    _check(z, "z", (batch, L, dim), dt, dev)
+    _check(B, "B", (batch, L, N), dt, dev)
+    _check(C, "C", (batch, L, N), dt, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(h0, "h0", (batch, dim, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((batch, L, dim), dtype=dt, device=dev)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _check(y, "y", (batch, L, dim), dt, dev)
+    _check(h_last, "h_last", (batch, dim, N), torch.float32, dev)
+    desc = make_desc(batch, L, dim, N, code, disc)
+    L_ = lib()
+    need = (L_.ssm_scan_workspace_size(ctypes.byref(desc)) if tuning is None
+            else L_.ssm_scan_workspace_size_tuned(ctypes.byref(desc), _tuning(tuning)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(h0), _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes]
+    if tuning is None:
+        rc = L_.ssm_scan_fwd(*args, _stream(stream, dev))
+    else:
+        rc = L_.ssm_scan_fwd_tuned(*args, _tuning(tuning), _stream(stream, dev))
+    if rc != 0:
+        raise SsmError(rc, "ssm_scan_fwd")
+    return y, h_last
+
+
+def ssm_state_update(x, delta, A, B, C, h, D=None, z=None, y=None, disc="euler", stream=None):
+    """One decode step on device tensors; h (batch, dim, N) float32 is updated in place.
+
+    x, delta, z: (batch, dim); B, C: (batch, N). Returns y (batch, dim).
+    """
+    import torch
+    batch, dim = x.shape
+    N = A.shape[1]
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    _check(x, "x", device=dev)
+    _check(delta, "delta", (batch, dim), dt, dev)
+    _check(z, "z", (batch, dim), dt, dev)
+    _check(B, "B", (batch, N), dt, dev)
+    _check(C, "C", (batch, N), dt, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(h, "h", (batch, dim, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((batch, dim), dtype=dt, device=dev)
+    _check(y, "y", (batch, dim), dt, dev)
+    rc = lib().ssm_state_update(batch, dim, N, code, _DISC[disc], _ptr(x), _ptr(delta), _ptr(A),
+                                _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h), _ptr(y), _stream(stream, dev))
+    if rc != 0:
+        raise SsmError(rc, "ssm_state_update")
+    return y

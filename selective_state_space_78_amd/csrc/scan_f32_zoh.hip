@@ -1,0 +1,11 @@
+// Scan kernels for f32 tensors with the zero-order-hold input term.
+#define SSM_SCAN_INSTANTIATE
+#include "scan_kernels.hpp"
+
+namespace ssm_detail {
+
+hipError_t launch_scan_f32_zoh(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st) {
+    return launch_scan_shape<float, true>(pl, p, nm, na, st);
+}
+
+}  // namespace ssm_detail

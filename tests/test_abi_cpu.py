@@ -1,0 +1,163 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+rejects bad arguments with the documented status before touching a device.
+
+No compute call is made here: every call below fails validation on the host,
+so the fake device addresses it passes are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_78_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIAS, EWS, EHIP, EALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ssm.LIBRARY):
+        pytest.skip("library not built")
+    return ssm.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(ssm.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_library_links_no_torch():
+    if not os.path.exists(ssm.LIBRARY):
+        pytest.skip("library not built")
+    data = open(ssm.LIBRARY, "rb").read()
+    assert b"libtorch" not in data and b"libc10" not in data
+
+
+def test_status_strings(L):
+    for code in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIAS, EWS, EHIP, EALIGN):
+        s = ssm.ssm_status_string(code)
+        assert s and s != "unknown status"
+    assert ssm.ssm_status_string(12345) == "unknown status"
+
+
+def desc(b=2, L=100, d=64, N=16, dtype=ssm.SSM_BF16, disc=0):
+    return ssm.ScanDesc(b, L, d, N, dtype, disc)
+
+
+def fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+GB = 1 << 30
+
+
+def scan_call(L, dsc, u=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB,
+              h0=0, y=8 * GB, h_last=9 * GB, ws=0, ws_bytes=0, tuning=None):
+    args = [ctypes.byref(dsc) if dsc is not None else None]
+    args += [fake(a) if a else None for a in (u, delta, A, B, C, D, z, h0, y, h_last, ws)]
+    args += [ws_bytes]
+    if tuning is None:
+        return L.ssm_scan_fwd(*args, None)
+    return L.ssm_scan_fwd_tuned(*args, ctypes.byref(ssm.ScanTuning(*tuning)), None)
+
+
+def test_scan_descriptor_errors(L):
+    assert scan_call(L, None) == ENULL
+    assert scan_call(L, desc(b=-1)) == ESHAPE
+    assert scan_call(L, desc(L=-5)) == ESHAPE
+    assert scan_call(L, desc(dtype=7)) == EDTYPE
+    assert scan_call(L, desc(disc=3)) == EUNSUP
+    assert scan_call(L, desc(N=0)) == EUNSUP
+    assert scan_call(L, desc(N=65)) == EUNSUP
+    assert scan_call(L, desc(b=1 << 40, L=1 << 40)) == ESHAPE
+
+
+def test_scan_empty_problem_is_ok(L):
+    # nothing to compute: returns before any device work
+    assert scan_call(L, desc(b=0)) == OK
+    assert scan_call(L, desc(d=0)) == OK
+
+
+def test_scan_null_pointers(L):
+    assert scan_call(L, desc(), A=0) == ENULL
+    assert scan_call(L, desc(), u=0) == ENULL
+    assert scan_call(L, desc(), delta=0) == ENULL
+    assert scan_call(L, desc(), B=0) == ENULL
+    assert scan_call(L, desc(), C=0) == ENULL
+    assert scan_call(L, desc(), y=0) == ENULL
+
+
+def test_scan_alignment(L):
+    assert scan_call(L, desc(), u=GB + 1) == EALIGN
+    assert scan_call(L, desc(dtype=ssm.SSM_F32), delta=2 * GB + 2) == EALIGN
+    assert scan_call(L, desc(), h_last=9 * GB + 2) == EALIGN
+    assert scan_call(L, desc(), A=3 * GB + 2) == EALIGN
+
+
+def test_scan_aliasing(L):
+    # y overlapping u, h_last overlapping z, h_last == y, workspace over B
+    assert scan_call(L, desc(), y=1 * GB + 64) == EALIAS
+    assert scan_call(L, desc(), h_last=7 * GB + 128) == EALIAS
+    assert scan_call(L, desc(), h_last=8 * GB) == EALIAS
+    assert scan_call(L, desc(), h0=10 * GB, h_last=10 * GB + 4) == EALIAS
+    assert scan_call(L, desc(L=4096, d=64, b=1), ws=4 * GB, ws_bytes=1 << 24, tuning=(4, 4)) == EALIAS
+
+
+def test_scan_workspace(L):
+    d = desc(b=1, L=4096, d=64, N=16)
+    need = L.ssm_scan_workspace_size_tuned(ctypes.byref(d), ctypes.byref(ssm.ScanTuning(4, 4)))
+    assert need == 3 * ((1 * 4 * 64 * 16 * 4 + 255) // 256 * 256)
+    assert scan_call(L, d, tuning=(4, 4)) == EWS
+    assert scan_call(L, d, ws=11 * GB, ws_bytes=need - 4, tuning=(4, 4)) == EWS
+    assert L.ssm_scan_workspace_size_tuned(ctypes.byref(d), ctypes.byref(ssm.ScanTuning(4, 1))) == 0
+    assert L.ssm_scan_workspace_size(None) == 0
+
+
+def test_scan_bad_tuning(L):
+    assert scan_call(L, desc(N=16), tuning=(3, 1)) == EUNSUP      # not a power of two
+    assert scan_call(L, desc(N=16), tuning=(32, 1)) == EUNSUP     # more groups than states
+    assert scan_call(L, desc(N=64), tuning=(2, 1)) == EUNSUP      # 32 states per wave
+    assert scan_call(L, desc(N=16), tuning=(4, 65)) == EUNSUP     # too many segments
+    assert scan_call(L, desc(N=16), tuning=(-1, 1)) == EUNSUP
+
+
+def test_plan_shapes(L):
+    # the flagship shapes get enough waves for 256 CUs x 4 SIMDs
+    assert ssm.ssm_scan_plan(8, 8192, 4096, 16) == (4, 1)
+    g, s = ssm.ssm_scan_plan(1, 131072, 5120, 16)
+    assert g * s * 80 >= 2048
+    assert ssm.ssm_scan_plan(1, 64, 16, 4)[1] == 1
+    g, s = ssm.ssm_scan_plan(4, 100, 64, 64)
+    assert 64 // g <= 16
+
+
+def decode_call(L, b=4, d=64, N=16, dtype=ssm.SSM_BF16, disc=0, x=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB,
+                C=5 * GB, D=6 * GB, z=7 * GB, h=8 * GB, y=9 * GB):
+    ptrs = [fake(a) if a else None for a in (x, delta, A, B, C, D, z, h, y)]
+    return L.ssm_state_update(b, d, N, dtype, disc, *ptrs, None)
+
+
+def test_decode_errors(L):
+    assert decode_call(L, b=-1) == ESHAPE
+    assert decode_call(L, dtype=9) == EDTYPE
+    assert decode_call(L, disc=2) == EUNSUP
+    assert decode_call(L, N=0) == EUNSUP
+    assert decode_call(L, N=80) == EUNSUP
+    assert decode_call(L, b=0) == OK
+    assert decode_call(L, h=0) == ENULL
+    assert decode_call(L, y=0) == ENULL
+    assert decode_call(L, x=GB + 1) == EALIGN
+    assert decode_call(L, y=8 * GB + 64) == EALIAS          # y inside h
+    assert decode_call(L, h=1 * GB) == EALIAS               # h over x
