@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--tuning", type=str, default=None, help="state_groups,segments")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (to scale profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -244,6 +246,13 @@ def main():
             "frac": gbps / HBM_PEAK_GBPS,
         },
     }
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = 1 << 30
     if not args.no_decode:
         print("bench: decode", file=sys.stderr, flush=True)
         out["decode"] = bench_decode(torch, ssm)

@@ -83,8 +83,10 @@ typedef struct {
     int32_t segments;
 } ssm_scan_tuning;
 
-/* Bytes of device workspace ssm_scan_fwd needs for `desc` (0 when it needs
- * none). Returns 0 for an invalid descriptor. */
+/* Bytes of device workspace ssm_scan_fwd needs for `desc`: B and C widened
+ * to fp32 (about 2 * batch * seqlen * dstate * 4 bytes) plus, when the
+ * sequence is split into segments, three (batch, segments, dim, dstate) fp32
+ * arrays. 0 when there is nothing to compute; 0 for an invalid descriptor. */
 size_t ssm_scan_workspace_size(const ssm_scan_desc *desc);
 
 /*
@@ -100,9 +102,9 @@ size_t ssm_scan_workspace_size(const ssm_scan_desc *desc);
  *   y         (batch, seqlen, dim)   dtype, written
  *   h_last    (batch, dim, dstate)   fp32 final state, written; may be NULL.
  *             h_last may equal h0 exactly (resume in place).
- *   workspace device scratch of at least ssm_scan_workspace_size(desc) bytes
- *             (may be NULL when that size is 0); its contents on entry do
- *             not matter and are clobbered.
+ *   workspace device scratch of at least ssm_scan_workspace_size(desc) bytes,
+ *             256-byte aligned (may be NULL when that size is 0); its
+ *             contents on entry do not matter and are clobbered.
  * delta is used as given (the caller applies softplus). Outputs must not
  * overlap any input, each other or the workspace. Pointers must be aligned to
  * their element size. seqlen == 0 writes h_last = h0 (or zeros) and no y.

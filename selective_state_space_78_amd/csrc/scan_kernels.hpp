@@ -6,19 +6,28 @@
 //  * One workgroup owns a tile of 64 consecutive channels of one batch row and
 //    one time segment. Lane = channel. The workgroup has G waves; wave w owns
 //    NPW = Npad/G of the states of all 64 channels, so a lane keeps its NPW
-//    states h[n] in VGPRs for the whole segment and B_t[n], C_t[n] are the same
-//    for the whole wave (read from LDS as broadcasts). Splitting states over
+//    states h[n] in VGPRs for the whole segment, and B_t[n], C_t[n] are the
+//    same for every lane of the wave: they are read with scalar loads into
+//    SGPRs and used directly as instruction operands. Splitting states over
 //    waves multiplies the parallelism of a channel tile by G at the cost of a
 //    few per-token instructions, instead of splitting time, which would cost
 //    a second pass of the recurrence.
-//  * Time is walked in chunks of TC tokens. The workgroup loads a chunk of u,
-//    delta, z (TC rows x 64 channels, 16-byte coalesced loads), and of B and C,
-//    into registers one chunk ahead, converts it to fp32 into LDS, and every
-//    wave walks the chunk sequentially from LDS. The expanded (t, d, n) decay
-//    and input terms exist only in registers and are never written.
+//  * A prologue widens B and C once to fp32, regrouped so that one wave's
+//    values are contiguous in time (and padded with zero rows and states), so
+//    that a few wide scalar loads fetch a batch of steps and are waited for
+//    once: scalar and LDS reads share one wait counter, and a scalar load per
+//    step would expose its latency at every LDS wait.
+//  * Time is walked in chunks of TC tokens. Each thread of the workgroup owns
+//    a piece of 4 channels of some rows of the chunk: it loads the piece's u,
+//    delta and z one chunk ahead into registers, stages (delta, delta*u)
+//    pairs into LDS (double-buffered) for all waves, and keeps D*u and
+//    silu(z) in registers for the outputs it will store. Every per-token
+//    product shared by the states is so formed once. The expanded (t, d, n)
+//    decay and input terms exist only in registers and are never written.
 //  * Each wave writes its partial readout sum_{n in wave} C_t[n] h_t[n] per
-//    (t, channel) to LDS; after a barrier the whole workgroup adds the G
-//    partials, the D skip and the SiLU gate, rounds, and stores y coalesced.
+//    (t, channel) to LDS; after a barrier every thread adds the G partials of
+//    its pieces and the skip, applies the gate, rounds to the output type and
+//    stores 4 channels at once.
 //  * Long sequences with few channels are split into S segments. An
 //    aggregate pass computes, per segment, the affine map h -> P*h + H that
 //    the segment applies to its incoming state (P = exp(A * sum delta),
@@ -30,7 +39,6 @@
 //    Scan).
 //  * Workgroup ids are remapped so that the tiles of one batch row (which
 //    share the B and C rows) run on the same XCD and hit the same L2.
-//
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,11 +50,11 @@
 
 namespace ssm_detail {
 
-
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTile = 64;        // channels per workgroup tile = lanes per wave
 constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies
 constexpr int kMaxSegments = 64;
+constexpr int kPadRows = 16;     // spare zero rows after the widened B and C (>= every TC)
 
 // ---------------------------------------------------------------------------
 // Element access. bf16 travels as its 16-bit pattern.
@@ -61,7 +69,7 @@ template <> struct Elem<float> {
 template <> struct Elem<uint16_t> {
     static constexpr int kBytes = 2;
     __device__ static float widen(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
-    // round to bf16 (nearest even, v_cvt_pk_bf16_f32) and keep it as a float
+    // round to bf16 (nearest even, v_cvt_pk_bf16_f32)
     __device__ static uint16_t to_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 };
 
@@ -73,24 +81,49 @@ __device__ __forceinline__ float silu(float z) {
 struct ScanParams {
     const void *u, *delta, *z, *B, *C;
     const float *A, *D, *h0;
+    float *Bf, *Cf;       // (batch, G, padded_len(L), Npad/G) fp32 widened B and C (workspace)
     const float *seg_h;   // (batch, nseg, dim, N) initial state of each segment, or null
     void *y;
     float *h_last;
     float *agg_P, *agg_H; // (batch, nseg, dim, N) segment maps (aggregate pass)
     int64_t L;
     int batch, dim, N;
-    int seg_len, nseg, nseg_launched;
+    int seg_len, nseg;
     int ntiles;
-    int vec;              // 16-byte loads of u/delta/z are aligned
-    int pair_store;       // y can be stored as aligned channel pairs
+    int vec;              // u, delta, z, y move 4 channels per aligned access
 };
 
 struct Plan {
     int npad, G, npw, S, seg_len;
 };
 
-// Launches the aggregate, carry and main passes for one element type and
-// discretisation (defined in the scan_<type>_<disc>.hip units).
+// Workspace layout for a plan: widened B and C, then (segments > 1) the
+// segment maps and segment initial states. Offsets in bytes, 256-aligned.
+struct WorkspaceLayout {
+    size_t bf, cf, agg_p, agg_h, seg_h, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Tokens per batch row in the widened B and C: L rounded up to 16, plus
+// kPadRows spare zero rows (keeps every chunk's run 64-byte aligned).
+__host__ __device__ inline int64_t padded_len(int64_t L) { return (L + 15) / 16 * 16 + kPadRows; }
+
+inline WorkspaceLayout workspace_layout(int64_t batch, int64_t L, int64_t dim, int64_t N, const Plan &pl) {
+    WorkspaceLayout w{};
+    const size_t bc = align256((size_t)batch * padded_len(L) * pl.npad * sizeof(float));
+    const size_t seg = pl.S > 1 ? align256((size_t)batch * pl.S * dim * N * sizeof(float)) : 0;
+    w.bf = 0;
+    w.cf = bc;
+    w.agg_p = 2 * bc;
+    w.agg_h = w.agg_p + seg;
+    w.seg_h = w.agg_h + seg;
+    w.total = w.seg_h + seg;
+    return w;
+}
+
+// Launches the prologue, aggregate, carry and main passes for one element
+// type and discretisation (defined in the scan_<type>_<disc>.hip units).
 hipError_t launch_scan_bf16_euler(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st);
 hipError_t launch_scan_bf16_zoh(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st);
 hipError_t launch_scan_f32_euler(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st);
@@ -104,10 +137,38 @@ inline int ilog2(int v) { int r = 0; while ((1 << r) < v) ++r; return r; }
 namespace ssm_detail {
 namespace {
 
+typedef const __attribute__((address_space(4))) float cfloat;   // scalar-load view
+
 // ---------------------------------------------------------------------------
-// Scan kernels
+// Prologue: B and C widened to fp32 and regrouped so that the values one wave
+// needs are contiguous in time: (batch, group, t, state-in-group) with Npad
+// states split into G groups of NPW, and kPadRows zero rows after each batch
+// row's L tokens (and zeros for padded states).
 
-
+template <typename T>
+__global__ __launch_bounds__(256) void widen_bc_kernel(const T *__restrict__ B, const T *__restrict__ C,
+                                                       float *__restrict__ Bf, float *__restrict__ Cf,
+                                                       int batch, int64_t L, int N, int groups, int npw) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t Lp = padded_len(L);
+    const int64_t total = (int64_t)batch * groups * Lp * npw;
+    if (i >= total) return;
+    const int q = (int)(i % npw);
+    int64_t r = i / npw;
+    const int64_t t = r % Lp;
+    r /= Lp;
+    const int g = (int)(r % groups);
+    const int64_t b = r / groups;
+    const int n = g * npw + q;
+    float vb = 0.0f, vc = 0.0f;
+    if (t < L && n < N) {
+        const int64_t src = (b * L + t) * N + n;
+        vb = Elem<T>::widen(B[src]);
+        vc = Elem<T>::widen(C[src]);
+    }
+    Bf[i] = vb;
+    Cf[i] = vc;
+}
 
 // Linear workgroup id -> (segment, batch row, channel tile). Consecutive ids
 // go round-robin over the XCDs; undo that so that each XCD receives a
@@ -124,151 +185,270 @@ __device__ __forceinline__ void map_block(const ScanParams &p, int &seg, int &b,
     seg = rest / p.batch;
 }
 
+template <typename T> struct RawOf;                      // four elements of a per-token tensor
+template <> struct RawOf<uint16_t> { typedef uint2 type; };
+template <> struct RawOf<float> { typedef uint4 type; };
+
+#ifndef SSM_BC_LDS
+#define SSM_BC_LDS 0
+#endif
+
 template <typename T, int NPW, int G, int TC, bool ZOH, bool AGG>
 struct ScanKernel {
+    // Where the inner loop reads B_t and C_t: scalar loads (0) or LDS broadcasts (1).
+    static constexpr bool kBcLds = SSM_BC_LDS;
     static constexpr int kThreads = kTile * G;
     static constexpr int kNP = NPW * G;                       // padded state count
-    static constexpr int kV = 16 / Elem<T>::kBytes;            // elements per 16-byte piece
-    static constexpr int kPieces = TC * kTile / kV;            // pieces per chunk per tensor
+    static constexpr int kV = 4;                               // channels per staged piece
+    static constexpr int kRowPieces = kTile / kV;              // pieces per 64-channel row
+    static constexpr int kPieces = TC * kRowPieces;            // pieces per chunk per tensor
     static constexpr int kPPT = (kPieces + kThreads - 1) / kThreads;
-    static constexpr int kBCE = TC * kNP;                      // B (or C) elements per chunk
-    static constexpr int kBPT = (kBCE + kThreads - 1) / kThreads;
+    static constexpr int kRowStep = kThreads / kRowPieces;      // rows between a thread's pieces
+    static constexpr int kYS = kTile + 4;                      // padded row of a partial-readout plane
+    static_assert(kThreads % kRowPieces == 0, "a thread keeps the same channels in every piece");
+    static_assert(TC <= kPadRows, "spare rows of the widened B and C");
+    typedef typename RawOf<T>::type Raw;
 
-    struct Smem {
-        float u[TC][kTile];
-        float dt[TC][kTile];
-        float z[AGG ? 1 : TC][kTile];
-        float B[TC][kNP];
-        float C[AGG ? 1 : TC][kNP];
-        float y[AGG ? 1 : G][AGG ? 1 : TC][kTile];
+    // LDS: the staged chunk as (delta, delta*u) pairs (u instead of delta*u
+    // for the hold rule), double-buffered, and the waves' partial readouts.
+    struct __align__(16) Smem {
+        float2 dx[2][TC][kTile];
+        float y[AGG ? 1 : G][AGG ? 1 : TC][AGG ? 1 : kYS];
+        float bc[kBcLds ? 2 : 1][2][G][TC][NPW];     // staged B, C of the chunk (kBcLds)
     };
-    static_assert(sizeof(Smem) <= 65536, "LDS per workgroup");
+    static constexpr int kBcFloats = 2 * G * TC * NPW;        // B and C floats per chunk
+    static constexpr int kBcPPT = (kBcFloats / 4 + kThreads - 1) / kThreads;
+    static_assert(sizeof(Smem) <= (kBcLds ? 163840 : 65536), "LDS per workgroup");
 
     struct Prefetch {
-        uint4 u[kPPT], dt[kPPT], z[kPPT];
-        T B[kBPT], C[kBPT];
+        Raw u[kPPT], dt[kPPT], z[kPPT];
+        float4 bc[kBcLds ? kBcPPT : 1];
     };
 
-    // Issue the global loads of one chunk [t0, t0 + tval) into registers.
-    __device__ static void load(const ScanParams &p, Prefetch &pf, int b, int d0, int64_t t0, int tval) {
-        const T *u = static_cast<const T *>(p.u);
-        const T *dt = static_cast<const T *>(p.delta);
-        const T *z = static_cast<const T *>(p.z);
-        const bool gate = !AGG && z != nullptr;
+    // B and C of one chunk from the widened workspace: per tensor, G runs of
+    // TC*NPW floats (one per state group), 16 bytes per thread.
+    __device__ static void load_bc(const ScanParams &p, Prefetch &pf, int b, int64_t t0) {
+        if constexpr (kBcLds) {
+#pragma unroll
+            for (int j = 0; j < kBcPPT; ++j) {
+                const int i4 = threadIdx.x + j * kThreads;       // float4 index within the chunk
+                if (i4 * 4 >= kBcFloats) continue;
+                const int f = i4 * 4;
+                const int tensor = f / (G * TC * NPW);
+                const int g = (f / (TC * NPW)) % G;
+                const int r = f % (TC * NPW);
+                const float *src = (tensor ? p.Cf : p.Bf) + (((int64_t)b * G + g) * padded_len(p.L) + t0) * NPW + r;
+                pf.bc[j] = *reinterpret_cast<const float4 *>(src);
+            }
+        }
+    }
+
+    __device__ static void commit_bc(const Prefetch &pf, float (*bc)[G][TC][NPW]) {
+        if constexpr (kBcLds) {
+            float *base = &bc[0][0][0][0];
+#pragma unroll
+            for (int j = 0; j < kBcPPT; ++j) {
+                const int i4 = threadIdx.x + j * kThreads;
+                if (i4 * 4 >= kBcFloats) continue;
+                reinterpret_cast<float4 *>(base)[i4] = pf.bc[j];
+            }
+        }
+    }
+    // D*u and silu(z) of the thread's staged pieces, kept in registers until
+    // the same thread finalizes those outputs
+    struct Held {
+        float sk[kPPT][kV], g[kPPT][kV];
+    };
+
+    __device__ static int piece_row(int j) { return threadIdx.x / kRowPieces + j * kRowStep; }
+
+    // Element-wise load of one piece (unaligned tensors), zero past dim.
+    __device__ static Raw gather(const T *src, int c0, int dim, bool on) {
+        if constexpr (sizeof(T) == 2) {
+            uint32_t w[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t lo = (on && c0 + 2 * i < dim) ? src[2 * i] : 0u;
+                const uint32_t hi = (on && c0 + 2 * i + 1 < dim) ? src[2 * i + 1] : 0u;
+                w[i] = lo | (hi << 16);
+            }
+            return make_uint2(w[0], w[1]);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = (on && c0 + i < dim) ? __float_as_uint(src[i]) : 0u;
+            return make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+
+    __device__ static void unpack(const Raw &r, float (&v)[kV]) {
+        if constexpr (sizeof(T) == 2) {
+            v[0] = __uint_as_float(r.x << 16);
+            v[1] = __uint_as_float(r.x & 0xffff0000u);
+            v[2] = __uint_as_float(r.y << 16);
+            v[3] = __uint_as_float(r.y & 0xffff0000u);
+        } else {
+            v[0] = __uint_as_float(r.x);
+            v[1] = __uint_as_float(r.y);
+            v[2] = __uint_as_float(r.z);
+            v[3] = __uint_as_float(r.w);
+        }
+    }
+
+    // Issue the global loads of one chunk: `base` is the element offset of
+    // (the chunk's first token row, the tile's first channel); rows [0, tval).
+    __device__ static void load(const ScanParams &p, Prefetch &pf, int64_t base, int tval, int col, int d0,
+                                bool colv) {
+        const T *u = static_cast<const T *>(p.u) + base;
+        const T *dt = static_cast<const T *>(p.delta) + base;
+        const T *z = static_cast<const T *>(p.z) + base;
+        const bool gate = !AGG && p.z != nullptr;
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
-            const int piece = threadIdx.x + j * kThreads;
-            const int t = piece / (kTile / kV);
-            const int c = (piece % (kTile / kV)) * kV;
-            uint4 ru = {0, 0, 0, 0}, rd = {0, 0, 0, 0}, rz = {0, 0, 0, 0};
-            if (piece < kPieces && t < tval && d0 + c < p.dim) {
-                const int64_t off = ((int64_t)b * p.L + t0 + t) * p.dim + d0 + c;
-                if (p.vec) {
-                    ru = *reinterpret_cast<const uint4 *>(u + off);
-                    rd = *reinterpret_cast<const uint4 *>(dt + off);
-                    if (gate) rz = *reinterpret_cast<const uint4 *>(z + off);
-                } else {
-                    T eu[kV], ed[kV], ez[kV];
+            const int row = piece_row(j);
+            if ((kPieces % kThreads != 0 && row >= TC) || row >= tval || !colv) continue;
+            const uint32_t off = (uint32_t)row * (uint32_t)p.dim + (uint32_t)col;
+            if (p.vec) {
+                pf.u[j] = *reinterpret_cast<const Raw *>(u + off);
+                pf.dt[j] = *reinterpret_cast<const Raw *>(dt + off);
+                if (gate) pf.z[j] = *reinterpret_cast<const Raw *>(z + off);
+            } else {
+                pf.u[j] = gather(u + off, d0 + col, p.dim, true);
+                pf.dt[j] = gather(dt + off, d0 + col, p.dim, true);
+                pf.z[j] = gather(z + off, d0 + col, p.dim, gate);
+            }
+        }
+    }
+
+    // Stage the prefetched chunk into LDS buffer `dx`, forming the per-token
+    // products once for all states, and keep D*u and silu(z) in `held`. Rows
+    // past tval (and channels past dim) are staged as delta = 0, x = 0: a step
+    // that leaves the state unchanged.
+    __device__ static void commit(const Prefetch &pf, float2 (*dx)[kTile], Held &held, int tval, int col,
+                                  bool colv, const float (&Dk)[kV], bool gate) {
 #pragma unroll
-                    for (int e = 0; e < kV; ++e) {
-                        const bool ok = d0 + c + e < p.dim;
-                        eu[e] = ok ? u[off + e] : T(0);
-                        ed[e] = ok ? dt[off + e] : T(0);
-                        ez[e] = (ok && gate) ? z[off + e] : T(0);
+        for (int j = 0; j < kPPT; ++j) {
+            const int row = piece_row(j);
+            if (kPieces % kThreads != 0 && row >= TC) continue;
+            float4 *dst = reinterpret_cast<float4 *>(&dx[row][col]);
+            if (row < tval && colv) {
+                float u[kV], d[kV];
+                unpack(pf.u[j], u);
+                unpack(pf.dt[j], d);
+                float xo[kV];
+#pragma unroll
+                for (int e = 0; e < kV; ++e) xo[e] = ZOH ? u[e] : d[e] * u[e];
+                dst[0] = make_float4(d[0], xo[0], d[1], xo[1]);
+                dst[1] = make_float4(d[2], xo[2], d[3], xo[3]);
+                if constexpr (!AGG) {
+#pragma unroll
+                    for (int e = 0; e < kV; ++e) held.sk[j][e] = Dk[e] * u[e];
+                    if (gate) {
+                        float z[kV];
+                        unpack(pf.z[j], z);
+#pragma unroll
+                        for (int e = 0; e < kV; ++e) held.g[j][e] = silu(z[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < kV; ++e) held.g[j][e] = 1.0f;
                     }
-                    memcpy(&ru, eu, 16);
-                    memcpy(&rd, ed, 16);
-                    memcpy(&rz, ez, 16);
-                }
-            }
-            pf.u[j] = ru;
-            pf.dt[j] = rd;
-            pf.z[j] = rz;
-        }
-        const T *Bp = static_cast<const T *>(p.B);
-        const T *Cp = static_cast<const T *>(p.C);
-#pragma unroll
-        for (int j = 0; j < kBPT; ++j) {
-            const int e = threadIdx.x + j * kThreads;
-            const int t = e / kNP, n = e % kNP;
-            T vb = T(0), vc = T(0);
-            if (e < kBCE && t < tval && n < p.N) {
-                const int64_t off = ((int64_t)b * p.L + t0 + t) * p.N + n;
-                vb = Bp[off];
-                if (!AGG) vc = Cp[off];
-            }
-            pf.B[j] = vb;
-            pf.C[j] = vc;
-        }
-    }
-
-    // Widen the prefetched chunk to fp32 into LDS.
-    __device__ static void commit(const Prefetch &pf, Smem &s) {
-#pragma unroll
-        for (int j = 0; j < kPPT; ++j) {
-            const int piece = threadIdx.x + j * kThreads;
-            if (piece >= kPieces) continue;
-            const int t = piece / (kTile / kV);
-            const int c = (piece % (kTile / kV)) * kV;
-            T eu[kV], ed[kV], ez[kV];
-            memcpy(eu, &pf.u[j], 16);
-            memcpy(ed, &pf.dt[j], 16);
-            memcpy(ez, &pf.z[j], 16);
-#pragma unroll
-            for (int e = 0; e < kV; ++e) {
-                s.u[t][c + e] = Elem<T>::widen(eu[e]);
-                s.dt[t][c + e] = Elem<T>::widen(ed[e]);
-                if (!AGG) s.z[t][c + e] = Elem<T>::widen(ez[e]);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kBPT; ++j) {
-            const int e = threadIdx.x + j * kThreads;
-            if (e >= kBCE) continue;
-            const int t = e / kNP, n = e % kNP;
-            s.B[t][n] = Elem<T>::widen(pf.B[j]);
-            if (!AGG) s.C[t][n] = Elem<T>::widen(pf.C[j]);
-        }
-    }
-
-    // Add the G partial readouts, the D skip and the gate; round and store y.
-    __device__ static void finalize(const ScanParams &p, const Smem &s, int b, int d0, int64_t t0,
-                                    int tval, float D0, float D1) {
-        const int c = (threadIdx.x & 31) * 2;
-        const bool gate = p.z != nullptr;
-        T *y = static_cast<T *>(p.y);
-        for (int t = threadIdx.x >> 5; t < tval; t += kThreads / 32) {
-            float y0 = 0.0f, y1 = 0.0f;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                y0 += s.y[g][t][c];
-                y1 += s.y[g][t][c + 1];
-            }
-            y0 = fmaf(D0, s.u[t][c], y0);
-            y1 = fmaf(D1, s.u[t][c + 1], y1);
-            if (gate) {
-                y0 *= silu(s.z[t][c]);
-                y1 *= silu(s.z[t][c + 1]);
-            }
-            const int64_t off = ((int64_t)b * p.L + t0 + t) * p.dim + d0 + c;
-            const bool ok0 = d0 + c < p.dim, ok1 = d0 + c + 1 < p.dim;
-            if constexpr (sizeof(T) == 2) {
-                const uint16_t r0 = Elem<uint16_t>::to_bits(y0), r1 = Elem<uint16_t>::to_bits(y1);
-                if (p.pair_store && ok1) {
-                    *reinterpret_cast<uint32_t *>(y + off) = (uint32_t)r0 | ((uint32_t)r1 << 16);
-                } else {
-                    if (ok0) y[off] = r0;
-                    if (ok1) y[off + 1] = r1;
                 }
             } else {
-                if (p.pair_store && ok1) {
-                    *reinterpret_cast<float2 *>(y + off) = make_float2(y0, y1);
+                const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                dst[0] = zero;
+                dst[1] = zero;
+            }
+        }
+    }
+
+    // For the thread's pieces: add the G partial readouts and the skip, apply
+    // the gate, round and store y (8 or 16 bytes per piece).
+    // yb points at (the chunk's first token row, the tile's first channel).
+    __device__ static void finalize(const ScanParams &p, const Smem &s, const Held &held, T *yb, int tval,
+                                    int col, int d0) {
+#pragma unroll
+        for (int j = 0; j < kPPT; ++j) {
+            const int row = piece_row(j);
+            if ((kPieces % kThreads != 0 && row >= TC) || row >= tval || d0 + col >= p.dim) continue;
+            float4 acc = *reinterpret_cast<const float4 *>(&s.y[0][row][col]);
+#pragma unroll
+            for (int g = 1; g < G; ++g) {
+                const float4 v = *reinterpret_cast<const float4 *>(&s.y[g][row][col]);
+                acc.x += v.x;
+                acc.y += v.y;
+                acc.z += v.z;
+                acc.w += v.w;
+            }
+            float o[kV] = {(acc.x + held.sk[j][0]) * held.g[j][0], (acc.y + held.sk[j][1]) * held.g[j][1],
+                           (acc.z + held.sk[j][2]) * held.g[j][2], (acc.w + held.sk[j][3]) * held.g[j][3]};
+            T *dst = yb + (uint32_t)row * (uint32_t)p.dim + col;
+            if constexpr (sizeof(T) == 2) {
+                typedef float f2v __attribute__((ext_vector_type(2)));
+                typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+                const f2v lo = {o[0], o[1]}, hi = {o[2], o[3]};
+                const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, b2v));
+                const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, b2v));
+                if (p.vec) {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(w0, w1);
                 } else {
-                    if (ok0) y[off] = y0;
-                    if (ok1) y[off + 1] = y1;
+                    const uint16_t e4[4] = {(uint16_t)(w0 & 0xffffu), (uint16_t)(w0 >> 16),
+                                            (uint16_t)(w1 & 0xffffu), (uint16_t)(w1 >> 16)};
+#pragma unroll
+                    for (int e = 0; e < kV; ++e)
+                        if (d0 + col + e < p.dim) dst[e] = e4[e];
+                }
+            } else {
+                if (p.vec) {
+                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < kV; ++e)
+                        if (d0 + col + e < p.dim) dst[e] = o[e];
                 }
             }
         }
+    }
+
+    struct Lane {
+        float A2[NPW], h[NPW];
+        float Az[ZOH ? NPW : 1], Ainv[ZOH ? NPW : 1];
+        float dsum, dcomp;   // compensated sum of delta (aggregate pass)
+    };
+
+    // Steps whose B and C values are fetched together (scalar registers: at
+    // most 64 values of B and C per batch).
+    static constexpr int kTB = (64 / (2 * NPW)) < TC ? (64 / (2 * NPW) > 0 ? 64 / (2 * NPW) : 1) : TC;
+    static_assert(TC % kTB == 0, "batches of steps tile the chunk");
+
+    // One token of this wave's states: update, and return the partial readout.
+    // bqv/cqv: the wave's B_t and C_t values (uniform, in scalar registers).
+    __device__ static __forceinline__ float step(Lane &l, const float2 (*dx)[kTile], int t, int lane,
+                                                 const float (&bqv)[NPW], const float (&cqv)[NPW]) {
+        const float2 v = dx[t][lane];
+        const float dd = v.x;
+        const float xx = v.y;
+        float part = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NPW; ++q) {
+            const float bq = bqv[q];
+            if constexpr (ZOH) {
+                const float em1 = expm1f(dd * l.Az[q]);
+                const float coef = (l.Az[q] != 0.0f) ? em1 * l.Ainv[q] : dd;
+                l.h[q] = fmaf(1.0f + em1, l.h[q], coef * bq * xx);
+            } else {
+                const float a = __builtin_amdgcn_exp2f(dd * l.A2[q]);
+                l.h[q] = fmaf(a, l.h[q], xx * bq);
+            }
+            if (!AGG) part = fmaf(cqv[q], l.h[q], part);
+        }
+        if (AGG) {
+            // Kahan summation of delta over the segment
+            const float yk = dd - l.dcomp;
+            const float tk = l.dsum + yk;
+            l.dcomp = (tk - l.dsum) - yk;
+            l.dsum = tk;
+        }
+        return part;
     }
 
     __device__ static void run(const ScanParams &p) {
@@ -276,26 +456,28 @@ struct ScanKernel {
         int seg, b, tile;
         map_block(p, seg, b, tile);
         const int lane = threadIdx.x & (kTile - 1);
-        const int w = threadIdx.x / kTile;
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kTile);
         const int d0 = tile * kTile;
         const int d = d0 + lane;
         const bool dval = d < p.dim;
         const int dc = dval ? d : p.dim - 1;
         const int64_t t_begin = (int64_t)seg * p.seg_len;
         const int64_t t_end = min(p.L, t_begin + (int64_t)p.seg_len);
+        const bool gate = !AGG && p.z != nullptr;
 
         // Per-lane constants and initial state of this wave's states.
-        float A2[NPW], h[NPW];
-        float Az[ZOH ? NPW : 1], Ainv[ZOH ? NPW : 1];
+        Lane l;
+        l.dsum = 0.0f;
+        l.dcomp = 0.0f;
 #pragma unroll
         for (int k = 0; k < NPW; ++k) {
             const int n = w * NPW + k;
             const bool nv = n < p.N;
             const float a = nv ? p.A[(int64_t)dc * p.N + n] : 0.0f;
-            A2[k] = a * kLog2e;
+            l.A2[k] = a * kLog2e;
             if constexpr (ZOH) {
-                Az[k] = a;
-                Ainv[k] = (a != 0.0f) ? 1.0f / a : 0.0f;
+                l.Az[k] = a;
+                l.Ainv[k] = (a != 0.0f) ? 1.0f / a : 0.0f;
             }
             float h_init = 0.0f;
             if (!AGG && nv) {
@@ -306,66 +488,93 @@ struct ScanKernel {
                 else if (p.h0 != nullptr)
                     h_init = p.h0[((int64_t)b * p.dim + dc) * p.N + n];
             }
-            h[k] = h_init;
+            l.h[k] = h_init;
         }
-        // finalize handles the channel pair (2*(tid%32), +1) for all its rows
-        float D0 = 0.0f, D1 = 0.0f;
-        if (!AGG && p.D != nullptr) {
-            const int c = d0 + (threadIdx.x & 31) * 2;
-            D0 = c < p.dim ? p.D[c] : 0.0f;
-            D1 = c + 1 < p.dim ? p.D[c + 1] : 0.0f;
-        }
-        float dsum = 0.0f, dcomp = 0.0f;   // compensated sum of delta (aggregate pass)
+        // This thread stages (and finalizes) channels [col, col + kV) of the tile.
+        const int col = (threadIdx.x % kRowPieces) * kV;
+        const bool colv = d0 + col < p.dim;
+        float Dk[kV];
+#pragma unroll
+        for (int e = 0; e < kV; ++e)
+            Dk[e] = (!AGG && p.D != nullptr && d0 + col + e < p.dim) ? p.D[d0 + col + e] : 0.0f;
 
         const int nchunks = (int)((t_end - t_begin + TC - 1) / TC);
+        const int64_t row0 = (int64_t)b * p.L + t_begin;        // token row of (b, t_begin)
         Prefetch pf;
+        Held held;
         if (nchunks > 0) {
-            load(p, pf, b, d0, t_begin, (int)min((int64_t)TC, t_end - t_begin));
-            commit(pf, s);
+            const int tv = (int)min((int64_t)TC, t_end - t_begin);
+            load(p, pf, row0 * p.dim + d0, tv, col, d0, colv);
+            load_bc(p, pf, b, t_begin);
+            commit(pf, s.dx[0], held, tv, col, colv, Dk, gate);
+            commit_bc(pf, s.bc[0]);
         }
         __syncthreads();
+
+        // this wave's B and C values, widened to fp32: NPW per token, contiguous in time
+        const int64_t grp = ((int64_t)b * G + w) * padded_len(p.L) + t_begin;
+        cfloat *bw = (cfloat *)(p.Bf) + grp * NPW;
+        cfloat *cw = (cfloat *)(p.Cf) + grp * NPW;
+        T *yb = AGG ? nullptr : static_cast<T *>(p.y) + row0 * p.dim + d0;
 
         for (int k = 0; k < nchunks; ++k) {
             const int64_t t0 = t_begin + (int64_t)k * TC;
             const int tval = (int)min((int64_t)TC, t_end - t0);
-            if (k + 1 < nchunks)
-                load(p, pf, b, d0, t0 + TC, (int)min((int64_t)TC, t_end - t0 - TC));
-
-            for (int t = 0; t < tval; ++t) {
-                const float uu = s.u[t][lane];
-                const float dd = s.dt[t][lane];
-                const float du = dd * uu;
-                float part = 0.0f;
-#pragma unroll
-                for (int q = 0; q < NPW; ++q) {
-                    const float bq = s.B[t][w * NPW + q];
-                    if constexpr (ZOH) {
-                        const float em1 = expm1f(dd * Az[q]);
-                        const float coef = (Az[q] != 0.0f) ? em1 * Ainv[q] : dd;
-                        h[q] = fmaf(1.0f + em1, h[q], coef * bq * uu);
-                    } else {
-                        const float a = __builtin_amdgcn_exp2f(dd * A2[q]);
-                        h[q] = fmaf(a, h[q], du * bq);
-                    }
-                    if (!AGG) part = fmaf(s.C[t][w * NPW + q], h[q], part);
-                }
-                if (AGG) {
-                    // Kahan summation of delta over the segment
-                    const float yk = dd - dcomp;
-                    const float tk = dsum + yk;
-                    dcomp = (tk - dsum) - yk;
-                    dsum = tk;
-                } else {
-                    s.y[w][t][lane] = part;
-                }
-            }
-            __syncthreads();
-            if (!AGG) finalize(p, s, b, d0, t0, tval, D0, D1);
+            const int tnext = (int)min((int64_t)TC, t_end - t0 - TC);
+            const float2 (*dx)[kTile] = s.dx[k & 1];
             if (k + 1 < nchunks) {
-                __syncthreads();
-                commit(pf, s);
-                __syncthreads();
+                load(p, pf, (row0 + (int64_t)(k + 1) * TC) * p.dim + d0, tnext, col, d0, colv);
+                load_bc(p, pf, b, t0 + TC);
             }
+
+#pragma unroll
+            for (int t0b = 0; t0b < TC; t0b += kTB) {
+                // fetch the batch's B and C with a few wide scalar loads, wait
+                // once, then run its steps with only LDS reads outstanding
+                float bq[kTB][NPW], cq[kTB][NPW];
+#pragma unroll
+                for (int i = 0; i < kTB; ++i)
+#pragma unroll
+                    for (int q = 0; q < NPW; ++q) {
+                        if constexpr (kBcLds) {
+                            bq[i][q] = s.bc[k & 1][0][w][t0b + i][q];
+                            cq[i][q] = AGG ? 0.0f : s.bc[k & 1][1][w][t0b + i][q];
+                        } else {
+                            bq[i][q] = bw[(t0b + i) * NPW + q];
+                            cq[i][q] = AGG ? 0.0f : cw[(t0b + i) * NPW + q];
+                        }
+                    }
+                if (tval == TC) {
+#pragma unroll
+                    for (int i = 0; i < kTB; ++i) {
+                        const float part = step(l, dx, t0b + i, lane, bq[i], cq[i]);
+                        if (!AGG) s.y[w][t0b + i][lane] = part;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kTB; ++i) {
+                        if (t0b + i < tval) {
+                            const float part = step(l, dx, t0b + i, lane, bq[i], cq[i]);
+                            if (!AGG) s.y[w][t0b + i][lane] = part;
+                        }
+                    }
+                }
+            }
+            if constexpr (!AGG) {
+                __syncthreads();                 // partial readouts complete
+                finalize(p, s, held, yb, tval, col, d0);
+            }
+            // The other buffer was last read before the barrier above (or,
+            // in the aggregate pass, in the previous chunk before the barrier
+            // below), so it can be refilled now; `held` was consumed above.
+            if (k + 1 < nchunks) {
+                commit(pf, s.dx[(k + 1) & 1], held, tnext, col, colv, Dk, gate);
+                commit_bc(pf, s.bc[(k + 1) & 1]);
+            }
+            __syncthreads();                     // next buffer ready; partial planes free
+            bw += TC * NPW;
+            cw += TC * NPW;
+            if (!AGG) yb += (int64_t)TC * p.dim;
         }
 
         if (!dval) return;
@@ -375,10 +584,10 @@ struct ScanKernel {
             if (n >= p.N) continue;
             if (AGG) {
                 const int64_t o = (((int64_t)b * p.nseg + seg) * p.dim + d) * p.N + n;
-                p.agg_P[o] = __builtin_amdgcn_exp2f(A2[k] * dsum);
-                p.agg_H[o] = h[k];
+                p.agg_P[o] = __builtin_amdgcn_exp2f(l.A2[k] * l.dsum);
+                p.agg_H[o] = l.h[k];
             } else if (p.h_last != nullptr && seg == p.nseg - 1) {
-                p.h_last[((int64_t)b * p.dim + d) * p.N + n] = h[k];
+                p.h_last[((int64_t)b * p.dim + d) * p.N + n] = l.h[k];
             }
         }
     }
@@ -451,10 +660,15 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryParams p) {
 
 template <typename T, int NPW, int G, int TC, bool ZOH>
 hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg, hipStream_t st) {
+    {
+        const int64_t total = (int64_t)p.batch * padded_len(p.L) * (NPW * G);
+        hipLaunchKernelGGL(widen_bc_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const T *>(p.B), static_cast<const T *>(p.C), p.Bf, p.Cf, p.batch, p.L,
+                           p.N, G, NPW);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
     if (nblocks_agg > 0) {
-        ScanParams pa = p;
-        pa.nseg_launched = p.nseg - 1;
-        hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, true>), dim3(nblocks_agg), dim3(kTile * G), 0, st, pa);
+        hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, true>), dim3(nblocks_agg), dim3(kTile * G), 0, st, p);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         CarryParams cp{};
         cp.P = p.agg_P;
@@ -480,10 +694,10 @@ hipError_t launch_scan_shape(const Plan &pl, const ScanParams &p, int nm, int na
     // (padded states, waves per tile) -> states per wave; chunk length keeps LDS <= 64 KiB
 #define SSM_CASE(NP, GG, TCC) \
     if (pl.npad == NP && pl.G == GG) return launch_scan_t<T, NP / GG, GG, TCC, ZOH>(p, nm, na, st);
-    SSM_CASE(4, 1, 32)  SSM_CASE(4, 2, 32)  SSM_CASE(4, 4, 32)
-    SSM_CASE(8, 1, 32)  SSM_CASE(8, 2, 32)  SSM_CASE(8, 4, 32)  SSM_CASE(8, 8, 16)
-    SSM_CASE(16, 1, 32) SSM_CASE(16, 2, 32) SSM_CASE(16, 4, 32) SSM_CASE(16, 8, 16) SSM_CASE(16, 16, 8)
-    SSM_CASE(32, 2, 32) SSM_CASE(32, 4, 16) SSM_CASE(32, 8, 16) SSM_CASE(32, 16, 8)
+    SSM_CASE(4, 1, 16)  SSM_CASE(4, 2, 16)  SSM_CASE(4, 4, 16)
+    SSM_CASE(8, 1, 16)  SSM_CASE(8, 2, 16)  SSM_CASE(8, 4, 16)  SSM_CASE(8, 8, 16)
+    SSM_CASE(16, 1, 16) SSM_CASE(16, 2, 16) SSM_CASE(16, 4, 16) SSM_CASE(16, 8, 16) SSM_CASE(16, 16, 8)
+    SSM_CASE(32, 2, 16) SSM_CASE(32, 4, 16) SSM_CASE(32, 8, 16) SSM_CASE(32, 16, 8)
     SSM_CASE(64, 4, 16) SSM_CASE(64, 8, 16) SSM_CASE(64, 16, 8)
 #undef SSM_CASE
     return hipErrorInvalidValue;

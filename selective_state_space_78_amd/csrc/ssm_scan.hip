@@ -175,7 +175,8 @@ Plan make_plan(const ssm_scan_desc &d, const ssm_scan_tuning *t) {
     if (d.seqlen > 0 && S > d.seqlen) S = (int)d.seqlen;
     if (S < 1) S = 1;
     pl.S = S;
-    const int64_t seg_len = d.seqlen > 0 ? (d.seqlen + S - 1) / S : 0;
+    // segments start on 16-token boundaries (whole chunks, aligned runs of B and C)
+    const int64_t seg_len = d.seqlen > 0 ? ((d.seqlen + S - 1) / S + 15) / 16 * 16 : 0;
     pl.seg_len = seg_len > INT32_MAX ? 0 : (int)seg_len;
     if (d.seqlen > 0) pl.S = (int)((d.seqlen + pl.seg_len - 1) / pl.seg_len);   // drop empty segments
     return pl;
@@ -190,11 +191,8 @@ bool plan_supported(const Plan &pl) {
 }
 
 size_t workspace_bytes_for(const ssm_scan_desc &d, const Plan &pl) {
-    if (pl.S <= 1) return 0;
-    // agg_P, agg_H and seg_h, each (batch, S, dim, N) fp32, 256-byte aligned
-    const size_t one = (size_t)d.batch * pl.S * d.dim * d.dstate * sizeof(float);
-    const size_t al = (one + 255) & ~(size_t)255;
-    return 3 * al;
+    if (d.batch == 0 || d.dim == 0 || d.seqlen == 0) return 0;
+    return workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, pl).total;
 }
 
 bool shape_compiled(const Plan &pl) {
@@ -249,7 +247,7 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
     for (const void *q : in_ptrs)
         if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
     if ((y && !aligned(y, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) || (h0 && !aligned(h0, 4)) ||
-        (h_last && !aligned(h_last, 4)) || (workspace && !aligned(workspace, 4)))
+        (h_last && !aligned(h_last, 4)) || (workspace && !aligned(workspace, 256)))
         return SSM_ERR_ALIGN;
 
     const size_t need = workspace_bytes_for(d, pl);
@@ -286,21 +284,24 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
     p.seg_len = pl.seg_len;
     p.nseg = pl.S;
     p.ntiles = (int)((d.dim + kTile - 1) / kTile);
-    p.vec = ((d.dim * es) % 16 == 0) && aligned(u, 16) && aligned(delta, 16) && (!z || aligned(z, 16));
-    p.pair_store = (d.dim % 2 == 0) && aligned(y, 2 * es);
-    if (pl.S > 1) {
-        const size_t one = (size_t)d.batch * pl.S * d.dim * d.dstate * sizeof(float);
-        const size_t al = (one + 255) & ~(size_t)255;
+    // 4-channel pieces move as single 8-byte (bf16) or 16-byte (fp32) accesses
+    p.vec = (d.dim % 4 == 0) && aligned(u, 4 * es) && aligned(delta, 4 * es) && (!z || aligned(z, 4 * es)) &&
+            aligned(y, 4 * es);
+    {
+        const WorkspaceLayout wl = workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, pl);
         char *ws = static_cast<char *>(workspace);
-        p.agg_P = reinterpret_cast<float *>(ws);
-        p.agg_H = reinterpret_cast<float *>(ws + al);
-        p.seg_h = reinterpret_cast<float *>(ws + 2 * al);
+        p.Bf = reinterpret_cast<float *>(ws + wl.bf);
+        p.Cf = reinterpret_cast<float *>(ws + wl.cf);
+        if (pl.S > 1) {
+            p.agg_P = reinterpret_cast<float *>(ws + wl.agg_p);
+            p.agg_H = reinterpret_cast<float *>(ws + wl.agg_h);
+            p.seg_h = reinterpret_cast<float *>(ws + wl.seg_h);
+        }
     }
     const int64_t blocks_per_seg = (int64_t)p.ntiles * d.batch;
     const int64_t nm = blocks_per_seg * pl.S;
     const int64_t na = pl.S > 1 ? blocks_per_seg * (pl.S - 1) : 0;
     if (nm > INT32_MAX) return SSM_ERR_SHAPE;
-    p.nseg_launched = pl.S;
 
     hipError_t e;
     const bool zoh = d.disc == SSM_DISC_ZOH;

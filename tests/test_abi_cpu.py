@@ -64,7 +64,7 @@ GB = 1 << 30
 
 
 def scan_call(L, dsc, u=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB,
-              h0=0, y=8 * GB, h_last=9 * GB, ws=0, ws_bytes=0, tuning=None):
+              h0=0, y=8 * GB, h_last=9 * GB, ws=11 * GB, ws_bytes=1 << 30, tuning=None):
     args = [ctypes.byref(dsc) if dsc is not None else None]
     args += [fake(a) if a else None for a in (u, delta, A, B, C, D, z, h0, y, h_last, ws)]
     args += [ws_bytes]
@@ -117,11 +117,17 @@ def test_scan_aliasing(L):
 
 def test_scan_workspace(L):
     d = desc(b=1, L=4096, d=64, N=16)
+    rnd = lambda v: (v + 255) // 256 * 256
+    bc = rnd((1 * 4096 + 16) * 16 * 4)          # widened B (and C): rows + 16 spare, 16 states
     need = L.ssm_scan_workspace_size_tuned(ctypes.byref(d), ctypes.byref(ssm.ScanTuning(4, 4)))
-    assert need == 3 * ((1 * 4 * 64 * 16 * 4 + 255) // 256 * 256)
-    assert scan_call(L, d, tuning=(4, 4)) == EWS
+    assert need == 2 * bc + 3 * rnd(1 * 4 * 64 * 16 * 4)
+    assert scan_call(L, d, ws=0, ws_bytes=0, tuning=(4, 4)) == EWS
     assert scan_call(L, d, ws=11 * GB, ws_bytes=need - 4, tuning=(4, 4)) == EWS
-    assert L.ssm_scan_workspace_size_tuned(ctypes.byref(d), ctypes.byref(ssm.ScanTuning(4, 1))) == 0
+    assert scan_call(L, d, ws=11 * GB + 128, ws_bytes=need, tuning=(4, 4)) == EALIGN
+    assert L.ssm_scan_workspace_size_tuned(ctypes.byref(d), ctypes.byref(ssm.ScanTuning(4, 1))) == 2 * bc
+    d5 = desc(b=1, L=4096, d=64, N=5)           # padded to 8 states
+    assert L.ssm_scan_workspace_size(ctypes.byref(d5)) >= 2 * rnd((4096 + 16) * 8 * 4)
+    assert L.ssm_scan_workspace_size(ctypes.byref(desc(L=0))) == 0
     assert L.ssm_scan_workspace_size(None) == 0
 
 
