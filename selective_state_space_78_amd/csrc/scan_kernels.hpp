@@ -25,9 +25,10 @@
 //    product shared by the states is so formed once. The expanded (t, d, n)
 //    decay and input terms exist only in registers and are never written.
 //  * Each wave writes its partial readout sum_{n in wave} C_t[n] h_t[n] per
-//    (t, channel) to LDS; after a barrier every thread adds the G partials of
-//    its pieces and the skip, applies the gate, rounds to the output type and
-//    stores 4 channels at once.
+//    (t, channel) to its own LDS plane; after a barrier every thread adds the
+//    G planes of its pieces and the skip, applies the gate, rounds to the
+//    output type and stores 4 channels at once. (Sharing planes through LDS
+//    float atomics was measured several times slower.)
 //  * Long sequences with few channels are split into S segments. An
 //    aggregate pass computes, per segment, the affine map h -> P*h + H that
 //    the segment applies to its incoming state (P = exp(A * sum delta),
@@ -189,14 +190,8 @@ template <typename T> struct RawOf;                      // four elements of a p
 template <> struct RawOf<uint16_t> { typedef uint2 type; };
 template <> struct RawOf<float> { typedef uint4 type; };
 
-#ifndef SSM_BC_LDS
-#define SSM_BC_LDS 0
-#endif
-
 template <typename T, int NPW, int G, int TC, bool ZOH, bool AGG>
 struct ScanKernel {
-    // Where the inner loop reads B_t and C_t: scalar loads (0) or LDS broadcasts (1).
-    static constexpr bool kBcLds = SSM_BC_LDS;
     static constexpr int kThreads = kTile * G;
     static constexpr int kNP = NPW * G;                       // padded state count
     static constexpr int kV = 4;                               // channels per staged piece
@@ -209,51 +204,20 @@ struct ScanKernel {
     static_assert(TC <= kPadRows, "spare rows of the widened B and C");
     typedef typename RawOf<T>::type Raw;
 
+    static constexpr int kPlanes = G;                          // one partial-readout plane per wave
+
     // LDS: the staged chunk as (delta, delta*u) pairs (u instead of delta*u
-    // for the hold rule), double-buffered, and the waves' partial readouts.
+    // for the hold rule), double-buffered, and the partial-readout planes.
     struct __align__(16) Smem {
         float2 dx[2][TC][kTile];
-        float y[AGG ? 1 : G][AGG ? 1 : TC][AGG ? 1 : kYS];
-        float bc[kBcLds ? 2 : 1][2][G][TC][NPW];     // staged B, C of the chunk (kBcLds)
+        float y[AGG ? 1 : kPlanes][AGG ? 1 : TC][AGG ? 1 : kYS];
     };
-    static constexpr int kBcFloats = 2 * G * TC * NPW;        // B and C floats per chunk
-    static constexpr int kBcPPT = (kBcFloats / 4 + kThreads - 1) / kThreads;
-    static_assert(sizeof(Smem) <= (kBcLds ? 163840 : 65536), "LDS per workgroup");
+    static_assert(sizeof(Smem) <= 65536, "LDS per workgroup");
 
     struct Prefetch {
         Raw u[kPPT], dt[kPPT], z[kPPT];
-        float4 bc[kBcLds ? kBcPPT : 1];
     };
 
-    // B and C of one chunk from the widened workspace: per tensor, G runs of
-    // TC*NPW floats (one per state group), 16 bytes per thread.
-    __device__ static void load_bc(const ScanParams &p, Prefetch &pf, int b, int64_t t0) {
-        if constexpr (kBcLds) {
-#pragma unroll
-            for (int j = 0; j < kBcPPT; ++j) {
-                const int i4 = threadIdx.x + j * kThreads;       // float4 index within the chunk
-                if (i4 * 4 >= kBcFloats) continue;
-                const int f = i4 * 4;
-                const int tensor = f / (G * TC * NPW);
-                const int g = (f / (TC * NPW)) % G;
-                const int r = f % (TC * NPW);
-                const float *src = (tensor ? p.Cf : p.Bf) + (((int64_t)b * G + g) * padded_len(p.L) + t0) * NPW + r;
-                pf.bc[j] = *reinterpret_cast<const float4 *>(src);
-            }
-        }
-    }
-
-    __device__ static void commit_bc(const Prefetch &pf, float (*bc)[G][TC][NPW]) {
-        if constexpr (kBcLds) {
-            float *base = &bc[0][0][0][0];
-#pragma unroll
-            for (int j = 0; j < kBcPPT; ++j) {
-                const int i4 = threadIdx.x + j * kThreads;
-                if (i4 * 4 >= kBcFloats) continue;
-                reinterpret_cast<float4 *>(base)[i4] = pf.bc[j];
-            }
-        }
-    }
     // D*u and silu(z) of the thread's staged pieces, kept in registers until
     // the same thread finalizes those outputs
     struct Held {
@@ -361,8 +325,8 @@ struct ScanKernel {
         }
     }
 
-    // For the thread's pieces: add the G partial readouts and the skip, apply
-    // the gate, round and store y (8 or 16 bytes per piece).
+    // For the thread's pieces: add the partial-readout planes and the skip,
+    // apply the gate, round and store y (8 or 16 bytes per piece).
     // yb points at (the chunk's first token row, the tile's first channel).
     __device__ static void finalize(const ScanParams &p, const Smem &s, const Held &held, T *yb, int tval,
                                     int col, int d0) {
@@ -372,7 +336,7 @@ struct ScanKernel {
             if ((kPieces % kThreads != 0 && row >= TC) || row >= tval || d0 + col >= p.dim) continue;
             float4 acc = *reinterpret_cast<const float4 *>(&s.y[0][row][col]);
 #pragma unroll
-            for (int g = 1; g < G; ++g) {
+            for (int g = 1; g < kPlanes; ++g) {
                 const float4 v = *reinterpret_cast<const float4 *>(&s.y[g][row][col]);
                 acc.x += v.x;
                 acc.y += v.y;
@@ -407,6 +371,11 @@ struct ScanKernel {
                 }
             }
         }
+    }
+
+    // A wave's partial readout for (t, lane) into its plane.
+    __device__ static __forceinline__ void put(Smem &s, int w, int t, int lane, float part) {
+        s.y[w][t][lane] = part;
     }
 
     struct Lane {
@@ -505,9 +474,7 @@ struct ScanKernel {
         if (nchunks > 0) {
             const int tv = (int)min((int64_t)TC, t_end - t_begin);
             load(p, pf, row0 * p.dim + d0, tv, col, d0, colv);
-            load_bc(p, pf, b, t_begin);
             commit(pf, s.dx[0], held, tv, col, colv, Dk, gate);
-            commit_bc(pf, s.bc[0]);
         }
         __syncthreads();
 
@@ -517,45 +484,44 @@ struct ScanKernel {
         cfloat *cw = (cfloat *)(p.Cf) + grp * NPW;
         T *yb = AGG ? nullptr : static_cast<T *>(p.y) + row0 * p.dim + d0;
 
+        // B and C of a batch of kTB steps, fetched with a few wide scalar loads
+        // and waited for once; the inner loop then has only LDS reads in
+        // flight. The first batch of each chunk is fetched before the previous
+        // chunk's staging work, so its latency overlaps that work.
+        float bq[kTB][NPW], cq[kTB][NPW];
+        auto fetch = [&](int t0b) {
+#pragma unroll
+            for (int i = 0; i < kTB; ++i)
+#pragma unroll
+                for (int q = 0; q < NPW; ++q) {
+                    bq[i][q] = bw[(t0b + i) * NPW + q];
+                    cq[i][q] = AGG ? 0.0f : cw[(t0b + i) * NPW + q];
+                }
+        };
+        fetch(0);
+
         for (int k = 0; k < nchunks; ++k) {
             const int64_t t0 = t_begin + (int64_t)k * TC;
             const int tval = (int)min((int64_t)TC, t_end - t0);
             const int tnext = (int)min((int64_t)TC, t_end - t0 - TC);
             const float2 (*dx)[kTile] = s.dx[k & 1];
-            if (k + 1 < nchunks) {
-                load(p, pf, (row0 + (int64_t)(k + 1) * TC) * p.dim + d0, tnext, col, d0, colv);
-                load_bc(p, pf, b, t0 + TC);
-            }
+            if (k + 1 < nchunks) load(p, pf, (row0 + (int64_t)(k + 1) * TC) * p.dim + d0, tnext, col, d0, colv);
 
 #pragma unroll
             for (int t0b = 0; t0b < TC; t0b += kTB) {
-                // fetch the batch's B and C with a few wide scalar loads, wait
-                // once, then run its steps with only LDS reads outstanding
-                float bq[kTB][NPW], cq[kTB][NPW];
-#pragma unroll
-                for (int i = 0; i < kTB; ++i)
-#pragma unroll
-                    for (int q = 0; q < NPW; ++q) {
-                        if constexpr (kBcLds) {
-                            bq[i][q] = s.bc[k & 1][0][w][t0b + i][q];
-                            cq[i][q] = AGG ? 0.0f : s.bc[k & 1][1][w][t0b + i][q];
-                        } else {
-                            bq[i][q] = bw[(t0b + i) * NPW + q];
-                            cq[i][q] = AGG ? 0.0f : cw[(t0b + i) * NPW + q];
-                        }
-                    }
+                if (t0b > 0) fetch(t0b);
                 if (tval == TC) {
 #pragma unroll
                     for (int i = 0; i < kTB; ++i) {
                         const float part = step(l, dx, t0b + i, lane, bq[i], cq[i]);
-                        if (!AGG) s.y[w][t0b + i][lane] = part;
+                        if (!AGG) put(s, w, t0b + i, lane, part);
                     }
                 } else {
 #pragma unroll
                     for (int i = 0; i < kTB; ++i) {
                         if (t0b + i < tval) {
                             const float part = step(l, dx, t0b + i, lane, bq[i], cq[i]);
-                            if (!AGG) s.y[w][t0b + i][lane] = part;
+                            if (!AGG) put(s, w, t0b + i, lane, part);
                         }
                     }
                 }
@@ -564,17 +530,17 @@ struct ScanKernel {
                 __syncthreads();                 // partial readouts complete
                 finalize(p, s, held, yb, tval, col, d0);
             }
+            bw += TC * NPW;
+            cw += TC * NPW;
+            if (!AGG) yb += (int64_t)TC * p.dim;
             // The other buffer was last read before the barrier above (or,
             // in the aggregate pass, in the previous chunk before the barrier
             // below), so it can be refilled now; `held` was consumed above.
             if (k + 1 < nchunks) {
+                fetch(0);
                 commit(pf, s.dx[(k + 1) & 1], held, tnext, col, colv, Dk, gate);
-                commit_bc(pf, s.bc[(k + 1) & 1]);
             }
             __syncthreads();                     // next buffer ready; partial planes free
-            bw += TC * NPW;
-            cw += TC * NPW;
-            if (!AGG) yb += (int64_t)TC * p.dim;
         }
 
         if (!dval) return;
@@ -689,6 +655,10 @@ hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg,
     return hipGetLastError();
 }
 
+#ifndef SSM_TC16
+#define SSM_TC16 16
+#endif
+
 template <typename T, bool ZOH>
 hipError_t launch_scan_shape(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st) {
     // (padded states, waves per tile) -> states per wave; chunk length keeps LDS <= 64 KiB
@@ -696,7 +666,7 @@ hipError_t launch_scan_shape(const Plan &pl, const ScanParams &p, int nm, int na
     if (pl.npad == NP && pl.G == GG) return launch_scan_t<T, NP / GG, GG, TCC, ZOH>(p, nm, na, st);
     SSM_CASE(4, 1, 16)  SSM_CASE(4, 2, 16)  SSM_CASE(4, 4, 16)
     SSM_CASE(8, 1, 16)  SSM_CASE(8, 2, 16)  SSM_CASE(8, 4, 16)  SSM_CASE(8, 8, 16)
-    SSM_CASE(16, 1, 16) SSM_CASE(16, 2, 16) SSM_CASE(16, 4, 16) SSM_CASE(16, 8, 16) SSM_CASE(16, 16, 8)
+    SSM_CASE(16, 1, 16) SSM_CASE(16, 2, 16) SSM_CASE(16, 4, SSM_TC16) SSM_CASE(16, 8, SSM_TC16) SSM_CASE(16, 16, 8)
     SSM_CASE(32, 2, 16) SSM_CASE(32, 4, 16) SSM_CASE(32, 8, 16) SSM_CASE(32, 16, 8)
     SSM_CASE(64, 4, 16) SSM_CASE(64, 8, 16) SSM_CASE(64, 16, 8)
 #undef SSM_CASE

@@ -38,6 +38,7 @@ struct DecodeParams {
     int64_t channels;     // batch * dim
     int dim, N, lpc_log2; // lanes per channel = 1 << lpc_log2, 4 states per lane
     int vec4;             // N % 4 == 0 and h, A 16-byte aligned
+    int bc4;              // N % 4 == 0 and B, C aligned to 4 elements
 };
 
 template <typename T, bool ZOH>
@@ -81,14 +82,40 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
             av[k] = ok ? ap[k] : 0.0f;
         }
     }
+    // this lane's four B and C values: one 8- or 16-byte load each when aligned
+    float bv[4], cv[4];
+    if (p.bc4) {
+        if (qv) {
+            if constexpr (sizeof(T) == 2) {
+                const uint2 rb = *reinterpret_cast<const uint2 *>(Bp + b * p.N + n0);
+                const uint2 rc = *reinterpret_cast<const uint2 *>(Cp + b * p.N + n0);
+                bv[0] = __uint_as_float(rb.x << 16); bv[1] = __uint_as_float(rb.x & 0xffff0000u);
+                bv[2] = __uint_as_float(rb.y << 16); bv[3] = __uint_as_float(rb.y & 0xffff0000u);
+                cv[0] = __uint_as_float(rc.x << 16); cv[1] = __uint_as_float(rc.x & 0xffff0000u);
+                cv[2] = __uint_as_float(rc.y << 16); cv[3] = __uint_as_float(rc.y & 0xffff0000u);
+            } else {
+                const float4 fb = *reinterpret_cast<const float4 *>(Bp + b * p.N + n0);
+                const float4 fc = *reinterpret_cast<const float4 *>(Cp + b * p.N + n0);
+                bv[0] = fb.x; bv[1] = fb.y; bv[2] = fb.z; bv[3] = fb.w;
+                cv[0] = fc.x; cv[1] = fc.y; cv[2] = fc.z; cv[3] = fc.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) bv[k] = cv[k] = 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool ok = n0 + k < p.N;
+            bv[k] = ok ? Elem<T>::widen(Bp[b * p.N + n0 + k]) : 0.0f;
+            cv[k] = ok ? Elem<T>::widen(Cp[b * p.N + n0 + k]) : 0.0f;
+        }
+    }
     const float du = dv * xv;
     float part = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int n = n0 + k;
-        const bool ok = n < p.N;
-        const float bk = ok ? Elem<T>::widen(Bp[b * p.N + n]) : 0.0f;
-        const float ck = ok ? Elem<T>::widen(Cp[b * p.N + n]) : 0.0f;
+        const float bk = bv[k], ck = cv[k];
         if constexpr (ZOH) {
             const float em1 = expm1f(dv * av[k]);
             const float coef = (av[k] != 0.0f) ? em1 / av[k] : dv;
@@ -159,18 +186,20 @@ Plan make_plan(const ssm_scan_desc &d, const ssm_scan_tuning *t) {
     Plan pl{};
     pl.npad = padded_states(d.dstate);
     const int64_t tiles = d.batch * ((d.dim + kTile - 1) / kTile);
-    const int64_t want_waves = 2048;
+    // waves wanted in flight: 4 per SIMD of 256 CUs (measured: the 1.4B-shaped
+    // layer runs fastest with 8 waves per tile, 4096 waves)
+    const int64_t want_waves = 4096;
     int G = (t && t->state_groups > 0) ? t->state_groups : 0;
     if (G == 0) {
         G = pl.npad > 16 ? pl.npad / 16 : 1;     // at most 16 states per wave
-        while (G < 4 && G < pl.npad && tiles * G < want_waves) G *= 2;
+        while (G < 8 && G < pl.npad && tiles * G < want_waves) G *= 2;
     }
     pl.G = G;
     pl.npw = pl.npad / G;
     int S = (t && t->segments > 0) ? t->segments : 0;
     if (S == 0) {
         S = 1;
-        while (S < kMaxSegments && tiles * G * S < want_waves && d.seqlen / (2 * S) >= 512) S *= 2;
+        while (S < kMaxSegments && tiles * G * S < want_waves / 2 && d.seqlen / (2 * S) >= 512) S *= 2;
     }
     if (d.seqlen > 0 && S > d.seqlen) S = (int)d.seqlen;
     if (S < 1) S = 1;
@@ -391,6 +420,7 @@ extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int3
     p.N = (int)dstate;
     p.lpc_log2 = ilog2((int)((dstate + 3) / 4));
     p.vec4 = (dstate % 4 == 0) && aligned(h, 16) && aligned(A, 16);
+    p.bc4 = (dstate % 4 == 0) && aligned(B, 4 * es) && aligned(C, 4 * es);
     const int64_t threads = ch << p.lpc_log2;
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > INT32_MAX) return SSM_ERR_SHAPE;

@@ -141,7 +141,7 @@ def test_scan_bad_tuning(L):
 
 def test_plan_shapes(L):
     # the flagship shapes get enough waves for 256 CUs x 4 SIMDs
-    assert ssm.ssm_scan_plan(8, 8192, 4096, 16) == (4, 1)
+    assert ssm.ssm_scan_plan(8, 8192, 4096, 16) == (8, 1)
     g, s = ssm.ssm_scan_plan(1, 131072, 5120, 16)
     assert g * s * 80 >= 2048
     assert ssm.ssm_scan_plan(1, 64, 16, 4)[1] == 1
