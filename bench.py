@@ -31,7 +31,15 @@ HBM_PEAK_GBPS = 8000.0
 # fp32 VALU issue rate without packed instructions: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 WORKLOAD = "mamba1.4b"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_scan_mamba1.4b.json")
+WORKLOADS = {
+    "mamba1.4b": "Mamba-1.4B-shaped layer scan: batch 8, L 8192, d_inner 4096, d_state 16, "
+                 "bf16 u/delta/B/C/z/y, fp32 A/D/state, D skip + SiLU gate + final state",
+    "mamba130m": "Mamba-130M-shaped layer scan: batch 4, L 2048, d_inner 1536, d_state 16, "
+                 "bf16 u/delta/B/C/z/y, fp32 A/D/state, D skip + SiLU gate + final state",
+    "long": "Long-context scan: batch 1, L 131072, d_inner 5120, d_state 16, delta bias log-uniform "
+            "[1e-4, 1e-1], bf16 u/delta/B/C/z/y, fp32 A/D/state, D skip + SiLU gate + final state",
+}
+PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "selective_state_space_78_amd", "csrc")
 
 
@@ -43,8 +51,10 @@ def valu_ops_per_token_ch(N: int, gate: bool) -> int:
 
 
 def source_digest() -> str:
+    """Digest of the scan kernels' device source (the kernel template and the
+    bf16 instantiation unit): counter summaries older than it are stale."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in ("scan_kernels.hpp", "scan_bf16_euler.hip"):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -65,15 +75,16 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms)))
 
 
-def measured_traffic(per_launch_tokens: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+def measured_traffic(workload: str, plan):
+    """HBM bytes per launch of the main scan kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source
+    in the same launch shape."""
     try:
-        with open(PROFILE_TRAFFIC) as f:
+        with open(os.path.join(PROFILES, "traffic_scan_%s.json" % workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_digest") != source_digest():
+    if rec.get("source_digest") != source_digest() or list(rec.get("launch", [])) != list(plan):
         return None
     return rec.get("bytes_per_launch")
 
@@ -159,6 +170,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--tuning", type=str, default=None, help="state_groups,segments")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=WORKLOAD,
+                    help="scan workload of the timed step (the default is the headline one)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale profiler byte counters)")
     args = ap.parse_args()
@@ -171,8 +184,8 @@ def main():
     import torch
     import selective_state_space_78_amd as ssm
 
-    cfg = si.CONFIGS[WORKLOAD]
-    print("bench: generating %s inputs" % WORKLOAD, file=sys.stderr, flush=True)
+    cfg = si.CONFIGS[args.workload]
+    print("bench: generating %s inputs" % args.workload, file=sys.stderr, flush=True)
     x = si.scan_inputs(cfg, seed=0)
     dev = {k: to_dev(v, torch) for k, v in x.items() if v is not None}
     y = torch.empty((cfg.batch, cfg.seqlen, cfg.dim), dtype=torch.bfloat16, device="cuda")
@@ -228,8 +241,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "Mamba-1.4B-shaped layer scan: batch 8, L 8192, d_inner 4096, d_state 16, "
-                        "bf16 u/delta/B/C/z/y, fp32 A/D/state, D skip + SiLU gate + final state",
+            "workload": WORKLOADS[args.workload],
             "global_batch": cfg.batch, "seq_len": cfg.seqlen, "dim": cfg.dim, "dstate": cfg.dstate,
             "io_dtype": "bf16", "parallelism": "none (1 GPU)",
             "launch": {"state_groups": plan[0], "segments": plan[1]},
@@ -243,7 +255,7 @@ def main():
             "frac": achieved_tops / VALU_PEAK_TOPS,
             "ops_per_token_ch": valu_ops_per_token_ch(cfg.dstate, cfg.gate),
             "mean_launch_ms": mean_launch_ms,
-            "traffic": measured_traffic(tok),
+            "traffic": measured_traffic(args.workload, plan),
         },
         "hbm": {
             "algorithmic_bytes_per_launch": nbytes,

@@ -199,7 +199,12 @@ Plan make_plan(const ssm_scan_desc &d, const ssm_scan_tuning *t) {
     int S = (t && t->segments > 0) ? t->segments : 0;
     if (S == 0) {
         S = 1;
-        while (S < kMaxSegments && tiles * G * S < want_waves / 2 && d.seqlen / (2 * S) >= 512) S *= 2;
+        // segments cost a second (aggregate) pass over their tokens: add them
+        // only while the waves are too few, and keep them >= 256 tokens
+        // (measured: 16 segments for L 131072 x 5120 channels, 8 for
+        // L 2048 x 6144 channels)
+        if (tiles * G < want_waves)
+            while (S < kMaxSegments && tiles * G * S < 2 * want_waves && d.seqlen / (2 * S) >= 256) S *= 2;
     }
     if (d.seqlen > 0 && S > d.seqlen) S = (int)d.seqlen;
     if (S < 1) S = 1;
