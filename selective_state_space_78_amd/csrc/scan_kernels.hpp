@@ -12,23 +12,27 @@
 //    waves multiplies the parallelism of a channel tile by G at the cost of a
 //    few per-token instructions, instead of splitting time, which would cost
 //    a second pass of the recurrence.
-//  * A prologue widens B and C once to fp32, regrouped so that one wave's
-//    values are contiguous in time (and padded with zero rows and states), so
-//    that a few wide scalar loads fetch a batch of steps and are waited for
-//    once: scalar and LDS reads share one wait counter, and a scalar load per
-//    step would expose its latency at every LDS wait.
-//  * Time is walked in chunks of TC tokens. Each thread of the workgroup owns
-//    a piece of 4 channels of some rows of the chunk: it loads the piece's u,
-//    delta and z one chunk ahead into registers, stages (delta, delta*u)
-//    pairs into LDS (double-buffered) for all waves, and keeps D*u and
-//    silu(z) in registers for the outputs it will store. Every per-token
-//    product shared by the states is so formed once. The expanded (t, d, n)
-//    decay and input terms exist only in registers and are never written.
+//  * A prologue copies B and C once into the workspace, regrouped so that one
+//    wave's values are contiguous in time (and padded with zero rows and
+//    states), so that a few wide scalar loads fetch a batch of steps and are
+//    waited for once: scalar and LDS reads share one wait counter, and a
+//    scalar load per step would expose its latency at every LDS wait. bf16
+//    B_t[n] and C_t[n] share one 32-bit word (the scalar unit splits it), so a
+//    chunk's values fit in 32 SGPRs; fp32 values take a word each.
+//  * Time is walked in chunks of TC tokens with one barrier per chunk. While
+//    the waves scan chunk k, every thread of the workgroup also stages a
+//    piece (2 or 4 channels) of chunk k+1: it loads u, delta and z two chunks
+//    ahead into registers, writes (delta, delta*u) pairs into LDS for all
+//    waves, and keeps D*u and silu(z) in registers; and it finalizes its
+//    piece of chunk k-1. Every per-token product shared by the states is so
+//    formed once. The expanded (t, d, n) decay and input terms exist only in
+//    registers and are never written.
 //  * Each wave writes its partial readout sum_{n in wave} C_t[n] h_t[n] per
-//    (t, channel) to its own LDS plane; after a barrier every thread adds the
-//    G planes of its pieces and the skip, applies the gate, rounds to the
-//    output type and stores 4 channels at once. (Sharing planes through LDS
-//    float atomics was measured several times slower.)
+//    (t, channel) to its own LDS plane; one chunk later every thread adds the
+//    G planes of its piece and the skip, applies the gate, rounds to the
+//    output type and stores its channels at once. Pairs and planes are
+//    double-buffered by chunk parity. (Sharing planes through LDS float
+//    atomics was measured several times slower.)
 //  * Long sequences with few channels are split into S segments. An
 //    aggregate pass computes, per segment, the affine map h -> P*h + H that
 //    the segment applies to its incoming state (P = exp(A * sum delta),
@@ -46,6 +50,8 @@
 
 #include <stdint.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "ssm_scan.h"
 
@@ -138,7 +144,7 @@ inline int ilog2(int v) { int r = 0; while ((1 << r) < v) ++r; return r; }
 namespace ssm_detail {
 namespace {
 
-typedef const __attribute__((address_space(4))) float cfloat;   // scalar-load view
+typedef const __attribute__((address_space(4))) uint32_t cword;   // scalar-load view
 
 // ---------------------------------------------------------------------------
 // Prologue: B and C widened to fp32 and regrouped so that the values one wave
@@ -161,14 +167,17 @@ __global__ __launch_bounds__(256) void widen_bc_kernel(const T *__restrict__ B, 
     const int g = (int)(r % groups);
     const int64_t b = r / groups;
     const int n = g * npw + q;
-    float vb = 0.0f, vc = 0.0f;
-    if (t < L && n < N) {
-        const int64_t src = (b * L + t) * N + n;
-        vb = Elem<T>::widen(B[src]);
-        vc = Elem<T>::widen(C[src]);
+    const bool on = t < L && n < N;
+    const int64_t src = (b * L + t) * N + n;
+    if constexpr (sizeof(T) == 2) {
+        // bf16: B and C stay bf16, packed into one word (C in the high half)
+        const uint32_t vb = on ? (uint32_t)B[src] : 0u;
+        const uint32_t vc = on ? (uint32_t)C[src] : 0u;
+        reinterpret_cast<uint32_t *>(Bf)[i] = vb | (vc << 16);
+    } else {
+        Bf[i] = on ? B[src] : 0.0f;
+        Cf[i] = on ? C[src] : 0.0f;
     }
-    Bf[i] = vb;
-    Cf[i] = vc;
 }
 
 // Linear workgroup id -> (segment, batch row, channel tile). Consecutive ids
@@ -186,33 +195,54 @@ __device__ __forceinline__ void map_block(const ScanParams &p, int &seg, int &b,
     seg = rest / p.batch;
 }
 
-template <typename T> struct RawOf;                      // four elements of a per-token tensor
-template <> struct RawOf<uint16_t> { typedef uint2 type; };
-template <> struct RawOf<float> { typedef uint4 type; };
+// Raw bits of KV consecutive elements of a per-token tensor (one 4, 8 or
+// 16-byte access).
+template <int W> struct Words;
+template <> struct Words<1> { typedef uint32_t type; };
+template <> struct Words<2> { typedef uint2 type; };
+template <> struct Words<4> { typedef uint4 type; };
+
+template <int W> __device__ __forceinline__ uint32_t word(const typename Words<W>::type &r, int i);
+template <> __device__ __forceinline__ uint32_t word<1>(const uint32_t &r, int) { return r; }
+template <> __device__ __forceinline__ uint32_t word<2>(const uint2 &r, int i) { return i == 0 ? r.x : r.y; }
+template <> __device__ __forceinline__ uint32_t word<4>(const uint4 &r, int i) {
+    return i == 0 ? r.x : i == 1 ? r.y : i == 2 ? r.z : r.w;
+}
+__device__ __forceinline__ void make_words(uint32_t &r, const uint32_t *w) { r = w[0]; }
+__device__ __forceinline__ void make_words(uint2 &r, const uint32_t *w) { r = make_uint2(w[0], w[1]); }
+__device__ __forceinline__ void make_words(uint4 &r, const uint32_t *w) { r = make_uint4(w[0], w[1], w[2], w[3]); }
+
+template <int KV> struct FloatsOf;
+template <> struct FloatsOf<2> { typedef float2 type; };
+template <> struct FloatsOf<4> { typedef float4 type; };
 
 template <typename T, int NPW, int G, int TC, bool ZOH, bool AGG>
 struct ScanKernel {
     static constexpr int kThreads = kTile * G;
     static constexpr int kNP = NPW * G;                       // padded state count
-    static constexpr int kV = 4;                               // channels per staged piece
+    // channels per staged piece: 2 when that gives every thread of the
+    // workgroup a piece of the chunk, else 4
+    static constexpr int kV = TC * kTile >= 4 * kThreads ? 4 : 2;
+    static constexpr int kWords = kV * (int)sizeof(T) / 4;
     static constexpr int kRowPieces = kTile / kV;              // pieces per 64-channel row
     static constexpr int kPieces = TC * kRowPieces;            // pieces per chunk per tensor
     static constexpr int kPPT = (kPieces + kThreads - 1) / kThreads;
     static constexpr int kRowStep = kThreads / kRowPieces;      // rows between a thread's pieces
-    static constexpr int kYS = kTile + 4;                      // padded row of a partial-readout plane
     static_assert(kThreads % kRowPieces == 0, "a thread keeps the same channels in every piece");
     static_assert(TC <= kPadRows, "spare rows of the widened B and C");
-    typedef typename RawOf<T>::type Raw;
-
-    static constexpr int kPlanes = G;                          // one partial-readout plane per wave
+    typedef typename Words<kWords>::type Raw;
+    typedef typename FloatsOf<kV>::type VecF;
 
     // LDS: the staged chunk as (delta, delta*u) pairs (u instead of delta*u
-    // for the hold rule), double-buffered, and the partial-readout planes.
+    // for the hold rule), and one partial-readout plane per wave, both
+    // double-buffered by chunk parity: while the waves scan chunk k, the
+    // staging threads read chunk k-1's planes and write chunk k+1's pairs,
+    // so one barrier per chunk orders everything.
     struct __align__(16) Smem {
         float2 dx[2][TC][kTile];
-        float y[AGG ? 1 : kPlanes][AGG ? 1 : TC][AGG ? 1 : kYS];
+        float y[AGG ? 1 : 2][AGG ? 1 : G][AGG ? 1 : TC][AGG ? 1 : kTile];
     };
-    static_assert(sizeof(Smem) <= 65536, "LDS per workgroup");
+    static_assert(sizeof(Smem) <= 81920, "two workgroups per CU in 160 KiB of LDS");
 
     struct Prefetch {
         Raw u[kPPT], dt[kPPT], z[kPPT];
@@ -225,37 +255,37 @@ struct ScanKernel {
     };
 
     __device__ static int piece_row(int j) { return threadIdx.x / kRowPieces + j * kRowStep; }
+    __device__ static bool piece_in_chunk(int j) { return kPieces % kThreads == 0 || piece_row(j) < TC; }
 
     // Element-wise load of one piece (unaligned tensors), zero past dim.
     __device__ static Raw gather(const T *src, int c0, int dim, bool on) {
+        uint32_t w[kWords];
         if constexpr (sizeof(T) == 2) {
-            uint32_t w[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < kWords; ++i) {
                 const uint32_t lo = (on && c0 + 2 * i < dim) ? src[2 * i] : 0u;
                 const uint32_t hi = (on && c0 + 2 * i + 1 < dim) ? src[2 * i + 1] : 0u;
                 w[i] = lo | (hi << 16);
             }
-            return make_uint2(w[0], w[1]);
         } else {
-            uint32_t w[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = (on && c0 + i < dim) ? __float_as_uint(src[i]) : 0u;
-            return make_uint4(w[0], w[1], w[2], w[3]);
+            for (int i = 0; i < kWords; ++i) w[i] = (on && c0 + i < dim) ? __float_as_uint(src[i]) : 0u;
         }
+        Raw r;
+        make_words(r, w);
+        return r;
     }
 
     __device__ static void unpack(const Raw &r, float (&v)[kV]) {
-        if constexpr (sizeof(T) == 2) {
-            v[0] = __uint_as_float(r.x << 16);
-            v[1] = __uint_as_float(r.x & 0xffff0000u);
-            v[2] = __uint_as_float(r.y << 16);
-            v[3] = __uint_as_float(r.y & 0xffff0000u);
-        } else {
-            v[0] = __uint_as_float(r.x);
-            v[1] = __uint_as_float(r.y);
-            v[2] = __uint_as_float(r.z);
-            v[3] = __uint_as_float(r.w);
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) {
+            const uint32_t x = word<kWords>(r, i);
+            if constexpr (sizeof(T) == 2) {
+                v[2 * i] = __uint_as_float(x << 16);
+                v[2 * i + 1] = __uint_as_float(x & 0xffff0000u);
+            } else {
+                v[i] = __uint_as_float(x);
+            }
         }
     }
 
@@ -270,7 +300,7 @@ struct ScanKernel {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
             const int row = piece_row(j);
-            if ((kPieces % kThreads != 0 && row >= TC) || row >= tval || !colv) continue;
+            if (!piece_in_chunk(j) || row >= tval || !colv) continue;
             const uint32_t off = (uint32_t)row * (uint32_t)p.dim + (uint32_t)col;
             if (p.vec) {
                 pf.u[j] = *reinterpret_cast<const Raw *>(u + off);
@@ -293,17 +323,15 @@ struct ScanKernel {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
             const int row = piece_row(j);
-            if (kPieces % kThreads != 0 && row >= TC) continue;
+            if (!piece_in_chunk(j)) continue;
             float4 *dst = reinterpret_cast<float4 *>(&dx[row][col]);
             if (row < tval && colv) {
                 float u[kV], d[kV];
                 unpack(pf.u[j], u);
                 unpack(pf.dt[j], d);
-                float xo[kV];
 #pragma unroll
-                for (int e = 0; e < kV; ++e) xo[e] = ZOH ? u[e] : d[e] * u[e];
-                dst[0] = make_float4(d[0], xo[0], d[1], xo[1]);
-                dst[1] = make_float4(d[2], xo[2], d[3], xo[3]);
+                for (int e = 0; e < kV; e += 2)
+                    dst[e / 2] = make_float4(d[e], ZOH ? u[e] : d[e] * u[e], d[e + 1], ZOH ? u[e + 1] : d[e + 1] * u[e + 1]);
                 if constexpr (!AGG) {
 #pragma unroll
                     for (int e = 0; e < kV; ++e) held.sk[j][e] = Dk[e] * u[e];
@@ -318,52 +346,64 @@ struct ScanKernel {
                     }
                 }
             } else {
-                const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                dst[0] = zero;
-                dst[1] = zero;
+#pragma unroll
+                for (int e = 0; e < kV; e += 2) dst[e / 2] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         }
     }
 
-    // For the thread's pieces: add the partial-readout planes and the skip,
-    // apply the gate, round and store y (8 or 16 bytes per piece).
+    // For the thread's pieces of one chunk: add the G partial-readout planes
+    // and the skip, apply the gate, round and store y (one access per piece).
     // yb points at (the chunk's first token row, the tile's first channel).
-    __device__ static void finalize(const ScanParams &p, const Smem &s, const Held &held, T *yb, int tval,
-                                    int col, int d0) {
+    __device__ static void finalize(const ScanParams &p, const float (*planes)[TC][kTile], const Held &held,
+                                    T *yb, int tval, int col, int d0) {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
             const int row = piece_row(j);
-            if ((kPieces % kThreads != 0 && row >= TC) || row >= tval || d0 + col >= p.dim) continue;
-            float4 acc = *reinterpret_cast<const float4 *>(&s.y[0][row][col]);
+            if (!piece_in_chunk(j) || row >= tval || d0 + col >= p.dim) continue;
+            float acc[kV];
+            {
+                const VecF v = *reinterpret_cast<const VecF *>(&planes[0][row][col]);
+                const float *pv = reinterpret_cast<const float *>(&v);
 #pragma unroll
-            for (int g = 1; g < kPlanes; ++g) {
-                const float4 v = *reinterpret_cast<const float4 *>(&s.y[g][row][col]);
-                acc.x += v.x;
-                acc.y += v.y;
-                acc.z += v.z;
-                acc.w += v.w;
+                for (int e = 0; e < kV; ++e) acc[e] = pv[e];
             }
-            float o[kV] = {(acc.x + held.sk[j][0]) * held.g[j][0], (acc.y + held.sk[j][1]) * held.g[j][1],
-                           (acc.z + held.sk[j][2]) * held.g[j][2], (acc.w + held.sk[j][3]) * held.g[j][3]};
+#pragma unroll
+            for (int g = 1; g < G; ++g) {
+                const VecF v = *reinterpret_cast<const VecF *>(&planes[g][row][col]);
+                const float *pv = reinterpret_cast<const float *>(&v);
+#pragma unroll
+                for (int e = 0; e < kV; ++e) acc[e] += pv[e];
+            }
+            float o[kV];
+#pragma unroll
+            for (int e = 0; e < kV; ++e) o[e] = (acc[e] + held.sk[j][e]) * held.g[j][e];
             T *dst = yb + (uint32_t)row * (uint32_t)p.dim + col;
             if constexpr (sizeof(T) == 2) {
                 typedef float f2v __attribute__((ext_vector_type(2)));
                 typedef __bf16 b2v __attribute__((ext_vector_type(2)));
-                const f2v lo = {o[0], o[1]}, hi = {o[2], o[3]};
-                const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, b2v));
-                const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, b2v));
+                uint32_t w[kWords];
+#pragma unroll
+                for (int i = 0; i < kWords; ++i) {
+                    const f2v pr = {o[2 * i], o[2 * i + 1]};
+                    w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2v));
+                }
                 if (p.vec) {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(w0, w1);
+                    Raw r;
+                    make_words(r, w);
+                    *reinterpret_cast<Raw *>(dst) = r;
                 } else {
-                    const uint16_t e4[4] = {(uint16_t)(w0 & 0xffffu), (uint16_t)(w0 >> 16),
-                                            (uint16_t)(w1 & 0xffffu), (uint16_t)(w1 >> 16)};
 #pragma unroll
                     for (int e = 0; e < kV; ++e)
-                        if (d0 + col + e < p.dim) dst[e] = e4[e];
+                        if (d0 + col + e < p.dim) dst[e] = (uint16_t)(e & 1 ? w[e / 2] >> 16 : w[e / 2] & 0xffffu);
                 }
             } else {
                 if (p.vec) {
-                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                    VecF v;
+                    float *pv = reinterpret_cast<float *>(&v);
+#pragma unroll
+                    for (int e = 0; e < kV; ++e) pv[e] = o[e];
+                    *reinterpret_cast<VecF *>(dst) = v;
                 } else {
 #pragma unroll
                     for (int e = 0; e < kV; ++e)
@@ -373,33 +413,43 @@ struct ScanKernel {
         }
     }
 
-    // A wave's partial readout for (t, lane) into its plane.
-    __device__ static __forceinline__ void put(Smem &s, int w, int t, int lane, float part) {
-        s.y[w][t][lane] = part;
-    }
-
     struct Lane {
         float A2[NPW], h[NPW];
         float Az[ZOH ? NPW : 1], Ainv[ZOH ? NPW : 1];
         float dsum, dcomp;   // compensated sum of delta (aggregate pass)
     };
 
-    // Steps whose B and C values are fetched together (scalar registers: at
-    // most 64 values of B and C per batch).
-    static constexpr int kTB = (64 / (2 * NPW)) < TC ? (64 / (2 * NPW) > 0 ? 64 / (2 * NPW) : 1) : TC;
+    // B_t[n] and C_t[n] reach the wave as scalar words: for bf16 inputs one
+    // word holds both (B low, C high) and the scalar unit splits them; fp32
+    // inputs take a word each.
+    static constexpr bool kPacked = sizeof(T) == 2;
+    static constexpr int kWPS = kPacked ? 1 : 2;               // words per state and step
+    // Steps whose B and C words are fetched together: at most 32 scalar
+    // registers for packed words (which leaves room for the rest of the
+    // kernel's scalars without spills), 64 for fp32 words
+    static constexpr int kBudget = kPacked ? 32 : 64;
+    static constexpr int kTBMax = kBudget / (kWPS * NPW) > 0 ? kBudget / (kWPS * NPW) : 1;
+    static constexpr int kTB = kTBMax < TC ? kTBMax : TC;
     static_assert(TC % kTB == 0, "batches of steps tile the chunk");
 
+    __device__ static __forceinline__ float b_of(const uint32_t (&w)[kWPS]) {
+        return __uint_as_float(kPacked ? w[0] << 16 : w[0]);
+    }
+    __device__ static __forceinline__ float c_of(const uint32_t (&w)[kWPS]) {
+        return __uint_as_float(kPacked ? w[0] & 0xffff0000u : w[kWPS - 1]);
+    }
+
     // One token of this wave's states: update, and return the partial readout.
-    // bqv/cqv: the wave's B_t and C_t values (uniform, in scalar registers).
+    // bc: the wave's B_t and C_t words (uniform, in scalar registers).
     __device__ static __forceinline__ float step(Lane &l, const float2 (*dx)[kTile], int t, int lane,
-                                                 const float (&bqv)[NPW], const float (&cqv)[NPW]) {
+                                                 const uint32_t (&bc)[NPW][kWPS]) {
         const float2 v = dx[t][lane];
         const float dd = v.x;
         const float xx = v.y;
         float part = 0.0f;
 #pragma unroll
         for (int q = 0; q < NPW; ++q) {
-            const float bq = bqv[q];
+            const float bq = b_of(bc[q]);
             if constexpr (ZOH) {
                 const float em1 = expm1f(dd * l.Az[q]);
                 const float coef = (l.Az[q] != 0.0f) ? em1 * l.Ainv[q] : dd;
@@ -408,7 +458,7 @@ struct ScanKernel {
                 const float a = __builtin_amdgcn_exp2f(dd * l.A2[q]);
                 l.h[q] = fmaf(a, l.h[q], xx * bq);
             }
-            if (!AGG) part = fmaf(cqv[q], l.h[q], part);
+            if (!AGG) part = q == 0 ? c_of(bc[q]) * l.h[q] : fmaf(c_of(bc[q]), l.h[q], part);
         }
         if (AGG) {
             // Kahan summation of delta over the segment
@@ -469,78 +519,93 @@ struct ScanKernel {
 
         const int nchunks = (int)((t_end - t_begin + TC - 1) / TC);
         const int64_t row0 = (int64_t)b * p.L + t_begin;        // token row of (b, t_begin)
+        auto rows_of = [&](int k) { return (int)min((int64_t)TC, t_end - t_begin - (int64_t)k * TC); };
         Prefetch pf;
-        Held held;
+        Held held[2];                                            // by chunk parity
+        auto load_chunk = [&](int k) {
+            load(p, pf, (row0 + (int64_t)k * TC) * p.dim + d0, rows_of(k), col, d0, colv);
+        };
         if (nchunks > 0) {
-            const int tv = (int)min((int64_t)TC, t_end - t_begin);
-            load(p, pf, row0 * p.dim + d0, tv, col, d0, colv);
-            commit(pf, s.dx[0], held, tv, col, colv, Dk, gate);
+            load_chunk(0);
+            commit(pf, s.dx[0], held[0], rows_of(0), col, colv, Dk, gate);
         }
+        if (nchunks > 1) load_chunk(1);
         __syncthreads();
 
-        // this wave's B and C values, widened to fp32: NPW per token, contiguous in time
+        // this wave's B and C words: NPW (x kWPS) per token, contiguous in time
         const int64_t grp = ((int64_t)b * G + w) * padded_len(p.L) + t_begin;
-        cfloat *bw = (cfloat *)(p.Bf) + grp * NPW;
-        cfloat *cw = (cfloat *)(p.Cf) + grp * NPW;
+        cword *bw = (cword *)(p.Bf) + grp * NPW;
+        cword *cw = (cword *)(p.Cf) + grp * NPW;
         T *yb = AGG ? nullptr : static_cast<T *>(p.y) + row0 * p.dim + d0;
 
         // B and C of a batch of kTB steps, fetched with a few wide scalar loads
-        // and waited for once; the inner loop then has only LDS reads in
-        // flight. The first batch of each chunk is fetched before the previous
-        // chunk's staging work, so its latency overlaps that work.
-        float bq[kTB][NPW], cq[kTB][NPW];
+        // and waited for once. Scalar and LDS reads share one wait counter, so
+        // the first batch of a chunk is fetched right after the barrier that
+        // opens it, ahead of the staging work, and lands before the first LDS
+        // wait.
+        uint32_t bc[kTB][NPW][kWPS];
         auto fetch = [&](int t0b) {
 #pragma unroll
             for (int i = 0; i < kTB; ++i)
 #pragma unroll
                 for (int q = 0; q < NPW; ++q) {
-                    bq[i][q] = bw[(t0b + i) * NPW + q];
-                    cq[i][q] = AGG ? 0.0f : cw[(t0b + i) * NPW + q];
+                    bc[i][q][0] = bw[(t0b + i) * NPW + q];
+                    if constexpr (!kPacked) bc[i][q][kWPS - 1] = AGG ? 0u : cw[(t0b + i) * NPW + q];
                 }
         };
-        fetch(0);
 
-        for (int k = 0; k < nchunks; ++k) {
-            const int64_t t0 = t_begin + (int64_t)k * TC;
-            const int tval = (int)min((int64_t)TC, t_end - t0);
-            const int tnext = (int)min((int64_t)TC, t_end - t0 - TC);
-            const float2 (*dx)[kTile] = s.dx[k & 1];
-            if (k + 1 < nchunks) load(p, pf, (row0 + (int64_t)(k + 1) * TC) * p.dim + d0, tnext, col, d0, colv);
-
+        // Chunk k (parity P): fetch its B and C, stage chunk k+1's inputs,
+        // store chunk k-1's outputs, scan chunk k, then one barrier.
+        auto chunk = [&](auto parity, int k) {
+            constexpr int P = decltype(parity)::value;
+            fetch(0);
+            Held next;
+            if (k + 1 < nchunks) commit(pf, s.dx[P ^ 1], next, rows_of(k + 1), col, colv, Dk, gate);
+            if constexpr (!AGG) {
+                if (k > 0) {
+                    finalize(p, s.y[P ^ 1], held[P ^ 1], yb, TC, col, d0);
+                    yb += (int64_t)TC * p.dim;
+                }
+                if (k + 1 < nchunks) held[P ^ 1] = next;   // chunk k-1's skip and gate are consumed
+            }
+            if (k + 2 < nchunks) load_chunk(k + 2);
+            const int tval = rows_of(k);
+            const float2 (*dx)[kTile] = s.dx[P];
 #pragma unroll
             for (int t0b = 0; t0b < TC; t0b += kTB) {
                 if (t0b > 0) fetch(t0b);
                 if (tval == TC) {
 #pragma unroll
                     for (int i = 0; i < kTB; ++i) {
-                        const float part = step(l, dx, t0b + i, lane, bq[i], cq[i]);
-                        if (!AGG) put(s, w, t0b + i, lane, part);
+                        const float part = step(l, dx, t0b + i, lane, bc[i]);
+                        if constexpr (!AGG) s.y[P][w][t0b + i][lane] = part;
                     }
                 } else {
 #pragma unroll
                     for (int i = 0; i < kTB; ++i) {
                         if (t0b + i < tval) {
-                            const float part = step(l, dx, t0b + i, lane, bq[i], cq[i]);
-                            if (!AGG) put(s, w, t0b + i, lane, part);
+                            const float part = step(l, dx, t0b + i, lane, bc[i]);
+                            if constexpr (!AGG) s.y[P][w][t0b + i][lane] = part;
                         }
                     }
                 }
             }
-            if constexpr (!AGG) {
-                __syncthreads();                 // partial readouts complete
-                finalize(p, s, held, yb, tval, col, d0);
-            }
             bw += TC * NPW;
             cw += TC * NPW;
-            if (!AGG) yb += (int64_t)TC * p.dim;
-            // The other buffer was last read before the barrier above (or,
-            // in the aggregate pass, in the previous chunk before the barrier
-            // below), so it can be refilled now; `held` was consumed above.
-            if (k + 1 < nchunks) {
-                fetch(0);
-                commit(pf, s.dx[(k + 1) & 1], held, tnext, col, colv, Dk, gate);
+            __syncthreads();
+        };
+        for (int k = 0; k < nchunks; k += 2) {
+            chunk(std::integral_constant<int, 0>(), k);
+            if (k + 1 < nchunks) chunk(std::integral_constant<int, 1>(), k + 1);
+        }
+        if constexpr (!AGG) {
+            if (nchunks > 0) {
+                const int tl = rows_of(nchunks - 1);
+                if ((nchunks - 1) & 1)
+                    finalize(p, s.y[1], held[1], yb, tl, col, d0);
+                else
+                    finalize(p, s.y[0], held[0], yb, tl, col, d0);
             }
-            __syncthreads();                     // next buffer ready; partial planes free
         }
 
         if (!dval) return;
@@ -655,20 +720,22 @@ hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg,
     return hipGetLastError();
 }
 
-#ifndef SSM_TC16
-#define SSM_TC16 16
+#ifndef SSM_TC_G8
+#define SSM_TC_G8 16
 #endif
 
 template <typename T, bool ZOH>
 hipError_t launch_scan_shape(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st) {
-    // (padded states, waves per tile) -> states per wave; chunk length keeps LDS <= 64 KiB
+    // (padded states, waves per tile, chunk length): LDS stays <= 80 KiB
+    // (two workgroups per CU) and every thread of a workgroup of up to 8
+    // waves stages a piece of each chunk
 #define SSM_CASE(NP, GG, TCC) \
     if (pl.npad == NP && pl.G == GG) return launch_scan_t<T, NP / GG, GG, TCC, ZOH>(p, nm, na, st);
-    SSM_CASE(4, 1, 16)  SSM_CASE(4, 2, 16)  SSM_CASE(4, 4, 16)
-    SSM_CASE(8, 1, 16)  SSM_CASE(8, 2, 16)  SSM_CASE(8, 4, 16)  SSM_CASE(8, 8, 16)
-    SSM_CASE(16, 1, 16) SSM_CASE(16, 2, 16) SSM_CASE(16, 4, SSM_TC16) SSM_CASE(16, 8, SSM_TC16) SSM_CASE(16, 16, 8)
-    SSM_CASE(32, 2, 16) SSM_CASE(32, 4, 16) SSM_CASE(32, 8, 16) SSM_CASE(32, 16, 8)
-    SSM_CASE(64, 4, 16) SSM_CASE(64, 8, 16) SSM_CASE(64, 16, 8)
+    SSM_CASE(4, 1, 16)  SSM_CASE(4, 2, 16)  SSM_CASE(4, 4, 8)
+    SSM_CASE(8, 1, 16)  SSM_CASE(8, 2, 16)  SSM_CASE(8, 4, 8)   SSM_CASE(8, 8, 16)
+    SSM_CASE(16, 1, 16) SSM_CASE(16, 2, 16) SSM_CASE(16, 4, 8)  SSM_CASE(16, 8, SSM_TC_G8) SSM_CASE(16, 16, 8)
+    SSM_CASE(32, 2, 16) SSM_CASE(32, 4, 8)  SSM_CASE(32, 8, 16) SSM_CASE(32, 16, 8)
+    SSM_CASE(64, 4, 8)  SSM_CASE(64, 8, 16) SSM_CASE(64, 16, 8)
 #undef SSM_CASE
     return hipErrorInvalidValue;
 }
