@@ -4,13 +4,15 @@
 // (argument validation, launch planning, dispatch) and the decode kernel; the
 // scan kernels live in scan_kernels.hpp.
 //
-// Decode: one thread per (channel, 4 states); h moves as 16-byte vectors, the
-// readout is reduced across the lanes of a channel with cross-lane shuffles.
+// Decode: one thread per (channel, 4 states); the state moves as 16-byte
+// vectors and a thread walks a few batch rows.
 
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "ssm_scan.h"
 #include "scan_kernels.hpp"
@@ -30,119 +32,186 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float *h0, float 
 // ---------------------------------------------------------------------------
 // Decode step
 
+// Decode: one thread per (channel, 4 states), so that a wave's 16-byte state
+// accesses are contiguous; the LPC lanes of a channel add their partial
+// readouts with DPP quad permutes (and cross-lane shuffles beyond 4 lanes). A
+// workgroup covers consecutive channels d of kDecodeRows batch rows; a thread
+// keeps its A values in registers for all its rows and issues the state loads
+// of its rows before the arithmetic. The state is read and written once.
+#ifndef SSM_DECODE_ROWS
+#define SSM_DECODE_ROWS 2
+#endif
+constexpr int kDecodeRows = SSM_DECODE_ROWS;
+
 struct DecodeParams {
     const void *x, *delta, *z, *B, *C;
     const float *A, *D;
     float *h;
     void *y;
-    int64_t channels;     // batch * dim
-    int dim, N, lpc_log2; // lanes per channel = 1 << lpc_log2, 4 states per lane
+    int batch, dim, N;
     int vec4;             // N % 4 == 0 and h, A 16-byte aligned
     int bc4;              // N % 4 == 0 and B, C aligned to 4 elements
 };
 
-template <typename T, bool ZOH>
-__global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int lpc = 1 << p.lpc_log2;
-    const int64_t c = gid >> p.lpc_log2;      // channel = b * dim + d
-    const int q = (int)(gid & (lpc - 1));
-    const bool cval = c < p.channels;
-    const int64_t cc = cval ? c : p.channels - 1;
-    const int64_t b = cc / p.dim;
-    const int d = (int)(cc % p.dim);
-    const T *x = static_cast<const T *>(p.x);
-    const T *dt = static_cast<const T *>(p.delta);
-    const T *Bp = static_cast<const T *>(p.B);
-    const T *Cp = static_cast<const T *>(p.C);
-    const float xv = Elem<T>::widen(x[cc]);
-    const float dv = Elem<T>::widen(dt[cc]);
-    const int n0 = q * 4;
+// v + (v of the lane whose index differs in bit m), for m = 1, 2 (inside
+// groups of 4 lanes) by DPP, else by a cross-lane shuffle
+template <int M> __device__ __forceinline__ float add_xor(float v) {
+    if constexpr (M == 1 || M == 2) {
+        constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;      // quad_perm [1,0,3,2] / [2,3,0,1]
+        return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, true));
+    } else {
+        return v + __shfl_xor(v, M, 64);
+    }
+}
 
-    float hv[4], av[4];
-    float *hp = p.h + cc * p.N + n0;
-    const float *ap = p.A + (int64_t)d * p.N + n0;
+template <typename T, bool ZOH, int LPC>
+__global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
+    typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type RawBC;   // 4 values of B or C
+    constexpr int kCPB = 256 / LPC;                // channels per workgroup
+    const int d = blockIdx.x * kCPB + (int)(threadIdx.x / LPC);
+    const int q = (int)(threadIdx.x % LPC);
+    const bool dvalid = d < p.dim;
+    const int dc = dvalid ? d : p.dim - 1;
+    const int n0 = q * 4;
     // with N % 4 == 0 a lane's four states are either all inside the channel
     // (n0 < N) or all past it (lanes added to round lanes-per-channel up to a
     // power of two); those lanes must not touch memory
     const bool qv = n0 < p.N;
+    const T *x = static_cast<const T *>(p.x);
+    const T *dt = static_cast<const T *>(p.delta);
+    const T *zp = static_cast<const T *>(p.z);
+    const T *Bp = static_cast<const T *>(p.B);
+    const T *Cp = static_cast<const T *>(p.C);
+
+    float av[4];
+    const float *ap = p.A + (int64_t)dc * p.N + n0;
     if (p.vec4) {
-        float4 h4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), a4 = h4;
-        if (qv) {
-            h4 = *reinterpret_cast<const float4 *>(hp);
-            a4 = *reinterpret_cast<const float4 *>(ap);
-        }
-        hv[0] = h4.x; hv[1] = h4.y; hv[2] = h4.z; hv[3] = h4.w;
+        const float4 a4 = qv ? *reinterpret_cast<const float4 *>(ap) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
     } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const bool ok = n0 + k < p.N;
-            hv[k] = ok ? hp[k] : 0.0f;
-            av[k] = ok ? ap[k] : 0.0f;
-        }
+        for (int k = 0; k < 4; ++k) av[k] = n0 + k < p.N ? ap[k] : 0.0f;
     }
-    // this lane's four B and C values: one 8- or 16-byte load each when aligned
-    float bv[4], cv[4];
-    if (p.bc4) {
-        if (qv) {
-            if constexpr (sizeof(T) == 2) {
-                const uint2 rb = *reinterpret_cast<const uint2 *>(Bp + b * p.N + n0);
-                const uint2 rc = *reinterpret_cast<const uint2 *>(Cp + b * p.N + n0);
-                bv[0] = __uint_as_float(rb.x << 16); bv[1] = __uint_as_float(rb.x & 0xffff0000u);
-                bv[2] = __uint_as_float(rb.y << 16); bv[3] = __uint_as_float(rb.y & 0xffff0000u);
-                cv[0] = __uint_as_float(rc.x << 16); cv[1] = __uint_as_float(rc.x & 0xffff0000u);
-                cv[2] = __uint_as_float(rc.y << 16); cv[3] = __uint_as_float(rc.y & 0xffff0000u);
+    const float Dd = p.D != nullptr ? p.D[dc] : 0.0f;
+
+    // groups of kDecodeRows rows, strided over the grid's y extent (<= 65535)
+    const int ngroups = (p.batch + kDecodeRows - 1) / kDecodeRows;
+    for (int grp = blockIdx.y; grp < ngroups; grp += gridDim.y) {
+        // loads of every row first (rows past the batch re-read the last row
+        // and store nothing)
+        float hv[kDecodeRows][4];
+        T xr[kDecodeRows], dr[kDecodeRows], zr[kDecodeRows];
+        RawBC br[kDecodeRows], cr[kDecodeRows];
+#pragma unroll
+        for (int r = 0; r < kDecodeRows; ++r) {
+            const int64_t b = min(grp * kDecodeRows + r, p.batch - 1);
+            const int64_t cc = b * p.dim + dc;
+            const float *hp = p.h + cc * p.N + n0;
+            if (p.vec4) {
+                const float4 h4 = qv ? *reinterpret_cast<const float4 *>(hp) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                hv[r][0] = h4.x; hv[r][1] = h4.y; hv[r][2] = h4.z; hv[r][3] = h4.w;
             } else {
-                const float4 fb = *reinterpret_cast<const float4 *>(Bp + b * p.N + n0);
-                const float4 fc = *reinterpret_cast<const float4 *>(Cp + b * p.N + n0);
-                bv[0] = fb.x; bv[1] = fb.y; bv[2] = fb.z; bv[3] = fb.w;
-                cv[0] = fc.x; cv[1] = fc.y; cv[2] = fc.z; cv[3] = fc.w;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) hv[r][k] = n0 + k < p.N ? hp[k] : 0.0f;
             }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) bv[k] = cv[k] = 0.0f;
+            xr[r] = x[cc];
+            dr[r] = dt[cc];
+            zr[r] = zp != nullptr ? zp[cc] : T(0);
+            if (p.bc4 && qv) {
+                br[r] = *reinterpret_cast<const RawBC *>(Bp + b * p.N + n0);
+                cr[r] = *reinterpret_cast<const RawBC *>(Cp + b * p.N + n0);
+            }
         }
-    } else {
+
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const bool ok = n0 + k < p.N;
-            bv[k] = ok ? Elem<T>::widen(Bp[b * p.N + n0 + k]) : 0.0f;
-            cv[k] = ok ? Elem<T>::widen(Cp[b * p.N + n0 + k]) : 0.0f;
+        for (int r = 0; r < kDecodeRows; ++r) {
+            const int64_t b = grp * kDecodeRows + r;
+            const int64_t bl = min(b, (int64_t)p.batch - 1);
+            float bv[4], cv[4];
+            if (p.bc4) {
+                if (qv) {
+                    if constexpr (sizeof(T) == 2) {
+                        const uint2 rb = br[r], rc = cr[r];
+                        bv[0] = __uint_as_float(rb.x << 16); bv[1] = __uint_as_float(rb.x & 0xffff0000u);
+                        bv[2] = __uint_as_float(rb.y << 16); bv[3] = __uint_as_float(rb.y & 0xffff0000u);
+                        cv[0] = __uint_as_float(rc.x << 16); cv[1] = __uint_as_float(rc.x & 0xffff0000u);
+                        cv[2] = __uint_as_float(rc.y << 16); cv[3] = __uint_as_float(rc.y & 0xffff0000u);
+                    } else {
+                        const uint4 rb = br[r], rc = cr[r];
+                        bv[0] = __uint_as_float(rb.x); bv[1] = __uint_as_float(rb.y);
+                        bv[2] = __uint_as_float(rb.z); bv[3] = __uint_as_float(rb.w);
+                        cv[0] = __uint_as_float(rc.x); cv[1] = __uint_as_float(rc.y);
+                        cv[2] = __uint_as_float(rc.z); cv[3] = __uint_as_float(rc.w);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) bv[k] = cv[k] = 0.0f;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const bool ok = n0 + k < p.N;
+                    bv[k] = ok ? Elem<T>::widen(Bp[bl * p.N + n0 + k]) : 0.0f;
+                    cv[k] = ok ? Elem<T>::widen(Cp[bl * p.N + n0 + k]) : 0.0f;
+                }
+            }
+            const float xv = Elem<T>::widen(xr[r]);
+            const float dv = Elem<T>::widen(dr[r]);
+            const float du = dv * xv;
+            float part = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (ZOH) {
+                    const float em1 = expm1f(dv * av[k]);
+                    const float coef = (av[k] != 0.0f) ? em1 / av[k] : dv;
+                    hv[r][k] = fmaf(1.0f + em1, hv[r][k], coef * bv[k] * xv);
+                } else {
+                    hv[r][k] = fmaf(__builtin_amdgcn_exp2f(dv * av[k] * kLog2e), hv[r][k], du * bv[k]);
+                }
+                part = fmaf(cv[k], hv[r][k], part);
+            }
+            // sum the partial readouts of the LPC lanes of this channel
+            if constexpr (LPC >= 2) part = add_xor<1>(part);
+            if constexpr (LPC >= 4) part = add_xor<2>(part);
+            if constexpr (LPC >= 8) part = add_xor<4>(part);
+            if constexpr (LPC >= 16) part = add_xor<8>(part);
+            if (!dvalid || b >= p.batch) continue;
+            const int64_t cc = b * p.dim + d;
+            float *hp = p.h + cc * p.N + n0;
+            if (p.vec4) {
+                if (qv) *reinterpret_cast<float4 *>(hp) = make_float4(hv[r][0], hv[r][1], hv[r][2], hv[r][3]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (n0 + k < p.N) hp[k] = hv[r][k];
+            }
+            if (q == 0) {
+                float yv = part + Dd * xv;
+                if (zp != nullptr) yv *= silu(Elem<T>::widen(zr[r]));
+                if constexpr (sizeof(T) == 2)
+                    static_cast<uint16_t *>(p.y)[cc] = Elem<uint16_t>::to_bits(yv);
+                else
+                    static_cast<float *>(p.y)[cc] = yv;
+            }
         }
     }
-    const float du = dv * xv;
-    float part = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float bk = bv[k], ck = cv[k];
-        if constexpr (ZOH) {
-            const float em1 = expm1f(dv * av[k]);
-            const float coef = (av[k] != 0.0f) ? em1 / av[k] : dv;
-            hv[k] = fmaf(1.0f + em1, hv[k], coef * bk * xv);
-        } else {
-            hv[k] = fmaf(__builtin_amdgcn_exp2f(dv * av[k] * kLog2e), hv[k], du * bk);
-        }
-        part = fmaf(ck, hv[k], part);
+}
+
+template <typename T, bool ZOH>
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
+    // lanes per channel: 4 states per lane, rounded up to a power of two
+    const int lpc = p.N <= 4 ? 1 : p.N <= 8 ? 2 : p.N <= 16 ? 4 : p.N <= 32 ? 8 : 16;
+    const int cpb = 256 / lpc;
+    const int ngroups = (p.batch + kDecodeRows - 1) / kDecodeRows;
+    const dim3 grid((unsigned)((p.dim + cpb - 1) / cpb), (unsigned)min(ngroups, 65535));
+    switch (lpc) {
+    case 1: hipLaunchKernelGGL((decode_kernel<T, ZOH, 1>), grid, dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<T, ZOH, 2>), grid, dim3(256), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<T, ZOH, 4>), grid, dim3(256), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<T, ZOH, 8>), grid, dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<T, ZOH, 16>), grid, dim3(256), 0, stream, p); break;
     }
-    // sum the partial readouts of the lpc lanes of this channel (in state order)
-    for (int m = lpc >> 1; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-    if (!cval) return;
-    if (p.vec4) {
-        if (qv) *reinterpret_cast<float4 *>(hp) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (n0 + k < p.N) hp[k] = hv[k];
-    }
-    if (q == 0) {
-        float yv = part + (p.D != nullptr ? p.D[d] : 0.0f) * xv;
-        if (p.z != nullptr) yv *= silu(Elem<T>::widen(static_cast<const T *>(p.z)[cc]));
-        if constexpr (sizeof(T) == 2)
-            static_cast<uint16_t *>(p.y)[cc] = Elem<uint16_t>::to_bits(yv);
-        else
-            static_cast<float *>(p.y)[cc] = yv;
-    }
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -420,27 +489,17 @@ extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int3
     DecodeParams p{};
     p.x = x; p.delta = delta; p.z = z; p.B = B; p.C = C;
     p.A = A; p.D = D; p.h = h; p.y = y;
-    p.channels = ch;
+    p.batch = (int)batch;
     p.dim = (int)dim;
     p.N = (int)dstate;
-    p.lpc_log2 = ilog2((int)((dstate + 3) / 4));
     p.vec4 = (dstate % 4 == 0) && aligned(h, 16) && aligned(A, 16);
     p.bc4 = (dstate % 4 == 0) && aligned(B, 4 * es) && aligned(C, 4 * es);
-    const int64_t threads = ch << p.lpc_log2;
-    const int64_t blocks = (threads + 255) / 256;
-    if (blocks > INT32_MAX) return SSM_ERR_SHAPE;
-    if (dtype == SSM_BF16) {
-        if (disc == SSM_DISC_ZOH)
-            hipLaunchKernelGGL((decode_kernel<uint16_t, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
-        else
-            hipLaunchKernelGGL((decode_kernel<uint16_t, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
-    } else {
-        if (disc == SSM_DISC_ZOH)
-            hipLaunchKernelGGL((decode_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
-        else
-            hipLaunchKernelGGL((decode_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
-    }
-    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    hipError_t e;
+    if (dtype == SSM_BF16)
+        e = disc == SSM_DISC_ZOH ? launch_decode<uint16_t, true>(p, stream) : launch_decode<uint16_t, false>(p, stream);
+    else
+        e = disc == SSM_DISC_ZOH ? launch_decode<float, true>(p, stream) : launch_decode<float, false>(p, stream);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 extern "C" const char *ssm_status_string(int status) {
