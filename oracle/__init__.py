@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the Mamba selective scan (S6) and its decode step.
+"""fp64 CPU oracle for the Mamba selective scan (S6), its backward and its decode step.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the smoke check and the
 bench's CPU-baseline leg, never by the product path. It shares no code with
@@ -48,9 +48,10 @@ def _ptr(a):
 
 
 class Oracle:
-    """ctypes handle on one compiled oracle library."""
+    """ctypes handle on one compiled oracle library. ``threads`` is the OpenMP
+    thread count used when a call passes ``nthreads=0`` (0: the runtime's)."""
 
-    def __init__(self, path: str):
+    def __init__(self, path: str, threads: int = 0):
         lib = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         lib.oracle_selective_scan.argtypes = [i64, i64, i64, i64, i32, i32,
@@ -60,8 +61,13 @@ class Oracle:
         lib.oracle_state_update.argtypes = [i64, i64, i64, i32, i32,
                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         lib.oracle_state_update.restype = i32
+        lib.oracle_selective_scan_bwd.argtypes = [i64, i64, i64, i64, i32, i32,
+                                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.oracle_selective_scan_bwd.restype = i32
         self.lib = lib
         self.path = path
+        self.threads = int(threads)
 
     @staticmethod
     def _per_token(arrays):
@@ -110,7 +116,7 @@ class Oracle:
         rc = self.lib.oracle_selective_scan(batch, L, dim, N, typ, _DISC[disc],
                                             _ptr(u), _ptr(delta), _ptr(A64), _ptr(B), _ptr(C),
                                             _ptr(D64), _ptr(zc), _ptr(h064),
-                                            nsel, _ptr(sel), _ptr(y), _ptr(hl), int(nthreads))
+                                            nsel, _ptr(sel), _ptr(y), _ptr(hl), int(nthreads or self.threads))
         if rc != 0:
             raise ValueError("oracle_selective_scan rejected its arguments")
         if channels is None:
@@ -118,6 +124,59 @@ class Oracle:
                 y = y.reshape(batch, dim, L).transpose(0, 2, 1).copy()
             hl = hl.reshape(batch, dim, N)
         return y, hl
+
+    def selective_scan_bwd(self, u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None,
+                           disc="euler", channels=None, want_bc=True, nthreads=0):
+        """Gradients of sum(dy * y) + sum(dh_last * h_last) with respect to every input.
+
+        Returns a dict. With ``channels=None``: du, ddelta, dz (batch, L, dim),
+        dA (dim, N), dD (dim), dh0 (batch, dim, N), dB, dC (batch, L, N). With
+        ``channels`` a sequence of (b, d) pairs: du, ddelta, dz (k, L), dA_c
+        (k, N) and dD_c (k) (each channel's share of dA[d] and dD[d]), dh0
+        (k, N), and dB, dC summed over the selected channels only.
+        """
+        u = np.ascontiguousarray(u)
+        batch, L, dim = u.shape
+        N = A.shape[1]
+        typ = self._per_token([u, delta, B, C, z])
+        delta = np.ascontiguousarray(delta)
+        B = np.ascontiguousarray(B)
+        C = np.ascontiguousarray(C)
+        A64 = np.ascontiguousarray(A, dtype=np.float64)
+        D64 = None if D is None else np.ascontiguousarray(D, dtype=np.float64)
+        zc = None if z is None else np.ascontiguousarray(z)
+        h064 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+        dy64 = np.ascontiguousarray(dy, dtype=np.float64)
+        assert dy64.shape == u.shape
+        dhl = None if dh_last is None else np.ascontiguousarray(dh_last, dtype=np.float64)
+        if dhl is not None:
+            assert dhl.shape == (batch, dim, N)
+        if channels is None:
+            sel, nsel = None, batch * dim
+        else:
+            sel = np.ascontiguousarray([b * dim + d for b, d in channels], dtype=np.int64)
+            nsel = len(sel)
+        du = np.empty((nsel, L)); dde = np.empty((nsel, L))
+        dz = np.empty((nsel, L)) if zc is not None else None
+        dA_c = np.empty((nsel, N)); dD_c = np.empty(nsel); dh0 = np.empty((nsel, N))
+        dB = np.empty((batch, L, N)) if want_bc else None
+        dC = np.empty((batch, L, N)) if want_bc else None
+        rc = self.lib.oracle_selective_scan_bwd(batch, L, dim, N, typ, _DISC[disc],
+                                                _ptr(u), _ptr(delta), _ptr(A64), _ptr(B), _ptr(C),
+                                                _ptr(D64), _ptr(zc), _ptr(h064), _ptr(dy64), _ptr(dhl),
+                                                nsel, _ptr(sel), _ptr(du), _ptr(dde), _ptr(dz),
+                                                _ptr(dA_c), _ptr(dD_c), _ptr(dh0), _ptr(dB), _ptr(dC),
+                                                int(nthreads or self.threads))
+        if rc != 0:
+            raise ValueError("oracle_selective_scan_bwd rejected its arguments")
+        if channels is not None:
+            return dict(du=du, ddelta=dde, dz=dz, dA_c=dA_c, dD_c=dD_c, dh0=dh0, dB=dB, dC=dC)
+
+        def per_token(a):
+            return None if a is None else a.reshape(batch, dim, L).transpose(0, 2, 1).copy()
+        return dict(du=per_token(du), ddelta=per_token(dde), dz=per_token(dz),
+                    dA=dA_c.reshape(batch, dim, N).sum(axis=0), dD=dD_c.reshape(batch, dim).sum(axis=0),
+                    dh0=dh0.reshape(batch, dim, N), dB=dB, dC=dC)
 
     def state_update(self, x, delta, A, B, C, h, D=None, z=None, disc="euler", nthreads=0):
         """One decode step. ``h`` (batch, dim, N) float64 is updated in place; returns y."""
@@ -133,7 +192,7 @@ class Oracle:
                                           _ptr(x), _ptr(np.ascontiguousarray(delta)), _ptr(A64),
                                           _ptr(np.ascontiguousarray(B)), _ptr(np.ascontiguousarray(C)),
                                           _ptr(D64), _ptr(None if z is None else np.ascontiguousarray(z)),
-                                          _ptr(h), _ptr(y), int(nthreads))
+                                          _ptr(h), _ptr(y), int(nthreads or self.threads))
         if rc != 0:
             raise ValueError("oracle_state_update rejected its arguments")
         return y
@@ -157,3 +216,7 @@ def selective_scan(*args, **kwargs):
 
 def state_update(*args, **kwargs):
     return load().state_update(*args, **kwargs)
+
+
+def selective_scan_bwd(*args, **kwargs):
+    return load().selective_scan_bwd(*args, **kwargs)

@@ -33,6 +33,25 @@
  * The decode step is the same body for a single token with the state carried
  * in and out (itwiki "순환 형태와 합성곱 형태"; ricepunchb "Mamba" §4.2).
  *
+ * The backward pass (oracle_selective_scan_bwd) returns the gradients of
+ *   loss = sum_{b,t,d} dy[b,t,d] * y[b,t,d] + sum_{b,d,n} dh_last[b,d,n] * h_last[b,d,n]
+ * with respect to every input, by the chain rule applied to the recurrence
+ * above, walked in reverse time with the adjoint state lam[n] = dloss/dh_t[n]
+ * (the backward of the selective scan that recomputes the states instead of
+ * storing them: doyouknow.kr "Mamba와 상태 공간 모델(SSM)의 부상 완벽 가이드"
+ * §3-3; here the oracle simply keeps every state of the channel in memory).
+ * With g(z) = z*sigmoid(z) and s_t the readout before the gate:
+ *   ds_t   = dy_t * g(z_t)                 dz_t = dy_t * s_t * g'(z_t)
+ *   lam_t  = C_t * ds_t + a_{t+1} * lam_{t+1}   (lam_{L-1} gets dh_last added)
+ *   dh_{t-1} path:  dA   += lam_t * h_{t-1} * a_t * delta_t
+ *                   ddelta_t += lam_t * h_{t-1} * a_t * A
+ *   input term:     simplified  bu = delta*B*u:   ddelta += lam*B*u, du += lam*delta*B, dB += lam*delta*u
+ *                   hold        bu = f*B*u, f = expm1(delta*A)/A, df/ddelta = a,
+ *                               df/dA = (delta*a - f)/A (A -> 0: delta^2/2):
+ *                               ddelta += lam*a*B*u, du += lam*f*B, dB += lam*f*u, dA += lam*df/dA*B*u
+ *   readout:        dC_t += ds_t * h_t,  dD += ds_t * u_t,  du_t += D * ds_t
+ *   dh0 = a_0 * lam_0.
+ *
  * Everything is evaluated in double precision, inputs widened exactly, the sum
  * over n taken in ascending order, with libm exp / expm1 (no fast-math).
  */
@@ -40,6 +59,8 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
+
+#include <stdlib.h>
 
 #ifdef _OPENMP
 #include <omp.h>
@@ -223,4 +244,211 @@ int oracle_state_update(int64_t batch, int64_t dim, int64_t N, int type, int dis
     }
     (void)nthreads;
     return 0;
+}
+
+/* d/dz of z*sigmoid(z) = sigmoid(z) * (1 + z*(1 - sigmoid(z))). */
+static double silu_grad(double z)
+{
+    const double sg = 1.0 / (1.0 + exp(-z));
+    return sg * (1.0 + z * (1.0 - sg));
+}
+
+/*
+ * Backward of one channel (b, d). hs: (L+1)*N scratch for the states h_{-1..L-1};
+ * ss: L scratch for the readouts before the gate. Per-channel results go to
+ * du, dde, dz (L each, may be NULL), dA_c (N), dD_c (1), dh0_c (N, may be
+ * NULL); dB and dC (batch, L, N) are accumulated into (may be NULL).
+ */
+static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
+                        int type, int disc,
+                        const void *u, const void *delta,
+                        const double *A, const void *B, const void *C,
+                        const double *D, const void *z, const double *h0,
+                        const double *dy, const double *dh_last,
+                        double *hs, double *ss, double *lam,
+                        double *du, double *dde, double *dz, double *dA_c, double *dD_c,
+                        double *dh0_c, double *dB, double *dC)
+{
+    const double dskip = D ? D[d] : 0.0;
+    /* forward, keeping every state: hs[(t+1)*N + n] = h_t[n] */
+    for (int64_t n = 0; n < N; ++n)
+        hs[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t row = b * L + t;
+        const double ut = load(u, type, row * dim + d);
+        const double dt = load(delta, type, row * dim + d);
+        double st = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double a_dn = A[d * N + n];
+            const double hn = exp(dt * a_dn) * hs[t * N + n] +
+                              input_term(disc, dt, a_dn, load(B, type, row * N + n), ut);
+            hs[(t + 1) * N + n] = hn;
+            st += load(C, type, row * N + n) * hn;
+        }
+        ss[t] = st + dskip * ut;
+    }
+    /* reverse */
+    for (int64_t n = 0; n < N; ++n) {
+        lam[n] = dh_last ? dh_last[(b * dim + d) * N + n] : 0.0;   /* a_{t+1} lam_{t+1} carried */
+        dA_c[n] = 0.0;
+    }
+    double dDacc = 0.0;
+    for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t row = b * L + t;
+        const double ut = load(u, type, row * dim + d);
+        const double dt = load(delta, type, row * dim + d);
+        const double dyt = dy[row * dim + d];
+        double ds = dyt;
+        if (z) {
+            const double zt = load(z, type, row * dim + d);
+            ds = dyt * silu(zt);
+            if (dz)
+                dz[t] = dyt * ss[t] * silu_grad(zt);
+        }
+        dDacc += ds * ut;
+        double dut = dskip * ds;
+        double ddt = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double a_dn = A[d * N + n];
+            const double Bt = load(B, type, row * N + n);
+            const double Ct = load(C, type, row * N + n);
+            const double abar = exp(dt * a_dn);
+            const double l = lam[n] + Ct * ds;                       /* lam_t */
+            const double hprev = hs[t * N + n];                      /* h_{t-1} */
+            const double da = l * hprev;                             /* dloss/dabar_t */
+            ddt += da * abar * a_dn;
+            dA_c[n] += da * abar * dt;
+            if (disc == ORACLE_ZOH) {
+                const double f = (a_dn != 0.0) ? expm1(dt * a_dn) / a_dn : dt;
+                const double dfdA = (a_dn != 0.0) ? (dt * abar - f) / a_dn : 0.5 * dt * dt;
+                ddt += l * abar * Bt * ut;
+                dut += l * f * Bt;
+                dA_c[n] += l * dfdA * Bt * ut;
+                if (dB)
+                    dB[row * N + n] += l * f * ut;
+            } else {
+                ddt += l * Bt * ut;
+                dut += l * dt * Bt;
+                if (dB)
+                    dB[row * N + n] += l * dt * ut;
+            }
+            if (dC)
+                dC[row * N + n] += ds * hs[(t + 1) * N + n];
+            lam[n] = abar * l;                                       /* a_t lam_t for t-1 */
+        }
+        if (du)
+            du[t] = dut;
+        if (dde)
+            dde[t] = ddt;
+    }
+    *dD_c = dDacc;
+    if (dh0_c)
+        for (int64_t n = 0; n < N; ++n)
+            dh0_c[n] = lam[n];
+}
+
+/*
+ * Backward of the selective scan over a set of channels.
+ *
+ *   inputs as oracle_selective_scan; dy: (batch, L, dim) doubles;
+ *   dh_last: (batch, dim, N) doubles or NULL (no gradient on the final state)
+ *   nsel, sel        : channels, each c = b*dim + d (sel == NULL: all, in order)
+ *   du, ddelta, dz   : (nsel, L) doubles, row k = channel sel[k]; each may be NULL
+ *                      (dz is written only when z is given)
+ *   dA_c             : (nsel, N) doubles, this channel's part of dA[d, :]
+ *   dD_c             : (nsel) doubles, this channel's part of dD[d]
+ *   dh0              : (nsel, N) doubles or NULL
+ *   dB, dC           : (batch, L, N) doubles or NULL, set to the sum over the
+ *                      selected channels (all channels give the full gradient)
+ * Returns 0, or -1 for a bad argument or an allocation failure.
+ */
+int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
+                              int type, int disc,
+                              const void *u, const void *delta, const double *A,
+                              const void *B, const void *C, const double *D,
+                              const void *z, const double *h0,
+                              const double *dy, const double *dh_last,
+                              int64_t nsel, const int64_t *sel,
+                              double *du, double *ddelta, double *dz,
+                              double *dA_c, double *dD_c, double *dh0,
+                              double *dB, double *dC, int nthreads)
+{
+    if (batch < 0 || L < 0 || dim < 0 || N < 1 || N > 4096)
+        return -1;
+    if (type != ORACLE_F64 && type != ORACLE_F32 && type != ORACLE_BF16)
+        return -1;
+    if (disc != ORACLE_EULER && disc != ORACLE_ZOH)
+        return -1;
+    if ((L > 0 && (!u || !delta || !B || !C || !dy)) || !A || !dA_c || !dD_c)
+        return -1;
+    if (!sel)
+        nsel = batch * dim;
+    const int64_t bln = batch * L * N;
+    if (dB)
+        for (int64_t i = 0; i < bln; ++i)
+            dB[i] = 0.0;
+    if (dC)
+        for (int64_t i = 0; i < bln; ++i)
+            dC[i] = 0.0;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+    /* per-thread dB / dC sums, added in thread order afterwards */
+    double *acc = NULL;
+    if (dB || dC) {
+        acc = (double *)calloc((size_t)nthreads * 2 * (size_t)(bln > 0 ? bln : 1), sizeof(double));
+        if (!acc)
+            return -1;
+    }
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        double *hs = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N));
+        double *ss = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        double *lam = (double *)malloc(sizeof(double) * (size_t)N);
+        double *myB = acc && dB ? acc + (size_t)tid * 2 * bln : NULL;
+        double *myC = acc && dC ? acc + (size_t)tid * 2 * bln + bln : NULL;
+        if (!hs || !ss || !lam)
+            bad = 1;
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t k = 0; k < nsel; ++k) {
+            const int64_t c = sel ? sel[k] : k;
+            if (bad || c < 0 || c >= batch * dim) {
+                bad = 1;
+                continue;
+            }
+            bwd_channel(c / dim, c % dim, L, dim, N, type, disc, u, delta, A, B, C, D, z, h0,
+                        dy, dh_last, hs, ss, lam,
+                        du ? du + k * L : NULL, ddelta ? ddelta + k * L : NULL,
+                        (dz && z) ? dz + k * L : NULL, dA_c + k * N, dD_c + k,
+                        dh0 ? dh0 + k * N : NULL, myB, myC);
+        }
+        free(hs);
+        free(ss);
+        free(lam);
+    }
+    if (acc) {
+        for (int th = 0; th < nthreads; ++th) {
+            const double *tb = acc + (size_t)th * 2 * bln;
+            for (int64_t i = 0; i < bln; ++i) {
+                if (dB)
+                    dB[i] += tb[i];
+                if (dC)
+                    dC[i] += tb[bln + i];
+            }
+        }
+        free(acc);
+    }
+    return bad ? -1 : 0;
 }

@@ -23,7 +23,10 @@ None of these re-types the oracle's loop. The independent statements are:
   * resuming from the last state reproduces the tail (ricepunchb §4.2:
     only the last hidden state is needed to continue),
   * with h0 = 0 and no gate the output is linear in u and causal,
-  * the SiLU gate and the D skip at points with a closed form.
+  * the SiLU gate and the D skip at points with a closed form,
+  * the backward pass equals central finite differences of the forward oracle
+    (the gradient of sum(dy*y) + sum(dh_last*h_last) by definition), and with
+    dy = 0 the state gradient reduces to the closed form exp(A*sum(delta)).
 """
 from __future__ import annotations
 
@@ -344,6 +347,124 @@ def pin_channel_selection(o):
         assert np.array_equal(ys[i], y[b, :, d]) and np.array_equal(hs[i], hl[b, d])
 
 
+# ---------------------------------------------------------------------------
+# Backward pass
+
+
+def _loss(o, x, dy, dhl, disc):
+    y, hl = o.selective_scan(**x, disc=disc)
+    return float((dy * y).sum() + (dhl * hl).sum())
+
+
+def _fd_grad(o, x, name, dy, dhl, disc, eps=1e-6):
+    arr = x[name]
+    g = np.zeros_like(arr)
+    for idx in np.ndindex(arr.shape):
+        xp = dict(x); xm = dict(x)
+        ap = arr.copy(); ap[idx] += eps
+        am = arr.copy(); am[idx] -= eps
+        xp[name] = ap; xm[name] = am
+        g[idx] = (_loss(o, xp, dy, dhl, disc) - _loss(o, xm, dy, dhl, disc)) / (2 * eps)
+    return g
+
+
+_GRAD_OF = dict(u="du", delta="ddelta", A="dA", B="dB", C="dC", D="dD", z="dz", h0="dh0")
+
+
+def pin_bwd_finite_differences(o):
+    """Every gradient equals the central difference of the forward oracle's loss."""
+    rng = np.random.default_rng(RNG_SEED + 20)
+    for disc in ("euler", "zoh"):
+        x = _case(rng, 2, 6, 2, 3, with_d=True, with_z=True, with_h0=True)
+        dy = rng.standard_normal(x["u"].shape)
+        dhl = rng.standard_normal(x["h0"].shape)
+        g = o.selective_scan_bwd(**x, dy=dy, dh_last=dhl, disc=disc)
+        for name, gname in _GRAD_OF.items():
+            fd = _fd_grad(o, x, name, dy, dhl, disc)
+            assert rel_err(g[gname], fd) < 1e-6, (disc, name, rel_err(g[gname], fd))
+
+
+def pin_bwd_zoh_at_a_zero(o):
+    """The hold rule's A -> 0 branch: its gradient in A (delta^2/2 B u) and the rest
+    match finite differences taken across A = 0."""
+    rng = np.random.default_rng(RNG_SEED + 21)
+    x = _case(rng, 1, 5, 2, 3, with_d=False, with_h0=True)
+    x["A"][0, 1] = 0.0
+    x["A"][1, :] = 0.0
+    dy = rng.standard_normal(x["u"].shape)
+    dhl = rng.standard_normal(x["h0"].shape)
+    g = o.selective_scan_bwd(**x, dy=dy, dh_last=dhl, disc="zoh")
+    for name in ("A", "u", "delta", "B"):
+        fd = _fd_grad(o, x, name, dy, dhl, "zoh", eps=1e-5)
+        assert rel_err(g[_GRAD_OF[name]], fd) < 1e-6, (name, rel_err(g[_GRAD_OF[name]], fd))
+
+
+def pin_bwd_state_only(o):
+    """dy = 0: the loss is dh_last . h_last, so dh0 = exp(A * sum_t delta_t) dh_last
+    exactly, and (simplified rule) du_t = sum_n dh_last exp(A sum_{s>t} delta_s) delta_t B_t."""
+    rng = np.random.default_rng(RNG_SEED + 22)
+    x = _case(rng, 2, 7, 3, 4, with_d=True, with_z=True, with_h0=True)
+    dy = np.zeros_like(x["u"])
+    dhl = rng.standard_normal(x["h0"].shape)
+    g = o.selective_scan_bwd(**x, dy=dy, dh_last=dhl)
+    tot = x["delta"].sum(axis=1)                                   # (b, d)
+    ref = np.exp(x["A"][None] * tot[:, :, None]) * dhl
+    assert rel_err(g["dh0"], ref) < 1e-13
+    after = np.cumsum(x["delta"][:, ::-1], axis=1)[:, ::-1] - x["delta"]   # sum_{s>t} delta_s
+    du = np.einsum("bdn,btdn,btd,btn->btd", dhl, np.exp(x["A"][None, None] * after[..., None]),
+                   x["delta"], x["B"])
+    assert rel_err(g["du"], du) < 1e-12
+    assert np.all(g["dz"] == 0) and np.all(g["dD"] == 0) and np.all(g["dC"] == 0)
+
+
+def pin_bwd_storage_types(o):
+    """bf16 and fp32 storage give the gradients of the same values held in fp64."""
+    rng = np.random.default_rng(RNG_SEED + 23)
+    x = _case(rng, 2, 9, 3, 4, with_d=True, with_z=True, with_h0=True)
+    dy = rng.standard_normal(x["u"].shape)
+    for kind in ("f32", "bf16"):
+        xs, x64 = dict(x), dict(x)
+        for k in ("u", "delta", "B", "C", "z"):
+            v32 = x[k].astype(np.float32)
+            if kind == "f32":
+                xs[k], x64[k] = v32, v32.astype(np.float64)
+            else:
+                bits = v32.view(np.uint32) >> 16
+                xs[k] = bits.astype(np.uint16)
+                x64[k] = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+        for disc in ("euler", "zoh"):
+            ga = o.selective_scan_bwd(**xs, dy=dy, disc=disc)
+            gb = o.selective_scan_bwd(**x64, dy=dy, disc=disc)
+            for k in ga:
+                assert np.array_equal(ga[k], gb[k]), (kind, disc, k)
+
+
+def pin_bwd_channel_selection(o):
+    """Per-channel rows match the full backward; dB, dC of two disjoint channel sets
+    add up to the full ones; the dA and dD shares add up over batch rows."""
+    rng = np.random.default_rng(RNG_SEED + 24)
+    x = _case(rng, 2, 8, 3, 4, with_d=True, with_z=True, with_h0=True)
+    dy = rng.standard_normal(x["u"].shape)
+    full = o.selective_scan_bwd(**x, dy=dy)
+    s1 = [(0, 0), (1, 2), (0, 1)]
+    s2 = [(0, 2), (1, 0), (1, 1)]
+    g1 = o.selective_scan_bwd(**x, dy=dy, channels=s1)
+    g2 = o.selective_scan_bwd(**x, dy=dy, channels=s2)
+    for g, chans in ((g1, s1), (g2, s2)):
+        for i, (b, d) in enumerate(chans):
+            for k in ("du", "ddelta", "dz"):
+                assert np.array_equal(g[k][i], full[k][b, :, d]), k
+            assert np.array_equal(g["dh0"][i], full["dh0"][b, d])
+    for k in ("dB", "dC"):
+        assert rel_err(g1[k] + g2[k], full[k]) < 1e-14, k
+    dA = np.zeros_like(full["dA"]); dD = np.zeros_like(full["dD"])
+    for g, chans in ((g1, s1), (g2, s2)):
+        for i, (b, d) in enumerate(chans):
+            dA[d] += g["dA_c"][i]
+            dD[d] += g["dD_c"][i]
+    assert rel_err(dA, full["dA"]) < 1e-14 and rel_err(dD, full["dD"]) < 1e-14
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_brute_force_storage_types,
@@ -358,5 +479,10 @@ ALL_PINS = [
     pin_decode_is_scan,
     pin_linear_causal,
     pin_gate_and_skip,
+    pin_bwd_finite_differences,
+    pin_bwd_zoh_at_a_zero,
+    pin_bwd_state_only,
+    pin_bwd_storage_types,
+    pin_bwd_channel_selection,
     pin_channel_selection,
 ]

@@ -13,19 +13,22 @@ import oracle
 import pins
 
 MUTANTS = {
-    "decay_sign": ("exp(dt * a_dn);", "exp(-dt * a_dn);"),
+    "decay_sign": ("const double abar = exp(dt * a_dn);\n            const double bu",
+                   "const double abar = exp(-dt * a_dn);\n            const double bu"),
     "drop_delta_in_input": ("return delta * b_tn * u;", "return b_tn * u;"),
     "zoh_missing_delta": ("expm1(delta * a_dn) / a_dn", "expm1(delta * a_dn) / (delta * a_dn)"),
     "zoh_limit_wrong": (": delta;\n        return coef", ": 1.0;\n        return coef"),
     "a_transposed": ("const double a_dn = A[d * N + n];\n            const double abar",
                      "const double a_dn = A[n * dim + d];\n            const double abar"),
-    "b_ignores_time": ("load(B, type, row * N + n), ut)", "load(B, type, b * L * N + n), ut)"),
+    "b_ignores_time": ("const double bu = input_term(disc, dt, a_dn, load(B, type, row * N + n), ut);",
+                       "const double bu = input_term(disc, dt, a_dn, load(B, type, b * L * N + n), ut);"),
     "c_from_b": ("yt += load(C, type, row * N + n) * h[n];", "yt += load(B, type, row * N + n) * h[n];"),
     "readout_before_update": (
         "            h[n] = abar * h[n] + bu;\n            yt += load(C, type, row * N + n) * h[n];",
         "            yt += load(C, type, row * N + n) * h[n];\n            h[n] = abar * h[n] + bu;"),
     "drop_skip": ("yt += dskip * ut;", "yt += 0.0 * ut;"),
-    "skip_wrong_channel": ("const double dskip = D ? D[d] : 0.0;", "const double dskip = D ? D[0] : 0.0;"),
+    "skip_wrong_channel": ("h[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;\n    const double dskip = D ? D[d] : 0.0;",
+                           "h[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;\n    const double dskip = D ? D[0] : 0.0;"),
     "gate_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "gate_is_sigmoid": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     "h0_transposed": ("h[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;",
@@ -38,6 +41,24 @@ MUTANTS = {
     "decode_no_skip": ("yt += (D ? D[d] : 0.0) * xt;", "yt += 0.0 * xt;"),
     "decode_no_gate": ("            yt *= silu(load(z, type, c));", "            yt *= 1.0;"),
     "last_state_not_written": ("hl[n] = h[n];", "hl[n] = 0.0 * h[n];"),
+    # backward
+    "bwd_no_decay_path": ("ddt += da * abar * a_dn;", "ddt += 0.0 * da * abar * a_dn;"),
+    "bwd_dA_missing_delta": ("dA_c[n] += da * abar * dt;", "dA_c[n] += da * abar;"),
+    "bwd_adjoint_not_decayed": ("lam[n] = abar * l;", "lam[n] = l;"),
+    "bwd_dC_uses_prev_state": ("dC[row * N + n] += ds * hs[(t + 1) * N + n];", "dC[row * N + n] += ds * hs[t * N + n];"),
+    "bwd_dB_missing_delta": ("dB[row * N + n] += l * dt * ut;", "dB[row * N + n] += l * ut;"),
+    "bwd_du_missing_delta": ("dut += l * dt * Bt;", "dut += l * Bt;"),
+    "bwd_silu_grad": ("return sg * (1.0 + z * (1.0 - sg));", "return sg;"),
+    "bwd_gate_not_applied": ("ds = dyt * silu(zt);", "ds = dyt;"),
+    "bwd_zoh_dfdA_sign": ("(dt * abar - f) / a_dn", "(f - dt * abar) / a_dn"),
+    "bwd_zoh_dfdA_limit": (": 0.5 * dt * dt;", ": dt * dt;"),
+    "bwd_zoh_ddelta": ("ddt += l * abar * Bt * ut;", "ddt += l * Bt * ut;"),
+    "bwd_zoh_dB": ("dB[row * N + n] += l * f * ut;", "dB[row * N + n] += l * dt * ut;"),
+    "bwd_skip_grad": ("double dut = dskip * ds;", "double dut = dskip * dyt;"),
+    "bwd_dD_ungated": ("dDacc += ds * ut;", "dDacc += dyt * ut;"),
+    "bwd_dh_last_ignored": ("lam[n] = dh_last ? dh_last[(b * dim + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
+    "bwd_hprev_is_current": ("const double hprev = hs[t * N + n];", "const double hprev = hs[(t + 1) * N + n];"),
+    "bwd_readout_adjoint_missing": ("const double l = lam[n] + Ct * ds;", "const double l = lam[n];"),
 }
 
 
@@ -60,7 +81,7 @@ def test_mutant_is_caught(name, tmp_path):
     with open(c_path, "w") as f:
         f.write(src)
     lib = oracle.build(source=c_path, output=os.path.join(tmp_path, "libmutant.so"), strict=False)
-    o = oracle.Oracle(lib)
+    o = oracle.Oracle(lib, threads=1)
     caught = []
     for pin in pins.ALL_PINS:
         try:

@@ -7,4 +7,5 @@ import pins
 
 @pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
 def test_pin(pin):
-    pin(oracle.load())
+    # small cases: one thread each (the suite runs in parallel workers)
+    pin(oracle.Oracle(oracle.load().path, threads=1))
