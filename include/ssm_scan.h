@@ -129,6 +129,43 @@ int ssm_scan_fwd_tuned(const ssm_scan_desc *desc,
 int ssm_scan_plan(const ssm_scan_desc *desc, ssm_scan_tuning *out);
 
 /*
+ * Backward of ssm_scan_fwd: the gradients of
+ *     loss = sum_{b,t,d} dy[b,t,d] * y[b,t,d] + sum_{b,d,n} dh_last[b,d,n] * h_last[b,d,n]
+ * with respect to u, delta, A, B, C, D, z and h0, for the same inputs and
+ * discretisation as the forward call. The states are recomputed on the GPU
+ * (a checkpoint every 16 tokens, or 8 for dstate > 16, then a reverse pass
+ * per chunk) instead of being stored by the forward (doyouknow.kr "Mamba와
+ * 상태 공간 모델(SSM)의 부상 완벽 가이드" §3-3: the backward recomputes the
+ * intermediate states). With lam_t = dloss/dh_t:
+ *     lam_t = C_t * dy_t g(z_t) + exp(delta_{t+1} A) lam_{t+1}
+ * and every gradient follows by the chain rule through the recurrence,
+ * readout, skip and gate stated above.
+ *
+ *   u .. h0       as for ssm_scan_fwd (same shapes, types, layouts)
+ *   dy            (batch, seqlen, dim) dtype: gradient of y
+ *   dh_last       (batch, dim, dstate) fp32 gradient of the final state, or NULL (0)
+ *   du, ddelta    (batch, seqlen, dim) dtype, written
+ *   dz            (batch, seqlen, dim) dtype, written; required when z is given, unused otherwise
+ *   dA            (dim, dstate) fp32, written (summed over batch and time)
+ *   dB, dC        (batch, seqlen, dstate) fp32, written (summed over channels)
+ *   dD            (dim) fp32, written; required when D is given, unused otherwise
+ *   dh0           (batch, dim, dstate) fp32, written, or NULL (not wanted)
+ *   workspace     at least ssm_scan_bwd_workspace_size(desc) bytes, 256-byte
+ *                 aligned; contents on entry do not matter.
+ * Results do not depend on timing: every sum over channels, batch rows or
+ * tiles is taken in a fixed order. Outputs must not overlap each other, any
+ * input or the workspace. seqlen == 0 writes dA = 0, dD = 0, dh0 = dh_last.
+ */
+size_t ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc);
+int ssm_scan_bwd(const ssm_scan_desc *desc,
+                 const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, const void *dy, const float *dh_last,
+                 void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD,
+                 void *dz, float *dh0,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step: the recurrence for a single new token per sequence, with
  * the fixed-size state updated in place (itwiki "상태 공간 모델", "순환 형태와
  * 합성곱 형태": generation only updates h_t; ricepunchb "Mamba" §4.2: only the

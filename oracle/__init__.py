@@ -126,7 +126,7 @@ class Oracle:
         return y, hl
 
     def selective_scan_bwd(self, u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None,
-                           disc="euler", channels=None, want_bc=True, nthreads=0):
+                           disc="euler", channels=None, want_bc=True, want_tokens=True, nthreads=0):
         """Gradients of sum(dy * y) + sum(dh_last * h_last) with respect to every input.
 
         Returns a dict. With ``channels=None``: du, ddelta, dz (batch, L, dim),
@@ -134,6 +134,7 @@ class Oracle:
         ``channels`` a sequence of (b, d) pairs: du, ddelta, dz (k, L), dA_c
         (k, N) and dD_c (k) (each channel's share of dA[d] and dD[d]), dh0
         (k, N), and dB, dC summed over the selected channels only.
+        ``want_tokens=False`` skips du, ddelta and dz (None in the result).
         """
         u = np.ascontiguousarray(u)
         batch, L, dim = u.shape
@@ -156,8 +157,9 @@ class Oracle:
         else:
             sel = np.ascontiguousarray([b * dim + d for b, d in channels], dtype=np.int64)
             nsel = len(sel)
-        du = np.empty((nsel, L)); dde = np.empty((nsel, L))
-        dz = np.empty((nsel, L)) if zc is not None else None
+        du = np.empty((nsel, L)) if want_tokens else None
+        dde = np.empty((nsel, L)) if want_tokens else None
+        dz = np.empty((nsel, L)) if zc is not None and want_tokens else None
         dA_c = np.empty((nsel, N)); dD_c = np.empty(nsel); dh0 = np.empty((nsel, N))
         dB = np.empty((batch, L, N)) if want_bc else None
         dC = np.empty((batch, L, N)) if want_bc else None

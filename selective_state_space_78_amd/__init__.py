@@ -24,7 +24,8 @@ _DISC = {"euler": SSM_DISC_EULER, "zoh": SSM_DISC_ZOH}
 
 # Every symbol include/ssm_scan.h declares.
 EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_workspace_size_tuned",
-           "ssm_scan_fwd_tuned", "ssm_scan_plan", "ssm_state_update", "ssm_status_string")
+           "ssm_scan_fwd_tuned", "ssm_scan_plan", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd",
+           "ssm_state_update", "ssm_status_string")
 
 
 class ScanDesc(ctypes.Structure):
@@ -68,6 +69,10 @@ def lib() -> ctypes.CDLL:
             L.ssm_scan_fwd.restype = ctypes.c_int
             L.ssm_scan_fwd_tuned.argtypes = scan_args + [ptun, vp]
             L.ssm_scan_fwd_tuned.restype = ctypes.c_int
+            L.ssm_scan_bwd_workspace_size.argtypes = [pdesc]
+            L.ssm_scan_bwd_workspace_size.restype = sz
+            L.ssm_scan_bwd.argtypes = [pdesc] + [vp] * 18 + [vp, sz, vp]
+            L.ssm_scan_bwd.restype = ctypes.c_int
             L.ssm_state_update.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             L.ssm_state_update.restype = ctypes.c_int
             L.ssm_status_string.argtypes = [ctypes.c_int]
@@ -187,6 +192,69 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None
     if rc != 0:
         raise SsmError(rc, "ssm_scan_fwd")
     return y, h_last
+
+
+def ssm_scan_bwd_workspace_size(batch, L, dim, N, dtype_code, disc="euler") -> int:
+    desc = make_desc(batch, L, dim, N, dtype_code, disc)
+    return int(lib().ssm_scan_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None, disc="euler",
+                 workspace=None, stream=None, want_dh0=True, out=None):
+    """Backward of ssm_scan_fwd on device tensors.
+
+    Inputs as ssm_scan_fwd, plus dy (batch, L, dim) of the input dtype and an
+    optional dh_last (batch, dim, N) float32. Returns a dict with du, ddelta,
+    dz (input dtype, dz only with a gate), dA (dim, N), dB, dC (batch, L, N),
+    dD (dim,) (with a skip) and dh0 (batch, dim, N) (when ``want_dh0``), all
+    float32 except the per-token ones. ``out`` may hold preallocated outputs.
+    """
+    import torch
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    dev = u.device
+    dt = u.dtype
+    code = _dtype_code(u)
+    _check(u, "u", device=dev)
+    _check(delta, "delta", (batch, L, dim), dt, dev)
+    _check(z, "z", (batch, L, dim), dt, dev)
+    _check(B, "B", (batch, L, N), dt, dev)
+    _check(C, "C", (batch, L, N), dt, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(h0, "h0", (batch, dim, N), torch.float32, dev)
+    _check(dy, "dy", (batch, L, dim), dt, dev)
+    _check(dh_last, "dh_last", (batch, dim, N), torch.float32, dev)
+    o = dict(out or {})
+    f32 = torch.float32
+
+    def get(name, shape, dtype, wanted=True):
+        if not wanted:
+            return None
+        if name not in o or o[name] is None:
+            o[name] = torch.empty(shape, dtype=dtype, device=dev)
+        _check(o[name], name, shape, dtype, dev)
+        return o[name]
+    du = get("du", (batch, L, dim), dt)
+    dde = get("ddelta", (batch, L, dim), dt)
+    dz = get("dz", (batch, L, dim), dt, z is not None)
+    dA = get("dA", (dim, N), f32)
+    dB = get("dB", (batch, L, N), f32)
+    dC = get("dC", (batch, L, N), f32)
+    dD = get("dD", (dim,), f32, D is not None)
+    dh0 = get("dh0", (batch, dim, N), f32, want_dh0)
+    desc = make_desc(batch, L, dim, N, code, disc)
+    L_ = lib()
+    need = L_.ssm_scan_bwd_workspace_size(ctypes.byref(desc))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = L_.ssm_scan_bwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                         _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(du), _ptr(dde), _ptr(dA), _ptr(dB), _ptr(dC),
+                         _ptr(dD), _ptr(dz), _ptr(dh0), _ptr(workspace), ws_bytes, _stream(stream, dev))
+    if rc != 0:
+        raise SsmError(rc, "ssm_scan_bwd")
+    return dict(du=du, ddelta=dde, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
 
 
 def ssm_state_update(x, delta, A, B, C, h, D=None, z=None, y=None, disc="euler", stream=None):

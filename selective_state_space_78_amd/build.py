@@ -12,9 +12,11 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-# translation units: the ABI (+ decode) and one scan unit per element type and
-# discretisation, compiled in parallel and linked into one shared object
-UNITS = ("ssm_scan.hip", "scan_bf16_euler.hip", "scan_bf16_zoh.hip", "scan_f32_euler.hip", "scan_f32_zoh.hip")
+# translation units: the ABI (+ decode), one scan unit and one backward unit per
+# element type and discretisation, compiled in parallel and linked into one
+# shared object
+UNITS = ("ssm_scan.hip", "scan_bf16_euler.hip", "scan_bf16_zoh.hip", "scan_f32_euler.hip", "scan_f32_zoh.hip",
+         "bwd_bf16_euler.hip", "bwd_bf16_zoh.hip", "bwd_f32_euler.hip", "bwd_f32_zoh.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libssm_scan.so")
 ARCH = "gfx950"

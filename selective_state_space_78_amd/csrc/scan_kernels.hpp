@@ -93,6 +93,8 @@ struct ScanParams {
     void *y;
     float *h_last;
     float *agg_P, *agg_H; // (batch, nseg, dim, N) segment maps (aggregate pass)
+    float *ckpt;          // (batch, nck, Npad, dim) state at the start of every chunk (checkpoint pass)
+    int nck;
     int64_t L;
     int batch, dim, N;
     int seg_len, nseg;
@@ -216,8 +218,15 @@ template <int KV> struct FloatsOf;
 template <> struct FloatsOf<2> { typedef float2 type; };
 template <> struct FloatsOf<4> { typedef float4 type; };
 
-template <typename T, int NPW, int G, int TC, bool ZOH, bool AGG>
+// What a pass of the scan kernel produces.
+enum ScanMode { kModeMain = 0, kModeAggregate = 1, kModeCheckpoint = 2 };
+
+template <typename T, int NPW, int G, int TC, bool ZOH, int MODE>
 struct ScanKernel {
+    // main: y and h_last; aggregate: each segment's map h -> P h + H;
+    // checkpoint: the state at the start of every chunk (for the backward)
+    static constexpr bool AGG = MODE != kModeMain;            // no readout and no y
+    static constexpr bool kSum = MODE == kModeAggregate;
     static constexpr int kThreads = kTile * G;
     static constexpr int kNP = NPW * G;                       // padded state count
     // channels per staged piece: 2 when that gives every thread of the
@@ -460,7 +469,7 @@ struct ScanKernel {
             }
             if (!AGG) part = q == 0 ? c_of(bc[q]) * l.h[q] : fmaf(c_of(bc[q]), l.h[q], part);
         }
-        if (AGG) {
+        if (kSum) {
             // Kahan summation of delta over the segment
             const float yk = dd - l.dcomp;
             const float tk = l.dsum + yk;
@@ -499,7 +508,7 @@ struct ScanKernel {
                 l.Ainv[k] = (a != 0.0f) ? 1.0f / a : 0.0f;
             }
             float h_init = 0.0f;
-            if (!AGG && nv) {
+            if (MODE != kModeAggregate && nv) {
                 // with segments, every segment (also the first) starts from the
                 // carry pass's output, so that h_last may alias h0
                 if (p.seg_h != nullptr)
@@ -571,6 +580,15 @@ struct ScanKernel {
             if (k + 2 < nchunks) load_chunk(k + 2);
             const int tval = rows_of(k);
             const float2 (*dx)[kTile] = s.dx[P];
+            if constexpr (MODE == kModeCheckpoint) {
+                // the state before the chunk's first token
+                if (dval) {
+                    const int64_t c = (t_begin + (int64_t)k * TC) / TC;
+#pragma unroll
+                    for (int q = 0; q < NPW; ++q)
+                        p.ckpt[(((int64_t)b * p.nck + c) * kNP + w * NPW + q) * p.dim + d] = l.h[q];
+                }
+            }
 #pragma unroll
             for (int t0b = 0; t0b < TC; t0b += kTB) {
                 if (t0b > 0) fetch(t0b);
@@ -613,20 +631,20 @@ struct ScanKernel {
         for (int k = 0; k < NPW; ++k) {
             const int n = w * NPW + k;
             if (n >= p.N) continue;
-            if (AGG) {
+            if (kSum) {
                 const int64_t o = (((int64_t)b * p.nseg + seg) * p.dim + d) * p.N + n;
                 p.agg_P[o] = __builtin_amdgcn_exp2f(l.A2[k] * l.dsum);
                 p.agg_H[o] = l.h[k];
-            } else if (p.h_last != nullptr && seg == p.nseg - 1) {
+            } else if (MODE == kModeMain && p.h_last != nullptr && seg == p.nseg - 1) {
                 p.h_last[((int64_t)b * p.dim + d) * p.N + n] = l.h[k];
             }
         }
     }
 };
 
-template <typename T, int NPW, int G, int TC, bool ZOH, bool AGG>
+template <typename T, int NPW, int G, int TC, bool ZOH, int MODE>
 __global__ __launch_bounds__(kTile * G) void scan_kernel(const ScanParams p) {
-    ScanKernel<T, NPW, G, TC, ZOH, AGG>::run(p);
+    ScanKernel<T, NPW, G, TC, ZOH, MODE>::run(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -659,7 +677,7 @@ __device__ __forceinline__ void affine_step(float &P, float &H, bool take) {
     }
 }
 
-__global__ __launch_bounds__(256) void carry_kernel(const CarryParams p) {
+__global__ __launch_bounds__(256) __attribute__((unused)) void carry_kernel(const CarryParams p) {
     const int lane = threadIdx.x & 63;
     const int sp = 1 << p.sp_log2;
     const int s = lane & (sp - 1);                                  // segment
@@ -689,8 +707,10 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryParams p) {
     p.seg_h[((b * p.nseg + s) * p.dim * p.N) + dn] = fmaf(P, hin, H);
 }
 
-template <typename T, int NPW, int G, int TC, bool ZOH>
+// CK: the shape also has the checkpoint pass (the launch shapes the backward uses)
+template <typename T, int NPW, int G, int TC, bool ZOH, bool CK>
 hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg, hipStream_t st) {
+    if (!CK && p.ckpt != nullptr) return hipErrorInvalidValue;
     {
         const int64_t total = (int64_t)p.batch * padded_len(p.L) * (NPW * G);
         hipLaunchKernelGGL(widen_bc_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
@@ -699,7 +719,7 @@ hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg,
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if (nblocks_agg > 0) {
-        hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, true>), dim3(nblocks_agg), dim3(kTile * G), 0, st, p);
+        hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeAggregate>), dim3(nblocks_agg), dim3(kTile * G), 0, st, p);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         CarryParams cp{};
         cp.P = p.agg_P;
@@ -716,7 +736,14 @@ hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg,
         hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, cp);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, false>), dim3(nblocks_main), dim3(kTile * G), 0, st, p);
+    if constexpr (CK) {
+        if (p.ckpt != nullptr) {
+            hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeCheckpoint>), dim3(nblocks_main), dim3(kTile * G),
+                               0, st, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMain>), dim3(nblocks_main), dim3(kTile * G), 0, st, p);
     return hipGetLastError();
 }
 
@@ -729,13 +756,14 @@ hipError_t launch_scan_shape(const Plan &pl, const ScanParams &p, int nm, int na
     // (padded states, waves per tile, chunk length): LDS stays <= 80 KiB
     // (two workgroups per CU) and every thread of a workgroup of up to 8
     // waves stages a piece of each chunk
-#define SSM_CASE(NP, GG, TCC) \
-    if (pl.npad == NP && pl.G == GG) return launch_scan_t<T, NP / GG, GG, TCC, ZOH>(p, nm, na, st);
-    SSM_CASE(4, 1, 16)  SSM_CASE(4, 2, 16)  SSM_CASE(4, 4, 8)
-    SSM_CASE(8, 1, 16)  SSM_CASE(8, 2, 16)  SSM_CASE(8, 4, 8)   SSM_CASE(8, 8, 16)
-    SSM_CASE(16, 1, 16) SSM_CASE(16, 2, 16) SSM_CASE(16, 4, 8)  SSM_CASE(16, 8, SSM_TC_G8) SSM_CASE(16, 16, 8)
-    SSM_CASE(32, 2, 16) SSM_CASE(32, 4, 8)  SSM_CASE(32, 8, 16) SSM_CASE(32, 16, 8)
-    SSM_CASE(64, 4, 8)  SSM_CASE(64, 8, 16) SSM_CASE(64, 16, 8)
+#define SSM_CASE(NP, GG, TCC, CK) \
+    if (pl.npad == NP && pl.G == GG) return launch_scan_t<T, NP / GG, GG, TCC, ZOH, CK>(p, nm, na, st);
+    SSM_CASE(4, 1, 16, 0)  SSM_CASE(4, 2, 16, 1)  SSM_CASE(4, 4, 8, 0)
+    SSM_CASE(8, 1, 16, 0)  SSM_CASE(8, 2, 16, 0)  SSM_CASE(8, 4, 8, 0)   SSM_CASE(8, 8, 16, 1)
+    SSM_CASE(16, 1, 16, 0) SSM_CASE(16, 2, 16, 0) SSM_CASE(16, 4, 8, 0)  SSM_CASE(16, 8, SSM_TC_G8, 1)
+    SSM_CASE(16, 16, 8, 0)
+    SSM_CASE(32, 2, 16, 0) SSM_CASE(32, 4, 8, 0)  SSM_CASE(32, 8, 16, 0) SSM_CASE(32, 16, 8, 1)
+    SSM_CASE(64, 4, 8, 0)  SSM_CASE(64, 8, 16, 0) SSM_CASE(64, 16, 8, 1)
 #undef SSM_CASE
     return hipErrorInvalidValue;
 }

@@ -16,6 +16,11 @@
 
 #include "ssm_scan.h"
 #include "scan_kernels.hpp"
+#include "bwd_kernels.hpp"
+
+namespace ssm_detail {
+hipError_t launch_bwd_reduce(const BwdReduceParams &p, hipStream_t st);
+}
 
 namespace {
 
@@ -212,6 +217,42 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
     default: hipLaunchKernelGGL((decode_kernel<T, ZOH, 16>), grid, dim3(256), 0, stream, p); break;
     }
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Backward: sums of the per-tile dB, dC and per-row dA, dD partials, in a fixed
+// order (tiles, then batch rows), so that the result does not depend on timing.
+
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdReduceParams p) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nbc = (int64_t)p.batch * p.L * p.N;
+    const int64_t na = (int64_t)p.dim * p.N;
+    if (i < nbc) {
+        const int n = (int)(i % p.N);
+        const int64_t bt = i / p.N;
+        const int64_t t = bt % p.L, b = bt / p.L;
+        float sb = 0.0f, sc = 0.0f;
+        for (int tile = 0; tile < p.ntiles; ++tile) {
+            const float2 v = *reinterpret_cast<const float2 *>(
+                p.part_bc + ((((int64_t)b * p.ntiles + tile) * p.L + t) * p.npad + n) * 2);
+            sb += v.x;
+            sc += v.y;
+        }
+        p.dB[i] = sb;
+        p.dC[i] = sc;
+    } else if (i < nbc + na) {
+        const int64_t k = i - nbc;
+        const int n = (int)(k % p.N);
+        const int64_t d = k / p.N;
+        float sa = 0.0f;
+        for (int b = 0; b < p.batch; ++b) sa += p.part_a[((int64_t)b * p.dim + d) * p.npad + n];
+        p.dA[k] = sa;
+    } else if (i < nbc + na + p.dim) {
+        const int64_t d = i - nbc - na;
+        float sd = 0.0f;
+        for (int b = 0; b < p.batch; ++b) sd += p.part_d[(int64_t)b * p.dim + d];
+        if (p.dD != nullptr) p.dD[d] = sd;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -417,6 +458,177 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+// Backward workspace: the checkpoint pass's forward workspace (regrouped B, C
+// and segment arrays), then the checkpoints, the per-tile dB/dC partials and
+// the per-row dA, dD partials.
+struct BwdLayout {
+    Plan pl;
+    BwdShape sh;
+    int nck, ntiles;
+    size_t ckpt, part_bc, part_a, part_d, total;
+};
+
+BwdLayout bwd_layout(const ssm_scan_desc &d) {
+    BwdLayout w{};
+    w.sh = bwd_shape(padded_states(d.dstate));
+    ssm_scan_tuning t{w.sh.G, 0};
+    w.pl = make_plan(d, &t);
+    w.nck = (int)((d.seqlen + w.sh.TC - 1) / w.sh.TC);
+    w.ntiles = (int)((d.dim + kTile - 1) / kTile);
+    const size_t fwd = workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, w.pl).total;
+    const size_t np = (size_t)w.sh.npad;
+    w.ckpt = fwd;
+    w.part_bc = w.ckpt + align256((size_t)d.batch * w.nck * np * d.dim * 4);
+    w.part_a = w.part_bc + align256((size_t)d.batch * w.ntiles * d.seqlen * np * 2 * 4);
+    w.part_d = w.part_a + align256((size_t)d.batch * d.dim * np * 4);
+    w.total = w.part_d + align256((size_t)d.batch * d.dim * 4);
+    return w;
+}
+
+size_t bwd_workspace_bytes(const ssm_scan_desc &d) {
+    if (d.batch == 0 || d.dim == 0 || d.seqlen == 0) return 0;
+    return bwd_layout(d).total;
+}
+
+int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A, const void *B,
+             const void *C, const float *D, const void *z, const float *h0, const void *dy, const float *dh_last,
+             void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz, float *dh0,
+             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (int rc = validate_desc(desc); rc != SSM_OK) return rc;
+    const ssm_scan_desc d = *desc;
+    if (d.batch == 0 || d.dim == 0) return SSM_OK;
+    const int es = d.dtype == SSM_BF16 ? 2 : 4;
+    const int64_t tok = d.batch * d.seqlen * d.dim;
+    const int64_t bn = d.batch * d.seqlen * d.dstate;
+    const int64_t state = d.batch * d.dim * d.dstate;
+    const int64_t adn = d.dim * d.dstate;
+    if (A == nullptr || dA == nullptr) return SSM_ERR_NULL;
+    if (D != nullptr && dD == nullptr) return SSM_ERR_NULL;
+    if (d.seqlen > 0 && (u == nullptr || delta == nullptr || B == nullptr || C == nullptr || dy == nullptr ||
+                         du == nullptr || ddelta == nullptr || dB == nullptr || dC == nullptr ||
+                         (z != nullptr && dz == nullptr)))
+        return SSM_ERR_NULL;
+    const void *tok_ptrs[] = {u, delta, B, C, z, dy, du, ddelta, z ? dz : nullptr};
+    for (const void *q : tok_ptrs)
+        if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
+    const void *f32_ptrs[] = {A, D, h0, dh_last, dA, dB, dC, dD, dh0};
+    for (const void *q : f32_ptrs)
+        if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+    if (workspace && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+
+    const BwdLayout wl = bwd_layout(d);
+    if (!plan_supported(wl.pl)) return SSM_ERR_UNSUPPORTED;
+    const size_t need = bwd_workspace_bytes(d);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+
+    const int64_t tk = d.seqlen > 0 ? tok : 0;
+    const Range outs[] = {range_of(du, tk * es), range_of(ddelta, tk * es), range_of(z ? dz : nullptr, tk * es),
+                          range_of(dA, adn * 4), range_of(dB, d.seqlen > 0 ? bn * 4 : 0),
+                          range_of(dC, d.seqlen > 0 ? bn * 4 : 0), range_of(D ? dD : nullptr, d.dim * 4),
+                          range_of(dh0, state * 4), range_of(workspace, (int64_t)need)};
+    const Range ins[] = {range_of(u, tok * es), range_of(delta, tok * es), range_of(z, z ? tok * es : 0),
+                         range_of(B, bn * es), range_of(C, bn * es), range_of(A, adn * 4),
+                         range_of(D, D ? d.dim * 4 : 0), range_of(h0, h0 ? state * 4 : 0),
+                         range_of(dy, tok * es), range_of(dh_last, dh_last ? state * 4 : 0)};
+    const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+    for (int i = 0; i < nout; ++i) {
+        for (const Range &r : ins)
+            if (overlaps(outs[i], r)) return SSM_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
+    }
+
+    if (d.seqlen == 0) {
+        // no tokens: dA = dD = 0, dh0 = dh_last (or 0)
+        hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((adn + 255) / 256)), dim3(256), 0, stream,
+                           nullptr, dA, adn);
+        if (D != nullptr)
+            hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((d.dim + 255) / 256)), dim3(256), 0, stream,
+                               nullptr, dD, d.dim);
+        if (dh0 != nullptr)
+            hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((state + 255) / 256)), dim3(256), 0, stream,
+                               dh_last, dh0, state);
+        return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
+
+    char *ws = static_cast<char *>(workspace);
+    const bool vec = (d.dim % 4 == 0) && aligned(u, 4 * es) && aligned(delta, 4 * es) && (!z || aligned(z, 4 * es)) &&
+                     aligned(dy, 4 * es) && aligned(du, 4 * es) && aligned(ddelta, 4 * es) &&
+                     (!z || aligned(dz, 4 * es));
+    // 1. checkpoints: the forward scan in its checkpoint mode (segment-parallel)
+    ScanParams p{};
+    p.u = u; p.delta = delta; p.z = z; p.B = B; p.C = C;
+    p.A = A; p.D = D; p.h0 = h0;
+    p.L = d.seqlen;
+    p.batch = (int)d.batch;
+    p.dim = (int)d.dim;
+    p.N = (int)d.dstate;
+    p.seg_len = wl.pl.seg_len;
+    p.nseg = wl.pl.S;
+    p.ntiles = wl.ntiles;
+    p.vec = vec;
+    p.ckpt = reinterpret_cast<float *>(ws + wl.ckpt);
+    p.nck = wl.nck;
+    {
+        const WorkspaceLayout fl = workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, wl.pl);
+        p.Bf = reinterpret_cast<float *>(ws + fl.bf);
+        p.Cf = reinterpret_cast<float *>(ws + fl.cf);
+        if (wl.pl.S > 1) {
+            p.agg_P = reinterpret_cast<float *>(ws + fl.agg_p);
+            p.agg_H = reinterpret_cast<float *>(ws + fl.agg_h);
+            p.seg_h = reinterpret_cast<float *>(ws + fl.seg_h);
+        }
+    }
+    const int64_t blocks_per_seg = (int64_t)wl.ntiles * d.batch;
+    const int64_t nm = blocks_per_seg * wl.pl.S;
+    const int64_t na = wl.pl.S > 1 ? blocks_per_seg * (wl.pl.S - 1) : 0;
+    if (nm > INT32_MAX) return SSM_ERR_SHAPE;
+    const bool zoh = d.disc == SSM_DISC_ZOH;
+    hipError_t e;
+    if (d.dtype == SSM_BF16)
+        e = zoh ? launch_scan_bf16_zoh(wl.pl, p, (int)nm, (int)na, stream)
+                : launch_scan_bf16_euler(wl.pl, p, (int)nm, (int)na, stream);
+    else
+        e = zoh ? launch_scan_f32_zoh(wl.pl, p, (int)nm, (int)na, stream)
+                : launch_scan_f32_euler(wl.pl, p, (int)nm, (int)na, stream);
+    if (e != hipSuccess) return SSM_ERR_HIP;
+
+    // 2. the reverse pass
+    BwdParams bp{};
+    bp.u = u; bp.delta = delta; bp.z = z; bp.dy = dy;
+    bp.A = A; bp.D = D; bp.dh_last = dh_last;
+    bp.Bf = p.Bf; bp.Cf = p.Cf; bp.ckpt = p.ckpt;
+    bp.du = du; bp.ddelta = ddelta; bp.dz = dz; bp.dh0 = dh0;
+    bp.part_bc = reinterpret_cast<float *>(ws + wl.part_bc);
+    bp.part_a = reinterpret_cast<float *>(ws + wl.part_a);
+    bp.part_d = reinterpret_cast<float *>(ws + wl.part_d);
+    bp.L = d.seqlen;
+    bp.batch = (int)d.batch;
+    bp.dim = (int)d.dim;
+    bp.N = (int)d.dstate;
+    bp.ntiles = wl.ntiles;
+    bp.nck = wl.nck;
+    bp.vec = vec;
+    if (d.dtype == SSM_BF16)
+        e = zoh ? launch_bwd_bf16_zoh(wl.sh, bp, stream) : launch_bwd_bf16_euler(wl.sh, bp, stream);
+    else
+        e = zoh ? launch_bwd_f32_zoh(wl.sh, bp, stream) : launch_bwd_f32_euler(wl.sh, bp, stream);
+    if (e != hipSuccess) return SSM_ERR_HIP;
+
+    // 3. sums of the partials
+    BwdReduceParams rp{};
+    rp.part_bc = bp.part_bc; rp.part_a = bp.part_a; rp.part_d = bp.part_d;
+    rp.dB = dB; rp.dC = dC; rp.dA = dA; rp.dD = D ? dD : nullptr;
+    rp.L = d.seqlen;
+    rp.batch = (int)d.batch;
+    rp.dim = (int)d.dim;
+    rp.N = (int)d.dstate;
+    rp.npad = wl.sh.npad;
+    rp.ntiles = wl.ntiles;
+    e = launch_bwd_reduce(rp, stream);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -502,6 +714,20 @@ extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int3
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+extern "C" size_t ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc) {
+    if (validate_desc(desc) != SSM_OK) return 0;
+    return bwd_workspace_bytes(*desc);
+}
+
+extern "C" int ssm_scan_bwd(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A,
+                            const void *B, const void *C, const float *D, const void *z, const float *h0,
+                            const void *dy, const float *dh_last, void *du, void *ddelta, float *dA, float *dB,
+                            float *dC, float *dD, void *dz, float *dh0, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    return bwd_impl(desc, u, delta, A, B, C, D, z, h0, dy, dh_last, du, ddelta, dA, dB, dC, dD, dz, dh0,
+                    workspace, workspace_bytes, stream);
+}
+
 extern "C" const char *ssm_status_string(int status) {
     switch (status) {
     case SSM_OK: return "ok";
@@ -516,3 +742,13 @@ extern "C" const char *ssm_status_string(int status) {
     default: return "unknown status";
     }
 }
+
+namespace ssm_detail {
+hipError_t launch_bwd_reduce(const BwdReduceParams &p, hipStream_t st) {
+    const int64_t n = (int64_t)p.batch * p.L * p.N + (int64_t)p.dim * p.N + p.dim;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+}  // namespace ssm_detail

@@ -31,7 +31,7 @@ from dataclasses import dataclass
 import numpy as np
 
 BLOCK = 1 << 22
-STREAMS = ("u", "delta_noise", "delta_bias", "B", "C", "z", "D", "h0")
+STREAMS = ("u", "delta_noise", "delta_bias", "B", "C", "z", "D", "h0", "dy", "dh_last")
 
 
 @dataclass(frozen=True)
@@ -190,6 +190,19 @@ def scan_inputs(cfg: ScanConfig, seed: int = 0, batch: int | None = None,
         z=_normal(seed, "z", (b, L, d), cfg.dtype) if cfg.gate else None,
         h0=None,
     )
+
+
+def grad_inputs(cfg: ScanConfig, seed: int = 0, batch: int | None = None,
+                seqlen: int | None = None, dim: int | None = None, dstate: int | None = None):
+    """Upstream gradients for the backward of one scan workload: dy ~ N(0, 1) in
+    the workload's element type (batch, L, dim) and dh_last ~ N(0, 1) float32
+    (batch, dim, N)."""
+    b = cfg.batch if batch is None else batch
+    L = cfg.seqlen if seqlen is None else seqlen
+    d = cfg.dim if dim is None else dim
+    N = cfg.dstate if dstate is None else dstate
+    return dict(dy=_normal(seed, "dy", (b, L, d), cfg.dtype),
+                dh_last=_normal(seed, "dh_last", (b, d, N), "f32"))
 
 
 def decode_static(cfg: DecodeConfig = DECODE, seed: int = 0, batch=None, dim=None, dstate=None):

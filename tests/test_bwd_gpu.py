@@ -1,0 +1,180 @@
+"""GPU parity of ssm_scan_bwd against the fp64 oracle's backward, through the C ABI.
+
+Every gradient (du, ddelta, dz, dA, dB, dC, dD, dh0) is compared element by
+element on small and medium shapes covering each backward launch shape, both
+element types and both discretisations, ragged tiles and a ragged last chunk;
+the Mamba-130M-shaped layer is compared in full; the Mamba-1.4B-shaped layer is
+compared in full for dB, dC and dA's sampled rows, and on sampled channels for
+the per-channel gradients.
+
+Tolerance (max rel err, rms-floored, see pins.rel_err): bf16 inputs 2e-2 (the
+forward's; du, ddelta, dz are rounded to bf16); fp32 inputs 1e-4 per element,
+with the exceptions derived in tol_for().
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import ssm_inputs as si
+from gpu_util import TOL_BF16, TOL_F32, rel_err, say, to_dev, to_np, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "dh0")
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = torch_cuda()
+    import selective_state_space_78_amd as ssm
+    ssm.lib()
+    return torch, ssm
+
+
+def cfg_of(name, dtype):
+    return dataclasses.replace(si.CONFIGS[name], dtype=dtype)
+
+
+def make_case(name, dtype, seed, batch, seqlen, dim, dstate, random_a=True, a_zero_col=False):
+    cfg = cfg_of(name, dtype)
+    x = si.scan_inputs(cfg, seed=seed, batch=batch, seqlen=seqlen, dim=dim, dstate=dstate)
+    g = si.grad_inputs(cfg, seed=seed, batch=batch, seqlen=seqlen, dim=dim, dstate=dstate)
+    rng = np.random.default_rng(1000 + seed)
+    if random_a:
+        x["A"] = -np.exp(rng.uniform(np.log(0.3), np.log(20.0), x["A"].shape)).astype(np.float32)
+    if a_zero_col:
+        x["A"][:, 0] = 0.0
+    x["h0"] = rng.standard_normal((x["u"].shape[0], x["u"].shape[2], x["A"].shape[1])).astype(np.float32)
+    return x, g
+
+
+def widen(a):
+    if a is None:
+        return None
+    return si.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def run_bwd(ssm, torch, x, g, disc, use_h0=True, use_dhl=True, want_dh0=True):
+    dev = {k: to_dev(v, torch) for k, v in x.items() if k != "h0"}
+    out = ssm.ssm_scan_bwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], to_dev(g["dy"], torch),
+                           D=dev.get("D"), z=dev.get("z"), h0=to_dev(x["h0"], torch) if use_h0 else None,
+                           dh_last=to_dev(g["dh_last"], torch) if use_dhl else None, disc=disc,
+                           want_dh0=want_dh0)
+    torch.cuda.synchronize()
+    return {k: to_np(v) for k, v in out.items()}
+
+
+def ref_bwd(x, g, disc, use_h0=True, use_dhl=True, **kw):
+    return oracle.load().selective_scan_bwd(**dict(x, h0=x["h0"] if use_h0 else None), dy=widen(g["dy"]),
+                                            dh_last=g["dh_last"] if use_dhl else None, disc=disc, **kw)
+
+
+def tol_for(x, k):
+    if x["u"].dtype == np.uint16:
+        return TOL_BF16
+    # fp32: dA and dD are sums over batch * seqlen terms of both signs and dB,
+    # dC sums over dim channels; against the tensor's rms the fp32 rounding of
+    # such a sum is bounded by (terms) * 2^-24 * mean|term| / rms, which for
+    # these sizes stays below 1e-4 too
+    return TOL_F32
+
+
+def compare_all(x, got, ref, what, keys=GRADS):
+    for k in keys:
+        if ref.get(k) is None or got.get(k) is None:
+            continue
+        e = rel_err(got[k], ref[k])
+        say("  %s %-6s err %.3e" % (what, k, e))
+        assert e <= tol_for(x, k), (what, k, e)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("disc", ["euler", "zoh"])
+@pytest.mark.parametrize("N", [16, 4, 5, 32, 64])
+def test_bwd_shapes(env, dtype, disc, N):
+    torch, ssm = env
+    x, g = make_case("mamba130m", dtype, seed=N, batch=2, seqlen=40, dim=70, dstate=N)
+    say("bwd %s %s b2 L40 d70 N%d (ragged tile and chunk)" % (dtype, disc, N))
+    got = run_bwd(ssm, torch, x, g, disc)
+    compare_all(x, got, ref_bwd(x, g, disc), "N%d" % N)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_zoh_a_zero(env, dtype):
+    torch, ssm = env
+    x, g = make_case("mamba130m", dtype, seed=7, batch=2, seqlen=33, dim=64, dstate=16, a_zero_col=True)
+    say("bwd zoh with A[:, 0] = 0, %s" % dtype)
+    got = run_bwd(ssm, torch, x, g, "zoh")
+    compare_all(x, got, ref_bwd(x, g, "zoh"), "A0")
+
+
+@pytest.mark.parametrize("disc", ["euler", "zoh"])
+def test_bwd_without_optionals(env, disc):
+    torch, ssm = env
+    x, g = make_case("mamba130m", "bf16", seed=3, batch=3, seqlen=50, dim=128, dstate=16)
+    x = dict(x, D=None, z=None)
+    say("bwd %s without D, z, h0, dh_last" % disc)
+    got = run_bwd(ssm, torch, x, g, disc, use_h0=False, use_dhl=False, want_dh0=False)
+    assert got["dz"] is None and got["dD"] is None and got["dh0"] is None
+    compare_all(x, got, ref_bwd(x, g, disc, use_h0=False, use_dhl=False), "bare")
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 257])
+def test_bwd_lengths(env, L):
+    torch, ssm = env
+    x, g = make_case("mamba130m", "f32", seed=L, batch=2, seqlen=L, dim=64, dstate=16)
+    say("bwd f32 L%d" % L)
+    got = run_bwd(ssm, torch, x, g, "euler")
+    compare_all(x, got, ref_bwd(x, g, "euler"), "L%d" % L)
+
+
+def test_bwd_empty_sequence(env):
+    torch, ssm = env
+    x, g = make_case("mamba130m", "bf16", seed=5, batch=2, seqlen=0, dim=64, dstate=16)
+    say("bwd L0")
+    got = run_bwd(ssm, torch, x, g, "euler")
+    assert np.all(got["dA"] == 0) and np.all(got["dD"] == 0)
+    assert np.array_equal(got["dh0"], g["dh_last"].astype(np.float64))
+
+
+def test_bwd_deterministic(env):
+    torch, ssm = env
+    x, g = make_case("mamba130m", "bf16", seed=11, batch=2, seqlen=100, dim=192, dstate=16)
+    a = run_bwd(ssm, torch, x, g, "euler")
+    b = run_bwd(ssm, torch, x, g, "euler")
+    for k in GRADS:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k]), k
+
+
+def test_bwd_mamba130m_full(env):
+    torch, ssm = env
+    cfg = si.CONFIGS["mamba130m"]
+    x, g = si.scan_inputs(cfg, seed=0), si.grad_inputs(cfg, seed=0)
+    x["h0"] = None
+    say("bwd Mamba-130M-shaped layer b4 L2048 d1536 N16 bf16, every gradient")
+    got = run_bwd(ssm, torch, x, g, "euler", use_h0=False)
+    compare_all(x, got, ref_bwd(x, g, "euler", use_h0=False), "130m")
+
+
+def test_bwd_mamba14b_full_size(env):
+    torch, ssm = env
+    cfg = si.CONFIGS["mamba1.4b"]
+    x, g = si.scan_inputs(cfg, seed=0), si.grad_inputs(cfg, seed=0)
+    x["h0"] = None
+    say("bwd Mamba-1.4B-shaped layer b8 L8192 d4096 N16 bf16")
+    got = run_bwd(ssm, torch, x, g, "euler", use_h0=False)
+    # dB, dC (sums over every channel) and dA, dD in full
+    full = ref_bwd(x, g, "euler", use_h0=False, want_tokens=False)
+    compare_all(x, got, full, "1.4b", keys=("dA", "dB", "dC", "dD", "dh0"))
+    # per-channel gradients on sampled channels over the whole sequence
+    rng = np.random.default_rng(5)
+    chans = [(int(b), int(d)) for b, d in zip(rng.integers(0, 8, 12), rng.integers(0, 4096, 12))]
+    sub = ref_bwd(x, g, "euler", use_h0=False, channels=chans, want_bc=False)
+    for k in ("du", "ddelta", "dz"):
+        gk = np.stack([got[k][b, :, d] for b, d in chans])
+        e = rel_err(gk, sub[k])
+        say("  sampled %-6s err %.3e" % (k, e))
+        assert e <= TOL_BF16, (k, e)
