@@ -5,11 +5,11 @@ One step = one ssm_scan_fwd over the Mamba-1.4B-shaped layer workload
 state; D skip, SiLU gate, final state written), inputs resident in HBM.
 Prints one JSON line: selective-scan Gtokens*ch/s, the dominant kernel's
 roofline position (measured with HIP events on the stream it runs on), the
-algorithmic HBM rate, the decode step measured alongside, and the fp64 CPU
-oracle timed on a bounded sample of the same workload (whose outputs are
-also compared with the GPU's timed outputs).
+algorithmic HBM rate, the backward of the same scan and the decode step
+measured alongside, and the fp64 CPU oracle timed on a bounded sample of the
+same workload (whose outputs are also compared with the GPU's timed outputs).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-bwd] [--no-decode]
 """
 from __future__ import annotations
 
@@ -162,6 +162,39 @@ def bench_decode(torch, ssm, steps=200, warmup=10, nsets=16):
     }
 
 
+def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2):
+    """Time ssm_scan_bwd (checkpoint pass + reverse pass + reduction) on the workload."""
+    g = si.grad_inputs(cfg, seed=0)
+    dy = to_dev(g["dy"], torch)
+    dhl = to_dev(g["dh_last"], torch)
+    need = ssm.ssm_scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, ssm.SSM_BF16)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    out = {}
+
+    def call():
+        r = ssm.ssm_scan_bwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dy, D=dev["D"], z=dev["z"],
+                             dh_last=dhl, workspace=ws, out=out)
+        out.update(r)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    return {
+        "workload": "backward of the same scan: gradients of u, delta, A, B, C, D, z, h0 from dy and dh_last",
+        "ms_per_call": ms,
+        "Gtokens*ch/s": cfg.tokens_ch / (ms * 1e-3) / 1e9,
+        "workspace_bytes": need,
+        "calls": steps,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +202,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--tuning", type=str, default=None, help="state_groups,segments")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=WORKLOAD,
                     help="scan workload of the timed step (the default is the headline one)")
@@ -271,6 +305,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = 1 << 30
+    if not args.no_bwd:
+        print("bench: backward", file=sys.stderr, flush=True)
+        out["backward"] = bench_backward(torch, ssm, cfg, dev)
     if not args.no_decode:
         print("bench: decode", file=sys.stderr, flush=True)
         out["decode"] = bench_decode(torch, ssm)

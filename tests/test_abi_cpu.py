@@ -167,3 +167,46 @@ def test_decode_errors(L):
     assert decode_call(L, x=GB + 1) == EALIGN
     assert decode_call(L, y=8 * GB + 64) == EALIAS          # y inside h
     assert decode_call(L, h=1 * GB) == EALIAS               # h over x
+
+
+def bwd_call(L, dsc, u=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB, h0=0,
+             dy=8 * GB, dhl=0, du=9 * GB, dde=10 * GB, dA=11 * GB, dB=12 * GB, dC=13 * GB, dD=14 * GB,
+             dz=15 * GB, dh0=0, ws=16 * GB, ws_bytes=1 << 30):
+    ptrs = [fake(a) if a else None for a in (u, delta, A, B, C, D, z, h0, dy, dhl, du, dde, dA, dB, dC, dD, dz,
+                                             dh0, ws)]
+    return L.ssm_scan_bwd(ctypes.byref(dsc) if dsc is not None else None, *ptrs, ws_bytes, None)
+
+
+def test_bwd_errors(L):
+    assert bwd_call(L, None) == ENULL
+    assert bwd_call(L, desc(b=-1)) == ESHAPE
+    assert bwd_call(L, desc(dtype=5)) == EDTYPE
+    assert bwd_call(L, desc(N=65)) == EUNSUP
+    assert bwd_call(L, desc(b=0)) == OK
+    assert bwd_call(L, desc(), dy=0) == ENULL
+    assert bwd_call(L, desc(), dA=0) == ENULL
+    assert bwd_call(L, desc(), dB=0) == ENULL
+    assert bwd_call(L, desc(), dz=0) == ENULL           # a gate needs its gradient
+    # no gate: dz is not required (the call gets past the null checks to the
+    # misaligned du; every call here fails before any launch)
+    assert bwd_call(L, desc(), z=0, dz=0, du=9 * GB + 1) == EALIGN
+    assert bwd_call(L, desc(), dD=0) == ENULL           # a skip needs its gradient
+    assert bwd_call(L, desc(), du=9 * GB + 1) == EALIGN
+    assert bwd_call(L, desc(), dA=11 * GB + 2) == EALIGN
+    assert bwd_call(L, desc(), ws=16 * GB + 64) == EALIGN
+    assert bwd_call(L, desc(), du=1 * GB + 64) == EALIAS      # du over u
+    assert bwd_call(L, desc(), dB=11 * GB + 4) == EALIAS      # dB over dA
+    assert bwd_call(L, desc(), ws=12 * GB) == EALIAS          # workspace over dB
+    assert bwd_call(L, desc(), dh0=8 * GB + 128) == EALIAS    # dh0 over dy
+
+
+def test_bwd_workspace(L):
+    d = desc(b=2, L=100, d=64, N=16)
+    need = L.ssm_scan_bwd_workspace_size(ctypes.byref(d))
+    rnd = lambda v: (v + 255) // 256 * 256
+    # at least: regrouped B, C; checkpoints every 16 tokens; per-tile dB/dC partials; dA, dD partials
+    assert need >= 2 * rnd(2 * (112 + 16) * 16 * 4) + rnd(2 * 7 * 16 * 64 * 4) + rnd(2 * 1 * 100 * 16 * 8)
+    assert bwd_call(L, d, ws=0, ws_bytes=0) == EWS
+    assert bwd_call(L, d, ws_bytes=need - 1) == EWS
+    assert L.ssm_scan_bwd_workspace_size(ctypes.byref(desc(L=0))) == 0
+    assert L.ssm_scan_bwd_workspace_size(None) == 0
