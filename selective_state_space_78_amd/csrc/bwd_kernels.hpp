@@ -96,21 +96,28 @@ hipError_t launch_bwd_reduce(const BwdReduceParams &p, hipStream_t st);
 namespace ssm_detail {
 namespace {
 
-// Sum of v over the 64 lanes of the wave, valid in lane 63: DPP row shifts by
-// 1, 2, 4, 8 (lane 15 of each row holds the row's sum), then row broadcasts of
-// lanes 15 and 31 into the following rows.
-__device__ __forceinline__ float wave_sum_to_63(float v) {
-    auto add = [](float x, float y) { return x + y; };
-#define SSM_DPP_ADD(CTRL, ROWS) \
-    v = add(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false)))
-    SSM_DPP_ADD(0x111, 0xF);   // row_shr:1
-    SSM_DPP_ADD(0x112, 0xF);   // row_shr:2
-    SSM_DPP_ADD(0x114, 0xF);   // row_shr:4
-    SSM_DPP_ADD(0x118, 0xF);   // row_shr:8
-    SSM_DPP_ADD(0x142, 0xA);   // row_bcast:15 into rows 1, 3
-    SSM_DPP_ADD(0x143, 0xC);   // row_bcast:31 into rows 2, 3
-#undef SSM_DPP_ADD
-    return v;
+// Sums of four values over the 64 lanes of the wave, valid in lane 63: DPP row
+// shifts by 1, 2, 4, 8 (lane 15 of each row then holds the row's sum; lanes
+// without a source add 0), then row broadcasts of lane 15 into rows 1 and 3
+// and of lane 31 into rows 2 and 3. Each step is one v_add_f32_dpp; the four
+// chains are interleaved so that every DPP read comes three instructions
+// after the write it depends on (the hardware wants two), and one s_nop
+// covers the first reads.
+__device__ __forceinline__ void wave_sum4_to_63(float &a, float &b, float &c, float &d) {
+#define SSM_DPP4(CTRL) \
+    "v_add_f32_dpp %0, %0, %0 " CTRL "\n\t" \
+    "v_add_f32_dpp %1, %1, %1 " CTRL "\n\t" \
+    "v_add_f32_dpp %2, %2, %2 " CTRL "\n\t" \
+    "v_add_f32_dpp %3, %3, %3 " CTRL "\n\t"
+    asm volatile("s_nop 1\n\t"
+                 SSM_DPP4("row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1")
+                 SSM_DPP4("row_shr:2 row_mask:0xf bank_mask:0xf bound_ctrl:1")
+                 SSM_DPP4("row_shr:4 row_mask:0xf bank_mask:0xf bound_ctrl:1")
+                 SSM_DPP4("row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1")
+                 SSM_DPP4("row_bcast:15 row_mask:0xa bank_mask:0xf")
+                 SSM_DPP4("row_bcast:31 row_mask:0xc bank_mask:0xf")
+                 : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+#undef SSM_DPP4
 }
 
 template <int KV> struct BwdFloats;
@@ -131,7 +138,8 @@ struct BwdKernel {
     static_assert(TC <= kPadRows, "spare rows of the regrouped B and C");
     static constexpr bool kPacked = sizeof(T) == 2;
     static constexpr int kWPS = kPacked ? 1 : 2;
-    static constexpr bool kKeepA = NPW <= 2;                        // keep the chunk's decays in registers
+    static constexpr bool kKeepA = NPW == 1;
+    static constexpr int kRed = (2 * NPW + 3) / 4 * 4;             // reduced values per step, in 4s                        // keep the chunk's decays in registers
     typedef typename Words<kWords>::type Raw;
     typedef typename BwdFloats<kV>::type VecF;
 
@@ -448,6 +456,9 @@ struct BwdKernel {
                 const float2 v = s.dx[t][lane];
                 const float dsv = s.ds[t][lane];
                 float pU = 0.0f, pD = 0.0f;
+                float vr[kRed];                  // (dB term, dC term) per state, zero padded to 4s
+#pragma unroll
+                for (int i = 2 * NPW; i < kRed; ++i) vr[i] = 0.0f;
 #pragma unroll
                 for (int q = 0; q < NPW; ++q) {
                     const uint32_t wb = bw[t * NPW + q];
@@ -485,14 +496,16 @@ struct BwdKernel {
                         pU = fmaf(l, bq, pU);
                         vb = l * v.y;
                     }
-                    const float vc = dsv * hs[t][q];
+                    vr[2 * q] = vb;
+                    vr[2 * q + 1] = dsv * hs[t][q];
                     mu[q] = a * l;
-                    const float sb = wave_sum_to_63(vb);
-                    const float sc = wave_sum_to_63(vc);
-                    if (lane == kTile - 1) {
-                        s.red[t][w * NPW + q][0] = sb;
-                        s.red[t][w * NPW + q][1] = sc;
-                    }
+                }
+                // the chunk's dB, dC terms of this wave's states, summed over the 64 channels
+#pragma unroll
+                for (int i = 0; i < kRed; i += 4) wave_sum4_to_63(vr[i], vr[i + 1], vr[i + 2], vr[i + 3]);
+                if (lane == kTile - 1) {
+#pragma unroll
+                    for (int i = 0; i < 2 * NPW; ++i) s.red[t][w * NPW + i / 2][i % 2] = vr[i];
                 }
                 s.pl[0][w][t][lane] = pU;
                 s.pl[1][w][t][lane] = pD;
@@ -557,8 +570,9 @@ struct BwdKernel {
     }
 };
 
+// at least 4 waves per SIMD: two 8-wave workgroups (or one 16-wave one) per CU
 template <typename T, int NPW, int G, int TC, bool ZOH>
-__global__ __launch_bounds__(kTile * G) void bwd_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kTile * G, 4) void bwd_kernel(const BwdParams p) {
     BwdKernel<T, NPW, G, TC, ZOH>::run(p);
 }
 
