@@ -96,28 +96,40 @@ hipError_t launch_bwd_reduce(const BwdReduceParams &p, hipStream_t st);
 namespace ssm_detail {
 namespace {
 
-// Sums of four values over the 64 lanes of the wave, valid in lane 63: DPP row
-// shifts by 1, 2, 4, 8 (lane 15 of each row then holds the row's sum; lanes
-// without a source add 0), then row broadcasts of lane 15 into rows 1 and 3
-// and of lane 31 into rows 2 and 3. Each step is one v_add_f32_dpp; the four
-// chains are interleaved so that every DPP read comes three instructions
-// after the write it depends on (the hardware wants two), and one s_nop
-// covers the first reads.
-__device__ __forceinline__ void wave_sum4_to_63(float &a, float &b, float &c, float &d) {
-#define SSM_DPP4(CTRL) \
-    "v_add_f32_dpp %0, %0, %0 " CTRL "\n\t" \
-    "v_add_f32_dpp %1, %1, %1 " CTRL "\n\t" \
-    "v_add_f32_dpp %2, %2, %2 " CTRL "\n\t" \
-    "v_add_f32_dpp %3, %3, %3 " CTRL "\n\t"
-    asm volatile("s_nop 1\n\t"
-                 SSM_DPP4("row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1")
-                 SSM_DPP4("row_shr:2 row_mask:0xf bank_mask:0xf bound_ctrl:1")
-                 SSM_DPP4("row_shr:4 row_mask:0xf bank_mask:0xf bound_ctrl:1")
-                 SSM_DPP4("row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1")
-                 SSM_DPP4("row_bcast:15 row_mask:0xa bank_mask:0xf")
-                 SSM_DPP4("row_bcast:31 row_mask:0xc bank_mask:0xf")
-                 : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-#undef SSM_DPP4
+// Sums of four values a, b, c, d over the 64 lanes of the wave, as a
+// transposing reduction: two levels of DPP quad permutes, each keeping half of
+// the values per lane (odd lanes keep c and d, then lanes 2 and 3 of a quad
+// keep the b/d sums), leave every lane with one value summed over its quad
+// (lane 0 of a quad: a, 1: c, 2: b, 3: d); row shifts by 4 and 8 add the
+// quads of a row into lanes 12..15; cross-row shuffles add the rows. The
+// sums end in lanes 60 (a), 61 (c), 62 (b) and 63 (d). Lane masks: m1 = odd
+// lanes, m2 = lanes with bit 1 set. The s_nops give every DPP read the two
+// wait states it needs after the write it depends on.
+__device__ __forceinline__ float wave_sum4_transposed(float a, float b, float c, float d) {
+    const uint64_t m1 = 0xAAAAAAAAAAAAAAAAull, m2 = 0xCCCCCCCCCCCCCCCCull;
+    float r1, k1, r2, k2, p, q, s;
+    asm volatile(
+        "v_cndmask_b32 %[r1], %[c], %[a], %[m1]\n\t"      // r1 = odd ? a : c   (sent to the partner)
+        "v_cndmask_b32 %[k1], %[a], %[c], %[m1]\n\t"      // k1 = odd ? c : a   (kept)
+        "v_cndmask_b32 %[r2], %[d], %[b], %[m1]\n\t"
+        "v_cndmask_b32 %[k2], %[b], %[d], %[m1]\n\t"
+        "s_nop 0\n\t"
+        "v_add_f32_dpp %[p], %[r1], %[k1] quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %[q], %[r2], %[k2] quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_cndmask_b32 %[r1], %[q], %[p], %[m2]\n\t"      // lanes 2, 3 send p, keep q
+        "v_cndmask_b32 %[k1], %[p], %[q], %[m2]\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %[s], %[r1], %[k1] quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %[s], %[s], %[s] row_shr:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %[s], %[s], %[s] row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        : [r1] "=&v"(r1), [k1] "=&v"(k1), [r2] "=&v"(r2), [k2] "=&v"(k2), [p] "=&v"(p), [q] "=&v"(q),
+          [s] "=&v"(s)
+        : [a] "v"(a), [b] "v"(b), [c] "v"(c), [d] "v"(d), [m1] "s"(m1), [m2] "s"(m2));
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    return s;
 }
 
 template <int KV> struct BwdFloats;
@@ -500,12 +512,15 @@ struct BwdKernel {
                     vr[2 * q + 1] = dsv * hs[t][q];
                     mu[q] = a * l;
                 }
-                // the chunk's dB, dC terms of this wave's states, summed over the 64 channels
+                // the chunk's dB, dC terms of this wave's states, summed over the 64
+                // channels: values (dB q, dC q, dB q+1, dC q+1) land in lanes 60
+                // (dB q), 61 (dB q+1), 62 (dC q), 63 (dC q+1)
 #pragma unroll
-                for (int i = 0; i < kRed; i += 4) wave_sum4_to_63(vr[i], vr[i + 1], vr[i + 2], vr[i + 3]);
-                if (lane == kTile - 1) {
-#pragma unroll
-                    for (int i = 0; i < 2 * NPW; ++i) s.red[t][w * NPW + i / 2][i % 2] = vr[i];
+                for (int i = 0; i < kRed; i += 4) {
+                    const float sum = wave_sum4_transposed(vr[i], vr[i + 1], vr[i + 2], vr[i + 3]);
+                    const int j = lane - (kTile - 4);
+                    const int q = i / 2 + (j & 1);
+                    if (j >= 0 && q < NPW) s.red[t][w * NPW + q][j >> 1] = sum;
                 }
                 s.pl[0][w][t][lane] = pU;
                 s.pl[1][w][t][lane] = pD;
