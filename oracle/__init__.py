@@ -55,15 +55,15 @@ class Oracle:
         lib = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         lib.oracle_selective_scan.argtypes = [i64, i64, i64, i64, i32, i32,
-                                              vp, vp, vp, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                               i64, vp, vp, vp, i32]
         lib.oracle_selective_scan.restype = i32
         lib.oracle_state_update.argtypes = [i64, i64, i64, i32, i32,
-                                            vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+                                            vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i32]
         lib.oracle_state_update.restype = i32
         lib.oracle_selective_scan_bwd.argtypes = [i64, i64, i64, i64, i32, i32,
-                                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                                  i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+                                                  vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         lib.oracle_selective_scan_bwd.restype = i32
         self.lib = lib
         self.path = path
@@ -80,13 +80,16 @@ class Oracle:
         return _TYPE_OF[t]
 
     def selective_scan(self, u, delta, A, B, C, D=None, z=None, h0=None,
-                       disc="euler", channels=None, nthreads=0, want_y=True):
+                       disc="euler", channels=None, nthreads=0, want_y=True,
+                       delta_bias=None, delta_softplus=False):
         """Scan (batch, L, dim) inputs.
 
         Returns ``(y, h_last)``. With ``channels=None`` every channel is
         computed and ``y`` is (batch, L, dim), ``h_last`` (batch, dim, N).
         With ``channels`` a sequence of (b, d) pairs, ``y`` is (k, L) and
         ``h_last`` is (k, N), row i belonging to ``channels[i]``.
+        ``delta_bias`` (dim,) is added to delta, and ``delta_softplus`` passes
+        the sum through softplus, before the recurrence uses it.
         """
         u = np.ascontiguousarray(u)
         batch, L, dim = u.shape
@@ -113,8 +116,10 @@ class Oracle:
             nsel = len(sel)
         y = np.empty((nsel, L), np.float64) if want_y else None
         hl = np.empty((nsel, N), np.float64)
+        dbias = None if delta_bias is None else np.ascontiguousarray(delta_bias, dtype=np.float64)
         rc = self.lib.oracle_selective_scan(batch, L, dim, N, typ, _DISC[disc],
-                                            _ptr(u), _ptr(delta), _ptr(A64), _ptr(B), _ptr(C),
+                                            _ptr(u), _ptr(delta), _ptr(dbias), int(bool(delta_softplus)),
+                                            _ptr(A64), _ptr(B), _ptr(C),
                                             _ptr(D64), _ptr(zc), _ptr(h064),
                                             nsel, _ptr(sel), _ptr(y), _ptr(hl), int(nthreads or self.threads))
         if rc != 0:
@@ -126,7 +131,8 @@ class Oracle:
         return y, hl
 
     def selective_scan_bwd(self, u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None,
-                           disc="euler", channels=None, want_bc=True, want_tokens=True, nthreads=0):
+                           disc="euler", channels=None, want_bc=True, want_tokens=True, nthreads=0,
+                           delta_bias=None, delta_softplus=False):
         """Gradients of sum(dy * y) + sum(dh_last * h_last) with respect to every input.
 
         Returns a dict. With ``channels=None``: du, ddelta, dz (batch, L, dim),
@@ -135,6 +141,9 @@ class Oracle:
         (k, N) and dD_c (k) (each channel's share of dA[d] and dD[d]), dh0
         (k, N), and dB, dC summed over the selected channels only.
         ``want_tokens=False`` skips du, ddelta and dz (None in the result).
+        With ``delta_bias`` / ``delta_softplus`` (as in selective_scan), ddelta is
+        the gradient of the raw delta and ddelta_bias (dim) (or its per-channel
+        share ddelta_bias_c) that of the bias.
         """
         u = np.ascontiguousarray(u)
         batch, L, dim = u.shape
@@ -160,27 +169,32 @@ class Oracle:
         du = np.empty((nsel, L)) if want_tokens else None
         dde = np.empty((nsel, L)) if want_tokens else None
         dz = np.empty((nsel, L)) if zc is not None and want_tokens else None
-        dA_c = np.empty((nsel, N)); dD_c = np.empty(nsel); dh0 = np.empty((nsel, N))
+        dA_c = np.empty((nsel, N)); dD_c = np.empty(nsel); dDb_c = np.empty(nsel); dh0 = np.empty((nsel, N))
+        dbias = None if delta_bias is None else np.ascontiguousarray(delta_bias, dtype=np.float64)
         dB = np.empty((batch, L, N)) if want_bc else None
         dC = np.empty((batch, L, N)) if want_bc else None
         rc = self.lib.oracle_selective_scan_bwd(batch, L, dim, N, typ, _DISC[disc],
-                                                _ptr(u), _ptr(delta), _ptr(A64), _ptr(B), _ptr(C),
+                                                _ptr(u), _ptr(delta), _ptr(dbias), int(bool(delta_softplus)),
+                                                _ptr(A64), _ptr(B), _ptr(C),
                                                 _ptr(D64), _ptr(zc), _ptr(h064), _ptr(dy64), _ptr(dhl),
                                                 nsel, _ptr(sel), _ptr(du), _ptr(dde), _ptr(dz),
-                                                _ptr(dA_c), _ptr(dD_c), _ptr(dh0), _ptr(dB), _ptr(dC),
+                                                _ptr(dA_c), _ptr(dD_c), _ptr(dDb_c), _ptr(dh0), _ptr(dB), _ptr(dC),
                                                 int(nthreads or self.threads))
         if rc != 0:
             raise ValueError("oracle_selective_scan_bwd rejected its arguments")
         if channels is not None:
-            return dict(du=du, ddelta=dde, dz=dz, dA_c=dA_c, dD_c=dD_c, dh0=dh0, dB=dB, dC=dC)
+            return dict(du=du, ddelta=dde, dz=dz, dA_c=dA_c, dD_c=dD_c, ddelta_bias_c=dDb_c, dh0=dh0,
+                        dB=dB, dC=dC)
 
         def per_token(a):
             return None if a is None else a.reshape(batch, dim, L).transpose(0, 2, 1).copy()
         return dict(du=per_token(du), ddelta=per_token(dde), dz=per_token(dz),
                     dA=dA_c.reshape(batch, dim, N).sum(axis=0), dD=dD_c.reshape(batch, dim).sum(axis=0),
+                    ddelta_bias=dDb_c.reshape(batch, dim).sum(axis=0),
                     dh0=dh0.reshape(batch, dim, N), dB=dB, dC=dC)
 
-    def state_update(self, x, delta, A, B, C, h, D=None, z=None, disc="euler", nthreads=0):
+    def state_update(self, x, delta, A, B, C, h, D=None, z=None, disc="euler", nthreads=0,
+                     delta_bias=None, delta_softplus=False):
         """One decode step. ``h`` (batch, dim, N) float64 is updated in place; returns y."""
         x = np.ascontiguousarray(x)
         batch, dim = x.shape
@@ -190,8 +204,10 @@ class Oracle:
         A64 = np.ascontiguousarray(A, dtype=np.float64)
         D64 = None if D is None else np.ascontiguousarray(D, dtype=np.float64)
         y = np.empty((batch, dim), np.float64)
+        dbias = None if delta_bias is None else np.ascontiguousarray(delta_bias, dtype=np.float64)
         rc = self.lib.oracle_state_update(batch, dim, N, typ, _DISC[disc],
-                                          _ptr(x), _ptr(np.ascontiguousarray(delta)), _ptr(A64),
+                                          _ptr(x), _ptr(np.ascontiguousarray(delta)), _ptr(dbias),
+                                          int(bool(delta_softplus)), _ptr(A64),
                                           _ptr(np.ascontiguousarray(B)), _ptr(np.ascontiguousarray(C)),
                                           _ptr(D64), _ptr(None if z is None else np.ascontiguousarray(z)),
                                           _ptr(h), _ptr(y), int(nthreads or self.threads))

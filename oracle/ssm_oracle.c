@@ -15,7 +15,8 @@
  *           (eommydocs "State Space Models (SSM)", §3.2 pseudo-code and §5.1
  *            SelectiveSSM._selective_scan start from a zero state)
  *   for t = 0 .. L-1:
- *     a[n]  = exp(delta[b,t,d] * A[d,n])                  (discretised A)
+ *     delta = delta[b,t,d] (+ delta_bias[d]), through softplus when asked
+ *     a[n]  = exp(delta * A[d,n])                          (discretised A)
  *     bu[n] = delta * B[b,t,n] * u[b,t,d]                  (simplified B, default)
  *           = (exp(delta*A)-1)/A * B[b,t,n] * u[b,t,d]     (zero-order hold)
  *     h[n]  = a[n]*h[n] + bu[n]                            (recurrence)
@@ -50,7 +51,9 @@
  *                               df/dA = (delta*a - f)/A (A -> 0: delta^2/2):
  *                               ddelta += lam*a*B*u, du += lam*f*B, dB += lam*f*u, dA += lam*df/dA*B*u
  *   readout:        dC_t += ds_t * h_t,  dD += ds_t * u_t,  du_t += D * ds_t
- *   dh0 = a_0 * lam_0.
+ *   dh0 = a_0 * lam_0; with a bias / softplus on delta, ddelta is taken with
+ *   respect to the raw delta (times sigmoid of the softplus argument) and
+ *   ddelta_bias[d] is its sum over batch and time.
  *
  * Everything is evaluated in double precision, inputs widened exactly, the sum
  * over n taken in ascending order, with libm exp / expm1 (no fast-math).
@@ -102,6 +105,33 @@ static double silu(double z)
     return z / (1.0 + exp(-z));
 }
 
+/* softplus(x) = log(1 + exp(x)), written so that neither branch overflows. */
+static double softplus(double x)
+{
+    return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+}
+
+/*
+ * The step size used by the recurrence: delta as given, plus the channel's
+ * bias when one is given, through softplus when asked (the projection output
+ * becomes a positive step: youngju.dev SelectiveSSM.forward, dt = softplus(...)).
+ * *dgrad receives d(step)/d(delta), the sigmoid of the softplus argument (1
+ * without softplus).
+ */
+static double step_size(const void *delta, int type, int64_t i, int64_t d,
+                        const double *bias, int sp, double *dgrad)
+{
+    double x = load(delta, type, i) + (bias ? bias[d] : 0.0);
+    if (!sp) {
+        if (dgrad)
+            *dgrad = 1.0;
+        return x;
+    }
+    if (dgrad)
+        *dgrad = 1.0 / (1.0 + exp(-x));
+    return softplus(x);
+}
+
 /*
  * Scan one channel (b, d) over L tokens.
  *   x_*  : the buffers of u, delta, z (batch, L, dim) and B, C (batch, L, N)
@@ -110,7 +140,7 @@ static double silu(double z)
  */
 static void scan_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
                          int type, int disc,
-                         const void *u, const void *delta,
+                         const void *u, const void *delta, const double *dbias, int sp,
                          const double *A, const void *B, const void *C,
                          const double *D, const void *z, const double *h0,
                          double *h, double *y, double *hl)
@@ -122,7 +152,7 @@ static void scan_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N
     for (int64_t t = 0; t < L; ++t) {
         const int64_t row = b * L + t;        /* token index (b, t) */
         const double ut = load(u, type, row * dim + d);
-        const double dt = load(delta, type, row * dim + d);
+        const double dt = step_size(delta, type, row * dim + d, d, dbias, sp, NULL);
         double yt = 0.0;
         for (int64_t n = 0; n < N; ++n) {
             const double a_dn = A[d * N + n];
@@ -158,7 +188,8 @@ static void scan_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N
  */
 int oracle_selective_scan(int64_t batch, int64_t L, int64_t dim, int64_t N,
                           int type, int disc,
-                          const void *u, const void *delta, const double *A,
+                          const void *u, const void *delta, const double *delta_bias, int delta_softplus,
+                          const double *A,
                           const void *B, const void *C, const double *D,
                           const void *z, const double *h0,
                           int64_t nsel, const int64_t *sel,
@@ -191,7 +222,7 @@ int oracle_selective_scan(int64_t batch, int64_t L, int64_t dim, int64_t N,
                 bad = 1;
                 continue;
             }
-            scan_channel(c / dim, c % dim, L, dim, N, type, disc, u, delta, A, B, C,
+            scan_channel(c / dim, c % dim, L, dim, N, type, disc, u, delta, delta_bias, delta_softplus, A, B, C,
                          D, z, h0, h, y ? y + k * L : NULL, h_last ? h_last + k * N : NULL);
         }
     }
@@ -209,7 +240,8 @@ int oracle_selective_scan(int64_t batch, int64_t L, int64_t dim, int64_t N,
  *   y           : (batch, dim) doubles
  */
 int oracle_state_update(int64_t batch, int64_t dim, int64_t N, int type, int disc,
-                        const void *x, const void *delta, const double *A,
+                        const void *x, const void *delta, const double *delta_bias, int delta_softplus,
+                        const double *A,
                         const void *B, const void *C, const double *D,
                         const void *z, double *h, double *y, int nthreads)
 {
@@ -229,7 +261,7 @@ int oracle_state_update(int64_t batch, int64_t dim, int64_t N, int type, int dis
     for (int64_t c = 0; c < batch * dim; ++c) {
         const int64_t b = c / dim, d = c % dim;
         const double xt = load(x, type, c);
-        const double dt = load(delta, type, c);
+        const double dt = step_size(delta, type, c, d, delta_bias, delta_softplus, NULL);
         double *hc = h + c * N;
         double yt = 0.0;
         for (int64_t n = 0; n < N; ++n) {
@@ -261,13 +293,13 @@ static double silu_grad(double z)
  */
 static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
                         int type, int disc,
-                        const void *u, const void *delta,
+                        const void *u, const void *delta, const double *dbias, int sp,
                         const double *A, const void *B, const void *C,
                         const double *D, const void *z, const double *h0,
                         const double *dy, const double *dh_last,
                         double *hs, double *ss, double *lam,
                         double *du, double *dde, double *dz, double *dA_c, double *dD_c,
-                        double *dh0_c, double *dB, double *dC)
+                        double *dDb_c, double *dh0_c, double *dB, double *dC)
 {
     const double dskip = D ? D[d] : 0.0;
     /* forward, keeping every state: hs[(t+1)*N + n] = h_t[n] */
@@ -276,7 +308,7 @@ static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
     for (int64_t t = 0; t < L; ++t) {
         const int64_t row = b * L + t;
         const double ut = load(u, type, row * dim + d);
-        const double dt = load(delta, type, row * dim + d);
+        const double dt = step_size(delta, type, row * dim + d, d, dbias, sp, NULL);
         double st = 0.0;
         for (int64_t n = 0; n < N; ++n) {
             const double a_dn = A[d * N + n];
@@ -292,11 +324,12 @@ static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
         lam[n] = dh_last ? dh_last[(b * dim + d) * N + n] : 0.0;   /* a_{t+1} lam_{t+1} carried */
         dA_c[n] = 0.0;
     }
-    double dDacc = 0.0;
+    double dDacc = 0.0, dDbacc = 0.0;
     for (int64_t t = L - 1; t >= 0; --t) {
         const int64_t row = b * L + t;
         const double ut = load(u, type, row * dim + d);
-        const double dt = load(delta, type, row * dim + d);
+        double dstep;                                                 /* d(step)/d(delta) */
+        const double dt = step_size(delta, type, row * dim + d, d, dbias, sp, &dstep);
         const double dyt = dy[row * dim + d];
         double ds = dyt;
         if (z) {
@@ -336,12 +369,15 @@ static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
                 dC[row * N + n] += ds * hs[(t + 1) * N + n];
             lam[n] = abar * l;                                       /* a_t lam_t for t-1 */
         }
+        ddt *= dstep;                               /* through the bias and softplus */
+        dDbacc += ddt;
         if (du)
             du[t] = dut;
         if (dde)
             dde[t] = ddt;
     }
     *dD_c = dDacc;
+    *dDb_c = dDbacc;
     if (dh0_c)
         for (int64_t n = 0; n < N; ++n)
             dh0_c[n] = lam[n];
@@ -364,13 +400,14 @@ static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
  */
 int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
                               int type, int disc,
-                              const void *u, const void *delta, const double *A,
+                              const void *u, const void *delta, const double *delta_bias,
+                              int delta_softplus, const double *A,
                               const void *B, const void *C, const double *D,
                               const void *z, const double *h0,
                               const double *dy, const double *dh_last,
                               int64_t nsel, const int64_t *sel,
                               double *du, double *ddelta, double *dz,
-                              double *dA_c, double *dD_c, double *dh0,
+                              double *dA_c, double *dD_c, double *dDb_c, double *dh0,
                               double *dB, double *dC, int nthreads)
 {
     if (batch < 0 || L < 0 || dim < 0 || N < 1 || N > 4096)
@@ -379,7 +416,7 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
         return -1;
     if (disc != ORACLE_EULER && disc != ORACLE_ZOH)
         return -1;
-    if ((L > 0 && (!u || !delta || !B || !C || !dy)) || !A || !dA_c || !dD_c)
+    if ((L > 0 && (!u || !delta || !B || !C || !dy)) || !A || !dA_c || !dD_c || !dDb_c)
         return -1;
     if (!sel)
         nsel = batch * dim;
@@ -428,10 +465,10 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
                 bad = 1;
                 continue;
             }
-            bwd_channel(c / dim, c % dim, L, dim, N, type, disc, u, delta, A, B, C, D, z, h0,
-                        dy, dh_last, hs, ss, lam,
+            bwd_channel(c / dim, c % dim, L, dim, N, type, disc, u, delta, delta_bias, delta_softplus,
+                        A, B, C, D, z, h0, dy, dh_last, hs, ss, lam,
                         du ? du + k * L : NULL, ddelta ? ddelta + k * L : NULL,
-                        (dz && z) ? dz + k * L : NULL, dA_c + k * N, dD_c + k,
+                        (dz && z) ? dz + k * L : NULL, dA_c + k * N, dD_c + k, dDb_c + k,
                         dh0 ? dh0 + k * N : NULL, myB, myC);
         }
         free(hs);

@@ -43,9 +43,11 @@ def rel_err(got, ref):
     ref = np.asarray(ref, dtype=np.float64)
     if ref.size == 0:
         return 0.0
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    floor = np.maximum(np.abs(ref), rms if rms > 0 else 1e-300)
-    return float(np.max(np.abs(got - ref) / floor))
+    with np.errstate(over="ignore", invalid="ignore"):
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        floor = np.maximum(np.abs(ref), rms if rms > 0 else 1e-300)
+        e = float(np.max(np.abs(got - ref) / floor))
+    return e if np.isfinite(e) else float("inf")
 
 
 def _case(rng, batch, L, dim, N, with_d=True, with_z=False, with_h0=False, a_zero=False):
@@ -465,6 +467,64 @@ def pin_bwd_channel_selection(o):
     assert rel_err(dA, full["dA"]) < 1e-14 and rel_err(dD, full["dD"]) < 1e-14
 
 
+def pin_delta_softplus(o):
+    """A per-channel bias and softplus on delta equal running on the precomputed
+    step log(1 + exp(delta + bias)) (numpy.logaddexp), for the scan and the
+    decode step; a bias alone is plain addition."""
+    rng = np.random.default_rng(RNG_SEED + 25)
+    x = _case(rng, 2, 12, 3, 4, with_d=True, with_z=True, with_h0=True)
+    raw = rng.normal(-3.0, 2.0, x["delta"].shape)
+    raw[0, 0, 0], raw[1, 3, 2] = 40.0, -40.0
+    bias = rng.normal(0.0, 1.0, 3)
+    for disc in ("euler", "zoh"):
+        y1, h1 = o.selective_scan(**dict(x, delta=raw), disc=disc, delta_bias=bias, delta_softplus=True)
+        y2, h2 = o.selective_scan(**dict(x, delta=np.logaddexp(0.0, raw + bias)), disc=disc)
+        assert rel_err(y1, y2) < 1e-13 and rel_err(h1, h2) < 1e-13, disc
+        y3, _ = o.selective_scan(**dict(x, delta=np.abs(raw)), disc=disc, delta_bias=bias)
+        y4, _ = o.selective_scan(**dict(x, delta=np.abs(raw) + bias), disc=disc)
+        assert rel_err(y3, y4) < 1e-13, disc
+    h = x["h0"].copy()
+    hb = x["h0"].copy()
+    ya = o.state_update(x["u"][:, 0], raw[:, 0], x["A"], x["B"][:, 0], x["C"][:, 0], h, D=x["D"], z=x["z"][:, 0],
+                        delta_bias=bias, delta_softplus=True)
+    yb = o.state_update(x["u"][:, 0], np.logaddexp(0.0, raw[:, 0] + bias), x["A"], x["B"][:, 0], x["C"][:, 0],
+                        hb, D=x["D"], z=x["z"][:, 0])
+    assert rel_err(ya, yb) < 1e-13 and rel_err(h, hb) < 1e-13
+
+
+def pin_bwd_delta_softplus(o):
+    """With bias and softplus on delta, ddelta (of the raw delta) and ddelta_bias
+    equal central differences of the forward oracle's loss."""
+    rng = np.random.default_rng(RNG_SEED + 26)
+    for disc in ("euler", "zoh"):
+        x = _case(rng, 2, 6, 2, 3, with_d=True, with_z=True, with_h0=True)
+        raw = rng.normal(-2.0, 1.0, x["delta"].shape)
+        bias = rng.normal(0.0, 0.5, 2)
+        dy = rng.standard_normal(x["u"].shape)
+        dhl = rng.standard_normal(x["h0"].shape)
+        g = o.selective_scan_bwd(**dict(x, delta=raw), dy=dy, dh_last=dhl, disc=disc, delta_bias=bias,
+                                 delta_softplus=True)
+
+        def loss(r, bb):
+            y, hl = o.selective_scan(**dict(x, delta=r), disc=disc, delta_bias=bb, delta_softplus=True)
+            return float((dy * y).sum() + (dhl * hl).sum())
+        eps = 1e-6
+        fd = np.zeros_like(raw)
+        for idx in np.ndindex(raw.shape):
+            rp, rm = raw.copy(), raw.copy()
+            rp[idx] += eps
+            rm[idx] -= eps
+            fd[idx] = (loss(rp, bias) - loss(rm, bias)) / (2 * eps)
+        assert rel_err(g["ddelta"], fd) < 1e-6, (disc, rel_err(g["ddelta"], fd))
+        fdb = np.zeros_like(bias)
+        for i in range(2):
+            bp, bm = bias.copy(), bias.copy()
+            bp[i] += eps
+            bm[i] -= eps
+            fdb[i] = (loss(raw, bp) - loss(raw, bm)) / (2 * eps)
+        assert rel_err(g["ddelta_bias"], fdb) < 1e-6, (disc, rel_err(g["ddelta_bias"], fdb))
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_brute_force_storage_types,
@@ -484,5 +544,7 @@ ALL_PINS = [
     pin_bwd_state_only,
     pin_bwd_storage_types,
     pin_bwd_channel_selection,
+    pin_delta_softplus,
+    pin_bwd_delta_softplus,
     pin_channel_selection,
 ]

@@ -59,6 +59,13 @@ MUTANTS = {
     "bwd_dh_last_ignored": ("lam[n] = dh_last ? dh_last[(b * dim + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
     "bwd_hprev_is_current": ("const double hprev = hs[t * N + n];", "const double hprev = hs[(t + 1) * N + n];"),
     "bwd_readout_adjoint_missing": ("const double l = lam[n] + Ct * ds;", "const double l = lam[n];"),
+    # step size: bias and softplus
+    "softplus_positive_branch": ("return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));",
+                                 "return x > 0.0 ? x : log1p(exp(x));"),
+    "delta_bias_ignored": ("double x = load(delta, type, i) + (bias ? bias[d] : 0.0);",
+                           "double x = load(delta, type, i);"),
+    "softplus_grad_missing": ("        ddt *= dstep;", "        ddt *= 1.0;"),
+    "softplus_grad_sign": ("*dgrad = 1.0 / (1.0 + exp(-x));", "*dgrad = 1.0 / (1.0 + exp(x));"),
 }
 
 
