@@ -49,7 +49,7 @@ typedef enum {
     SSM_ERR_NULL = -1,        /* a required pointer is NULL */
     SSM_ERR_SHAPE = -2,       /* a negative size, or sizes whose byte count overflows */
     SSM_ERR_DTYPE = -3,       /* unknown element type */
-    SSM_ERR_UNSUPPORTED = -4, /* dstate outside 1..64, unknown discretisation, bad tuning */
+    SSM_ERR_UNSUPPORTED = -4, /* dstate outside 1..64, unknown discretisation or flag, bad tuning */
     SSM_ERR_ALIAS = -5,       /* an output overlaps an input or another output */
     SSM_ERR_WORKSPACE = -6,   /* workspace missing or smaller than ssm_scan_workspace_size() */
     SSM_ERR_HIP = -7,         /* the HIP runtime refused a launch (e.g. not a gfx950 device) */
@@ -63,7 +63,12 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 /* Discretisation of B (A is always exp(delta*A)). */
 typedef enum { SSM_DISC_EULER = 0, SSM_DISC_ZOH = 1 } ssm_disc;
 
-/* Sizes and types of one scan. */
+/* Sizes and types of one scan, and how the step size is formed.
+ * The step used by the recurrence is delta[b,t,d] (+ delta_bias[d] when the
+ * bias is given), passed through softplus(x) = log(1 + exp(x)) when
+ * delta_softplus is nonzero: the projection output becomes a positive step
+ * inside the kernel (youngju.dev SelectiveSSM.forward, dt = softplus(...)).
+ * Zero-initialise the struct for "delta used as given". */
 typedef struct {
     int64_t batch;   /* b  >= 0 */
     int64_t seqlen;  /* L  >= 0 */
@@ -71,6 +76,9 @@ typedef struct {
     int64_t dstate;  /* N  in 1..64 */
     int32_t dtype;   /* ssm_dtype */
     int32_t disc;    /* ssm_disc */
+    int32_t delta_softplus;   /* 0 or 1 */
+    int32_t reserved;         /* must be 0 */
+    const float *delta_bias;  /* (dim) fp32 device pointer, or NULL */
 } ssm_scan_desc;
 
 /* Optional launch shape, for tuning and for tests of every kernel variant.
@@ -150,6 +158,9 @@ int ssm_scan_plan(const ssm_scan_desc *desc, ssm_scan_tuning *out);
  *   dB, dC        (batch, seqlen, dstate) fp32, written (summed over channels)
  *   dD            (dim) fp32, written; required when D is given, unused otherwise
  *   dh0           (batch, dim, dstate) fp32, written, or NULL (not wanted)
+ *   ddelta_bias   (dim) fp32, written when desc->delta_bias is given (else unused)
+ * With a delta bias or softplus in the descriptor, ddelta is the gradient of
+ * the raw delta (the chain rule through the bias and softplus).
  *   workspace     at least ssm_scan_bwd_workspace_size(desc) bytes, 256-byte
  *                 aligned; contents on entry do not matter.
  * Results do not depend on timing: every sum over channels, batch rows or
@@ -162,7 +173,7 @@ int ssm_scan_bwd(const ssm_scan_desc *desc,
                  const void *B, const void *C, const float *D, const void *z,
                  const float *h0, const void *dy, const float *dh_last,
                  void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD,
-                 void *dz, float *dh0,
+                 void *dz, float *dh0, float *ddelta_bias,
                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -172,6 +183,8 @@ int ssm_scan_bwd(const ssm_scan_desc *desc,
  * last hidden state is needed to produce the next token).
  *
  *   x, delta, z  (batch, dim)          dtype; z may be NULL (no gate)
+ *   delta_bias   (dim) fp32 or NULL; delta_softplus 0 or 1: the step is
+ *                softplus(delta + bias) as for the scan descriptor
  *   A            (dim, dstate)         fp32
  *   B, C         (batch, dstate)       dtype
  *   D            (dim) fp32 or NULL
@@ -180,7 +193,8 @@ int ssm_scan_bwd(const ssm_scan_desc *desc,
  * Equal to ssm_scan_fwd with seqlen 1, h0 = h and h_last = h.
  */
 int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t dtype, int32_t disc,
-                     const void *x, const void *delta, const float *A,
+                     const void *x, const void *delta, const float *delta_bias, int32_t delta_softplus,
+                     const float *A,
                      const void *B, const void *C, const float *D, const void *z,
                      float *h, void *y, hipStream_t stream);
 

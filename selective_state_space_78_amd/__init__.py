@@ -30,7 +30,9 @@ EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_workspace_size_t
 
 class ScanDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
-                ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32), ("disc", ctypes.c_int32)]
+                ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32), ("disc", ctypes.c_int32),
+                ("delta_softplus", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("delta_bias", ctypes.c_void_p)]
 
 
 class ScanTuning(ctypes.Structure):
@@ -71,9 +73,10 @@ def lib() -> ctypes.CDLL:
             L.ssm_scan_fwd_tuned.restype = ctypes.c_int
             L.ssm_scan_bwd_workspace_size.argtypes = [pdesc]
             L.ssm_scan_bwd_workspace_size.restype = sz
-            L.ssm_scan_bwd.argtypes = [pdesc] + [vp] * 18 + [vp, sz, vp]
+            L.ssm_scan_bwd.argtypes = [pdesc] + [vp] * 19 + [vp, sz, vp]
             L.ssm_scan_bwd.restype = ctypes.c_int
-            L.ssm_state_update.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            L.ssm_state_update.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                           vp]
             L.ssm_state_update.restype = ctypes.c_int
             L.ssm_status_string.argtypes = [ctypes.c_int]
             L.ssm_status_string.restype = ctypes.c_char_p
@@ -125,8 +128,10 @@ def _tuning(tuning):
     return ctypes.byref(ScanTuning(int(g), int(s)))
 
 
-def make_desc(batch, seqlen, dim, dstate, dtype, disc="euler") -> ScanDesc:
-    return ScanDesc(int(batch), int(seqlen), int(dim), int(dstate), int(dtype), _DISC[disc])
+def make_desc(batch, seqlen, dim, dstate, dtype, disc="euler", delta_bias=None, delta_softplus=False) -> ScanDesc:
+    """The scan descriptor; ``delta_bias`` is a device tensor (dim,) float32 or None."""
+    return ScanDesc(int(batch), int(seqlen), int(dim), int(dstate), int(dtype), _DISC[disc],
+                    int(bool(delta_softplus)), 0, None if delta_bias is None else delta_bias.data_ptr())
 
 
 def ssm_scan_workspace_size(batch, seqlen, dim, dstate, dtype=SSM_BF16, disc="euler", tuning=None) -> int:
@@ -147,14 +152,17 @@ def ssm_scan_plan(batch, seqlen, dim, dstate, dtype=SSM_BF16, disc="euler"):
 
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None,
-                 disc="euler", workspace=None, tuning=None, stream=None, want_h_last=True):
+                 disc="euler", workspace=None, tuning=None, stream=None, want_h_last=True,
+                 delta_bias=None, delta_softplus=False):
     """Selective scan forward on device tensors.
 
     u, delta, z: (batch, L, dim); B, C: (batch, L, N) of the same dtype
     (bfloat16 or float32); A: (dim, N) float32; D: (dim,) float32; h0:
     (batch, dim, N) float32. Outputs y (batch, L, dim) and h_last
     (batch, dim, N) are allocated when not given. Returns (y, h_last).
-    ``tuning`` is an optional (state_groups, segments) pair.
+    ``tuning`` is an optional (state_groups, segments) pair. ``delta_bias``
+    (dim,) float32 and ``delta_softplus`` form the step in the kernel:
+    softplus(delta + bias).
     """
     import torch
     batch, L, dim = u.shape
@@ -176,7 +184,8 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None
         h_last = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _check(y, "y", (batch, L, dim), dt, dev)
     _check(h_last, "h_last", (batch, dim, N), torch.float32, dev)
-    desc = make_desc(batch, L, dim, N, code, disc)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    desc = make_desc(batch, L, dim, N, code, disc, delta_bias, delta_softplus)
     L_ = lib()
     need = (L_.ssm_scan_workspace_size(ctypes.byref(desc)) if tuning is None
             else L_.ssm_scan_workspace_size_tuned(ctypes.byref(desc), _tuning(tuning)))
@@ -194,20 +203,22 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None
     return y, h_last
 
 
-def ssm_scan_bwd_workspace_size(batch, L, dim, N, dtype_code, disc="euler") -> int:
-    desc = make_desc(batch, L, dim, N, dtype_code, disc)
+def ssm_scan_bwd_workspace_size(batch, L, dim, N, dtype_code, disc="euler", delta_bias=None,
+                                delta_softplus=False) -> int:
+    desc = make_desc(batch, L, dim, N, dtype_code, disc, delta_bias, delta_softplus)
     return int(lib().ssm_scan_bwd_workspace_size(ctypes.byref(desc)))
 
 
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None, disc="euler",
-                 workspace=None, stream=None, want_dh0=True, out=None):
+                 workspace=None, stream=None, want_dh0=True, out=None, delta_bias=None, delta_softplus=False):
     """Backward of ssm_scan_fwd on device tensors.
 
     Inputs as ssm_scan_fwd, plus dy (batch, L, dim) of the input dtype and an
     optional dh_last (batch, dim, N) float32. Returns a dict with du, ddelta,
     dz (input dtype, dz only with a gate), dA (dim, N), dB, dC (batch, L, N),
     dD (dim,) (with a skip) and dh0 (batch, dim, N) (when ``want_dh0``), all
-    float32 except the per-token ones. ``out`` may hold preallocated outputs.
+    float32 except the per-token ones, and ddelta_bias (dim,) with a
+    ``delta_bias``. ``out`` may hold preallocated outputs.
     """
     import torch
     batch, L, dim = u.shape
@@ -243,21 +254,28 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None, d
     dC = get("dC", (batch, L, N), f32)
     dD = get("dD", (dim,), f32, D is not None)
     dh0 = get("dh0", (batch, dim, N), f32, want_dh0)
-    desc = make_desc(batch, L, dim, N, code, disc)
+    _check(delta_bias, "delta_bias", (dim,), f32, dev)
+    ddb = get("ddelta_bias", (dim,), f32, delta_bias is not None)
+    desc = make_desc(batch, L, dim, N, code, disc, delta_bias, delta_softplus)
     L_ = lib()
     need = L_.ssm_scan_bwd_workspace_size(ctypes.byref(desc))
+    if workspace is not None and workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace has %d bytes, ssm_scan_bwd needs %d" % (
+            workspace.numel() * workspace.element_size(), need))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = L_.ssm_scan_bwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                          _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(du), _ptr(dde), _ptr(dA), _ptr(dB), _ptr(dC),
-                         _ptr(dD), _ptr(dz), _ptr(dh0), _ptr(workspace), ws_bytes, _stream(stream, dev))
+                         _ptr(dD), _ptr(dz), _ptr(dh0), _ptr(ddb), _ptr(workspace), ws_bytes,
+                         _stream(stream, dev))
     if rc != 0:
         raise SsmError(rc, "ssm_scan_bwd")
-    return dict(du=du, ddelta=dde, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
+    return dict(du=du, ddelta=dde, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0, ddelta_bias=ddb)
 
 
-def ssm_state_update(x, delta, A, B, C, h, D=None, z=None, y=None, disc="euler", stream=None):
+def ssm_state_update(x, delta, A, B, C, h, D=None, z=None, y=None, disc="euler", stream=None,
+                     delta_bias=None, delta_softplus=False):
     """One decode step on device tensors; h (batch, dim, N) float32 is updated in place.
 
     x, delta, z: (batch, dim); B, C: (batch, N). Returns y (batch, dim).
@@ -279,7 +297,9 @@ def ssm_state_update(x, delta, A, B, C, h, D=None, z=None, y=None, disc="euler",
     if y is None:
         y = torch.empty((batch, dim), dtype=dt, device=dev)
     _check(y, "y", (batch, dim), dt, dev)
-    rc = lib().ssm_state_update(batch, dim, N, code, _DISC[disc], _ptr(x), _ptr(delta), _ptr(A),
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    rc = lib().ssm_state_update(batch, dim, N, code, _DISC[disc], _ptr(x), _ptr(delta), _ptr(delta_bias),
+                                int(bool(delta_softplus)), _ptr(A),
                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h), _ptr(y), _stream(stream, dev))
     if rc != 0:
         raise SsmError(rc, "ssm_state_update")

@@ -48,6 +48,8 @@ namespace ssm_detail {
 
 struct BwdParams {
     const void *u, *delta, *z, *dy;
+    const float *delta_bias;   // as in ScanParams
+    int delta_softplus;
     const float *A, *D, *dh_last;
     const float *Bf, *Cf;      // the checkpoint pass's regrouped B and C (same groups as here)
     const float *ckpt;         // (batch, nck, Npad, dim)
@@ -56,14 +58,15 @@ struct BwdParams {
     float *part_bc;            // (batch, ntiles, L, Npad, 2): per-tile sums over channels of dB, dC terms
     float *part_a;             // (batch, dim, Npad): per-row dA
     float *part_d;             // (batch, dim): per-row dD
+    float *part_db;            // (batch, dim): per-row delta-bias gradient (with a bias)
     int64_t L;
     int batch, dim, N, ntiles, nck;
     int vec;                   // u, delta, z, dy, du, ddelta, dz move 2 or 4 channels per aligned access
 };
 
 struct BwdReduceParams {
-    const float *part_bc, *part_a, *part_d;
-    float *dB, *dC, *dA, *dD;
+    const float *part_bc, *part_a, *part_d, *part_db;
+    float *dB, *dC, *dA, *dD, *ddelta_bias;
     int64_t L;
     int batch, dim, N, npad, ntiles;
 };
@@ -168,6 +171,7 @@ struct BwdKernel {
     };
     struct Held {
         float dt[kPPT][kV], u[kPPT][kV], ds[kPPT][kV], gz[kPPT][kV];   // gz = dy g'(z)
+        float sg[kPPT][kV];            // d step / d delta (sigmoid of the softplus argument, or 1)
     };
 
     __device__ static int piece_row(int j) { return threadIdx.x / kRowPieces + j * kRowStep; }
@@ -268,7 +272,7 @@ struct BwdKernel {
     // x = 0, ds = 0: a step that changes neither the state nor any stored
     // gradient.
     __device__ static void commit(const Prefetch &pf, Smem &s, Held &held, float (&dDacc)[kPPT][kV], int tval,
-                                  int col, bool colv, bool gate) {
+                                  int col, bool colv, bool gate, const float (&dbk)[kV], int prep) {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
             const int row = piece_row(j);
@@ -281,6 +285,17 @@ struct BwdKernel {
                 unpack(pf.u[j], u);
                 unpack(pf.dt[j], d);
                 unpack(pf.dy[j], g);
+#pragma unroll
+                for (int e = 0; e < kV; ++e) {
+                    held.sg[j][e] = 1.0f;
+                    if (prep == 2) {
+                        const float xs = d[e] + dbk[e];
+                        d[e] = softplus_f(xs);
+                        held.sg[j][e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-xs * kLog2e));
+                    } else if (prep == 1) {
+                        d[e] += dbk[e];
+                    }
+                }
                 if (gate) {
                     float z[kV];
                     unpack(pf.z[j], z);
@@ -369,13 +384,17 @@ struct BwdKernel {
         }
         const int col = (threadIdx.x % kRowPieces) * kV;
         const bool colv = d0 + col < p.dim;
-        float Dk[kV], dDacc[kPPT][kV];
+        float Dk[kV], dbk[kV], dDacc[kPPT][kV], dbacc[kPPT][kV];
 #pragma unroll
-        for (int e = 0; e < kV; ++e) Dk[e] = (p.D != nullptr && d0 + col + e < p.dim) ? p.D[d0 + col + e] : 0.0f;
+        for (int e = 0; e < kV; ++e) {
+            Dk[e] = (p.D != nullptr && d0 + col + e < p.dim) ? p.D[d0 + col + e] : 0.0f;
+            dbk[e] = (p.delta_bias != nullptr && d0 + col + e < p.dim) ? p.delta_bias[d0 + col + e] : 0.0f;
+        }
+        const int prep = p.delta_softplus ? 2 : (p.delta_bias != nullptr ? 1 : 0);
 #pragma unroll
         for (int j = 0; j < kPPT; ++j)
 #pragma unroll
-            for (int e = 0; e < kV; ++e) dDacc[j][e] = 0.0f;
+            for (int e = 0; e < kV; ++e) dDacc[j][e] = dbacc[j][e] = 0.0f;
 
         const int nck = p.nck;                                  // chunks of this row, walked last to first
         const int64_t row0 = (int64_t)b * p.L;
@@ -401,7 +420,7 @@ struct BwdKernel {
             const int tval = rows_of(c);
             const int64_t t0 = (int64_t)c * TC;
             // 1. stage this chunk; prefetch the previous one and its checkpoint
-            commit(pf, s, held, dDacc, tval, col, colv, gate);
+            commit(pf, s, held, dDacc, tval, col, colv, gate, dbk, prep);
             float hstart[NPW];
 #pragma unroll
             for (int q = 0; q < NPW; ++q) hstart[q] = hnext[q];
@@ -544,6 +563,8 @@ struct BwdKernel {
                         ou[e] = fmaf(held.dt[j][e], su[e], Dk[e] * held.ds[j][e]);
                         od[e] = fmaf(held.u[j][e], su[e], sd[e]);
                     }
+                    od[e] *= held.sg[j][e];          // gradient of the raw delta
+                    dbacc[j][e] += od[e];
                 }
                 const int64_t off = (row0 + t0 + row) * p.dim + d0 + col;
                 store(static_cast<T *>(p.du) + off, ou, d0 + col, p.dim, p.vec);
@@ -581,6 +602,23 @@ struct BwdKernel {
 #pragma unroll
             for (int r = 0; r < TC; ++r) acc += dsum[r][threadIdx.x];
             p.part_d[(int64_t)b * p.dim + d0 + threadIdx.x] = acc;
+        }
+        if (p.part_db != nullptr) {
+            // the same for the delta-bias gradient, through the second plane set
+            float (*bsum)[kTile] = s.pl[1][0];
+#pragma unroll
+            for (int j = 0; j < kPPT; ++j) {
+                if (!piece_in_chunk(j)) continue;
+#pragma unroll
+                for (int e = 0; e < kV; ++e) bsum[piece_row(j)][col + e] = dbacc[j][e];
+            }
+            __syncthreads();
+            if (threadIdx.x < kTile && d0 + (int)threadIdx.x < p.dim) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int r = 0; r < TC; ++r) acc += bsum[r][threadIdx.x];
+                p.part_db[(int64_t)b * p.dim + d0 + threadIdx.x] = acc;
+            }
         }
     }
 };

@@ -85,8 +85,21 @@ __device__ __forceinline__ float silu(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
+// softplus(x) = log(1 + exp(x)) = max(x, 0) + log1p(exp(-|x|)). log1p(e) is
+// taken as log(u) * e / (u - 1) with u = 1 + e, which cancels the rounding of
+// 1 + e, so a tiny e keeps its relative precision.
+__device__ __forceinline__ float softplus_f(float x) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+    const float u = 1.0f + e;
+    const float dd = u - 1.0f;
+    const float l = dd == 0.0f ? e : __builtin_amdgcn_logf(u) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(dd));
+    return fmaxf(x, 0.0f) + l;
+}
+
 struct ScanParams {
     const void *u, *delta, *z, *B, *C;
+    const float *delta_bias;  // (dim) added to delta before the recurrence uses it, or null
+    int delta_softplus;       // the step is softplus(delta + bias)
     const float *A, *D, *h0;
     float *Bf, *Cf;       // (batch, G, padded_len(L), Npad/G) fp32 widened B and C (workspace)
     const float *seg_h;   // (batch, nseg, dim, N) initial state of each segment, or null
@@ -328,7 +341,7 @@ struct ScanKernel {
     // past tval (and channels past dim) are staged as delta = 0, x = 0: a step
     // that leaves the state unchanged.
     __device__ static void commit(const Prefetch &pf, float2 (*dx)[kTile], Held &held, int tval, int col,
-                                  bool colv, const float (&Dk)[kV], bool gate) {
+                                  bool colv, const float (&Dk)[kV], bool gate, const float (&dbk)[kV], int prep) {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
             const int row = piece_row(j);
@@ -338,6 +351,11 @@ struct ScanKernel {
                 float u[kV], d[kV];
                 unpack(pf.u[j], u);
                 unpack(pf.dt[j], d);
+                if (prep) {
+                    // the step: delta + bias, through softplus when asked
+#pragma unroll
+                    for (int e = 0; e < kV; ++e) d[e] = prep == 2 ? softplus_f(d[e] + dbk[e]) : d[e] + dbk[e];
+                }
 #pragma unroll
                 for (int e = 0; e < kV; e += 2)
                     dst[e / 2] = make_float4(d[e], ZOH ? u[e] : d[e] * u[e], d[e + 1], ZOH ? u[e + 1] : d[e + 1] * u[e + 1]);
@@ -521,10 +539,14 @@ struct ScanKernel {
         // This thread stages (and finalizes) channels [col, col + kV) of the tile.
         const int col = (threadIdx.x % kRowPieces) * kV;
         const bool colv = d0 + col < p.dim;
-        float Dk[kV];
+        float Dk[kV], dbk[kV];
 #pragma unroll
-        for (int e = 0; e < kV; ++e)
+        for (int e = 0; e < kV; ++e) {
             Dk[e] = (!AGG && p.D != nullptr && d0 + col + e < p.dim) ? p.D[d0 + col + e] : 0.0f;
+            dbk[e] = (p.delta_bias != nullptr && d0 + col + e < p.dim) ? p.delta_bias[d0 + col + e] : 0.0f;
+        }
+        // 0: delta as given; 1: plus the bias; 2: softplus of that
+        const int prep = p.delta_softplus ? 2 : (p.delta_bias != nullptr ? 1 : 0);
 
         const int nchunks = (int)((t_end - t_begin + TC - 1) / TC);
         const int64_t row0 = (int64_t)b * p.L + t_begin;        // token row of (b, t_begin)
@@ -536,7 +558,7 @@ struct ScanKernel {
         };
         if (nchunks > 0) {
             load_chunk(0);
-            commit(pf, s.dx[0], held[0], rows_of(0), col, colv, Dk, gate);
+            commit(pf, s.dx[0], held[0], rows_of(0), col, colv, Dk, gate, dbk, prep);
         }
         if (nchunks > 1) load_chunk(1);
         __syncthreads();
@@ -569,7 +591,7 @@ struct ScanKernel {
             constexpr int P = decltype(parity)::value;
             fetch(0);
             Held next;
-            if (k + 1 < nchunks) commit(pf, s.dx[P ^ 1], next, rows_of(k + 1), col, colv, Dk, gate);
+            if (k + 1 < nchunks) commit(pf, s.dx[P ^ 1], next, rows_of(k + 1), col, colv, Dk, gate, dbk, prep);
             if constexpr (!AGG) {
                 if (k > 0) {
                     finalize(p, s.y[P ^ 1], held[P ^ 1], yb, TC, col, d0);

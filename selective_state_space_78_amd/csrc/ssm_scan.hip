@@ -50,6 +50,8 @@ constexpr int kDecodeRows = SSM_DECODE_ROWS;
 
 struct DecodeParams {
     const void *x, *delta, *z, *B, *C;
+    const float *delta_bias;   // (dim) or null
+    int delta_softplus;
     const float *A, *D;
     float *h;
     void *y;
@@ -98,6 +100,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
         for (int k = 0; k < 4; ++k) av[k] = n0 + k < p.N ? ap[k] : 0.0f;
     }
     const float Dd = p.D != nullptr ? p.D[dc] : 0.0f;
+    const float dbias = p.delta_bias != nullptr ? p.delta_bias[dc] : 0.0f;
 
     // groups of kDecodeRows rows, strided over the grid's y extent (<= 65535)
     const int ngroups = (p.batch + kDecodeRows - 1) / kDecodeRows;
@@ -161,7 +164,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
                 }
             }
             const float xv = Elem<T>::widen(xr[r]);
-            const float dv = Elem<T>::widen(dr[r]);
+            float dv = Elem<T>::widen(dr[r]) + dbias;
+            if (p.delta_softplus) dv = softplus_f(dv);
             const float du = dv * xv;
             float part = 0.0f;
 #pragma unroll
@@ -252,6 +256,11 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdReduceParams p
         float sd = 0.0f;
         for (int b = 0; b < p.batch; ++b) sd += p.part_d[(int64_t)b * p.dim + d];
         if (p.dD != nullptr) p.dD[d] = sd;
+        if (p.ddelta_bias != nullptr) {
+            float sb = 0.0f;
+            for (int b = 0; b < p.batch; ++b) sb += p.part_db[(int64_t)b * p.dim + d];
+            p.ddelta_bias[d] = sb;
+        }
     }
 }
 
@@ -355,6 +364,8 @@ int validate_desc(const ssm_scan_desc *d) {
     if (d->dtype != SSM_F32 && d->dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (d->disc != SSM_DISC_EULER && d->disc != SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
     if (d->dstate < 1 || d->dstate > 64) return SSM_ERR_UNSUPPORTED;
+    if ((d->delta_softplus != 0 && d->delta_softplus != 1) || d->reserved != 0) return SSM_ERR_UNSUPPORTED;
+    if (d->delta_bias != nullptr && !aligned(d->delta_bias, 4)) return SSM_ERR_ALIGN;
     // byte counts of the largest tensors must fit; kernel indices are 32-bit
     // for batch, dim and segment lengths
     int64_t bl, bld, bytes;
@@ -402,7 +413,8 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
     const Range r_ws = range_of(workspace, (int64_t)need);
     const Range inputs[] = {range_of(u, tok * es), range_of(delta, tok * es), range_of(z, z ? tok * es : 0),
                             range_of(B, bn * es), range_of(C, bn * es), range_of(A, d.dim * d.dstate * 4),
-                            range_of(D, D ? d.dim * 4 : 0), range_of(h0, h0 ? state * 4 : 0)};
+                            range_of(D, D ? d.dim * 4 : 0), range_of(h0, h0 ? state * 4 : 0),
+                            range_of(d.delta_bias, d.delta_bias ? d.dim * 4 : 0)};
     for (const Range &r : inputs) {
         if (overlaps(r_y, r) || overlaps(r_ws, r)) return SSM_ERR_ALIAS;
         // h_last may be exactly h0 (in-place resume), nothing else
@@ -419,6 +431,7 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
 
     ScanParams p{};
     p.u = u; p.delta = delta; p.z = z; p.B = B; p.C = C;
+    p.delta_bias = d.delta_bias; p.delta_softplus = d.delta_softplus;
     p.A = A; p.D = D; p.h0 = h0;
     p.y = y; p.h_last = h_last;
     p.L = d.seqlen;
@@ -465,7 +478,7 @@ struct BwdLayout {
     Plan pl;
     BwdShape sh;
     int nck, ntiles;
-    size_t ckpt, part_bc, part_a, part_d, total;
+    size_t ckpt, part_bc, part_a, part_d, part_db, total;
 };
 
 BwdLayout bwd_layout(const ssm_scan_desc &d) {
@@ -481,7 +494,8 @@ BwdLayout bwd_layout(const ssm_scan_desc &d) {
     w.part_bc = w.ckpt + align256((size_t)d.batch * w.nck * np * d.dim * 4);
     w.part_a = w.part_bc + align256((size_t)d.batch * w.ntiles * d.seqlen * np * 2 * 4);
     w.part_d = w.part_a + align256((size_t)d.batch * d.dim * np * 4);
-    w.total = w.part_d + align256((size_t)d.batch * d.dim * 4);
+    w.part_db = w.part_d + align256((size_t)d.batch * d.dim * 4);
+    w.total = w.part_db + (d.delta_bias != nullptr ? align256((size_t)d.batch * d.dim * 4) : 0);
     return w;
 }
 
@@ -493,7 +507,7 @@ size_t bwd_workspace_bytes(const ssm_scan_desc &d) {
 int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A, const void *B,
              const void *C, const float *D, const void *z, const float *h0, const void *dy, const float *dh_last,
              void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz, float *dh0,
-             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+             float *ddelta_bias, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (int rc = validate_desc(desc); rc != SSM_OK) return rc;
     const ssm_scan_desc d = *desc;
     if (d.batch == 0 || d.dim == 0) return SSM_OK;
@@ -504,6 +518,9 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     const int64_t adn = d.dim * d.dstate;
     if (A == nullptr || dA == nullptr) return SSM_ERR_NULL;
     if (D != nullptr && dD == nullptr) return SSM_ERR_NULL;
+    const float *dbias = d.delta_bias;
+    if (dbias != nullptr && ddelta_bias == nullptr) return SSM_ERR_NULL;
+    if (dbias == nullptr) ddelta_bias = nullptr;
     if (d.seqlen > 0 && (u == nullptr || delta == nullptr || B == nullptr || C == nullptr || dy == nullptr ||
                          du == nullptr || ddelta == nullptr || dB == nullptr || dC == nullptr ||
                          (z != nullptr && dz == nullptr)))
@@ -511,7 +528,7 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     const void *tok_ptrs[] = {u, delta, B, C, z, dy, du, ddelta, z ? dz : nullptr};
     for (const void *q : tok_ptrs)
         if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
-    const void *f32_ptrs[] = {A, D, h0, dh_last, dA, dB, dC, dD, dh0};
+    const void *f32_ptrs[] = {A, D, h0, dh_last, dA, dB, dC, dD, dh0, ddelta_bias};
     for (const void *q : f32_ptrs)
         if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
     if (workspace && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
@@ -525,11 +542,13 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     const Range outs[] = {range_of(du, tk * es), range_of(ddelta, tk * es), range_of(z ? dz : nullptr, tk * es),
                           range_of(dA, adn * 4), range_of(dB, d.seqlen > 0 ? bn * 4 : 0),
                           range_of(dC, d.seqlen > 0 ? bn * 4 : 0), range_of(D ? dD : nullptr, d.dim * 4),
-                          range_of(dh0, state * 4), range_of(workspace, (int64_t)need)};
+                          range_of(dh0, state * 4), range_of(ddelta_bias, d.dim * 4),
+                          range_of(workspace, (int64_t)need)};
     const Range ins[] = {range_of(u, tok * es), range_of(delta, tok * es), range_of(z, z ? tok * es : 0),
                          range_of(B, bn * es), range_of(C, bn * es), range_of(A, adn * 4),
                          range_of(D, D ? d.dim * 4 : 0), range_of(h0, h0 ? state * 4 : 0),
-                         range_of(dy, tok * es), range_of(dh_last, dh_last ? state * 4 : 0)};
+                         range_of(dy, tok * es), range_of(dh_last, dh_last ? state * 4 : 0),
+                         range_of(dbias, dbias ? d.dim * 4 : 0)};
     const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
     for (int i = 0; i < nout; ++i) {
         for (const Range &r : ins)
@@ -548,6 +567,9 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
         if (dh0 != nullptr)
             hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((state + 255) / 256)), dim3(256), 0, stream,
                                dh_last, dh0, state);
+        if (ddelta_bias != nullptr)
+            hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((d.dim + 255) / 256)), dim3(256), 0, stream,
+                               nullptr, ddelta_bias, d.dim);
         return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
     }
 
@@ -558,6 +580,7 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     // 1. checkpoints: the forward scan in its checkpoint mode (segment-parallel)
     ScanParams p{};
     p.u = u; p.delta = delta; p.z = z; p.B = B; p.C = C;
+    p.delta_bias = dbias; p.delta_softplus = d.delta_softplus;
     p.A = A; p.D = D; p.h0 = h0;
     p.L = d.seqlen;
     p.batch = (int)d.batch;
@@ -596,12 +619,14 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     // 2. the reverse pass
     BwdParams bp{};
     bp.u = u; bp.delta = delta; bp.z = z; bp.dy = dy;
+    bp.delta_bias = dbias; bp.delta_softplus = d.delta_softplus;
     bp.A = A; bp.D = D; bp.dh_last = dh_last;
     bp.Bf = p.Bf; bp.Cf = p.Cf; bp.ckpt = p.ckpt;
     bp.du = du; bp.ddelta = ddelta; bp.dz = dz; bp.dh0 = dh0;
     bp.part_bc = reinterpret_cast<float *>(ws + wl.part_bc);
     bp.part_a = reinterpret_cast<float *>(ws + wl.part_a);
     bp.part_d = reinterpret_cast<float *>(ws + wl.part_d);
+    bp.part_db = dbias ? reinterpret_cast<float *>(ws + wl.part_db) : nullptr;
     bp.L = d.seqlen;
     bp.batch = (int)d.batch;
     bp.dim = (int)d.dim;
@@ -617,8 +642,8 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
 
     // 3. sums of the partials
     BwdReduceParams rp{};
-    rp.part_bc = bp.part_bc; rp.part_a = bp.part_a; rp.part_d = bp.part_d;
-    rp.dB = dB; rp.dC = dC; rp.dA = dA; rp.dD = D ? dD : nullptr;
+    rp.part_bc = bp.part_bc; rp.part_a = bp.part_a; rp.part_d = bp.part_d; rp.part_db = bp.part_db;
+    rp.dB = dB; rp.dC = dC; rp.dA = dA; rp.dD = D ? dD : nullptr; rp.ddelta_bias = ddelta_bias;
     rp.L = d.seqlen;
     rp.batch = (int)d.batch;
     rp.dim = (int)d.dim;
@@ -669,13 +694,15 @@ extern "C" int ssm_scan_fwd(const ssm_scan_desc *desc, const void *u, const void
 }
 
 extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t dtype, int32_t disc,
-                                const void *x, const void *delta, const float *A, const void *B,
+                                const void *x, const void *delta, const float *delta_bias,
+                                int32_t delta_softplus, const float *A, const void *B,
                                 const void *C, const float *D, const void *z, float *h, void *y,
                                 hipStream_t stream) {
     if (batch < 0 || dim < 0) return SSM_ERR_SHAPE;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (disc != SSM_DISC_EULER && disc != SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
     if (dstate < 1 || dstate > 64) return SSM_ERR_UNSUPPORTED;
+    if (delta_softplus != 0 && delta_softplus != 1) return SSM_ERR_UNSUPPORTED;
     if (batch > INT32_MAX || dim > INT32_MAX) return SSM_ERR_SHAPE;
     int64_t ch, st, bytes;
     if (!mul_ok(batch, dim, &ch) || !mul_ok(ch, dstate * 4 * 16, &bytes)) return SSM_ERR_SHAPE;
@@ -688,18 +715,21 @@ extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int3
     const void *in_ptrs[] = {x, delta, B, C, z, y};
     for (const void *q : in_ptrs)
         if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
-    if (!aligned(A, 4) || !aligned(h, 4) || (D && !aligned(D, 4))) return SSM_ERR_ALIGN;
+    if (!aligned(A, 4) || !aligned(h, 4) || (D && !aligned(D, 4)) || (delta_bias && !aligned(delta_bias, 4)))
+        return SSM_ERR_ALIGN;
     const Range r_y = range_of(y, ch * es);
     const Range r_h = range_of(h, st * 4);
     const Range inputs[] = {range_of(x, ch * es), range_of(delta, ch * es), range_of(z, z ? ch * es : 0),
                             range_of(B, batch * dstate * es), range_of(C, batch * dstate * es),
-                            range_of(A, dim * dstate * 4), range_of(D, D ? dim * 4 : 0)};
+                            range_of(A, dim * dstate * 4), range_of(D, D ? dim * 4 : 0),
+                            range_of(delta_bias, delta_bias ? dim * 4 : 0)};
     for (const Range &r : inputs)
         if (overlaps(r_y, r) || overlaps(r_h, r)) return SSM_ERR_ALIAS;
     if (overlaps(r_y, r_h)) return SSM_ERR_ALIAS;
 
     DecodeParams p{};
     p.x = x; p.delta = delta; p.z = z; p.B = B; p.C = C;
+    p.delta_bias = delta_bias; p.delta_softplus = delta_softplus;
     p.A = A; p.D = D; p.h = h; p.y = y;
     p.batch = (int)batch;
     p.dim = (int)dim;
@@ -722,10 +752,10 @@ extern "C" size_t ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc) {
 extern "C" int ssm_scan_bwd(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A,
                             const void *B, const void *C, const float *D, const void *z, const float *h0,
                             const void *dy, const float *dh_last, void *du, void *ddelta, float *dA, float *dB,
-                            float *dC, float *dD, void *dz, float *dh0, void *workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+                            float *dC, float *dD, void *dz, float *dh0, float *ddelta_bias, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
     return bwd_impl(desc, u, delta, A, B, C, D, z, h0, dy, dh_last, du, ddelta, dA, dB, dC, dD, dz, dh0,
-                    workspace, workspace_bytes, stream);
+                    ddelta_bias, workspace, workspace_bytes, stream);
 }
 
 extern "C" const char *ssm_status_string(int status) {

@@ -192,6 +192,26 @@ def scan_inputs(cfg: ScanConfig, seed: int = 0, batch: int | None = None,
     )
 
 
+def raw_delta_inputs(cfg: ScanConfig, seed: int = 0, batch: int | None = None,
+                     seqlen: int | None = None, dim: int | None = None):
+    """The step before its bias and softplus, for the in-kernel step option:
+    delta_raw = 0.5 N(0, 1) (batch, L, dim) in the workload's element type and
+    the per-channel bias (dim,) float32, so that softplus(delta_raw + bias)
+    follows the same recipe as ``scan_inputs``' delta."""
+    b = cfg.batch if batch is None else batch
+    L = cfg.seqlen if seqlen is None else seqlen
+    d = cfg.dim if dim is None else dim
+    total = b * L * d
+
+    def fill(rng, lo, hi):
+        val = (0.5 * rng.standard_normal(hi - lo, dtype=np.float32)).astype(np.float32)
+        return to_bf16_bits(val) if cfg.dtype == "bf16" else val
+
+    out_dtype = np.uint16 if cfg.dtype == "bf16" else np.float32
+    raw = _blocked(_stream(seed, "delta_noise"), total, fill, out_dtype).reshape(b, L, d)
+    return dict(delta=raw, delta_bias=delta_bias(seed, d, cfg.bias).astype(np.float32))
+
+
 def grad_inputs(cfg: ScanConfig, seed: int = 0, batch: int | None = None,
                 seqlen: int | None = None, dim: int | None = None, dstate: int | None = None):
     """Upstream gradients for the backward of one scan workload: dy ~ N(0, 1) in

@@ -52,8 +52,8 @@ def test_status_strings(L):
     assert ssm.ssm_status_string(12345) == "unknown status"
 
 
-def desc(b=2, L=100, d=64, N=16, dtype=ssm.SSM_BF16, disc=0):
-    return ssm.ScanDesc(b, L, d, N, dtype, disc)
+def desc(b=2, L=100, d=64, N=16, dtype=ssm.SSM_BF16, disc=0, softplus=0, reserved=0, bias=None):
+    return ssm.ScanDesc(b, L, d, N, dtype, disc, softplus, reserved, bias)
 
 
 def fake(addr):
@@ -82,6 +82,10 @@ def test_scan_descriptor_errors(L):
     assert scan_call(L, desc(N=0)) == EUNSUP
     assert scan_call(L, desc(N=65)) == EUNSUP
     assert scan_call(L, desc(b=1 << 40, L=1 << 40)) == ESHAPE
+    assert scan_call(L, desc(softplus=2)) == EUNSUP
+    assert scan_call(L, desc(reserved=1)) == EUNSUP
+    assert scan_call(L, desc(bias=10 * GB + 2)) == EALIGN
+    assert scan_call(L, desc(bias=8 * GB + 64)) == EALIAS        # bias inside the output y
 
 
 def test_scan_empty_problem_is_ok(L):
@@ -150,13 +154,14 @@ def test_plan_shapes(L):
 
 
 def decode_call(L, b=4, d=64, N=16, dtype=ssm.SSM_BF16, disc=0, x=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB,
-                C=5 * GB, D=6 * GB, z=7 * GB, h=8 * GB, y=9 * GB):
+                C=5 * GB, D=6 * GB, z=7 * GB, h=8 * GB, y=9 * GB, softplus=0):
     ptrs = [fake(a) if a else None for a in (x, delta, A, B, C, D, z, h, y)]
-    return L.ssm_state_update(b, d, N, dtype, disc, *ptrs, None)
+    return L.ssm_state_update(b, d, N, dtype, disc, ptrs[0], ptrs[1], None, softplus, *ptrs[2:], None)
 
 
 def test_decode_errors(L):
     assert decode_call(L, b=-1) == ESHAPE
+    assert decode_call(L, softplus=2) == EUNSUP
     assert decode_call(L, dtype=9) == EDTYPE
     assert decode_call(L, disc=2) == EUNSUP
     assert decode_call(L, N=0) == EUNSUP
@@ -171,9 +176,9 @@ def test_decode_errors(L):
 
 def bwd_call(L, dsc, u=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB, h0=0,
              dy=8 * GB, dhl=0, du=9 * GB, dde=10 * GB, dA=11 * GB, dB=12 * GB, dC=13 * GB, dD=14 * GB,
-             dz=15 * GB, dh0=0, ws=16 * GB, ws_bytes=1 << 30):
+             dz=15 * GB, dh0=0, ddb=0, ws=16 * GB, ws_bytes=1 << 30):
     ptrs = [fake(a) if a else None for a in (u, delta, A, B, C, D, z, h0, dy, dhl, du, dde, dA, dB, dC, dD, dz,
-                                             dh0, ws)]
+                                             dh0, ddb, ws)]
     return L.ssm_scan_bwd(ctypes.byref(dsc) if dsc is not None else None, *ptrs, ws_bytes, None)
 
 
@@ -198,6 +203,8 @@ def test_bwd_errors(L):
     assert bwd_call(L, desc(), dB=11 * GB + 4) == EALIAS      # dB over dA
     assert bwd_call(L, desc(), ws=12 * GB) == EALIAS          # workspace over dB
     assert bwd_call(L, desc(), dh0=8 * GB + 128) == EALIAS    # dh0 over dy
+    assert bwd_call(L, desc(bias=17 * GB)) == ENULL           # a delta bias needs its gradient
+    assert bwd_call(L, desc(bias=17 * GB), ddb=17 * GB + 4) == EALIAS
 
 
 def test_bwd_workspace(L):

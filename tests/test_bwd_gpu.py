@@ -178,3 +178,22 @@ def test_bwd_mamba14b_full_size(env):
         e = rel_err(gk, sub[k])
         say("  sampled %-6s err %.3e" % (k, e))
         assert e <= TOL_BF16, (k, e)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("disc", ["euler", "zoh"])
+def test_bwd_delta_bias_softplus(env, dtype, disc):
+    torch, ssm = env
+    x, g = make_case("mamba130m", dtype, seed=31, batch=2, seqlen=70, dim=136, dstate=16)
+    cfg = cfg_of("mamba130m", dtype)
+    r = si.raw_delta_inputs(cfg, seed=31, batch=2, seqlen=70, dim=136)
+    x = dict(x, delta=r["delta"])
+    say("bwd %s %s with delta bias + softplus" % (dtype, disc))
+    dev = {k: to_dev(v, torch) for k, v in x.items() if k != "h0"}
+    out = ssm.ssm_scan_bwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], to_dev(g["dy"], torch),
+                           D=dev["D"], z=dev["z"], h0=to_dev(x["h0"], torch), dh_last=to_dev(g["dh_last"], torch),
+                           disc=disc, delta_bias=to_dev(r["delta_bias"], torch), delta_softplus=True)
+    torch.cuda.synchronize()
+    got = {k: to_np(v) for k, v in out.items()}
+    ref = ref_bwd(x, g, disc, delta_bias=r["delta_bias"], delta_softplus=True)
+    compare_all(x, got, ref, "softplus", keys=GRADS + ("ddelta_bias",))

@@ -134,3 +134,29 @@ def test_decode_workload_1000_steps(env):
     eh = rel_err(h[idx_b, idx_d].cpu().numpy(), href_s[:, 0, :])
     say("decode workload: sampled y over 1000 steps %.3e, final sampled state %.3e" % (ey, eh))
     assert ey <= TOL_BF16 and eh <= TOL_BF16
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_delta_bias_softplus(env, dtype):
+    """Decode with the step formed in the kernel: softplus(delta + bias)."""
+    torch, ssm = env
+    cfg, st, sets = decode_case(6, 200, 16, dtype, steps=3, seed=9)
+    rng = np.random.default_rng(77)
+    bias = st["bias"].astype(np.float32)
+    h = to_dev(st["h"], torch)
+    href = st["h"].astype(np.float64)
+    A, D = to_dev(st["A"], torch), to_dev(st["D"], torch)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    for k, s in enumerate(sets):
+        raw = (0.5 * rng.standard_normal(s["delta"].shape)).astype(np.float32)
+        if dtype == "bf16":
+            raw = si.to_bf16_bits(raw)
+        y = ssm.ssm_state_update(to_dev(s["x"], torch), to_dev(raw, torch), A, to_dev(s["B"], torch),
+                                 to_dev(s["C"], torch), h, D=D, z=to_dev(s["z"], torch),
+                                 delta_bias=to_dev(bias, torch), delta_softplus=True)
+        yr = oracle.load().state_update(s["x"], raw, st["A"], s["B"], s["C"], href, D=st["D"], z=s["z"],
+                                        delta_bias=bias, delta_softplus=True)
+        torch.cuda.synchronize()
+        ey, eh = rel_err(to_np(y), yr), rel_err(h.cpu().numpy(), href)
+        say("decode softplus %s step %d: y %.3e h %.3e" % (dtype, k, ey, eh))
+        assert ey <= tol and eh <= tol, (k, ey, eh)

@@ -267,3 +267,38 @@ def test_config_mamba1p4b_full_size(env):
 def test_config_long_full_size(env):
     """Long context (b1 L131072 d5120 N16, log-uniform delta bias), bench launch shape."""
     full_size_check(env, "long")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("disc", ["euler", "zoh"])
+def test_delta_bias_softplus(env, dtype, disc):
+    """The step formed in the kernel: softplus(delta + bias), and bias alone."""
+    import dataclasses
+    torch, ssm = env
+    cfg = dataclasses.replace(si.CONFIGS["mamba130m"], dtype=dtype)
+    x0 = si.scan_inputs(cfg, seed=21, batch=2, seqlen=300, dim=136)
+    r = si.raw_delta_inputs(cfg, seed=21, batch=2, seqlen=300, dim=136)
+    x = dict(x0, delta=r["delta"])
+    tol = tol_of(x)
+    dev = {k: to_dev(v, torch) for k, v in x.items() if k != "h0"}
+    # softplus(raw + bias); and a bias alone on the (positive) steps
+    small = np.random.default_rng(3).uniform(0.0, 0.01, 136).astype(np.float32)
+    cases = [(True, x, r["delta_bias"]), (False, x0, small)]
+    for sp, xc, bnp in cases:
+        yr, hr = oracle.load().selective_scan(**xc, disc=disc, delta_bias=bnp, delta_softplus=sp)
+        dlt = to_dev(xc["delta"], torch)
+        bias = to_dev(bnp, torch)
+        for tuning in (None, (4, 3)):
+            say("delta %s bias%s %s %s tuning %s" % (dtype, " + softplus" if sp else "", disc, dtype, tuning))
+            y, hl = ssm.ssm_scan_fwd(dev["u"], dlt, dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                                     disc=disc, tuning=tuning, delta_bias=bias, delta_softplus=sp)
+            torch.cuda.synchronize()
+            ey, eh = rel_err(to_np(y), yr), rel_err(to_np(hl), hr)
+            say("  y %.3e h %.3e" % (ey, eh))
+            assert ey <= tol and eh <= tol, (sp, tuning, ey, eh)
+    # softplus alone (no bias), every channel's step from the raw delta
+    yr, hr = oracle.load().selective_scan(**x, disc=disc, delta_softplus=True)
+    y, hl = ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                             disc=disc, delta_softplus=True)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(y), yr) <= tol and rel_err(to_np(hl), hr) <= tol
