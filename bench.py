@@ -75,10 +75,12 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms)))
 
 
-def measured_traffic(workload: str, plan):
+def measured_traffic(workload: str, plan, default_options=True):
     """HBM bytes per launch of the main scan kernel from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source
-    in the same launch shape."""
+    in the same launch shape (and with the default step and discretisation)."""
+    if not default_options:
+        return None
     try:
         with open(os.path.join(PROFILES, "traffic_scan_%s.json" % workload)) as f:
             rec = json.load(f)
@@ -89,7 +91,7 @@ def measured_traffic(workload: str, plan):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(x, y_dev, torch, budget_s=15.0):
+def cpu_baseline(x, y_dev, torch, budget_s=15.0, opts=None):
     """The fp64 oracle, as it stands, on batch row 0 of the same workload for a
     bounded number of channels over the full sequence. Its outputs are also
     compared with the GPU's timed outputs for those channels."""
@@ -105,12 +107,13 @@ def cpu_baseline(x, y_dev, torch, budget_s=15.0):
     # order, every token, k bounded by the time budget and the workload
     probe = [(0, d) for d in range(min(dim, 4 * threads))]
     t0 = time.perf_counter()
-    o.selective_scan(**x, channels=probe, nthreads=threads, want_y=False)
+    opts = opts or {}
+    o.selective_scan(**x, channels=probe, nthreads=threads, want_y=False, **opts)
     per_ch = (time.perf_counter() - t0) / len(probe)
     k = int(min(batch * dim, max(threads, budget_s / max(per_ch, 1e-12))))
     chans = [(c // dim, c % dim) for c in range(k)]
     t0 = time.perf_counter()
-    yr, hr = o.selective_scan(**x, channels=chans, nthreads=threads)
+    yr, hr = o.selective_scan(**x, channels=chans, nthreads=threads, **opts)
     sec = time.perf_counter() - t0
     # compare with the GPU's timed outputs for a subset of the sampled channels
     sub = list(range(0, k, max(1, k // 256)))
@@ -162,18 +165,20 @@ def bench_decode(torch, ssm, steps=200, warmup=10, nsets=16):
     }
 
 
-def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2):
+def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_opts=None):
     """Time ssm_scan_bwd (checkpoint pass + reverse pass + reduction) on the workload."""
     g = si.grad_inputs(cfg, seed=0)
     dy = to_dev(g["dy"], torch)
     dhl = to_dev(g["dh_last"], torch)
-    need = ssm.ssm_scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, ssm.SSM_BF16)
+    step_opts = step_opts or {}
+    need = ssm.ssm_scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, ssm.SSM_BF16, disc,
+                                           **step_opts)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     out = {}
 
     def call():
         r = ssm.ssm_scan_bwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dy, D=dev["D"], z=dev["z"],
-                             dh_last=dhl, workspace=ws, out=out)
+                             dh_last=dhl, workspace=ws, out=out, disc=disc, **step_opts)
         out.update(r)
 
     for _ in range(warmup):
@@ -203,6 +208,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--disc", choices=["euler", "zoh"], default="euler",
+                    help="discretisation of B (default: the simplified delta*B)")
+    ap.add_argument("--delta-softplus", action="store_true",
+                    help="form the step in the kernel: softplus(delta_raw + bias)")
     ap.add_argument("--tuning", type=str, default=None, help="state_groups,segments")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=WORKLOAD,
                     help="scan workload of the timed step (the default is the headline one)")
@@ -222,6 +231,14 @@ def main():
     print("bench: generating %s inputs" % args.workload, file=sys.stderr, flush=True)
     x = si.scan_inputs(cfg, seed=0)
     dev = {k: to_dev(v, torch) for k, v in x.items() if v is not None}
+    step_opts = {}
+    oracle_opts = {"disc": args.disc}
+    if args.delta_softplus:
+        r = si.raw_delta_inputs(cfg, seed=0)
+        x = dict(x, delta=r["delta"])
+        dev["delta"] = to_dev(r["delta"], torch)
+        step_opts = dict(delta_bias=to_dev(r["delta_bias"], torch), delta_softplus=True)
+        oracle_opts.update(delta_bias=r["delta_bias"], delta_softplus=True)
     y = torch.empty((cfg.batch, cfg.seqlen, cfg.dim), dtype=torch.bfloat16, device="cuda")
     h_last = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device="cuda")
     tuning = tuple(int(v) for v in args.tuning.split(",")) if args.tuning else None
@@ -231,7 +248,7 @@ def main():
 
     def step():
         ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
-                         y=y, h_last=h_last, workspace=ws, tuning=tuning)
+                         y=y, h_last=h_last, workspace=ws, tuning=tuning, disc=args.disc, **step_opts)
 
     print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -278,6 +295,7 @@ def main():
             "workload": WORKLOADS[args.workload],
             "global_batch": cfg.batch, "seq_len": cfg.seqlen, "dim": cfg.dim, "dstate": cfg.dstate,
             "io_dtype": "bf16", "parallelism": "none (1 GPU)",
+            "disc": args.disc, "step": "softplus(delta + bias) in the kernel" if args.delta_softplus else "delta as given",
             "launch": {"state_groups": plan[0], "segments": plan[1]},
         },
         "roofline": {
@@ -289,7 +307,7 @@ def main():
             "frac": achieved_tops / VALU_PEAK_TOPS,
             "ops_per_token_ch": valu_ops_per_token_ch(cfg.dstate, cfg.gate),
             "mean_launch_ms": mean_launch_ms,
-            "traffic": measured_traffic(args.workload, plan),
+            "traffic": measured_traffic(args.workload, plan, args.disc == "euler" and not args.delta_softplus),
         },
         "hbm": {
             "algorithmic_bytes_per_launch": nbytes,
@@ -307,13 +325,13 @@ def main():
         out["calib_copy_bytes"] = 1 << 30
     if not args.no_bwd:
         print("bench: backward", file=sys.stderr, flush=True)
-        out["backward"] = bench_backward(torch, ssm, cfg, dev)
+        out["backward"] = bench_backward(torch, ssm, cfg, dev, disc=args.disc, step_opts=step_opts)
     if not args.no_decode:
         print("bench: decode", file=sys.stderr, flush=True)
         out["decode"] = bench_decode(torch, ssm)
     if not args.no_cpu:
         print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(x, y, torch)
+        out["cpu_baseline"] = cpu_baseline(x, y, torch, opts=oracle_opts)
     print(json.dumps(out), flush=True)
 
 

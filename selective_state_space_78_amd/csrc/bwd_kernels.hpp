@@ -450,10 +450,10 @@ struct BwdKernel {
                         const float bq = __uint_as_float(kPacked ? wb << 16 : wb);
                         const float cq = __uint_as_float(kPacked ? wb & 0xffff0000u : cw[t * NPW + q]);
                         if constexpr (ZOH) {
-                            const float em1 = expm1f(v.x * A[q]);
-                            const float coef = A[q] != 0.0f ? em1 * Ainv[q] : v.x;
-                            h[q] = fmaf(1.0f + em1, h[q], coef * bq * v.y);
-                            if constexpr (kKeepA) as[t][q] = em1;
+                            const float a = __builtin_amdgcn_exp2f(v.x * A2[q]);
+                            const float ph = expm1_over_x(v.x * A[q], a);
+                            h[q] = fmaf(a, h[q], ph * (v.x * v.y * bq));
+                            if constexpr (kKeepA) as[t][q] = a;
                         } else {
                             const float a = __builtin_amdgcn_exp2f(v.x * A2[q]);
                             h[q] = fmaf(a, h[q], v.y * bq);
@@ -495,13 +495,7 @@ struct BwdKernel {
                     const uint32_t wb = bw[t * NPW + q];
                     const float bq = __uint_as_float(kPacked ? wb << 16 : wb);
                     const float cq = __uint_as_float(kPacked ? wb & 0xffff0000u : cw[t * NPW + q]);
-                    float a, em1 = 0.0f;
-                    if constexpr (ZOH) {
-                        em1 = kKeepA ? as[t][q] : expm1f(v.x * A[q]);
-                        a = 1.0f + em1;
-                    } else {
-                        a = kKeepA ? as[t][q] : __builtin_amdgcn_exp2f(v.x * A2[q]);
-                    }
+                    const float a = kKeepA ? as[t][q] : __builtin_amdgcn_exp2f(v.x * A2[q]);
                     const float l = fmaf(cq, dsv, mu[q]);
                     const float hp = t > 0 ? hs[t - 1][q] : hstart[q];
                     const float daa = l * hp * a;
@@ -509,9 +503,10 @@ struct BwdKernel {
                     dA[q] = fmaf(daa, v.x, dA[q]);
                     float vb;
                     if constexpr (ZOH) {
-                        const float f = A[q] != 0.0f ? em1 * Ainv[q] : v.x;
-                        // d f / d A = (delta a - f) / A, by its series near 0 (cancellation)
+                        // f = expm1(delta A)/A = delta phi(delta A)
                         const float xa = v.x * A[q];
+                        const float f = v.x * expm1_over_x(xa, a);
+                        // d f / d A = (delta a - f) / A, by its series near 0 (cancellation)
                         float dfdA;
                         if (fabsf(xa) < 0.125f)
                             dfdA = v.x * v.x *
@@ -623,9 +618,11 @@ struct BwdKernel {
     }
 };
 
-// at least 4 waves per SIMD: two 8-wave workgroups (or one 16-wave one) per CU
+// the simplified rule fits 128 VGPRs: at least 4 waves per SIMD (two 8-wave
+// workgroups, or one 16-wave one, per CU); the hold rule's reverse step needs
+// more registers, and capping it at 128 spilled 80-170 of them to scratch
 template <typename T, int NPW, int G, int TC, bool ZOH>
-__global__ __launch_bounds__(kTile * G, 4) void bwd_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kTile * G, ZOH ? 2 : 4) void bwd_kernel(const BwdParams p) {
     BwdKernel<T, NPW, G, TC, ZOH>::run(p);
 }
 

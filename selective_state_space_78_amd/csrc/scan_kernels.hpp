@@ -96,6 +96,23 @@ __device__ __forceinline__ float softplus_f(float x) {
     return fmaxf(x, 0.0f) + l;
 }
 
+// The zero-order-hold input coefficient (exp(x) - 1)/x for x = delta*A (so the
+// held input term is phi * delta * B * u), given a = exp(x) as the decay
+// already computes it. |x| < 0.5: Taylor series to x^7 (truncation below
+// 1.2e-8 relative; x = 0, i.e. A = 0, gives 1, the limit); otherwise
+// (a - 1)/x, where a - 1 loses at most 1.5e-7 relative.
+__device__ __forceinline__ float expm1_over_x(float x, float a) {
+    float p = fmaf(x, 1.0f / 40320.0f, 1.0f / 5040.0f);
+    p = fmaf(x, p, 1.0f / 720.0f);
+    p = fmaf(x, p, 1.0f / 120.0f);
+    p = fmaf(x, p, 1.0f / 24.0f);
+    p = fmaf(x, p, 1.0f / 6.0f);
+    p = fmaf(x, p, 0.5f);
+    p = fmaf(x, p, 1.0f);
+    const float q = (a - 1.0f) * __builtin_amdgcn_rcpf(x);
+    return fabsf(x) < 0.5f ? p : q;
+}
+
 struct ScanParams {
     const void *u, *delta, *z, *B, *C;
     const float *delta_bias;  // (dim) added to delta before the recurrence uses it, or null
@@ -442,7 +459,7 @@ struct ScanKernel {
 
     struct Lane {
         float A2[NPW], h[NPW];
-        float Az[ZOH ? NPW : 1], Ainv[ZOH ? NPW : 1];
+        float Az[ZOH ? NPW : 1];
         float dsum, dcomp;   // compensated sum of delta (aggregate pass)
     };
 
@@ -473,14 +490,15 @@ struct ScanKernel {
         const float2 v = dx[t][lane];
         const float dd = v.x;
         const float xx = v.y;
+        const float du = ZOH ? dd * xx : 0.0f;       // hold rule: xx is u
         float part = 0.0f;
 #pragma unroll
         for (int q = 0; q < NPW; ++q) {
             const float bq = b_of(bc[q]);
             if constexpr (ZOH) {
-                const float em1 = expm1f(dd * l.Az[q]);
-                const float coef = (l.Az[q] != 0.0f) ? em1 * l.Ainv[q] : dd;
-                l.h[q] = fmaf(1.0f + em1, l.h[q], coef * bq * xx);
+                const float a = __builtin_amdgcn_exp2f(dd * l.A2[q]);
+                const float ph = expm1_over_x(dd * l.Az[q], a);
+                l.h[q] = fmaf(a, l.h[q], ph * (du * bq));
             } else {
                 const float a = __builtin_amdgcn_exp2f(dd * l.A2[q]);
                 l.h[q] = fmaf(a, l.h[q], xx * bq);
@@ -521,10 +539,7 @@ struct ScanKernel {
             const bool nv = n < p.N;
             const float a = nv ? p.A[(int64_t)dc * p.N + n] : 0.0f;
             l.A2[k] = a * kLog2e;
-            if constexpr (ZOH) {
-                l.Az[k] = a;
-                l.Ainv[k] = (a != 0.0f) ? 1.0f / a : 0.0f;
-            }
+            if constexpr (ZOH) l.Az[k] = a;
             float h_init = 0.0f;
             if (MODE != kModeAggregate && nv) {
                 // with segments, every segment (also the first) starts from the

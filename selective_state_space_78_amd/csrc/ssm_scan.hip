@@ -171,9 +171,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 if constexpr (ZOH) {
-                    const float em1 = expm1f(dv * av[k]);
-                    const float coef = (av[k] != 0.0f) ? em1 / av[k] : dv;
-                    hv[r][k] = fmaf(1.0f + em1, hv[r][k], coef * bv[k] * xv);
+                    const float a = __builtin_amdgcn_exp2f(dv * av[k] * kLog2e);
+                    hv[r][k] = fmaf(a, hv[r][k], dv * expm1_over_x(dv * av[k], a) * bv[k] * xv);
                 } else {
                     hv[r][k] = fmaf(__builtin_amdgcn_exp2f(dv * av[k] * kLog2e), hv[r][k], du * bv[k]);
                 }
