@@ -47,6 +47,16 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _conv(weight, bias, dim):
+    """fp64 copies of the convolution prologue's weights (dim, W) and bias (dim,)."""
+    if weight is None:
+        return None, None, 0
+    w = np.ascontiguousarray(weight, dtype=np.float64)
+    assert w.ndim == 2 and w.shape[0] == dim
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    return w, b, int(w.shape[1])
+
+
 class Oracle:
     """ctypes handle on one compiled oracle library. ``threads`` is the OpenMP
     thread count used when a call passes ``nthreads=0`` (0: the runtime's)."""
@@ -54,16 +64,16 @@ class Oracle:
     def __init__(self, path: str, threads: int = 0):
         lib = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
-        lib.oracle_selective_scan.argtypes = [i64, i64, i64, i64, i32, i32,
+        lib.oracle_selective_scan.argtypes = [i64, i64, i64, i64, i32, i32, i32, vp, vp,
                                               vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                               i64, vp, vp, vp, i32]
         lib.oracle_selective_scan.restype = i32
         lib.oracle_state_update.argtypes = [i64, i64, i64, i32, i32,
                                             vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i32]
         lib.oracle_state_update.restype = i32
-        lib.oracle_selective_scan_bwd.argtypes = [i64, i64, i64, i64, i32, i32,
+        lib.oracle_selective_scan_bwd.argtypes = [i64, i64, i64, i64, i32, i32, i32, vp, vp,
                                                   vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                                  i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+                                                  i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         lib.oracle_selective_scan_bwd.restype = i32
         self.lib = lib
         self.path = path
@@ -81,7 +91,7 @@ class Oracle:
 
     def selective_scan(self, u, delta, A, B, C, D=None, z=None, h0=None,
                        disc="euler", channels=None, nthreads=0, want_y=True,
-                       delta_bias=None, delta_softplus=False):
+                       delta_bias=None, delta_softplus=False, conv_weight=None, conv_bias=None):
         """Scan (batch, L, dim) inputs.
 
         Returns ``(y, h_last)``. With ``channels=None`` every channel is
@@ -89,7 +99,9 @@ class Oracle:
         With ``channels`` a sequence of (b, d) pairs, ``y`` is (k, L) and
         ``h_last`` is (k, N), row i belonging to ``channels[i]``.
         ``delta_bias`` (dim,) is added to delta, and ``delta_softplus`` passes
-        the sum through softplus, before the recurrence uses it.
+        the sum through softplus, before the recurrence uses it. With
+        ``conv_weight`` (dim, W) (and ``conv_bias`` (dim,)), ``u`` holds x and
+        the scan input is silu(causal depthwise conv1d(x) + bias).
         """
         u = np.ascontiguousarray(u)
         batch, L, dim = u.shape
@@ -117,7 +129,8 @@ class Oracle:
         y = np.empty((nsel, L), np.float64) if want_y else None
         hl = np.empty((nsel, N), np.float64)
         dbias = None if delta_bias is None else np.ascontiguousarray(delta_bias, dtype=np.float64)
-        rc = self.lib.oracle_selective_scan(batch, L, dim, N, typ, _DISC[disc],
+        cw, cb, W = _conv(conv_weight, conv_bias, dim)
+        rc = self.lib.oracle_selective_scan(batch, L, dim, N, typ, _DISC[disc], W, _ptr(cw), _ptr(cb),
                                             _ptr(u), _ptr(delta), _ptr(dbias), int(bool(delta_softplus)),
                                             _ptr(A64), _ptr(B), _ptr(C),
                                             _ptr(D64), _ptr(zc), _ptr(h064),
@@ -132,7 +145,7 @@ class Oracle:
 
     def selective_scan_bwd(self, u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None,
                            disc="euler", channels=None, want_bc=True, want_tokens=True, nthreads=0,
-                           delta_bias=None, delta_softplus=False):
+                           delta_bias=None, delta_softplus=False, conv_weight=None, conv_bias=None):
         """Gradients of sum(dy * y) + sum(dh_last * h_last) with respect to every input.
 
         Returns a dict. With ``channels=None``: du, ddelta, dz (batch, L, dim),
@@ -143,7 +156,9 @@ class Oracle:
         ``want_tokens=False`` skips du, ddelta and dz (None in the result).
         With ``delta_bias`` / ``delta_softplus`` (as in selective_scan), ddelta is
         the gradient of the raw delta and ddelta_bias (dim) (or its per-channel
-        share ddelta_bias_c) that of the bias.
+        share ddelta_bias_c) that of the bias. With the convolution prologue,
+        du is the gradient of x and dconv_weight (dim, W), dconv_bias (dim)
+        (or their shares dconv_weight_c, dconv_bias_c) are added.
         """
         u = np.ascontiguousarray(u)
         batch, L, dim = u.shape
@@ -171,26 +186,32 @@ class Oracle:
         dz = np.empty((nsel, L)) if zc is not None and want_tokens else None
         dA_c = np.empty((nsel, N)); dD_c = np.empty(nsel); dDb_c = np.empty(nsel); dh0 = np.empty((nsel, N))
         dbias = None if delta_bias is None else np.ascontiguousarray(delta_bias, dtype=np.float64)
+        cw, cb, W = _conv(conv_weight, conv_bias, dim)
+        dcw_c = np.empty((nsel, W)) if W else None
+        dcb_c = np.empty(nsel) if W else None
         dB = np.empty((batch, L, N)) if want_bc else None
         dC = np.empty((batch, L, N)) if want_bc else None
-        rc = self.lib.oracle_selective_scan_bwd(batch, L, dim, N, typ, _DISC[disc],
+        rc = self.lib.oracle_selective_scan_bwd(batch, L, dim, N, typ, _DISC[disc], W, _ptr(cw), _ptr(cb),
                                                 _ptr(u), _ptr(delta), _ptr(dbias), int(bool(delta_softplus)),
                                                 _ptr(A64), _ptr(B), _ptr(C),
                                                 _ptr(D64), _ptr(zc), _ptr(h064), _ptr(dy64), _ptr(dhl),
                                                 nsel, _ptr(sel), _ptr(du), _ptr(dde), _ptr(dz),
-                                                _ptr(dA_c), _ptr(dD_c), _ptr(dDb_c), _ptr(dh0), _ptr(dB), _ptr(dC),
+                                                _ptr(dA_c), _ptr(dD_c), _ptr(dDb_c), _ptr(dcw_c), _ptr(dcb_c),
+                                                _ptr(dh0), _ptr(dB), _ptr(dC),
                                                 int(nthreads or self.threads))
         if rc != 0:
             raise ValueError("oracle_selective_scan_bwd rejected its arguments")
         if channels is not None:
             return dict(du=du, ddelta=dde, dz=dz, dA_c=dA_c, dD_c=dD_c, ddelta_bias_c=dDb_c, dh0=dh0,
-                        dB=dB, dC=dC)
+                        dB=dB, dC=dC, dconv_weight_c=dcw_c, dconv_bias_c=dcb_c)
 
         def per_token(a):
             return None if a is None else a.reshape(batch, dim, L).transpose(0, 2, 1).copy()
         return dict(du=per_token(du), ddelta=per_token(dde), dz=per_token(dz),
                     dA=dA_c.reshape(batch, dim, N).sum(axis=0), dD=dD_c.reshape(batch, dim).sum(axis=0),
                     ddelta_bias=dDb_c.reshape(batch, dim).sum(axis=0),
+                    dconv_weight=None if not W else dcw_c.reshape(batch, dim, W).sum(axis=0),
+                    dconv_bias=None if not W else dcb_c.reshape(batch, dim).sum(axis=0),
                     dh0=dh0.reshape(batch, dim, N), dB=dB, dC=dC)
 
     def state_update(self, x, delta, A, B, C, h, D=None, z=None, disc="euler", nthreads=0,

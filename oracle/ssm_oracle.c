@@ -14,6 +14,11 @@
  *   h[n]  = h0[b,d,n], or 0 when no initial state is given
  *           (eommydocs "State Space Models (SSM)", §3.2 pseudo-code and §5.1
  *            SelectiveSSM._selective_scan start from a zero state)
+ *   with a causal depthwise convolution of width W (the prologue of the Mamba
+ *   block: youngju.dev MambaBlock.forward, x_conv = silu(conv1d(x)) with
+ *   left padding W-1 and the first L outputs kept), the scan input is
+ *     u[b,t,d] = silu(cb[d] + sum_{k<W} cw[d,k] * x[b, t-(W-1)+k, d]),  x[t<0] = 0
+ *   and the buffer passed as u holds x; otherwise u is used as given.
  *   for t = 0 .. L-1:
  *     delta = delta[b,t,d] (+ delta_bias[d]), through softplus when asked
  *     a[n]  = exp(delta * A[d,n])                          (discretised A)
@@ -51,6 +56,9 @@
  *                               df/dA = (delta*a - f)/A (A -> 0: delta^2/2):
  *                               ddelta += lam*a*B*u, du += lam*f*B, dB += lam*f*u, dA += lam*df/dA*B*u
  *   readout:        dC_t += ds_t * h_t,  dD += ds_t * u_t,  du_t += D * ds_t
+ *   With the convolution prologue, du above is the gradient of u = silu(pre);
+ *   dpre_t = du_t * silu'(pre_t) gives dx[t-(W-1)+k] += cw[k] dpre_t,
+ *   dcw[k] += dpre_t x[t-(W-1)+k] and dcb += dpre_t, and the returned du is dx.
  *   dh0 = a_0 * lam_0; with a bias / softplus on delta, ddelta is taken with
  *   respect to the raw delta (times sigmoid of the softplus argument) and
  *   ddelta_bias[d] is its sum over batch and time.
@@ -86,6 +94,29 @@ static double load(const void *p, int type, int64_t i)
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* The causal depthwise convolution (width W, weights cw (dim, W), bias cb)
+ * and SiLU of x, for token t of channel (b, d); *pre receives the
+ * convolution before the SiLU. Without a convolution (W == 0): x itself. */
+static double scan_input(const void *x, int type, int64_t b, int64_t t, int64_t L, int64_t dim, int64_t d,
+                         int W, const double *cw, const double *cb, double *pre)
+{
+    if (W == 0) {
+        const double v = load(x, type, (b * L + t) * dim + d);
+        if (pre)
+            *pre = v;
+        return v;
+    }
+    double acc = cb ? cb[d] : 0.0;
+    for (int k = 0; k < W; ++k) {
+        const int64_t s = t - (W - 1) + k;
+        if (s >= 0)
+            acc += cw[d * W + k] * load(x, type, (b * L + s) * dim + d);
+    }
+    if (pre)
+        *pre = acc;
+    return acc / (1.0 + exp(-acc));
 }
 
 /* Input part of one state's update for one token: the B̄·u term. */
@@ -139,7 +170,7 @@ static double step_size(const void *delta, int type, int64_t i, int64_t d,
  *   hl   : N final states (contiguous), may be NULL
  */
 static void scan_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
-                         int type, int disc,
+                         int type, int disc, int W, const double *cw, const double *cb,
                          const void *u, const void *delta, const double *dbias, int sp,
                          const double *A, const void *B, const void *C,
                          const double *D, const void *z, const double *h0,
@@ -151,7 +182,7 @@ static void scan_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N
 
     for (int64_t t = 0; t < L; ++t) {
         const int64_t row = b * L + t;        /* token index (b, t) */
-        const double ut = load(u, type, row * dim + d);
+        const double ut = scan_input(u, type, b, t, L, dim, d, W, cw, cb, NULL);
         const double dt = step_size(delta, type, row * dim + d, d, dbias, sp, NULL);
         double yt = 0.0;
         for (int64_t n = 0; n < N; ++n) {
@@ -187,7 +218,8 @@ static void scan_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N
  * Returns 0, or -1 for a bad argument.
  */
 int oracle_selective_scan(int64_t batch, int64_t L, int64_t dim, int64_t N,
-                          int type, int disc,
+                          int type, int disc, int conv_width, const double *conv_weight,
+                          const double *conv_bias,
                           const void *u, const void *delta, const double *delta_bias, int delta_softplus,
                           const double *A,
                           const void *B, const void *C, const double *D,
@@ -202,6 +234,8 @@ int oracle_selective_scan(int64_t batch, int64_t L, int64_t dim, int64_t N,
     if (disc != ORACLE_EULER && disc != ORACLE_ZOH)
         return -1;
     if ((L > 0 && (!u || !delta || !B || !C)) || !A)
+        return -1;
+    if (conv_width < 0 || conv_width > 64 || (conv_width > 0 && !conv_weight))
         return -1;
     if (!sel)
         nsel = batch * dim;
@@ -222,7 +256,8 @@ int oracle_selective_scan(int64_t batch, int64_t L, int64_t dim, int64_t N,
                 bad = 1;
                 continue;
             }
-            scan_channel(c / dim, c % dim, L, dim, N, type, disc, u, delta, delta_bias, delta_softplus, A, B, C,
+            scan_channel(c / dim, c % dim, L, dim, N, type, disc, conv_width, conv_weight, conv_bias,
+                         u, delta, delta_bias, delta_softplus, A, B, C,
                          D, z, h0, h, y ? y + k * L : NULL, h_last ? h_last + k * N : NULL);
         }
     }
@@ -292,14 +327,14 @@ static double silu_grad(double z)
  * NULL); dB and dC (batch, L, N) are accumulated into (may be NULL).
  */
 static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
-                        int type, int disc,
+                        int type, int disc, int W, const double *cw, const double *cb,
                         const void *u, const void *delta, const double *dbias, int sp,
                         const double *A, const void *B, const void *C,
                         const double *D, const void *z, const double *h0,
                         const double *dy, const double *dh_last,
-                        double *hs, double *ss, double *lam,
+                        double *hs, double *ss, double *lam, double *gu, double *pre,
                         double *du, double *dde, double *dz, double *dA_c, double *dD_c,
-                        double *dDb_c, double *dh0_c, double *dB, double *dC)
+                        double *dDb_c, double *dcw_c, double *dcb_c, double *dh0_c, double *dB, double *dC)
 {
     const double dskip = D ? D[d] : 0.0;
     /* forward, keeping every state: hs[(t+1)*N + n] = h_t[n] */
@@ -307,7 +342,7 @@ static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
         hs[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
     for (int64_t t = 0; t < L; ++t) {
         const int64_t row = b * L + t;
-        const double ut = load(u, type, row * dim + d);
+        const double ut = scan_input(u, type, b, t, L, dim, d, W, cw, cb, &pre[t]);
         const double dt = step_size(delta, type, row * dim + d, d, dbias, sp, NULL);
         double st = 0.0;
         for (int64_t n = 0; n < N; ++n) {
@@ -327,7 +362,7 @@ static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
     double dDacc = 0.0, dDbacc = 0.0;
     for (int64_t t = L - 1; t >= 0; --t) {
         const int64_t row = b * L + t;
-        const double ut = load(u, type, row * dim + d);
+        const double ut = W ? pre[t] / (1.0 + exp(-pre[t])) : load(u, type, row * dim + d);
         double dstep;                                                 /* d(step)/d(delta) */
         const double dt = step_size(delta, type, row * dim + d, d, dbias, sp, &dstep);
         const double dyt = dy[row * dim + d];
@@ -371,13 +406,40 @@ static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
         }
         ddt *= dstep;                               /* through the bias and softplus */
         dDbacc += ddt;
-        if (du)
-            du[t] = dut;
+        gu[t] = dut;
         if (dde)
             dde[t] = ddt;
     }
     *dD_c = dDacc;
     *dDb_c = dDbacc;
+    if (W == 0) {
+        if (du)
+            for (int64_t t = 0; t < L; ++t)
+                du[t] = gu[t];
+    } else {
+        /* through the SiLU and the convolution: du becomes the gradient of x */
+        for (int k = 0; k < W; ++k)
+            dcw_c[k] = 0.0;
+        double dcb = 0.0;
+        if (du)
+            for (int64_t t = 0; t < L; ++t)
+                du[t] = 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double p = pre[t];
+            const double sg = 1.0 / (1.0 + exp(-p));
+            const double dp = gu[t] * sg * (1.0 + p * (1.0 - sg));
+            dcb += dp;
+            for (int k = 0; k < W; ++k) {
+                const int64_t s = t - (W - 1) + k;
+                if (s < 0)
+                    continue;
+                dcw_c[k] += dp * load(u, type, (b * L + s) * dim + d);
+                if (du)
+                    du[s] += cw[d * W + k] * dp;
+            }
+        }
+        *dcb_c = dcb;
+    }
     if (dh0_c)
         for (int64_t n = 0; n < N; ++n)
             dh0_c[n] = lam[n];
@@ -399,7 +461,8 @@ static void bwd_channel(int64_t b, int64_t d, int64_t L, int64_t dim, int64_t N,
  * Returns 0, or -1 for a bad argument or an allocation failure.
  */
 int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
-                              int type, int disc,
+                              int type, int disc, int conv_width, const double *conv_weight,
+                              const double *conv_bias,
                               const void *u, const void *delta, const double *delta_bias,
                               int delta_softplus, const double *A,
                               const void *B, const void *C, const double *D,
@@ -407,8 +470,8 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
                               const double *dy, const double *dh_last,
                               int64_t nsel, const int64_t *sel,
                               double *du, double *ddelta, double *dz,
-                              double *dA_c, double *dD_c, double *dDb_c, double *dh0,
-                              double *dB, double *dC, int nthreads)
+                              double *dA_c, double *dD_c, double *dDb_c, double *dcw_c, double *dcb_c,
+                              double *dh0, double *dB, double *dC, int nthreads)
 {
     if (batch < 0 || L < 0 || dim < 0 || N < 1 || N > 4096)
         return -1;
@@ -417,6 +480,8 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
     if (disc != ORACLE_EULER && disc != ORACLE_ZOH)
         return -1;
     if ((L > 0 && (!u || !delta || !B || !C || !dy)) || !A || !dA_c || !dD_c || !dDb_c)
+        return -1;
+    if (conv_width < 0 || conv_width > 64 || (conv_width > 0 && (!conv_weight || !dcw_c || !dcb_c)))
         return -1;
     if (!sel)
         nsel = batch * dim;
@@ -452,9 +517,11 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
         double *hs = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N));
         double *ss = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
         double *lam = (double *)malloc(sizeof(double) * (size_t)N);
+        double *gu = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        double *pre = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
         double *myB = acc && dB ? acc + (size_t)tid * 2 * bln : NULL;
         double *myC = acc && dC ? acc + (size_t)tid * 2 * bln + bln : NULL;
-        if (!hs || !ss || !lam)
+        if (!hs || !ss || !lam || !gu || !pre)
             bad = 1;
 #ifdef _OPENMP
 #pragma omp for schedule(static)
@@ -465,15 +532,19 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
                 bad = 1;
                 continue;
             }
-            bwd_channel(c / dim, c % dim, L, dim, N, type, disc, u, delta, delta_bias, delta_softplus,
-                        A, B, C, D, z, h0, dy, dh_last, hs, ss, lam,
+            bwd_channel(c / dim, c % dim, L, dim, N, type, disc, conv_width, conv_weight, conv_bias,
+                        u, delta, delta_bias, delta_softplus,
+                        A, B, C, D, z, h0, dy, dh_last, hs, ss, lam, gu, pre,
                         du ? du + k * L : NULL, ddelta ? ddelta + k * L : NULL,
                         (dz && z) ? dz + k * L : NULL, dA_c + k * N, dD_c + k, dDb_c + k,
+                        conv_width ? dcw_c + k * conv_width : NULL, conv_width ? dcb_c + k : NULL,
                         dh0 ? dh0 + k * N : NULL, myB, myC);
         }
         free(hs);
         free(ss);
         free(lam);
+        free(gu);
+        free(pre);
     }
     if (acc) {
         for (int th = 0; th < nthreads; ++th) {

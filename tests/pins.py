@@ -24,6 +24,8 @@ None of these re-types the oracle's loop. The independent statements are:
     only the last hidden state is needed to continue),
   * with h0 = 0 and no gate the output is linear in u and causal,
   * the SiLU gate and the D skip at points with a closed form,
+  * the convolution prologue equals numpy.convolve with reversed taps and the
+    SiLU (youngju.dev MambaBlock.forward), and
   * the backward pass equals central finite differences of the forward oracle
     (the gradient of sum(dy*y) + sum(dh_last*h_last) by definition), and with
     dy = 0 the state gradient reduces to the closed form exp(A*sum(delta)).
@@ -525,6 +527,61 @@ def pin_bwd_delta_softplus(o):
         assert rel_err(g["ddelta_bias"], fdb) < 1e-6, (disc, rel_err(g["ddelta_bias"], fdb))
 
 
+def _np_conv_silu(x, w, cb):
+    """silu(causal depthwise conv1d(x)): numpy.convolve per channel with the
+    taps reversed, first L outputs (left padding W-1)."""
+    b, L, dim = x.shape
+    pre = np.empty_like(x)
+    for i in range(b):
+        for d in range(dim):
+            pre[i, :, d] = np.convolve(x[i, :, d], w[d, ::-1])[:L] + (cb[d] if cb is not None else 0.0)
+    return pre / (1.0 + np.exp(-pre))
+
+
+def pin_conv_prologue(o):
+    """The convolution prologue equals running on silu(numpy.convolve(x, w) + b)."""
+    rng = np.random.default_rng(RNG_SEED + 27)
+    for W in (1, 2, 4):
+        x = _case(rng, 2, 11, 3, 4, with_d=True, with_z=True, with_h0=True)
+        w = rng.normal(0.0, 0.5, (3, W))
+        cb = rng.normal(0.0, 0.5, 3)
+        for disc in ("euler", "zoh"):
+            y1, h1 = o.selective_scan(**x, disc=disc, conv_weight=w, conv_bias=cb)
+            y2, h2 = o.selective_scan(**dict(x, u=_np_conv_silu(x["u"], w, cb)), disc=disc)
+            assert rel_err(y1, y2) < 1e-13 and rel_err(h1, h2) < 1e-13, (W, disc)
+        y3, _ = o.selective_scan(**x, conv_weight=w)
+        y4, _ = o.selective_scan(**dict(x, u=_np_conv_silu(x["u"], w, None)))
+        assert rel_err(y3, y4) < 1e-13, W
+
+
+def pin_bwd_conv(o):
+    """With the convolution prologue, the gradients of x, the taps and the conv
+    bias equal central differences of the forward oracle's loss."""
+    rng = np.random.default_rng(RNG_SEED + 28)
+    for disc in ("euler", "zoh"):
+        x = _case(rng, 2, 7, 2, 3, with_d=True, with_z=True, with_h0=True)
+        w = rng.normal(0.0, 0.5, (2, 4))
+        cb = rng.normal(0.0, 0.5, 2)
+        dy = rng.standard_normal(x["u"].shape)
+        dhl = rng.standard_normal(x["h0"].shape)
+        g = o.selective_scan_bwd(**x, dy=dy, dh_last=dhl, disc=disc, conv_weight=w, conv_bias=cb)
+
+        def loss(xx, ww, bb):
+            y, hl = o.selective_scan(**dict(x, u=xx), disc=disc, conv_weight=ww, conv_bias=bb)
+            return float((dy * y).sum() + (dhl * hl).sum())
+        eps = 1e-6
+        for name, arr, key in (("x", x["u"], "du"), ("w", w, "dconv_weight"), ("b", cb, "dconv_bias")):
+            fd = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                ap, am = arr.copy(), arr.copy()
+                ap[idx] += eps
+                am[idx] -= eps
+                args_p = {"x": (ap, w, cb), "w": (x["u"], ap, cb), "b": (x["u"], w, ap)}[name]
+                args_m = {"x": (am, w, cb), "w": (x["u"], am, cb), "b": (x["u"], w, am)}[name]
+                fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert rel_err(g[key], fd) < 1e-6, (disc, name, rel_err(g[key], fd))
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_brute_force_storage_types,
@@ -546,5 +603,7 @@ ALL_PINS = [
     pin_bwd_channel_selection,
     pin_delta_softplus,
     pin_bwd_delta_softplus,
+    pin_conv_prologue,
+    pin_bwd_conv,
     pin_channel_selection,
 ]

@@ -66,6 +66,16 @@ MUTANTS = {
                            "double x = load(delta, type, i);"),
     "softplus_grad_missing": ("        ddt *= dstep;", "        ddt *= 1.0;"),
     "softplus_grad_sign": ("*dgrad = 1.0 / (1.0 + exp(-x));", "*dgrad = 1.0 / (1.0 + exp(x));"),
+    # convolution prologue
+    "conv_tap_shift": ("const int64_t s = t - (W - 1) + k;\n        if (s >= 0)",
+                       "const int64_t s = t - W + k;\n        if (s >= 0)"),
+    "conv_no_silu": ("    return acc / (1.0 + exp(-acc));", "    return acc;"),
+    "conv_taps_reversed": ("acc += cw[d * W + k] * load(x, type, (b * L + s) * dim + d);",
+                           "acc += cw[d * W + (W - 1 - k)] * load(x, type, (b * L + s) * dim + d);"),
+    "conv_grad_no_silu_grad": ("const double dp = gu[t] * sg * (1.0 + p * (1.0 - sg));", "const double dp = gu[t];"),
+    "conv_dx_wrong_tap": ("du[s] += cw[d * W + k] * dp;", "du[s] += cw[d * W] * dp;"),
+    "conv_dw_uses_output_time": ("dcw_c[k] += dp * load(u, type, (b * L + s) * dim + d);",
+                                 "dcw_c[k] += dp * load(u, type, (b * L + t) * dim + d);"),
 }
 
 
