@@ -49,7 +49,8 @@ typedef enum {
     SSM_ERR_NULL = -1,        /* a required pointer is NULL */
     SSM_ERR_SHAPE = -2,       /* a negative size, or sizes whose byte count overflows */
     SSM_ERR_DTYPE = -3,       /* unknown element type */
-    SSM_ERR_UNSUPPORTED = -4, /* dstate outside 1..64, unknown discretisation or flag, bad tuning */
+    SSM_ERR_UNSUPPORTED = -4, /* dstate outside 1..64, unknown discretisation or flag, conv_width
+                                 outside 0..4, bad tuning */
     SSM_ERR_ALIAS = -5,       /* an output overlaps an input or another output */
     SSM_ERR_WORKSPACE = -6,   /* workspace missing or smaller than ssm_scan_workspace_size() */
     SSM_ERR_HIP = -7,         /* the HIP runtime refused a launch (e.g. not a gfx950 device) */
@@ -68,7 +69,12 @@ typedef enum { SSM_DISC_EULER = 0, SSM_DISC_ZOH = 1 } ssm_disc;
  * bias is given), passed through softplus(x) = log(1 + exp(x)) when
  * delta_softplus is nonzero: the projection output becomes a positive step
  * inside the kernel (youngju.dev SelectiveSSM.forward, dt = softplus(...)).
- * Zero-initialise the struct for "delta used as given". */
+ * With conv_width W > 0 the Mamba block's prologue runs in the kernel (youngju.dev
+ * MambaBlock.forward, x_conv = silu(conv1d(x)), a causal depthwise convolution
+ * with left padding W-1): the buffer passed as u holds x, and the scan input is
+ *     u[b,t,d] = silu(conv_bias[d] + sum_{k<W} conv_weight[d,k] * x[b,t-(W-1)+k,d]),
+ * x before t = 0 being zero; the D skip uses this u.
+ * Zero-initialise the struct for "delta used as given, no convolution". */
 typedef struct {
     int64_t batch;   /* b  >= 0 */
     int64_t seqlen;  /* L  >= 0 */
@@ -77,8 +83,10 @@ typedef struct {
     int32_t dtype;   /* ssm_dtype */
     int32_t disc;    /* ssm_disc */
     int32_t delta_softplus;   /* 0 or 1 */
-    int32_t reserved;         /* must be 0 */
+    int32_t conv_width;       /* 0 (u used as given) or W in 1..4: see below */
     const float *delta_bias;  /* (dim) fp32 device pointer, or NULL */
+    const float *conv_weight; /* (dim, W) fp32 device pointer when conv_width > 0 */
+    const float *conv_bias;   /* (dim) fp32 device pointer, or NULL */
 } ssm_scan_desc;
 
 /* Optional launch shape, for tuning and for tests of every kernel variant.

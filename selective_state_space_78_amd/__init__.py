@@ -31,8 +31,8 @@ EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_workspace_size_t
 class ScanDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32), ("disc", ctypes.c_int32),
-                ("delta_softplus", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("delta_bias", ctypes.c_void_p)]
+                ("delta_softplus", ctypes.c_int32), ("conv_width", ctypes.c_int32),
+                ("delta_bias", ctypes.c_void_p), ("conv_weight", ctypes.c_void_p), ("conv_bias", ctypes.c_void_p)]
 
 
 class ScanTuning(ctypes.Structure):
@@ -128,10 +128,14 @@ def _tuning(tuning):
     return ctypes.byref(ScanTuning(int(g), int(s)))
 
 
-def make_desc(batch, seqlen, dim, dstate, dtype, disc="euler", delta_bias=None, delta_softplus=False) -> ScanDesc:
-    """The scan descriptor; ``delta_bias`` is a device tensor (dim,) float32 or None."""
+def make_desc(batch, seqlen, dim, dstate, dtype, disc="euler", delta_bias=None, delta_softplus=False,
+              conv_weight=None, conv_bias=None) -> ScanDesc:
+    """The scan descriptor; ``delta_bias`` (dim,), ``conv_weight`` (dim, W) and
+    ``conv_bias`` (dim,) are float32 device tensors or None."""
+    ptr = lambda t: None if t is None else t.data_ptr()
+    W = 0 if conv_weight is None else int(conv_weight.shape[1])
     return ScanDesc(int(batch), int(seqlen), int(dim), int(dstate), int(dtype), _DISC[disc],
-                    int(bool(delta_softplus)), 0, None if delta_bias is None else delta_bias.data_ptr())
+                    int(bool(delta_softplus)), W, ptr(delta_bias), ptr(conv_weight), ptr(conv_bias))
 
 
 def ssm_scan_workspace_size(batch, seqlen, dim, dstate, dtype=SSM_BF16, disc="euler", tuning=None) -> int:
@@ -153,7 +157,7 @@ def ssm_scan_plan(batch, seqlen, dim, dstate, dtype=SSM_BF16, disc="euler"):
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None,
                  disc="euler", workspace=None, tuning=None, stream=None, want_h_last=True,
-                 delta_bias=None, delta_softplus=False):
+                 delta_bias=None, delta_softplus=False, conv_weight=None, conv_bias=None):
     """Selective scan forward on device tensors.
 
     u, delta, z: (batch, L, dim); B, C: (batch, L, N) of the same dtype
@@ -162,7 +166,9 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None
     (batch, dim, N) are allocated when not given. Returns (y, h_last).
     ``tuning`` is an optional (state_groups, segments) pair. ``delta_bias``
     (dim,) float32 and ``delta_softplus`` form the step in the kernel:
-    softplus(delta + bias).
+    softplus(delta + bias). With ``conv_weight`` (dim, W <= 4) float32 (and
+    ``conv_bias`` (dim,)), ``u`` holds x and the scan input is
+    silu(causal depthwise conv1d(x) + bias), formed in the kernel.
     """
     import torch
     batch, L, dim = u.shape
@@ -185,7 +191,10 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None
     _check(y, "y", (batch, L, dim), dt, dev)
     _check(h_last, "h_last", (batch, dim, N), torch.float32, dev)
     _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
-    desc = make_desc(batch, L, dim, N, code, disc, delta_bias, delta_softplus)
+    if conv_weight is not None:
+        _check(conv_weight, "conv_weight", (dim, conv_weight.shape[1]), torch.float32, dev)
+    _check(conv_bias, "conv_bias", (dim,), torch.float32, dev)
+    desc = make_desc(batch, L, dim, N, code, disc, delta_bias, delta_softplus, conv_weight, conv_bias)
     L_ = lib()
     need = (L_.ssm_scan_workspace_size(ctypes.byref(desc)) if tuning is None
             else L_.ssm_scan_workspace_size_tuned(ctypes.byref(desc), _tuning(tuning)))

@@ -62,6 +62,7 @@ constexpr int kTile = 64;        // channels per workgroup tile = lanes per wave
 constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies
 constexpr int kMaxSegments = 64;
 constexpr int kPadRows = 16;     // spare zero rows after the widened B and C (>= every TC)
+constexpr int kConvMax = 4;      // widest convolution prologue
 
 // ---------------------------------------------------------------------------
 // Element access. bf16 travels as its 16-bit pattern.
@@ -117,6 +118,8 @@ struct ScanParams {
     const void *u, *delta, *z, *B, *C;
     const float *delta_bias;  // (dim) added to delta before the recurrence uses it, or null
     int delta_softplus;       // the step is softplus(delta + bias)
+    int conv_w;               // 0, or the width of the causal convolution prologue (u holds x)
+    const float *conv_weight, *conv_bias;   // (dim, conv_w), (dim) or null
     const float *A, *D, *h0;
     float *Bf, *Cf;       // (batch, G, padded_len(L), Npad/G) fp32 widened B and C (workspace)
     const float *seg_h;   // (batch, nseg, dim, N) initial state of each segment, or null
@@ -285,6 +288,7 @@ struct ScanKernel {
 
     struct Prefetch {
         Raw u[kPPT], dt[kPPT], z[kPPT];
+        Raw xh[kPPT][kConvMax - 1];    // with the convolution prologue: x of the rows t-1, t-2, t-3
     };
 
     // D*u and silu(z) of the thread's staged pieces, kept in registers until
@@ -330,8 +334,10 @@ struct ScanKernel {
 
     // Issue the global loads of one chunk: `base` is the element offset of
     // (the chunk's first token row, the tile's first channel); rows [0, tval).
+    // pos0: sequence position of the chunk's first row (the convolution's
+    // history rows before position 0 are zero)
     __device__ static void load(const ScanParams &p, Prefetch &pf, int64_t base, int tval, int col, int d0,
-                                bool colv) {
+                                bool colv, int64_t pos0) {
         const T *u = static_cast<const T *>(p.u) + base;
         const T *dt = static_cast<const T *>(p.delta) + base;
         const T *z = static_cast<const T *>(p.z) + base;
@@ -350,7 +356,40 @@ struct ScanKernel {
                 pf.dt[j] = gather(dt + off, d0 + col, p.dim, true);
                 pf.z[j] = gather(z + off, d0 + col, p.dim, gate);
             }
+#pragma unroll
+            for (int k = 1; k < kConvMax; ++k) {
+                if (k >= p.conv_w) break;
+                // rows before position 0 are zero; their address is clamped to
+                // the current row so that every load stays inside x
+                const bool has = pos0 + row - k >= 0;
+                const T *src = u + (int64_t)off - (has ? (int64_t)k * p.dim : 0);
+                Raw r = p.vec ? *reinterpret_cast<const Raw *>(src) : gather(src, d0 + col, p.dim, true);
+                if (!has) {
+                    const uint32_t zw[4] = {0u, 0u, 0u, 0u};
+                    make_words(r, zw);
+                }
+                pf.xh[j][k - 1] = r;
+            }
         }
+    }
+
+    // The convolution prologue for one piece: x (in u on entry) and its
+    // history rows become silu(bias + sum_k w[k] x[t-(W-1)+k]).
+    __device__ static void conv_silu(const Prefetch &pf, int j, float (&u)[kV], int cw,
+                                     const float (&wk)[kV][kConvMax], const float (&cbk)[kV]) {
+        float acc[kV];
+#pragma unroll
+        for (int e = 0; e < kV; ++e) acc[e] = fmaf(wk[e][cw - 1], u[e], cbk[e]);
+#pragma unroll
+        for (int k = 1; k < kConvMax; ++k) {
+            if (k >= cw) break;
+            float xv[kV];
+            unpack(pf.xh[j][k - 1], xv);
+#pragma unroll
+            for (int e = 0; e < kV; ++e) acc[e] = fmaf(wk[e][cw - 1 - k], xv[e], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < kV; ++e) u[e] = silu(acc[e]);
     }
 
     // Stage the prefetched chunk into LDS buffer `dx`, forming the per-token
@@ -358,7 +397,8 @@ struct ScanKernel {
     // past tval (and channels past dim) are staged as delta = 0, x = 0: a step
     // that leaves the state unchanged.
     __device__ static void commit(const Prefetch &pf, float2 (*dx)[kTile], Held &held, int tval, int col,
-                                  bool colv, const float (&Dk)[kV], bool gate, const float (&dbk)[kV], int prep) {
+                                  bool colv, const float (&Dk)[kV], bool gate, const float (&dbk)[kV], int prep,
+                                  int cw, const float (&wk)[kV][kConvMax], const float (&cbk)[kV]) {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
             const int row = piece_row(j);
@@ -368,6 +408,7 @@ struct ScanKernel {
                 float u[kV], d[kV];
                 unpack(pf.u[j], u);
                 unpack(pf.dt[j], d);
+                if (cw) conv_silu(pf, j, u, cw, wk, cbk);
                 if (prep) {
                     // the step: delta + bias, through softplus when asked
 #pragma unroll
@@ -562,6 +603,17 @@ struct ScanKernel {
         }
         // 0: delta as given; 1: plus the bias; 2: softplus of that
         const int prep = p.delta_softplus ? 2 : (p.delta_bias != nullptr ? 1 : 0);
+        // convolution prologue taps and bias of this thread's channels
+        const int convw = p.conv_w;
+        float wk[kV][kConvMax], cbk[kV];
+#pragma unroll
+        for (int e = 0; e < kV; ++e) {
+            const bool cv = convw > 0 && d0 + col + e < p.dim;
+            cbk[e] = (cv && p.conv_bias != nullptr) ? p.conv_bias[d0 + col + e] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < kConvMax; ++k)
+                wk[e][k] = (cv && k < convw) ? p.conv_weight[(int64_t)(d0 + col + e) * convw + k] : 0.0f;
+        }
 
         const int nchunks = (int)((t_end - t_begin + TC - 1) / TC);
         const int64_t row0 = (int64_t)b * p.L + t_begin;        // token row of (b, t_begin)
@@ -569,11 +621,11 @@ struct ScanKernel {
         Prefetch pf;
         Held held[2];                                            // by chunk parity
         auto load_chunk = [&](int k) {
-            load(p, pf, (row0 + (int64_t)k * TC) * p.dim + d0, rows_of(k), col, d0, colv);
+            load(p, pf, (row0 + (int64_t)k * TC) * p.dim + d0, rows_of(k), col, d0, colv, t_begin + (int64_t)k * TC);
         };
         if (nchunks > 0) {
             load_chunk(0);
-            commit(pf, s.dx[0], held[0], rows_of(0), col, colv, Dk, gate, dbk, prep);
+            commit(pf, s.dx[0], held[0], rows_of(0), col, colv, Dk, gate, dbk, prep, convw, wk, cbk);
         }
         if (nchunks > 1) load_chunk(1);
         __syncthreads();
@@ -606,7 +658,8 @@ struct ScanKernel {
             constexpr int P = decltype(parity)::value;
             fetch(0);
             Held next;
-            if (k + 1 < nchunks) commit(pf, s.dx[P ^ 1], next, rows_of(k + 1), col, colv, Dk, gate, dbk, prep);
+            if (k + 1 < nchunks)
+                commit(pf, s.dx[P ^ 1], next, rows_of(k + 1), col, colv, Dk, gate, dbk, prep, convw, wk, cbk);
             if constexpr (!AGG) {
                 if (k > 0) {
                     finalize(p, s.y[P ^ 1], held[P ^ 1], yb, TC, col, d0);

@@ -363,8 +363,12 @@ int validate_desc(const ssm_scan_desc *d) {
     if (d->dtype != SSM_F32 && d->dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (d->disc != SSM_DISC_EULER && d->disc != SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
     if (d->dstate < 1 || d->dstate > 64) return SSM_ERR_UNSUPPORTED;
-    if ((d->delta_softplus != 0 && d->delta_softplus != 1) || d->reserved != 0) return SSM_ERR_UNSUPPORTED;
-    if (d->delta_bias != nullptr && !aligned(d->delta_bias, 4)) return SSM_ERR_ALIGN;
+    if (d->delta_softplus != 0 && d->delta_softplus != 1) return SSM_ERR_UNSUPPORTED;
+    if (d->conv_width < 0 || d->conv_width > kConvMax) return SSM_ERR_UNSUPPORTED;
+    if (d->conv_width > 0 && d->conv_weight == nullptr) return SSM_ERR_NULL;
+    if ((d->delta_bias != nullptr && !aligned(d->delta_bias, 4)) ||
+        (d->conv_width > 0 && !aligned(d->conv_weight, 4)) || (d->conv_bias != nullptr && !aligned(d->conv_bias, 4)))
+        return SSM_ERR_ALIGN;
     // byte counts of the largest tensors must fit; kernel indices are 32-bit
     // for batch, dim and segment lengths
     int64_t bl, bld, bytes;
@@ -413,7 +417,9 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
     const Range inputs[] = {range_of(u, tok * es), range_of(delta, tok * es), range_of(z, z ? tok * es : 0),
                             range_of(B, bn * es), range_of(C, bn * es), range_of(A, d.dim * d.dstate * 4),
                             range_of(D, D ? d.dim * 4 : 0), range_of(h0, h0 ? state * 4 : 0),
-                            range_of(d.delta_bias, d.delta_bias ? d.dim * 4 : 0)};
+                            range_of(d.delta_bias, d.delta_bias ? d.dim * 4 : 0),
+                            range_of(d.conv_width ? d.conv_weight : nullptr, d.dim * d.conv_width * 4),
+                            range_of(d.conv_width ? d.conv_bias : nullptr, d.dim * 4)};
     for (const Range &r : inputs) {
         if (overlaps(r_y, r) || overlaps(r_ws, r)) return SSM_ERR_ALIAS;
         // h_last may be exactly h0 (in-place resume), nothing else
@@ -431,6 +437,7 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
     ScanParams p{};
     p.u = u; p.delta = delta; p.z = z; p.B = B; p.C = C;
     p.delta_bias = d.delta_bias; p.delta_softplus = d.delta_softplus;
+    p.conv_w = d.conv_width; p.conv_weight = d.conv_weight; p.conv_bias = d.conv_width ? d.conv_bias : nullptr;
     p.A = A; p.D = D; p.h0 = h0;
     p.y = y; p.h_last = h_last;
     p.L = d.seqlen;
@@ -509,6 +516,7 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
              float *ddelta_bias, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (int rc = validate_desc(desc); rc != SSM_OK) return rc;
     const ssm_scan_desc d = *desc;
+    if (d.conv_width != 0) return SSM_ERR_UNSUPPORTED;   // the backward takes u as given
     if (d.batch == 0 || d.dim == 0) return SSM_OK;
     const int es = d.dtype == SSM_BF16 ? 2 : 4;
     const int64_t tok = d.batch * d.seqlen * d.dim;

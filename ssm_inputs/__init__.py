@@ -31,7 +31,7 @@ from dataclasses import dataclass
 import numpy as np
 
 BLOCK = 1 << 22
-STREAMS = ("u", "delta_noise", "delta_bias", "B", "C", "z", "D", "h0", "dy", "dh_last")
+STREAMS = ("u", "delta_noise", "delta_bias", "B", "C", "z", "D", "h0", "dy", "dh_last", "conv")
 
 
 @dataclass(frozen=True)
@@ -210,6 +210,17 @@ def raw_delta_inputs(cfg: ScanConfig, seed: int = 0, batch: int | None = None,
     out_dtype = np.uint16 if cfg.dtype == "bf16" else np.float32
     raw = _blocked(_stream(seed, "delta_noise"), total, fill, out_dtype).reshape(b, L, d)
     return dict(delta=raw, delta_bias=delta_bias(seed, d, cfg.bias).astype(np.float32))
+
+
+def conv_inputs(dim: int, width: int = 4, seed: int = 0):
+    """Taps (dim, width) and bias (dim,) of the causal depthwise convolution
+    prologue, float32, uniform in +-1/sqrt(width) (a depthwise convolution's
+    fan-in is its width)."""
+    rng = np.random.Generator(np.random.PCG64(_stream(seed, "conv")))
+    bound = 1.0 / np.sqrt(width)
+    w = rng.uniform(-bound, bound, (dim, width)).astype(np.float32)
+    b = rng.uniform(-bound, bound, dim).astype(np.float32)
+    return dict(conv_weight=w, conv_bias=b)
 
 
 def grad_inputs(cfg: ScanConfig, seed: int = 0, batch: int | None = None,

@@ -52,8 +52,8 @@ def test_status_strings(L):
     assert ssm.ssm_status_string(12345) == "unknown status"
 
 
-def desc(b=2, L=100, d=64, N=16, dtype=ssm.SSM_BF16, disc=0, softplus=0, reserved=0, bias=None):
-    return ssm.ScanDesc(b, L, d, N, dtype, disc, softplus, reserved, bias)
+def desc(b=2, L=100, d=64, N=16, dtype=ssm.SSM_BF16, disc=0, softplus=0, conv=0, bias=None, cw=None, cb=None):
+    return ssm.ScanDesc(b, L, d, N, dtype, disc, softplus, conv, bias, cw, cb)
 
 
 def fake(addr):
@@ -83,7 +83,11 @@ def test_scan_descriptor_errors(L):
     assert scan_call(L, desc(N=65)) == EUNSUP
     assert scan_call(L, desc(b=1 << 40, L=1 << 40)) == ESHAPE
     assert scan_call(L, desc(softplus=2)) == EUNSUP
-    assert scan_call(L, desc(reserved=1)) == EUNSUP
+    assert scan_call(L, desc(conv=5)) == EUNSUP
+    assert scan_call(L, desc(conv=-1)) == EUNSUP
+    assert scan_call(L, desc(conv=4)) == ENULL                   # taps missing
+    assert scan_call(L, desc(conv=4, cw=10 * GB + 2)) == EALIGN
+    assert scan_call(L, desc(conv=4, cw=8 * GB + 64)) == EALIAS  # taps inside y
     assert scan_call(L, desc(bias=10 * GB + 2)) == EALIGN
     assert scan_call(L, desc(bias=8 * GB + 64)) == EALIAS        # bias inside the output y
 
@@ -205,6 +209,7 @@ def test_bwd_errors(L):
     assert bwd_call(L, desc(), dh0=8 * GB + 128) == EALIAS    # dh0 over dy
     assert bwd_call(L, desc(bias=17 * GB)) == ENULL           # a delta bias needs its gradient
     assert bwd_call(L, desc(bias=17 * GB), ddb=17 * GB + 4) == EALIAS
+    assert bwd_call(L, desc(conv=4, cw=17 * GB)) == EUNSUP
 
 
 def test_bwd_workspace(L):

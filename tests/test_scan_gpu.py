@@ -302,3 +302,63 @@ def test_delta_bias_softplus(env, dtype, disc):
                              disc=disc, delta_softplus=True)
     torch.cuda.synchronize()
     assert rel_err(to_np(y), yr) <= tol and rel_err(to_np(hl), hr) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("disc", ["euler", "zoh"])
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+def test_conv_prologue(env, dtype, disc, W):
+    """silu(causal depthwise conv1d(x) + bias) formed in the kernel, across chunk
+    and segment boundaries, with and without the other options."""
+    import dataclasses
+    torch, ssm = env
+    cfg = dataclasses.replace(si.CONFIGS["mamba130m"], dtype=dtype)
+    x = si.scan_inputs(cfg, seed=40 + W, batch=2, seqlen=301, dim=136)
+    c = si.conv_inputs(136, W, seed=W)
+    dev = {k: to_dev(v, torch) for k, v in x.items() if k != "h0"}
+    cw, cb = to_dev(c["conv_weight"], torch), to_dev(c["conv_bias"], torch)
+    tol = tol_of(x)
+    yr, hr = oracle.load().selective_scan(**x, disc=disc, **c)
+    for tuning in (None, (8, 1), (4, 3), (2, 7)):
+        y, hl = ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                                 disc=disc, tuning=tuning, conv_weight=cw, conv_bias=cb)
+        torch.cuda.synchronize()
+        ey, eh = rel_err(to_np(y), yr), rel_err(to_np(hl), hr)
+        say("conv W%d %s %s tuning %s: y %.3e h %.3e" % (W, dtype, disc, tuning, ey, eh))
+        assert ey <= tol and eh <= tol, (tuning, ey, eh)
+    # no conv bias, an odd channel count (element-wise loads), softplus step too
+    r = si.raw_delta_inputs(cfg, seed=40 + W, batch=2, seqlen=301, dim=136)
+    xo = {k: (v[..., :133] if k in ("u", "delta", "z") else v) for k, v in x.items()}
+    xo["delta"] = r["delta"][..., :133]
+    xo["A"], xo["D"] = x["A"][:133], x["D"][:133]
+    c2 = dict(conv_weight=c["conv_weight"][:133])
+    yr, hr = oracle.load().selective_scan(**xo, disc=disc, delta_bias=r["delta_bias"][:133], delta_softplus=True, **c2)
+    devo = {k: to_dev(np.ascontiguousarray(v), torch) for k, v in xo.items() if k != "h0"}
+    y, hl = ssm.ssm_scan_fwd(devo["u"], devo["delta"], devo["A"], devo["B"], devo["C"], devo["D"], devo["z"],
+                             disc=disc, conv_weight=to_dev(np.ascontiguousarray(c2["conv_weight"]), torch),
+                             delta_bias=to_dev(np.ascontiguousarray(r["delta_bias"][:133]), torch),
+                             delta_softplus=True)
+    torch.cuda.synchronize()
+    ey, eh = rel_err(to_np(y), yr), rel_err(to_np(hl), hr)
+    say("conv W%d %s %s, d 133, no conv bias, softplus step: y %.3e h %.3e" % (W, dtype, disc, ey, eh))
+    assert ey <= tol and eh <= tol
+
+
+def test_conv_prologue_full_size(env):
+    """The Mamba-1.4B-shaped layer with the width-4 prologue, sampled channels."""
+    torch, ssm = env
+    cfg = si.CONFIGS["mamba1.4b"]
+    x = si.scan_inputs(cfg, seed=0)
+    c = si.conv_inputs(cfg.dim, 4, seed=0)
+    dev = {k: to_dev(v, torch) for k, v in x.items() if v is not None}
+    y, hl = ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                             conv_weight=to_dev(c["conv_weight"], torch), conv_bias=to_dev(c["conv_bias"], torch))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    chans = [(int(b), int(d)) for b, d in zip(rng.integers(0, 8, 16), rng.integers(0, 4096, 16))]
+    yr, hr = oracle.load().selective_scan(**x, channels=chans, **c)
+    yg = np.stack([to_np(y[b, :, d]) for b, d in chans])
+    hg = np.stack([to_np(hl[b, d]) for b, d in chans])
+    ey, eh = rel_err(yg, yr), rel_err(hg, hr)
+    say("conv full size sampled: y %.3e h %.3e" % (ey, eh))
+    assert ey <= TOL_BF16 and eh <= TOL_BF16
