@@ -212,6 +212,8 @@ def main():
                     help="discretisation of B (default: the simplified delta*B)")
     ap.add_argument("--delta-softplus", action="store_true",
                     help="form the step in the kernel: softplus(delta_raw + bias)")
+    ap.add_argument("--conv", action="store_true",
+                    help="run the width-4 causal conv1d + SiLU prologue in the kernel (u holds x)")
     ap.add_argument("--tuning", type=str, default=None, help="state_groups,segments")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=WORKLOAD,
                     help="scan workload of the timed step (the default is the headline one)")
@@ -239,6 +241,10 @@ def main():
         dev["delta"] = to_dev(r["delta"], torch)
         step_opts = dict(delta_bias=to_dev(r["delta_bias"], torch), delta_softplus=True)
         oracle_opts.update(delta_bias=r["delta_bias"], delta_softplus=True)
+    if args.conv:
+        c = si.conv_inputs(cfg.dim, 4, seed=0)
+        step_opts.update(conv_weight=to_dev(c["conv_weight"], torch), conv_bias=to_dev(c["conv_bias"], torch))
+        oracle_opts.update(c)
     y = torch.empty((cfg.batch, cfg.seqlen, cfg.dim), dtype=torch.bfloat16, device="cuda")
     h_last = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device="cuda")
     tuning = tuple(int(v) for v in args.tuning.split(",")) if args.tuning else None
@@ -296,6 +302,7 @@ def main():
             "global_batch": cfg.batch, "seq_len": cfg.seqlen, "dim": cfg.dim, "dstate": cfg.dstate,
             "io_dtype": "bf16", "parallelism": "none (1 GPU)",
             "disc": args.disc, "step": "softplus(delta + bias) in the kernel" if args.delta_softplus else "delta as given",
+            "prologue": "silu(causal conv1d width 4) in the kernel" if args.conv else "none",
             "launch": {"state_groups": plan[0], "segments": plan[1]},
         },
         "roofline": {
@@ -307,7 +314,8 @@ def main():
             "frac": achieved_tops / VALU_PEAK_TOPS,
             "ops_per_token_ch": valu_ops_per_token_ch(cfg.dstate, cfg.gate),
             "mean_launch_ms": mean_launch_ms,
-            "traffic": measured_traffic(args.workload, plan, args.disc == "euler" and not args.delta_softplus),
+            "traffic": measured_traffic(args.workload, plan,
+                                        args.disc == "euler" and not args.delta_softplus and not args.conv),
         },
         "hbm": {
             "algorithmic_bytes_per_launch": nbytes,
@@ -323,7 +331,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = 1 << 30
-    if not args.no_bwd:
+    if not args.no_bwd and not args.conv:
         print("bench: backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(torch, ssm, cfg, dev, disc=args.disc, step_opts=step_opts)
     if not args.no_decode:

@@ -254,7 +254,10 @@ template <> struct FloatsOf<4> { typedef float4 type; };
 // What a pass of the scan kernel produces.
 enum ScanMode { kModeMain = 0, kModeAggregate = 1, kModeCheckpoint = 2 };
 
-template <typename T, int NPW, int G, int TC, bool ZOH, int MODE>
+// FEAT: the step and input prologue (delta bias, softplus, convolution) are
+// compiled in; without it the kernel carries none of their state (their
+// uniform values alone pushed the scalar registers into spills).
+template <typename T, int NPW, int G, int TC, bool ZOH, int MODE, bool FEAT>
 struct ScanKernel {
     // main: y and h_last; aggregate: each segment's map h -> P h + H;
     // checkpoint: the state at the start of every chunk (for the backward)
@@ -288,7 +291,7 @@ struct ScanKernel {
 
     struct Prefetch {
         Raw u[kPPT], dt[kPPT], z[kPPT];
-        Raw xh[kPPT][kConvMax - 1];    // with the convolution prologue: x of the rows t-1, t-2, t-3
+        Raw xh[kPPT][FEAT ? kConvMax - 1 : 1];   // with the convolution prologue: x of the rows t-1, t-2, t-3
     };
 
     // D*u and silu(z) of the thread's staged pieces, kept in registers until
@@ -356,19 +359,31 @@ struct ScanKernel {
                 pf.dt[j] = gather(dt + off, d0 + col, p.dim, true);
                 pf.z[j] = gather(z + off, d0 + col, p.dim, gate);
             }
+            if (FEAT && p.conv_w > 1) {
+                if (pos0 >= kConvMax - 1 && p.vec) {
+                    // every history row exists: one uniform base per row back
 #pragma unroll
-            for (int k = 1; k < kConvMax; ++k) {
-                if (k >= p.conv_w) break;
-                // rows before position 0 are zero; their address is clamped to
-                // the current row so that every load stays inside x
-                const bool has = pos0 + row - k >= 0;
-                const T *src = u + (int64_t)off - (has ? (int64_t)k * p.dim : 0);
-                Raw r = p.vec ? *reinterpret_cast<const Raw *>(src) : gather(src, d0 + col, p.dim, true);
-                if (!has) {
-                    const uint32_t zw[4] = {0u, 0u, 0u, 0u};
-                    make_words(r, zw);
+                    for (int k = 1; k < (FEAT ? kConvMax : 1); ++k) {
+                        if (k >= p.conv_w) break;
+                        const T *uk = u - (int64_t)k * p.dim;
+                        pf.xh[j][k - 1] = *reinterpret_cast<const Raw *>(uk + off);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 1; k < (FEAT ? kConvMax : 1); ++k) {
+                        if (k >= p.conv_w) break;
+                        // rows before position 0 are zero; their address is clamped
+                        // to the current row so that every load stays inside x
+                        const bool has = pos0 + row - k >= 0;
+                        const T *src = u + (int64_t)off - (has ? (int64_t)k * p.dim : 0);
+                        Raw r = p.vec ? *reinterpret_cast<const Raw *>(src) : gather(src, d0 + col, p.dim, true);
+                        if (!has) {
+                            const uint32_t zw[4] = {0u, 0u, 0u, 0u};
+                            make_words(r, zw);
+                        }
+                        pf.xh[j][k - 1] = r;
+                    }
                 }
-                pf.xh[j][k - 1] = r;
             }
         }
     }
@@ -381,7 +396,7 @@ struct ScanKernel {
 #pragma unroll
         for (int e = 0; e < kV; ++e) acc[e] = fmaf(wk[e][cw - 1], u[e], cbk[e]);
 #pragma unroll
-        for (int k = 1; k < kConvMax; ++k) {
+        for (int k = 1; k < (FEAT ? kConvMax : 1); ++k) {
             if (k >= cw) break;
             float xv[kV];
             unpack(pf.xh[j][k - 1], xv);
@@ -408,8 +423,8 @@ struct ScanKernel {
                 float u[kV], d[kV];
                 unpack(pf.u[j], u);
                 unpack(pf.dt[j], d);
-                if (cw) conv_silu(pf, j, u, cw, wk, cbk);
-                if (prep) {
+                if (FEAT && cw) conv_silu(pf, j, u, cw, wk, cbk);
+                if (FEAT && prep) {
                     // the step: delta + bias, through softplus when asked
 #pragma unroll
                     for (int e = 0; e < kV; ++e) d[e] = prep == 2 ? softplus_f(d[e] + dbk[e]) : d[e] + dbk[e];
@@ -511,8 +526,8 @@ struct ScanKernel {
     static constexpr int kWPS = kPacked ? 1 : 2;               // words per state and step
     // Steps whose B and C words are fetched together: at most 32 scalar
     // registers for packed words (which leaves room for the rest of the
-    // kernel's scalars without spills), 64 for fp32 words
-    static constexpr int kBudget = kPacked ? 32 : 64;
+    // kernel's scalars without spills; 16 with the prologue), 64 for fp32 words
+    static constexpr int kBudget = kPacked ? (FEAT ? 16 : 32) : 64;   // the prologue's state needs scalars too
     static constexpr int kTBMax = kBudget / (kWPS * NPW) > 0 ? kBudget / (kWPS * NPW) : 1;
     static constexpr int kTB = kTBMax < TC ? kTBMax : TC;
     static_assert(TC % kTB == 0, "batches of steps tile the chunk");
@@ -599,12 +614,12 @@ struct ScanKernel {
 #pragma unroll
         for (int e = 0; e < kV; ++e) {
             Dk[e] = (!AGG && p.D != nullptr && d0 + col + e < p.dim) ? p.D[d0 + col + e] : 0.0f;
-            dbk[e] = (p.delta_bias != nullptr && d0 + col + e < p.dim) ? p.delta_bias[d0 + col + e] : 0.0f;
+            dbk[e] = (FEAT && p.delta_bias != nullptr && d0 + col + e < p.dim) ? p.delta_bias[d0 + col + e] : 0.0f;
         }
         // 0: delta as given; 1: plus the bias; 2: softplus of that
-        const int prep = p.delta_softplus ? 2 : (p.delta_bias != nullptr ? 1 : 0);
+        const int prep = !FEAT ? 0 : p.delta_softplus ? 2 : (p.delta_bias != nullptr ? 1 : 0);
         // convolution prologue taps and bias of this thread's channels
-        const int convw = p.conv_w;
+        const int convw = FEAT ? p.conv_w : 0;
         float wk[kV][kConvMax], cbk[kV];
 #pragma unroll
         for (int e = 0; e < kV; ++e) {
@@ -732,9 +747,9 @@ struct ScanKernel {
     }
 };
 
-template <typename T, int NPW, int G, int TC, bool ZOH, int MODE>
+template <typename T, int NPW, int G, int TC, bool ZOH, int MODE, bool FEAT>
 __global__ __launch_bounds__(kTile * G) void scan_kernel(const ScanParams p) {
-    ScanKernel<T, NPW, G, TC, ZOH, MODE>::run(p);
+    ScanKernel<T, NPW, G, TC, ZOH, MODE, FEAT>::run(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -798,8 +813,8 @@ __global__ __launch_bounds__(256) __attribute__((unused)) void carry_kernel(cons
 }
 
 // CK: the shape also has the checkpoint pass (the launch shapes the backward uses)
-template <typename T, int NPW, int G, int TC, bool ZOH, bool CK>
-hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg, hipStream_t st) {
+template <typename T, int NPW, int G, int TC, bool ZOH, bool CK, bool FEAT>
+hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg, hipStream_t st) {
     if (!CK && p.ckpt != nullptr) return hipErrorInvalidValue;
     {
         const int64_t total = (int64_t)p.batch * padded_len(p.L) * (NPW * G);
@@ -809,7 +824,7 @@ hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg,
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if (nblocks_agg > 0) {
-        hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeAggregate>), dim3(nblocks_agg), dim3(kTile * G), 0, st, p);
+        hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeAggregate, FEAT>), dim3(nblocks_agg), dim3(kTile * G), 0, st, p);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         CarryParams cp{};
         cp.P = p.agg_P;
@@ -828,13 +843,20 @@ hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg,
     }
     if constexpr (CK) {
         if (p.ckpt != nullptr) {
-            hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeCheckpoint>), dim3(nblocks_main), dim3(kTile * G),
+            hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeCheckpoint, FEAT>), dim3(nblocks_main), dim3(kTile * G),
                                0, st, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMain>), dim3(nblocks_main), dim3(kTile * G), 0, st, p);
+    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMain, FEAT>), dim3(nblocks_main), dim3(kTile * G), 0, st, p);
     return hipGetLastError();
+}
+
+template <typename T, int NPW, int G, int TC, bool ZOH, bool CK>
+hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg, hipStream_t st) {
+    const bool feat = p.delta_bias != nullptr || p.delta_softplus || p.conv_w > 0;
+    return feat ? launch_scan_tf<T, NPW, G, TC, ZOH, CK, true>(p, nblocks_main, nblocks_agg, st)
+                : launch_scan_tf<T, NPW, G, TC, ZOH, CK, false>(p, nblocks_main, nblocks_agg, st);
 }
 
 #ifndef SSM_TC_G8
