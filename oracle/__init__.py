@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the Mamba selective scan (S6), its backward and its decode step.
+"""fp64 CPU oracle for the Mamba selective scan (S6), its backward, its decode
+step and the Mamba-2 SSD layer.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the smoke check and the
 bench's CPU-baseline leg, never by the product path. It shares no code with
@@ -75,6 +76,9 @@ class Oracle:
                                                   vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                                   i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         lib.oracle_selective_scan_bwd.restype = i32
+        lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32,
+                                   vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32]
+        lib.oracle_ssd.restype = i32
         self.lib = lib
         self.path = path
         self.threads = int(threads)
@@ -237,6 +241,52 @@ class Oracle:
         return y
 
 
+    def ssd(self, x, dt, A, B, C, D=None, z=None, h0=None, disc="euler", dt_bias=None,
+            dt_softplus=False, heads=None, want_y=True, nthreads=0):
+        """Mamba-2 SSD layer, sequential form (see ``oracle_ssd`` in ssm_oracle.c).
+
+        x, z (batch, L, H, P); dt (batch, L, H); B, C (batch, L, G, N); A, D,
+        dt_bias (H,); h0 (batch, H, P, N). Returns ``(y, h_last)``: with
+        ``heads=None`` y is (batch, L, H, P) and h_last (batch, H, P, N); with
+        ``heads`` a sequence of (b, h) pairs, y is (k, L, P) and h_last (k, P, N).
+        """
+        x = np.ascontiguousarray(x)
+        batch, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        typ = self._per_token([x, dt, B, C, z])
+        dt = np.ascontiguousarray(dt)
+        B = np.ascontiguousarray(B)
+        C = np.ascontiguousarray(C)
+        assert dt.shape == (batch, L, H) and B.shape == (batch, L, G, N) and C.shape == B.shape
+        A64 = np.ascontiguousarray(A, dtype=np.float64)
+        assert A64.shape == (H,)
+        D64 = None if D is None else np.ascontiguousarray(D, dtype=np.float64)
+        zc = None if z is None else np.ascontiguousarray(z)
+        if zc is not None:
+            assert zc.shape == x.shape
+        h064 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+        if h064 is not None:
+            assert h064.shape == (batch, H, P, N)
+        bias = None if dt_bias is None else np.ascontiguousarray(dt_bias, dtype=np.float64)
+        if heads is None:
+            sel, nsel = None, batch * H
+        else:
+            sel = np.ascontiguousarray([b * H + h for b, h in heads], dtype=np.int64)
+            nsel = len(sel)
+        y = np.empty((nsel, L, P)) if want_y else None
+        hl = np.empty((nsel, P, N))
+        rc = self.lib.oracle_ssd(batch, L, H, P, G, N, typ, _DISC[disc], _ptr(x), _ptr(dt), _ptr(bias),
+                                 int(bool(dt_softplus)), _ptr(A64), _ptr(B), _ptr(C), _ptr(D64), _ptr(zc),
+                                 _ptr(h064), nsel, _ptr(sel), _ptr(y), _ptr(hl), int(nthreads or self.threads))
+        if rc != 0:
+            raise ValueError("oracle_ssd rejected its arguments")
+        if heads is None:
+            if y is not None:
+                y = y.reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy()
+            hl = hl.reshape(batch, H, P, N)
+        return y, hl
+
+
 def load(path: str | None = None) -> Oracle:
     """Load (building first if needed) the oracle library at ``path``."""
     path = path or LIBRARY
@@ -259,3 +309,7 @@ def state_update(*args, **kwargs):
 
 def selective_scan_bwd(*args, **kwargs):
     return load().selective_scan_bwd(*args, **kwargs)
+
+
+def ssd(*args, **kwargs):
+    return load().ssd(*args, **kwargs)

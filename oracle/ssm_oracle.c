@@ -560,3 +560,113 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Mamba-2 structured state-space duality (SSD) layer, sequential form.
+ *
+ * Restricting the state matrix of each head to a scalar times the identity
+ * (itwiki "상태 공간 모델", section "Mamba-2와 상태 공간 쌍대성"; eommydocs
+ * "State Space Models (SSM)", §2.4 "Mamba-2") gives, per batch row b and
+ * head h with scalar a = A[h] and head dimension P:
+ *
+ *   H[p][n] = h0[b,h,p,n], or 0 when no initial state is given
+ *   for t = 0 .. L-1:
+ *     dt    = dt[b,t,h] (+ dt_bias[h]), through softplus when asked
+ *     abar  = exp(dt * a)                              (one decay per head)
+ *     wbar  = dt, or expm1(dt*a)/a (zero-order hold; dt when a == 0)
+ *     H[p][n] = abar * H[p][n] + wbar * x[b,t,h,p] * B[b,t,g,n]
+ *     y[b,t,h,p] = sum_n C[b,t,g,n] * H[p][n] + D[h] * x[b,t,h,p]
+ *     y *= silu(z[b,t,h,p])     when a gate is given
+ *   h_last[b,h,:,:] = H
+ * with g = h / (H_heads / G) the group whose B and C the head reads (B, C
+ * shared by the heads of a group, as the key projection of youngju.dev
+ * SSDBlock is shared by the head dimension of each head). Every channel p of
+ * a head is the selective-scan recurrence above with A[d,n] = a for all n;
+ * the chunked, attention-like evaluation of youngju.dev SSDBlock._chunk_scan
+ * reaches the same y and is pinned against this form.
+ *
+ *   x, z : (batch, L, H, P);  dt: (batch, L, H);  B, C: (batch, L, G, N),
+ *          row-major, element type `type`
+ *   A    : (H) doubles; D: (H) doubles or NULL; dt_bias: (H) doubles or NULL
+ *   h0   : (batch, H, P, N) doubles or NULL
+ *   nsel, sel : heads to compute, each c = b*H + h (sel == NULL: all, in order)
+ *   y    : (nsel, L, P) doubles or NULL;  h_last: (nsel, P, N) doubles or NULL
+ * Returns 0, or -1 for a bad argument.
+ */
+static void ssd_head(int64_t b, int64_t hh, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                     int type, int disc, const void *x, const void *dt, const double *dt_bias, int sp,
+                     const double *A, const void *B, const void *C, const double *D, const void *z,
+                     const double *h0, double *st, double *y, double *hl)
+{
+    const int64_t g = hh / (H / G);
+    const double a = A[hh];
+    for (int64_t i = 0; i < P * N; ++i)
+        st[i] = h0 ? h0[(b * H + hh) * P * N + i] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t row = b * L + t;
+        const double step = step_size(dt, type, row * H + hh, hh, dt_bias, sp, NULL);
+        const double abar = exp(step * a);
+        const double wbar = (disc == ORACLE_ZOH && a != 0.0) ? expm1(step * a) / a : step;
+        const int64_t bc = (row * G + g) * N;
+        for (int64_t p = 0; p < P; ++p) {
+            const double xv = load(x, type, (row * H + hh) * P + p);
+            double yt = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double *s = &st[p * N + n];
+                *s = abar * *s + wbar * xv * load(B, type, bc + n);
+                yt += load(C, type, bc + n) * *s;
+            }
+            yt += (D ? D[hh] : 0.0) * xv;
+            if (z)
+                yt *= silu(load(z, type, (row * H + hh) * P + p));
+            if (y)
+                y[t * P + p] = yt;
+        }
+    }
+    if (hl)
+        for (int64_t i = 0; i < P * N; ++i)
+            hl[i] = st[i];
+}
+
+int oracle_ssd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+               int type, int disc, const void *x, const void *dt, const double *dt_bias, int dt_softplus,
+               const double *A, const void *B, const void *C, const double *D, const void *z,
+               const double *h0, int64_t nsel, const int64_t *sel, double *y, double *h_last,
+               int nthreads)
+{
+    if (batch < 0 || L < 0 || H < 1 || P < 1 || G < 1 || N < 1 || H % G != 0)
+        return -1;
+    if (type != ORACLE_F64 && type != ORACLE_F32 && type != ORACLE_BF16)
+        return -1;
+    if (disc != ORACLE_EULER && disc != ORACLE_ZOH)
+        return -1;
+    if ((L > 0 && (!x || !dt || !B || !C)) || !A)
+        return -1;
+    if (!sel)
+        nsel = batch * H;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        double *st = malloc(sizeof(double) * (size_t)(P * N));
+        if (!st)
+            bad = 1;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t k = 0; k < nsel; ++k) {
+            const int64_t c = sel ? sel[k] : k;
+            if (!st || c < 0 || c >= batch * H) {
+                bad = 1;
+                continue;
+            }
+            ssd_head(c / H, c % H, L, H, P, G, N, type, disc, x, dt, dt_bias, dt_softplus, A, B, C, D, z,
+                     h0, st, y ? y + k * L * P : NULL, h_last ? h_last + k * P * N : NULL);
+        }
+        free(st);
+    }
+    return bad ? -1 : 0;
+}

@@ -72,6 +72,86 @@ CONFIGS = {
 DECODE = DecodeConfig("decode", 256, 5120, 16, 1000)
 
 
+@dataclass(frozen=True)
+class SsdConfig:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    gate: bool = False
+    skip: bool = False
+    dtype: str = "bf16"
+
+    @property
+    def tokens_ch(self) -> int:
+        return self.batch * self.seqlen * self.nheads * self.headdim
+
+
+# Mamba-2 SSD layers. "ssd-block" has the head shape of youngju.dev SSDBlock's
+# defaults (d_model 768 as 8 heads of 96, d_state 128); "mamba2-ssd" puts the
+# same layer at the scale of the Mamba-1.4B-shaped scan workload (batch 8,
+# 8192 tokens, 4096 channels as 64 heads of 64, d_state 128, one group).
+SSD_CONFIGS = {
+    "ssd-block": SsdConfig("ssd-block", 2, 1000, 8, 96, 1, 128),
+    "mamba2-ssd": SsdConfig("mamba2-ssd", 8, 8192, 64, 64, 1, 128),
+}
+
+
+def ssd_inputs(cfg: SsdConfig, seed: int = 0, batch=None, seqlen=None, nheads=None, headdim=None,
+               ngroups=None, dstate=None, gate=None, skip=None):
+    """Inputs of one SSD layer (sizes and options may be overridden):
+    x, z ~ N(0, 1) (batch, L, H, P); dt = softplus(0.5 N(0,1) + bias[h])
+    (batch, L, H) with the scan recipe's per-head bias; B, C ~ N(0, 1)
+    (batch, L, G, N); A[h] = -(h + 1) (youngju.dev SSDBlock: A_log =
+    log(1..n_heads)); D ~ N(1, 0.1) per head when the skip is on. bf16
+    tensors are uint16 patterns."""
+    b = cfg.batch if batch is None else batch
+    L = cfg.seqlen if seqlen is None else seqlen
+    H = cfg.nheads if nheads is None else nheads
+    P = cfg.headdim if headdim is None else headdim
+    G = cfg.ngroups if ngroups is None else ngroups
+    N = cfg.dstate if dstate is None else dstate
+    gate = cfg.gate if gate is None else gate
+    skip = cfg.skip if skip is None else skip
+    bias = delta_bias(seed, H, "uniform")
+    return dict(
+        x=_normal(seed, "u", (b, L, H, P), cfg.dtype),
+        dt=_delta(seed, (b, L, H), bias, cfg.dtype),
+        A=-np.arange(1, H + 1, dtype=np.float32),
+        B=_normal(seed, "B", (b, L, G, N), cfg.dtype),
+        C=_normal(seed, "C", (b, L, G, N), cfg.dtype),
+        D=d_skip(seed, H, "normal") if skip else None,
+        z=_normal(seed, "z", (b, L, H, P), cfg.dtype) if gate else None,
+        h0=None,
+    )
+
+
+def ssd_bytes(cfg: SsdConfig, h_last: bool = True) -> int:
+    """Bytes one SSD layer must move: x, dt, B, C (and z) once, y once, A and D,
+    and the final state."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    tok = cfg.batch * cfg.seqlen
+    nbytes = (2 + (1 if cfg.gate else 0)) * cfg.tokens_ch * es      # x, y (+ z)
+    nbytes += tok * cfg.nheads * es                                 # dt
+    nbytes += 2 * tok * cfg.ngroups * cfg.dstate * es               # B, C
+    nbytes += cfg.nheads * 4 * (2 if cfg.skip else 1)               # A (+ D)
+    if h_last:
+        nbytes += cfg.batch * cfg.nheads * cfg.headdim * cfg.dstate * 4
+    return nbytes
+
+
+def ssd_flops(cfg: SsdConfig, chunk: int = 64) -> int:
+    """Matrix-core flops of the chunked evaluation at chunk length Q, per
+    (token, head): scores Q N / 2 and the masked product Q P / 2 (the causal
+    half), the state readout N P and the state update N P, two flops each."""
+    Q, N, P = chunk, cfg.dstate, cfg.headdim
+    per = 2 * (Q * N // 2 + Q * P // 2 + 2 * N * P)
+    return per * cfg.batch * cfg.seqlen * cfg.nheads
+
+
 def _threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))

@@ -28,7 +28,13 @@ None of these re-types the oracle's loop. The independent statements are:
     SiLU (youngju.dev MambaBlock.forward), and
   * the backward pass equals central finite differences of the forward oracle
     (the gradient of sum(dy*y) + sum(dh_last*h_last) by definition), and with
-    dy = 0 the state gradient reduces to the closed form exp(A*sum(delta)).
+    dy = 0 the state gradient reduces to the closed form exp(A*sum(delta)),
+  * the Mamba-2 SSD layer is the selective scan with A a scalar per head
+    (itwiki "Mamba-2와 상태 공간 쌍대성"), equals the chunked attention-like
+    evaluation of youngju.dev SSDBlock._chunk_scan with the state carried
+    across chunks (oracle.ssd_chunked) for every chunk size, reduces to a
+    causally masked matrix product when A = 0, and to the current token alone
+    when A is very negative.
 """
 from __future__ import annotations
 
@@ -582,6 +588,133 @@ def pin_bwd_conv(o):
             assert rel_err(g[key], fd) < 1e-6, (disc, name, rel_err(g[key], fd))
 
 
+# ---------------------------------------------------------------------------
+# Mamba-2 SSD layer (oracle_ssd)
+
+def _ssd_case(rng, batch, L, H, P, G, N, with_d=True, with_z=False, with_h0=False):
+    return dict(
+        x=rng.standard_normal((batch, L, H, P)),
+        dt=np.exp(rng.uniform(np.log(1e-3), np.log(0.5), (batch, L, H))),
+        A=-np.exp(rng.uniform(np.log(0.2), np.log(8.0), H)),
+        B=rng.standard_normal((batch, L, G, N)),
+        C=rng.standard_normal((batch, L, G, N)),
+        D=rng.standard_normal(H) if with_d else None,
+        z=rng.standard_normal((batch, L, H, P)) if with_z else None,
+        h0=rng.standard_normal((batch, H, P, N)) if with_h0 else None,
+    )
+
+
+def _ssd_via_scan(o, c, disc, dt_bias=None, dt_softplus=False):
+    """The SSD layer as one selective scan per group: the group's heads side by
+    side as channels d = h_local*P + p, A[d, n] = A[h] for every n, each
+    channel stepping with its head's dt (itwiki, "Mamba-2와 상태 공간 쌍대성":
+    the SSD layer is the selective SSM whose A is a scalar times the identity)."""
+    x = c["x"]
+    batch, L, H, P = x.shape
+    G, N = c["B"].shape[2], c["B"].shape[3]
+    hpg = H // G
+    y = np.empty_like(x)
+    hl = np.empty((batch, H, P, N))
+    for g in range(G):
+        hs = slice(g * hpg, (g + 1) * hpg)
+        rep = lambda a: np.repeat(a[:, :, hs], P, axis=2)        # (b, L, hpg) -> (b, L, hpg*P)
+        u = x[:, :, hs, :].reshape(batch, L, hpg * P)
+        A = np.repeat(c["A"][hs], P)[:, None] * np.ones((1, N))
+        kw = dict(D=None if c["D"] is None else np.repeat(c["D"][hs], P),
+                  z=None if c["z"] is None else c["z"][:, :, hs, :].reshape(batch, L, hpg * P),
+                  h0=None if c["h0"] is None else c["h0"][:, hs].reshape(batch, hpg * P, N),
+                  delta_bias=None if dt_bias is None else np.repeat(dt_bias[hs], P),
+                  delta_softplus=dt_softplus)
+        yy, hh = o.selective_scan(u, rep(c["dt"]), A, c["B"][:, :, g, :].copy(), c["C"][:, :, g, :].copy(),
+                                  disc=disc, **kw)
+        y[:, :, hs, :] = yy.reshape(batch, L, hpg, P)
+        hl[:, hs] = hh.reshape(batch, hpg, P, N)
+    return y, hl
+
+
+def pin_ssd_is_scalar_a_scan(o):
+    rng = np.random.default_rng(RNG_SEED + 40)
+    for disc in ("euler", "zoh"):
+        for G in (1, 2):
+            c = _ssd_case(rng, 2, 9, 4, 3, G, 5, with_z=True, with_h0=True)
+            y, hl = o.ssd(**c, disc=disc)
+            ry, rh = _ssd_via_scan(o, c, disc)
+            assert rel_err(y, ry) < 1e-12 and rel_err(hl, rh) < 1e-12, (disc, G)
+    c = _ssd_case(rng, 2, 6, 4, 2, 2, 3, with_h0=True)
+    c["dt"] = 0.5 * rng.standard_normal(c["dt"].shape)
+    bias = rng.uniform(-2.0, 0.5, 4)
+    y, hl = o.ssd(**c, dt_bias=bias, dt_softplus=True)
+    ry, rh = _ssd_via_scan(o, c, "euler", dt_bias=bias, dt_softplus=True)
+    assert rel_err(y, ry) < 1e-12 and rel_err(hl, rh) < 1e-12
+
+
+def pin_ssd_chunked_form(o):
+    from oracle.ssd_chunked import ssd_chunked
+    rng = np.random.default_rng(RNG_SEED + 41)
+    for disc in ("euler", "zoh"):
+        c = _ssd_case(rng, 2, 23, 4, 3, 2, 5, with_z=True, with_h0=True)
+        y, hl = o.ssd(**c, disc=disc)
+        for chunk in (1, 4, 7, 23, 64):
+            cy, ch = ssd_chunked(**c, disc=disc, chunk=chunk)
+            assert rel_err(cy, y) < 1e-10 and rel_err(ch, hl) < 1e-10, (disc, chunk)
+
+
+def pin_ssd_a_zero_masked_matmul(o):
+    """A = 0: no decay, so y is a causally masked product
+    y_t = sum_{s<=t} (C_t . B_s) dt_s x_s + C_t . h0 + D x_t (both discretisations:
+    the hold coefficient's A -> 0 limit is dt)."""
+    rng = np.random.default_rng(RNG_SEED + 42)
+    c = _ssd_case(rng, 2, 11, 3, 4, 1, 6, with_h0=True)
+    c["A"] = np.zeros(3)
+    scores = np.einsum("btn,bsn->bts", c["C"][:, :, 0], c["B"][:, :, 0])
+    mask = np.tril(np.ones((11, 11)))
+    ref = np.einsum("bts,bsh,bshp->bthp", scores * mask, c["dt"], c["x"])
+    ref += np.einsum("btn,bhpn->bthp", c["C"][:, :, 0], c["h0"]) + c["D"][None, None, :, None] * c["x"]
+    for disc in ("euler", "zoh"):
+        y, _ = o.ssd(**c, disc=disc)
+        assert rel_err(y, ref) < 1e-12, disc
+
+
+def pin_ssd_fast_forgetting(o):
+    """A very negative A with a positive step forgets everything before the
+    current token: y_t = (C_t . B_t) wbar_t x_t + D x_t, wbar = dt (simplified)
+    or expm1(dt A)/A -> -1/A (hold)."""
+    rng = np.random.default_rng(RNG_SEED + 43)
+    c = _ssd_case(rng, 1, 8, 2, 3, 1, 4, with_h0=True)
+    c["dt"] = rng.uniform(0.5, 1.0, c["dt"].shape)
+    c["A"] = np.array([-2e3, -5e3])
+    cb = np.einsum("btn,btn->bt", c["C"][:, :, 0], c["B"][:, :, 0])
+    for disc in ("euler", "zoh"):
+        w = c["dt"] if disc == "euler" else np.broadcast_to(-1.0 / c["A"], c["dt"].shape)
+        ref = cb[:, :, None, None] * w[..., None] * c["x"] + c["D"][None, None, :, None] * c["x"]
+        y, hl = o.ssd(**c, disc=disc)
+        assert rel_err(y, ref) < 1e-12, disc
+        last = w[:, -1, :, None, None] * c["x"][:, -1, :, :, None] * c["B"][:, -1, 0][:, None, None, :]
+        assert rel_err(hl, last) < 1e-12, disc
+
+
+def pin_ssd_head_selection_and_types(o):
+    rng = np.random.default_rng(RNG_SEED + 44)
+    c = _ssd_case(rng, 2, 10, 4, 3, 2, 4, with_z=True, with_h0=True)
+    y, hl = o.ssd(**c)
+    heads = [(1, 3), (0, 0), (1, 1)]
+    ys, hs = o.ssd(**c, heads=heads)
+    for k, (b, h) in enumerate(heads):
+        assert np.array_equal(ys[k], y[b, :, h]) and np.array_equal(hs[k], hl[b, h])
+    # f32 and bf16 storage: the oracle widens exactly
+    for name, cast in (("f32", lambda a: a.astype(np.float32)), ("bf16", _to_bf16)):
+        cc = dict(c, **{k: cast(c[k]) for k in ("x", "dt", "B", "C", "z")})
+        yt, ht = o.ssd(**cc)
+        wide = dict(c, **{k: brute._widen(cc[k]) for k in ("x", "dt", "B", "C", "z")})
+        yw, hw = o.ssd(**wide)
+        assert rel_err(yt, yw) < 1e-13 and rel_err(ht, hw) < 1e-13, name
+
+
+def _to_bf16(a):
+    bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    return ((bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_brute_force_storage_types,
@@ -606,4 +739,9 @@ ALL_PINS = [
     pin_conv_prologue,
     pin_bwd_conv,
     pin_channel_selection,
+    pin_ssd_is_scalar_a_scan,
+    pin_ssd_chunked_form,
+    pin_ssd_a_zero_masked_matmul,
+    pin_ssd_fast_forgetting,
+    pin_ssd_head_selection_and_types,
 ]

@@ -76,6 +76,22 @@ MUTANTS = {
     "conv_dx_wrong_tap": ("du[s] += cw[d * W + k] * dp;", "du[s] += cw[d * W] * dp;"),
     "conv_dw_uses_output_time": ("dcw_c[k] += dp * load(u, type, (b * L + s) * dim + d);",
                                  "dcw_c[k] += dp * load(u, type, (b * L + t) * dim + d);"),
+    # Mamba-2 SSD layer
+    "ssd_group_index": ("const int64_t g = hh / (H / G);", "const int64_t g = hh % G;"),
+    "ssd_decay_sign": ("const double abar = exp(step * a);", "const double abar = exp(-step * a);"),
+    "ssd_hold_coefficient": ("? expm1(step * a) / a : step;", "? expm1(step * a) : step;"),
+    "ssd_input_missing_step": ("*s = abar * *s + wbar * xv * load(B, type, bc + n);",
+                               "*s = abar * *s + xv * load(B, type, bc + n);"),
+    "ssd_b_c_swapped": ("yt += load(C, type, bc + n) * *s;", "yt += load(B, type, bc + n) * *s;"),
+    "ssd_skip_wrong_head": ("yt += (D ? D[hh] : 0.0) * xv;", "yt += (D ? D[0] : 0.0) * xv;"),
+    "ssd_gate_wrong_index": ("yt *= silu(load(z, type, (row * H + hh) * P + p));",
+                             "yt *= silu(load(z, type, (row * H + hh) * P));"),
+    "ssd_h0_transposed": ("st[i] = h0 ? h0[(b * H + hh) * P * N + i] : 0.0;",
+                          "st[i] = h0 ? h0[(b * H + hh) * P * N + (i % N) * P + i / N] : 0.0;"),
+    "ssd_dt_wrong_head": ("step_size(dt, type, row * H + hh, hh, dt_bias, sp, NULL);",
+                          "step_size(dt, type, row * H, hh, dt_bias, sp, NULL);"),
+    "ssd_x_wrong_stride": ("const double xv = load(x, type, (row * H + hh) * P + p);",
+                           "const double xv = load(x, type, (row * P + p) * H + hh);"),
 }
 
 
