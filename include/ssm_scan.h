@@ -1,8 +1,9 @@
 /*
  * ssm_scan.h — C ABI of the MI355X (gfx950) selective-scan library.
  *
- * The library computes the Mamba selective scan (S6) forward pass and its
- * one-token decode step with hand-written HIP kernels. Every pointer that
+ * The library computes the Mamba selective scan (S6) forward pass, its
+ * backward, its one-token decode step and the Mamba-2 SSD layer with
+ * hand-written HIP kernels. Every pointer that
  * names tensor data is a DEVICE pointer owned by the caller; the library
  * allocates and frees nothing. Work is enqueued asynchronously on the given
  * HIP stream: buffers must stay alive until the stream has finished with
@@ -205,6 +206,56 @@ int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t dtype, 
                      const float *A,
                      const void *B, const void *C, const float *D, const void *z,
                      float *h, void *y, hipStream_t stream);
+
+/*
+ * Mamba-2 SSD layer (structured state-space duality). Each head h has a
+ * scalar decay rate A[h] (the state matrix restricted to a scalar times the
+ * identity: itwiki "상태 공간 모델", section "Mamba-2와 상태 공간 쌍대성";
+ * eommydocs "State Space Models (SSM)", §2.4) and a (headdim x dstate) state;
+ * the heads of a group share B and C. Per batch row b, head h, p < headdim:
+ *
+ *   dt_t    = dt[b,t,h] (+ dt_bias[h]), through softplus when dt_softplus
+ *   H_t     = exp(dt_t A[h]) H_{t-1} + wbar_t x[b,t,h,:] B[b,t,g,:]^T     H_{-1} = h0 (or 0)
+ *   wbar_t  = dt_t (SSM_DISC_EULER) or (exp(dt_t A[h]) - 1)/A[h] (SSM_DISC_ZOH)
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] H_t[p,n] + D[h] x[b,t,h,p],  times silu(z[b,t,h,p]) with a gate
+ *
+ * with g = h / (nheads / ngroups). The library evaluates it chunk by chunk
+ * in the attention-like form of youngju.dev "mamba-state-space-model-
+ * selective-ssm", SSDBlock._chunk_scan (scores C_i . B_j times the causal
+ * decay exp(A (cum dt_i - cum dt_j)), applied to wbar x), with the state
+ * carried from chunk to chunk, on bf16 matrix cores with fp32 accumulation;
+ * the state is kept in fp32 and rounded to bf16 only as a matrix operand.
+ */
+typedef struct {
+    int64_t batch;     /* >= 0 */
+    int64_t seqlen;    /* >= 0 */
+    int32_t nheads;    /* H >= 1 */
+    int32_t headdim;   /* P: 64, 96 or 128 */
+    int32_t ngroups;   /* G >= 1, dividing nheads */
+    int32_t dstate;    /* N: 64 or 128 */
+    int32_t dtype;     /* SSM_BF16 (SSM_F32 is reported as SSM_ERR_UNSUPPORTED) */
+    int32_t disc;      /* ssm_disc */
+    int32_t dt_softplus;    /* 0 or 1 */
+    int32_t reserved;       /* 0 */
+    const float *dt_bias;   /* (nheads) fp32 device pointer, or NULL */
+} ssm_ssd_desc;
+
+/*
+ *   x, z      (batch, seqlen, nheads, headdim)  bf16, row-major; z may be NULL (no gate)
+ *   dt        (batch, seqlen, nheads)           bf16
+ *   A         (nheads) fp32 (negative for a decaying state); D (nheads) fp32 or NULL
+ *   B, C      (batch, seqlen, ngroups, dstate)  bf16
+ *   h0        (batch, nheads, headdim, dstate)  fp32, or NULL for zeros
+ *   y         (batch, seqlen, nheads, headdim)  bf16, written
+ *   h_last    (batch, nheads, headdim, dstate)  fp32, written, or NULL; may equal h0 exactly
+ * x, z, y, B, C, h0 and h_last must be 16-byte aligned (dt 2-byte, A, D,
+ * dt_bias 4-byte): SSM_ERR_ALIGN otherwise. Outputs must not overlap inputs
+ * or each other (SSM_ERR_ALIAS). No workspace. seqlen == 0 writes h_last = h0
+ * (or zeros) and no y.
+ */
+int ssm_ssd_fwd(const ssm_ssd_desc *desc, const void *x, const void *dt, const float *A,
+                const void *B, const void *C, const float *D, const void *z, const float *h0,
+                void *y, float *h_last, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *ssm_status_string(int status);

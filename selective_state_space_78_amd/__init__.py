@@ -7,7 +7,8 @@ links no torch. There is no fallback: if the library is missing, every call
 raises.
 
 Names follow the C ABI: ``ssm_scan_fwd``, ``ssm_scan_workspace_size``,
-``ssm_scan_plan``, ``ssm_state_update``, ``ssm_status_string``.
+``ssm_scan_plan``, ``ssm_scan_bwd``, ``ssm_state_update``, ``ssm_ssd_fwd``,
+``ssm_status_string``.
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ _DISC = {"euler": SSM_DISC_EULER, "zoh": SSM_DISC_ZOH}
 # Every symbol include/ssm_scan.h declares.
 EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_workspace_size_tuned",
            "ssm_scan_fwd_tuned", "ssm_scan_plan", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd",
-           "ssm_state_update", "ssm_status_string")
+           "ssm_state_update", "ssm_ssd_fwd", "ssm_status_string")
 
 
 class ScanDesc(ctypes.Structure):
@@ -33,6 +34,13 @@ class ScanDesc(ctypes.Structure):
                 ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32), ("disc", ctypes.c_int32),
                 ("delta_softplus", ctypes.c_int32), ("conv_width", ctypes.c_int32),
                 ("delta_bias", ctypes.c_void_p), ("conv_weight", ctypes.c_void_p), ("conv_bias", ctypes.c_void_p)]
+
+
+class SsdDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int32),
+                ("headdim", ctypes.c_int32), ("ngroups", ctypes.c_int32), ("dstate", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("disc", ctypes.c_int32), ("dt_softplus", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("dt_bias", ctypes.c_void_p)]
 
 
 class ScanTuning(ctypes.Structure):
@@ -78,6 +86,8 @@ def lib() -> ctypes.CDLL:
             L.ssm_state_update.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                            vp]
             L.ssm_state_update.restype = ctypes.c_int
+            L.ssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 11
+            L.ssm_ssd_fwd.restype = ctypes.c_int
             L.ssm_status_string.argtypes = [ctypes.c_int]
             L.ssm_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -313,3 +323,46 @@ def ssm_state_update(x, delta, A, B, C, h, D=None, z=None, y=None, disc="euler",
     if rc != 0:
         raise SsmError(rc, "ssm_state_update")
     return y
+
+
+def make_ssd_desc(batch, seqlen, nheads, headdim, ngroups, dstate, dtype=SSM_BF16, disc="euler",
+                  dt_bias=None, dt_softplus=False) -> SsdDesc:
+    return SsdDesc(int(batch), int(seqlen), int(nheads), int(headdim), int(ngroups), int(dstate), int(dtype),
+                   _DISC[disc], int(bool(dt_softplus)), 0, None if dt_bias is None else dt_bias.data_ptr())
+
+
+def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, h0=None, y=None, h_last=None, disc="euler",
+                dt_bias=None, dt_softplus=False, want_h_last=True, stream=None):
+    """Mamba-2 SSD layer on device tensors.
+
+    x, z: (batch, L, H, P) bfloat16; dt: (batch, L, H) bfloat16; B, C:
+    (batch, L, G, N) bfloat16; A, D, dt_bias: (H,) float32; h0: (batch, H, P, N)
+    float32. Outputs y (batch, L, H, P) and h_last (batch, H, P, N) are
+    allocated when not given. Returns (y, h_last).
+    """
+    import torch
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    code = _dtype_code(x)
+    _check(x, "x", device=dev)
+    _check(dt, "dt", (batch, L, H), x.dtype, dev)
+    _check(z, "z", (batch, L, H, P), x.dtype, dev)
+    _check(B, "B", (batch, L, G, N), x.dtype, dev)
+    _check(C, "C", (batch, L, G, N), x.dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(h0, "h0", (batch, H, P, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((batch, L, H, P), dtype=x.dtype, device=dev)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
+    _check(y, "y", (batch, L, H, P), x.dtype, dev)
+    _check(h_last, "h_last", (batch, H, P, N), torch.float32, dev)
+    desc = make_ssd_desc(batch, L, H, P, G, N, code, disc, dt_bias, dt_softplus)
+    rc = lib().ssm_ssd_fwd(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                           _ptr(h0), _ptr(y), _ptr(h_last), _stream(stream, dev))
+    if rc != 0:
+        raise SsmError(rc, "ssm_ssd_fwd")
+    return y, h_last

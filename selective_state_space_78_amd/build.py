@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 # element type and discretisation, compiled in parallel and linked into one
 # shared object
 UNITS = ("ssm_scan.hip", "scan_bf16_euler.hip", "scan_bf16_zoh.hip", "scan_f32_euler.hip", "scan_f32_zoh.hip",
-         "bwd_bf16_euler.hip", "bwd_bf16_zoh.hip", "bwd_f32_euler.hip", "bwd_f32_zoh.hip")
+         "bwd_bf16_euler.hip", "bwd_bf16_zoh.hip", "bwd_f32_euler.hip", "bwd_f32_zoh.hip",
+         "ssd_euler.hip", "ssd_zoh.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libssm_scan.so")
 ARCH = "gfx950"

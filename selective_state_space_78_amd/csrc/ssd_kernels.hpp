@@ -1,0 +1,453 @@
+// Mamba-2 SSD (state-space duality) layer on gfx950 matrix cores.
+//
+// With the state matrix of a head restricted to a scalar a times the identity
+// (itwiki "상태 공간 모델", section "Mamba-2와 상태 공간 쌍대성"), the layer
+// is, per batch row and head, h_t = exp(a dt_t) h_{t-1} + wbar_t x_t B_t^T and
+// y_t = h_t C_t (+ D x_t, * silu(z_t)), with a (P x N) state. Inside a chunk
+// of Q tokens that is a causally masked product plus the state carried in
+// (youngju.dev "mamba-state-space-model-selective-ssm", SSDBlock._chunk_scan,
+// for the chunk-internal part); with S_i = sum_{c0<=r<=i} a dt_r:
+//
+//   y_i   = sum_{j<=i} (C_i . B_j) exp(S_i - S_j) wbar_j x_j  +  exp(S_i) C_i . H
+//   H_out = exp(S_last) H + sum_j exp(S_last - S_j) wbar_j x_j B_j^T
+//
+// Kernel design:
+//  * One workgroup (4 waves) owns one (batch row, head) and walks its chunks
+//    of Q = 64 tokens in order; the fp32 state never leaves registers. Wave w
+//    holds the state rows n in [w N/4, (w+1) N/4) for every p, as MFMA
+//    accumulators (h^T tiles: lane = p column, 4 consecutive n).
+//  * Every product is a 16x16x32 bf16 MFMA with fp32 accumulation:
+//      scores  G^T[j][i] = B_j . C_i        (K = n; operands straight from L2)
+//      readout Y^T[p][i] = H[p][:] . C_i    (K = n; H from LDS as bf16)
+//      intra   Y^T[p][i] += sum_j X~[j][p] M^T[j][i]   (K = j)
+//      update  h^T[n][p] += sum_j B[j][n] X~d[j][p]    (K = j)
+//    Y^T rather than Y makes the score tile's accumulator layout (lane = i,
+//    4 consecutive j) usable as the next product's operand without a trip
+//    through LDS: the K order of that product is permuted to match, and the
+//    X~ operand is read in the same order.
+//  * Products over tokens need token-contiguous operands, so each chunk is
+//    staged into LDS transposed: X~ = wbar x, X~d = wbar exp(S_last - S_j) x
+//    (both P x Q) and B^T (N x Q); and the state as bf16 (P x N) for the
+//    readout. Waves split the staging (lane = token) and then the work: wave w
+//    computes the outputs of tokens [16w, 16w+16) and its state rows.
+//  * Tokens past the end of the sequence enter with step 0 and zero x and B,
+//    so they neither decay nor feed the state; their outputs are not stored.
+//  * Workgroup ids are remapped so that the heads of one batch row, which read
+//    the same B and C rows, run on the same XCD and share its L2.
+#pragma once
+
+#include "scan_kernels.hpp"
+
+namespace ssm_detail {
+
+struct SsdParams {
+    const uint16_t *x, *dt, *B, *C, *z;   // bf16 bit patterns
+    const float *dt_bias, *A, *D, *h0;
+    uint16_t *y;
+    float *h_last;
+    int64_t L;
+    int batch, H, G, hpg;   // heads, groups, heads per group
+    int dt_softplus;
+};
+
+// Head dimensions 64, 96, 128 and state sizes 64, 128.
+#define SSM_SSD_SHAPES(X) X(64, 64) X(64, 128) X(96, 64) X(96, 128) X(128, 64) X(128, 128)
+
+inline bool ssd_shape_supported(int P, int N) {
+#define SSM_SSD_IS(PP, NN) if (P == PP && N == NN) return true;
+    SSM_SSD_SHAPES(SSM_SSD_IS)
+#undef SSM_SSD_IS
+    return false;
+}
+
+hipError_t launch_ssd_euler(const SsdParams &p, int P, int N, hipStream_t st);
+hipError_t launch_ssd_zoh(const SsdParams &p, int P, int N, hipStream_t st);
+
+#ifdef SSM_SSD_INSTANTIATE
+
+typedef __bf16 ssd_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 ssd_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float ssd_f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSsdQ = 64;        // tokens per chunk
+constexpr int kSsdThreads = 256; // 4 waves
+
+__device__ __forceinline__ float ssd_bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ uint16_t ssd_to_bf(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+__device__ __forceinline__ uint32_t ssd_pack(float lo, float hi) {
+    const ssd_bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ ssd_f32x4 ssd_mfma(const ssd_bf16x8 &a, const ssd_bf16x8 &b, const ssd_f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ ssd_bf16x8 ssd_ld16(const uint16_t *p) {
+    return __builtin_bit_cast(ssd_bf16x8, *reinterpret_cast<const uint4 *>(p));
+}
+
+// Two 4-element pieces (8 bytes each) as one operand.
+__device__ __forceinline__ ssd_bf16x8 ssd_ld8x2(const uint16_t *p0, const uint16_t *p1) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(p0);
+    const uint2 b = *reinterpret_cast<const uint2 *>(p1);
+    const uint4 v = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(ssd_bf16x8, v);
+}
+
+// A float as two bf16 values whose sum carries 16 significant bits.
+__device__ __forceinline__ void ssd_split(float v, __bf16 &hi, __bf16 &lo) {
+    hi = (__bf16)v;
+    lo = (__bf16)(v - (float)hi);
+}
+
+// Two floats as the hi and lo words of packed bf16 pairs.
+__device__ __forceinline__ void ssd_split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    __bf16 ah, al, bh, bl;
+    ssd_split(a, ah, al);
+    ssd_split(b, bh, bl);
+    const ssd_bf16x2 h2 = {ah, bh}, l2 = {al, bl};
+    hi = __builtin_bit_cast(uint32_t, h2);
+    lo = __builtin_bit_cast(uint32_t, l2);
+}
+
+// One chunk's global inputs as a lane (= token) of each wave loads them, one
+// chunk ahead of their use.
+template <int P, int N>
+struct SsdStage {
+    static constexpr int PT = P / 16, NK = N / 32, NW = N / 4;
+    static constexpr int XPW = (PT + 3) / 4;   // x tiles staged per wave
+    uint32_t dt;                 // bf16 step of token `lane`
+    uint4 x[XPW][2];             // x[token][16 pt .. 16 pt + 15], pt = w, w + 4, ...
+    uint4 b[NW / 8];             // B[token][w NW .. (w+1) NW)
+    ssd_bf16x8 c[NK];            // C[I0 + r16][32 s + 8 g4 ..]: readout and score operands
+    uint2 xe[PT], ze[PT];        // x, z[I0 + r16][16 pt + 4 g4 ..]: skip and gate of the epilogue
+};
+
+template <int P, int N, bool ZOH>
+__global__ __launch_bounds__(kSsdThreads, 1) void ssd_fwd_kernel(const SsdParams p) {
+    constexpr int Q = kSsdQ;
+    constexpr int PT = P / 16;     // p tiles
+    constexpr int NK = N / 32;     // MFMA steps over n
+    constexpr int NW = N / 4;      // state rows per wave
+    constexpr int NTW = NW / 16;   // state row tiles per wave
+    constexpr int QS = Q + 8;      // LDS row stride of token-contiguous tiles (conflict-free 16-byte reads)
+    constexpr int HS = N + 8;      // LDS row stride of n-contiguous tiles
+    typedef SsdStage<P, N> Stage;
+    static_assert(P % 16 == 0 && N % 64 == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) uint16_t sXT[P * QS];   // x^T of the chunk
+    __shared__ __attribute__((aligned(16))) uint16_t sXh[P * QS];   // (wbar exp(S_last - S_j) x)^T, hi
+    __shared__ __attribute__((aligned(16))) uint16_t sXl[P * QS];   // ... lo
+    __shared__ __attribute__((aligned(16))) uint16_t sBT[N * QS];   // B^T
+    __shared__ __attribute__((aligned(16))) uint16_t sBR[Q * HS];   // B, token rows
+    __shared__ __attribute__((aligned(16))) uint16_t sHh[P * HS];   // state entering the chunk, hi
+    __shared__ __attribute__((aligned(16))) uint16_t sHl[P * HS];   // ... lo
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int I0 = 16 * w;   // this wave's output tokens within a chunk
+
+    const int nb = gridDim.x, bid = blockIdx.x;
+    const int qx = nb / kXcds, rx = nb % kXcds, xcd = bid % kXcds;
+    const int logical = xcd * qx + min(xcd, rx) + bid / kXcds;
+    const int h = logical % p.H, b = logical / p.H;
+    const int grp = h / p.hpg;
+
+    const float a = p.A[h];
+    const float a2 = a * kLog2e;
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const float dskip = p.D ? p.D[h] : 0.0f;
+    const int64_t L = p.L;
+    const int64_t xs = (int64_t)p.H * P;   // token stride of x, z, y
+    const int64_t bs = (int64_t)p.G * N;   // token stride of B, C
+    const uint16_t *xb = p.x + (int64_t)b * L * xs + (int64_t)h * P;
+    const uint16_t *zb = p.z ? p.z + (int64_t)b * L * xs + (int64_t)h * P : nullptr;
+    uint16_t *yb = p.y + (int64_t)b * L * xs + (int64_t)h * P;
+    const uint16_t *Bb = p.B + (int64_t)b * L * bs + (int64_t)grp * N;
+    const uint16_t *Cb = p.C + (int64_t)b * L * bs + (int64_t)grp * N;
+    const uint16_t *db = p.dt + (int64_t)b * L * p.H + h;
+
+    // Global loads of the chunk starting at c: rows past the end are clamped
+    // to the last token (their values are never used or are masked).
+    auto load_stage = [&](int64_t c, Stage &st) {
+        const int nv = (int)min<int64_t>(Q, L - c);
+        const int64_t tl = c + min(lane, nv - 1);
+        st.dt = db[tl * p.H];
+#pragma unroll
+        for (int k = 0; k < Stage::XPW; ++k) {
+            const int pt = 4 * k + w;
+            if (pt < PT) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(xb + tl * xs + 16 * pt);
+                st.x[k][0] = src[0];
+                st.x[k][1] = src[1];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NW / 8; ++k)
+            st.b[k] = *reinterpret_cast<const uint4 *>(Bb + tl * bs + w * NW + 8 * k);
+        const int64_t ti = c + min(I0 + r16, nv - 1);
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+            st.c[s] = ssd_ld16(Cb + ti * bs + 32 * s + 8 * g4);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            if (p.D)
+                st.xe[pt] = *reinterpret_cast<const uint2 *>(xb + ti * xs + 16 * pt + 4 * g4);
+            if (zb)
+                st.ze[pt] = *reinterpret_cast<const uint2 *>(zb + ti * xs + 16 * pt + 4 * g4);
+        }
+    };
+
+    // State: hacc[i][pt][r] = h[p = 16 pt + r16][n = 16 (w NTW + i) + 4 g4 + r].
+    ssd_f32x4 hacc[NTW][PT];
+    const float *h0b = p.h0 ? p.h0 + ((int64_t)b * p.H + h) * P * N : nullptr;
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const int n = 16 * (w * NTW + i) + 4 * g4;
+            hacc[i][pt] = h0b ? *reinterpret_cast<const ssd_f32x4 *>(h0b + (16 * pt + r16) * N + n)
+                              : ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+
+    Stage st;
+    if (L > 0)
+        load_stage(0, st);
+
+    for (int64_t c0 = 0; c0 < L; c0 += Q) {
+        // the state entering this chunk, as hi + lo bf16 (every wave has
+        // finished reading the previous one: barrier at the end of the last chunk)
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                uint2 hi, lo;
+                ssd_split2(hacc[i][pt][0], hacc[i][pt][1], hi.x, lo.x);
+                ssd_split2(hacc[i][pt][2], hacc[i][pt][3], hi.y, lo.y);
+                const int o = (16 * pt + r16) * HS + 16 * (w * NTW + i) + 4 * g4;
+                *reinterpret_cast<uint2 *>(&sHh[o]) = hi;
+                *reinterpret_cast<uint2 *>(&sHl[o]) = lo;
+            }
+
+        const int nv = (int)min<int64_t>(Q, L - c0);   // valid tokens in this chunk
+        const bool valid = lane < nv;
+
+        // step, decay and input weight of token `lane` (every wave computes all 64)
+        float step = 0.0f;
+        if (valid) {
+            step = ssd_bf(st.dt) + bias;
+            if (p.dt_softplus)
+                step = softplus_f(step);
+        }
+        const float la = step * a2;                 // log2 of the token's decay
+        float wbar = step;
+        if (ZOH)
+            wbar = step * expm1_over_x(step * a, __builtin_amdgcn_exp2f(la));
+        float S = la;                               // inclusive prefix sum over the chunk
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float v = __shfl_up(S, o);
+            if (lane >= o)
+                S += v;
+        }
+        const float Slast = __shfl(S, 63);
+        const float fd = wbar * __builtin_amdgcn_exp2f(Slast - S);
+
+        // stage x (raw, and weighted for the state update as hi + lo) and B
+        // (transposed and as token rows); lane = token, tokens past the end zero
+#pragma unroll
+        for (int k = 0; k < Stage::XPW; ++k) {
+            const int pt = 4 * k + w;
+            if (pt < PT) {
+                const uint4 v0 = st.x[k][0], v1 = st.x[k][1];
+                const uint32_t wd[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t bits = valid ? (e & 1 ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu) : 0u;
+                    __bf16 hi, lo;
+                    ssd_split(ssd_bf(bits) * fd, hi, lo);
+                    const int o = (16 * pt + e) * QS + lane;
+                    sXT[o] = (uint16_t)bits;
+                    sXh[o] = __builtin_bit_cast(uint16_t, hi);
+                    sXl[o] = __builtin_bit_cast(uint16_t, lo);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NW / 8; ++k) {
+            const uint4 v = valid ? st.b[k] : uint4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<uint4 *>(&sBR[lane * HS + w * NW + 8 * k]) = v;
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sBT[(w * NW + 8 * k + e) * QS + lane] = (uint16_t)(e & 1 ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu);
+        }
+
+        // this chunk's operands stay in registers; fetch the next chunk's
+        ssd_bf16x8 cop[NK];
+        uint2 xe[PT], ze[PT];
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+            cop[s] = st.c[s];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            xe[pt] = st.xe[pt];
+            ze[pt] = st.ze[pt];
+        }
+        if (c0 + Q < L)
+            load_stage(c0 + Q, st);
+        __syncthreads();
+
+        // ---- outputs of tokens [I0, I0 + 16): lane column i = I0 + r16
+        const float Si = __shfl(S, I0 + r16);
+
+        // readout of the state entering the chunk (hi + lo)
+        ssd_f32x4 yacc[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            yacc[pt] = ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < NK; ++s) {
+                const int o = (16 * pt + r16) * HS + 32 * s + 8 * g4;
+                yacc[pt] = ssd_mfma(ssd_ld16(&sHh[o]), cop[s], yacc[pt]);
+                yacc[pt] = ssd_mfma(ssd_ld16(&sHl[o]), cop[s], yacc[pt]);
+            }
+        }
+        {
+            const float ei = __builtin_amdgcn_exp2f(Si);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                yacc[pt] *= ei;
+        }
+
+        // scores of key tiles J <= w, decayed, weighted, masked, as hi + lo
+        // operands: element 4 (J%2) + r of mop*[J/2] is M^T[16 J + 4 g4 + r][i]
+        ssd_bf16x8 mh[2], ml[2];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            if (J <= w) {
+                ssd_f32x4 gt = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < NK; ++s)
+                    gt = ssd_mfma(ssd_ld16(&sBR[(16 * J + r16) * HS + 32 * s + 8 * g4]), cop[s], gt);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int jj = 16 * J + 4 * g4 + r;
+                    const float Sj = __shfl(S, jj);
+                    const float wj = __shfl(wbar, jj);
+                    const bool keep = J < w || 4 * g4 + r <= r16;
+                    const float m = keep ? gt[r] * __builtin_amdgcn_exp2f(Si - Sj) * wj : 0.0f;
+                    __bf16 hi, lo;
+                    ssd_split(m, hi, lo);
+                    mh[J >> 1][4 * (J & 1) + r] = hi;
+                    ml[J >> 1][4 * (J & 1) + r] = lo;
+                }
+            } else if ((J & 1) && J - 1 <= w) {
+                // odd key tile past the diagonal, paired with a computed one: zeros
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    mh[J >> 1][4 + r] = (__bf16)0.0f;
+                    ml[J >> 1][4 + r] = (__bf16)0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int Jp = 0; Jp < 2; ++Jp) {
+            if (2 * Jp <= w) {
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const uint16_t *row = &sXT[(16 * pt + r16) * QS + 32 * Jp + 4 * g4];
+                    const ssd_bf16x8 xo = ssd_ld8x2(row, row + 16);
+                    yacc[pt] = ssd_mfma(xo, mh[Jp], yacc[pt]);
+                    yacc[pt] = ssd_mfma(xo, ml[Jp], yacc[pt]);
+                }
+            }
+        }
+
+        // skip, gate, store: yacc[pt][r] = y[i][p = 16 pt + 4 g4 + r]
+        if (I0 + r16 < nv) {
+            const int64_t off = (c0 + I0 + r16) * xs + 4 * g4;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                float v[4] = {yacc[pt][0], yacc[pt][1], yacc[pt][2], yacc[pt][3]};
+                if (p.D) {
+                    v[0] += dskip * ssd_bf(xe[pt].x & 0xffffu);
+                    v[1] += dskip * ssd_bf(xe[pt].x >> 16);
+                    v[2] += dskip * ssd_bf(xe[pt].y & 0xffffu);
+                    v[3] += dskip * ssd_bf(xe[pt].y >> 16);
+                }
+                if (zb) {
+                    v[0] *= silu(ssd_bf(ze[pt].x & 0xffffu));
+                    v[1] *= silu(ssd_bf(ze[pt].x >> 16));
+                    v[2] *= silu(ssd_bf(ze[pt].y & 0xffffu));
+                    v[3] *= silu(ssd_bf(ze[pt].y >> 16));
+                }
+                const uint2 o = {ssd_pack(v[0], v[1]), ssd_pack(v[2], v[3])};
+                *reinterpret_cast<uint2 *>(yb + off + 16 * pt) = o;
+            }
+        }
+
+        // ---- state update of rows [w NW, (w+1) NW)
+        {
+            const float dec = __builtin_amdgcn_exp2f(Slast);
+#pragma unroll
+            for (int i = 0; i < NTW; ++i)
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+                    hacc[i][pt] *= dec;
+#pragma unroll
+            for (int ks = 0; ks < Q / 32; ++ks) {
+                ssd_bf16x8 bop[NTW];
+#pragma unroll
+                for (int i = 0; i < NTW; ++i)
+                    bop[i] = ssd_ld16(&sBT[(16 * (w * NTW + i) + r16) * QS + 32 * ks + 8 * g4]);
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const int o = (16 * pt + r16) * QS + 32 * ks + 8 * g4;
+                    const ssd_bf16x8 xh = ssd_ld16(&sXh[o]);
+                    const ssd_bf16x8 xl = ssd_ld16(&sXl[o]);
+#pragma unroll
+                    for (int i = 0; i < NTW; ++i) {
+                        hacc[i][pt] = ssd_mfma(bop[i], xh, hacc[i][pt]);
+                        hacc[i][pt] = ssd_mfma(bop[i], xl, hacc[i][pt]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (p.h_last) {
+        float *hl = p.h_last + ((int64_t)b * p.H + h) * P * N;
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                *reinterpret_cast<ssd_f32x4 *>(hl + (16 * pt + r16) * N + 16 * (w * NTW + i) + 4 * g4) = hacc[i][pt];
+    }
+}
+
+template <int P, int N, bool ZOH>
+hipError_t launch_ssd_pn(const SsdParams &p, hipStream_t st) {
+    const int64_t blocks = (int64_t)p.batch * p.H;
+    hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH>), dim3((unsigned)blocks), dim3(kSsdThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+template <bool ZOH>
+hipError_t launch_ssd_t(const SsdParams &p, int P, int N, hipStream_t st) {
+#define SSM_SSD_CASE(PP, NN) \
+    if (P == PP && N == NN)  \
+        return launch_ssd_pn<PP, NN, ZOH>(p, st);
+    SSM_SSD_SHAPES(SSM_SSD_CASE)
+#undef SSM_SSD_CASE
+    return hipErrorInvalidValue;
+}
+
+#endif  // SSM_SSD_INSTANTIATE
+
+}  // namespace ssm_detail

@@ -17,6 +17,7 @@
 #include "ssm_scan.h"
 #include "scan_kernels.hpp"
 #include "bwd_kernels.hpp"
+#include "ssd_kernels.hpp"
 
 namespace ssm_detail {
 hipError_t launch_bwd_reduce(const BwdReduceParams &p, hipStream_t st);
@@ -765,13 +766,82 @@ extern "C" int ssm_scan_bwd(const ssm_scan_desc *desc, const void *u, const void
                     ddelta_bias, workspace, workspace_bytes, stream);
 }
 
+extern "C" int ssm_ssd_fwd(const ssm_ssd_desc *desc, const void *x, const void *dt, const float *A,
+                           const void *B, const void *C, const float *D, const void *z, const float *h0,
+                           void *y, float *h_last, hipStream_t stream) {
+    if (desc == nullptr) return SSM_ERR_NULL;
+    const ssm_ssd_desc &d = *desc;
+    if (d.batch < 0 || d.seqlen < 0 || d.nheads < 1 || d.ngroups < 1 || d.nheads % d.ngroups != 0)
+        return SSM_ERR_SHAPE;
+    if (d.dtype != SSM_F32 && d.dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (d.dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+    if (d.disc != SSM_DISC_EULER && d.disc != SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
+    if (d.dt_softplus != 0 && d.dt_softplus != 1) return SSM_ERR_UNSUPPORTED;
+    if (!ssd_shape_supported(d.headdim, d.dstate)) return SSM_ERR_UNSUPPORTED;
+    const int64_t P = d.headdim, N = d.dstate, H = d.nheads, G = d.ngroups;
+    int64_t bl, heads, tok_elems, bc_elems, st_elems;
+    if (!mul_ok(d.batch, d.seqlen, &bl) || !mul_ok(d.batch, H, &heads) || !mul_ok(bl, H * P, &tok_elems) ||
+        !mul_ok(bl, G * N, &bc_elems) || !mul_ok(heads, P * N * 4, &st_elems) || tok_elems > INT64_MAX / 4 ||
+        heads > INT32_MAX)
+        return SSM_ERR_SHAPE;
+    st_elems /= 4;
+    if (heads == 0) return SSM_OK;
+    if (A == nullptr) return SSM_ERR_NULL;
+    if (bl > 0 && (x == nullptr || dt == nullptr || B == nullptr || C == nullptr || y == nullptr))
+        return SSM_ERR_NULL;
+    // x, z, y, B, C move in 8- and 16-byte pieces, states in 16-byte pieces
+    const void *wide[] = {x, z, y, B, C, h0, h_last};
+    for (const void *q : wide)
+        if (q && !aligned(q, 16)) return SSM_ERR_ALIGN;
+    if (!aligned(dt, 2) || !aligned(A, 4) || (D && !aligned(D, 4)) || (d.dt_bias && !aligned(d.dt_bias, 4)))
+        return SSM_ERR_ALIGN;
+    const Range r_y = range_of(y, tok_elems * 2);
+    const Range r_hl = range_of(h_last, h_last ? st_elems * 4 : 0);
+    const Range inputs[] = {range_of(x, tok_elems * 2), range_of(z, z ? tok_elems * 2 : 0),
+                            range_of(dt, bl * H * 2), range_of(B, bc_elems * 2), range_of(C, bc_elems * 2),
+                            range_of(A, H * 4), range_of(D, D ? H * 4 : 0),
+                            range_of(d.dt_bias, d.dt_bias ? H * 4 : 0), range_of(h0, h0 ? st_elems * 4 : 0)};
+    const int n_in = (int)(sizeof(inputs) / sizeof(inputs[0]));
+    for (int k = 0; k < n_in; ++k) {
+        const Range &r = inputs[k];
+        if (overlaps(r_y, r)) return SSM_ERR_ALIAS;
+        // h_last may be h0 itself (the state continued in place): the last input
+        const bool in_place = k == n_in - 1 && h_last == h0;
+        if (overlaps(r_hl, r) && !in_place) return SSM_ERR_ALIAS;
+    }
+    if (overlaps(r_y, r_hl)) return SSM_ERR_ALIAS;
+    if (bl == 0 && h_last == nullptr) return SSM_OK;
+
+    SsdParams p{};
+    p.x = static_cast<const uint16_t *>(x);
+    p.dt = static_cast<const uint16_t *>(dt);
+    p.B = static_cast<const uint16_t *>(B);
+    p.C = static_cast<const uint16_t *>(C);
+    p.z = static_cast<const uint16_t *>(z);
+    p.dt_bias = d.dt_bias;
+    p.A = A;
+    p.D = D;
+    p.h0 = h0;
+    p.y = static_cast<uint16_t *>(y);
+    p.h_last = h_last;
+    p.L = d.seqlen;
+    p.batch = (int)d.batch;
+    p.H = (int)H;
+    p.G = (int)G;
+    p.hpg = (int)(H / G);
+    p.dt_softplus = d.dt_softplus;
+    const hipError_t e = d.disc == SSM_DISC_ZOH ? launch_ssd_zoh(p, (int)P, (int)N, stream)
+                                                : launch_ssd_euler(p, (int)P, (int)N, stream);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 extern "C" const char *ssm_status_string(int status) {
     switch (status) {
     case SSM_OK: return "ok";
     case SSM_ERR_NULL: return "a required pointer is NULL";
     case SSM_ERR_SHAPE: return "invalid or too large sizes";
     case SSM_ERR_DTYPE: return "unknown element type";
-    case SSM_ERR_UNSUPPORTED: return "unsupported dstate, discretisation or launch shape";
+    case SSM_ERR_UNSUPPORTED: return "unsupported dstate, head size, element type, discretisation or launch shape";
     case SSM_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
     case SSM_ERR_WORKSPACE: return "workspace missing or too small";
     case SSM_ERR_HIP: return "the HIP runtime refused a kernel launch";

@@ -222,3 +222,54 @@ def test_bwd_workspace(L):
     assert bwd_call(L, d, ws_bytes=need - 1) == EWS
     assert L.ssm_scan_bwd_workspace_size(ctypes.byref(desc(L=0))) == 0
     assert L.ssm_scan_bwd_workspace_size(None) == 0
+
+
+def ssd_desc(b=2, L=100, H=4, P=64, G=1, N=128, dtype=ssm.SSM_BF16, disc=0, softplus=0, bias=None):
+    return ssm.SsdDesc(b, L, H, P, G, N, dtype, disc, softplus, 0, bias)
+
+
+def ssd_call(L, dsc, x=1 * GB, dt=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB, h0=0,
+             y=8 * GB, h_last=9 * GB):
+    args = [ctypes.byref(dsc) if dsc is not None else None]
+    args += [fake(a) if a else None for a in (x, dt, A, B, C, D, z, h0, y, h_last)]
+    return L.ssm_ssd_fwd(*args, None)
+
+
+def test_ssd_descriptor_errors(L):
+    assert ssd_call(L, None) == ENULL
+    assert ssd_call(L, ssd_desc(b=-1)) == ESHAPE
+    assert ssd_call(L, ssd_desc(L=-1)) == ESHAPE
+    assert ssd_call(L, ssd_desc(H=0)) == ESHAPE
+    assert ssd_call(L, ssd_desc(H=6, G=4)) == ESHAPE          # groups must divide heads
+    assert ssd_call(L, ssd_desc(dtype=9)) == EDTYPE
+    assert ssd_call(L, ssd_desc(dtype=ssm.SSM_F32)) == EUNSUP  # bf16 matrix-core path only
+    assert ssd_call(L, ssd_desc(P=48)) == EUNSUP
+    assert ssd_call(L, ssd_desc(N=16)) == EUNSUP
+    assert ssd_call(L, ssd_desc(disc=2)) == EUNSUP
+    assert ssd_call(L, ssd_desc(softplus=3)) == EUNSUP
+    assert ssd_call(L, ssd_desc(b=1 << 40, L=1 << 30)) == ESHAPE
+
+
+def test_ssd_pointer_errors(L):
+    assert ssd_call(L, ssd_desc(), x=0) == ENULL
+    assert ssd_call(L, ssd_desc(), dt=0) == ENULL
+    assert ssd_call(L, ssd_desc(), A=0) == ENULL
+    assert ssd_call(L, ssd_desc(), y=0) == ENULL
+    assert ssd_call(L, ssd_desc(), x=1 * GB + 8) == EALIGN
+    assert ssd_call(L, ssd_desc(), B=4 * GB + 2) == EALIGN
+    assert ssd_call(L, ssd_desc(), h_last=9 * GB + 4) == EALIGN
+    assert ssd_call(L, ssd_desc(), dt=2 * GB + 1) == EALIGN
+    assert ssd_call(L, ssd_desc(), A=3 * GB + 2) == EALIGN
+
+
+def test_ssd_alias_errors(L):
+    assert ssd_call(L, ssd_desc(), y=1 * GB + 4096) == EALIAS          # y inside x
+    assert ssd_call(L, ssd_desc(), h_last=5 * GB) == EALIAS             # h_last on C
+    assert ssd_call(L, ssd_desc(), h_last=8 * GB + 256) == EALIAS       # h_last inside y
+    assert ssd_call(L, ssd_desc(), h0=10 * GB, h_last=10 * GB + 16) == EALIAS   # shifted, not in place
+
+
+def test_ssd_nothing_to_do(L):
+    # no heads, or no tokens and no state wanted: success without a launch
+    assert ssd_call(L, ssd_desc(b=0)) == OK
+    assert ssd_call(L, ssd_desc(L=0), x=0, dt=0, B=0, C=0, y=0, h_last=0) == OK
