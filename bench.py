@@ -9,7 +9,10 @@ algorithmic HBM rate, the backward of the same scan and the decode step
 measured alongside, and the fp64 CPU oracle timed on a bounded sample of the
 same workload (whose outputs are also compared with the GPU's timed outputs).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-bwd] [--no-decode]
+The Mamba-2 SSD layer (ssm_ssd_fwd) on its own workload is measured alongside
+in the same way (roofline position and the oracle on a sample of heads).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-bwd] [--no-decode] [--no-ssd]
 """
 from __future__ import annotations
 
@@ -200,6 +203,86 @@ def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_
     }
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_ssd(torch, ssm, steps=20, warmup=3, cpu=True, budget_s=10.0):
+    """The Mamba-2 SSD layer (ssm_ssd_fwd) on the mamba2-ssd workload, with its
+    roofline position and the fp64 oracle on a bounded sample of heads."""
+    cfg = si.SSD_CONFIGS["mamba2-ssd"]
+    x = si.ssd_inputs(cfg, seed=0)
+    d = {k: to_dev(v, torch) for k, v in x.items()}
+    y = torch.empty((cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim), dtype=torch.bfloat16, device="cuda")
+    hl = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device="cuda")
+
+    def call():
+        ssm.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], y=y, h_last=hl)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = si.ssd_bytes(cfg)
+    flops = si.ssd_flops(cfg)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "workload": "Mamba-2 SSD layer: batch %d, L %d, %d heads x %d, d_state %d, %d group, bf16 x/dt/B/C/y, "
+                    "fp32 A and state, final state written" % (cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim,
+                                                               cfg.dstate, cfg.ngroups),
+        "ms_per_call": ms,
+        "Gtokens*ch/s": cfg.tokens_ch / (ms * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "ssd_fwd_kernel",
+            "achieved": gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": nbytes,
+            "traffic": None,
+            "mfma": {"algorithmic_flops_per_launch": flops, "achieved_TFLOPs": tflops,
+                     "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "note": "bf16 dense peak; the kernel issues the readout, masked-product and update "
+                             "MFMAs twice (hi + lo bf16 operands)"},
+        },
+    }
+    if cpu:
+        import oracle
+        o = oracle.load()
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        threads = max(1, min(16, cores))
+        probe = [(0, h) for h in range(threads)]
+        t0 = time.perf_counter()
+        o.ssd(**x, heads=probe, nthreads=threads, want_y=False)
+        per_head = (time.perf_counter() - t0) / len(probe)
+        k = int(min(cfg.batch * cfg.nheads, max(threads, budget_s / max(per_head, 1e-12))))
+        heads = [(c // cfg.nheads, c % cfg.nheads) for c in range(k)]
+        t0 = time.perf_counter()
+        yr, _ = o.ssd(**x, heads=heads, nthreads=threads)
+        sec = time.perf_counter() - t0
+        yg = np.stack([y[b, :, h].float().cpu().numpy() for b, h in heads])
+        out["cpu_baseline"] = {
+            "value": k * cfg.seqlen * cfg.headdim / sec / 1e9,
+            "unit": "Gtokens*ch/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": "first %d of %d heads in (batch, head) order, all %d tokens x %d channels, fp64, %.1f s" % (
+                k, cfg.batch * cfg.nheads, cfg.seqlen, cfg.headdim, sec),
+            "parity_max_rel_err_vs_gpu": rel_err(yg, yr),
+        }
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,6 +300,7 @@ def main():
     ap.add_argument("--tuning", type=str, default=None, help="state_groups,segments")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=WORKLOAD,
                     help="scan workload of the timed step (the default is the headline one)")
+    ap.add_argument("--no-ssd", action="store_true", help="skip the Mamba-2 SSD layer measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale profiler byte counters)")
     args = ap.parse_args()
@@ -337,6 +421,9 @@ def main():
     if not args.no_decode:
         print("bench: decode", file=sys.stderr, flush=True)
         out["decode"] = bench_decode(torch, ssm)
+    if not args.no_ssd:
+        print("bench: Mamba-2 SSD layer", file=sys.stderr, flush=True)
+        out["ssd"] = bench_ssd(torch, ssm, cpu=not args.no_cpu)
     if not args.no_cpu:
         print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(x, y, torch, opts=oracle_opts)

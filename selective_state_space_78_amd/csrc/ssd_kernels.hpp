@@ -70,6 +70,16 @@ typedef __bf16 ssd_bf16x2 __attribute__((ext_vector_type(2)));
 typedef float ssd_f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSsdQ = 64;        // tokens per chunk
+
+// Scheduling fences between the phases of a chunk: they keep the scheduler
+// from hoisting one phase's operand loads into the previous phase past the
+// register budget.
+#ifndef SSM_SSD_PHASE_FENCE_UPDATE
+#define SSM_SSD_PHASE_FENCE_UPDATE __builtin_amdgcn_sched_barrier(0);
+#endif
+#ifndef SSM_SSD_PHASE_FENCE_SCORES
+#define SSM_SSD_PHASE_FENCE_SCORES __builtin_amdgcn_sched_barrier(0);
+#endif
 constexpr int kSsdThreads = 256; // 4 waves
 
 __device__ __forceinline__ float ssd_bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -89,12 +99,45 @@ __device__ __forceinline__ ssd_bf16x8 ssd_ld16(const uint16_t *p) {
     return __builtin_bit_cast(ssd_bf16x8, *reinterpret_cast<const uint4 *>(p));
 }
 
-// Two 4-element pieces (8 bytes each) as one operand.
-__device__ __forceinline__ ssd_bf16x8 ssd_ld8x2(const uint16_t *p0, const uint16_t *p1) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(p0);
-    const uint2 b = *reinterpret_cast<const uint2 *>(p1);
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive 16-bit values V_s[0..3], and
+// lane 4q + c receives V_q[c], V_{q+4}[c], V_{q+8}[c], V_{q+12}[c]. With lane s
+// pointing at row r0 + (s >> 2), columns c0 + 4 (s & 3) of a row-major tile,
+// lane 4q + c gets column c0 + 4q + c of rows r0 .. r0 + 3: a column of the
+// tile, as a matrix-core operand whose K runs along the rows needs it.
+__device__ __forceinline__ uint2 ssd_ld_tr(const uint16_t *p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Two transposing reads (K positions 0..3 and 4..7) as one operand.
+__device__ __forceinline__ ssd_bf16x8 ssd_ld_tr2(const uint16_t *p0, const uint16_t *p1) {
+    const uint2 a = ssd_ld_tr(p0);
+    const uint2 b = ssd_ld_tr(p1);
     const uint4 v = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(ssd_bf16x8, v);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Kogge-Stone steps within
+// rows of 16 (DPP row shifts), then the row totals carried across rows (DPP
+// row broadcasts of lanes 15 and 31). Lanes without a source add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float ssd_dpp_add(float v, bool take) {
+    const float u = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                          ROW_MASK, 0xF, false));
+    return take ? v + u : v;
+}
+
+__device__ __forceinline__ float ssd_prefix_sum(float v, int lane) {
+    const int r = lane & 15;
+    v = ssd_dpp_add<0x111, 0xF>(v, r >= 1);              // row_shr:1
+    v = ssd_dpp_add<0x112, 0xF>(v, r >= 2);              // row_shr:2
+    v = ssd_dpp_add<0x114, 0xF>(v, r >= 4);              // row_shr:4
+    v = ssd_dpp_add<0x118, 0xF>(v, r >= 8);              // row_shr:8
+    v = ssd_dpp_add<0x142, 0xA>(v, (lane & 16) != 0);    // row_bcast:15 -> rows 1, 3
+    v = ssd_dpp_add<0x143, 0xC>(v, (lane & 32) != 0);    // row_bcast:31 -> rows 2, 3
+    return v;
 }
 
 // A float as two bf16 values whose sum carries 16 significant bits.
@@ -115,46 +158,50 @@ __device__ __forceinline__ void ssd_split2(float a, float b, uint32_t &hi, uint3
 
 // One chunk's global inputs as a lane (= token) of each wave loads them, one
 // chunk ahead of their use.
-template <int P, int N>
+template <int P, int N, int HPW>
 struct SsdStage {
-    static constexpr int PT = P / 16, NK = N / 32, NW = N / 4;
+    static constexpr int PT = P / 16;
     static constexpr int XPW = (PT + 3) / 4;   // x tiles staged per wave
-    uint32_t dt;                 // bf16 step of token `lane`
-    uint4 x[XPW][2];             // x[token][16 pt .. 16 pt + 15], pt = w, w + 4, ...
-    uint4 b[NW / 8];             // B[token][w NW .. (w+1) NW)
-    ssd_bf16x8 c[NK];            // C[I0 + r16][32 s + 8 g4 ..]: readout and score operands
-    uint2 xe[PT], ze[PT];        // x, z[I0 + r16][16 pt + 4 g4 ..]: skip and gate of the epilogue
+    static constexpr int NBW = N / (4 * HPW);  // B columns staged per wave
+    uint16_t dt;                 // bf16 step of token `lane` for this wave's head
+    uint4 x[XPW][2];             // x[token][16 pt .. 16 pt + 15], pt = wl, wl + 4, ...
+    uint4 b[NBW / 8];            // B[token][w NBW .. (w+1) NBW)
 };
 
-template <int P, int N, bool ZOH>
-__global__ __launch_bounds__(kSsdThreads, 1) void ssd_fwd_kernel(const SsdParams p) {
+// HPW heads of one group per workgroup, four waves per head; the heads share
+// the staged B tiles.
+template <int P, int N, bool ZOH, int HPW>
+__global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const SsdParams p) {
     constexpr int Q = kSsdQ;
     constexpr int PT = P / 16;     // p tiles
     constexpr int NK = N / 32;     // MFMA steps over n
     constexpr int NW = N / 4;      // state rows per wave
     constexpr int NTW = NW / 16;   // state row tiles per wave
-    constexpr int QS = Q + 8;      // LDS row stride of token-contiguous tiles (conflict-free 16-byte reads)
+    constexpr int XS = P + 16;     // LDS row stride of token rows of x (conflict-free transposing reads)
     constexpr int HS = N + 8;      // LDS row stride of n-contiguous tiles
-    typedef SsdStage<P, N> Stage;
-    static_assert(P % 16 == 0 && N % 64 == 0, "tile shape");
+    typedef SsdStage<P, N, HPW> Stage;
+    constexpr int NBW = Stage::NBW;
+    static_assert(P % 16 == 0 && N % 64 == 0 && NBW % 8 == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sXT[P * QS];   // x^T of the chunk
-    __shared__ __attribute__((aligned(16))) uint16_t sXh[P * QS];   // (wbar exp(S_last - S_j) x)^T, hi
-    __shared__ __attribute__((aligned(16))) uint16_t sXl[P * QS];   // ... lo
-    __shared__ __attribute__((aligned(16))) uint16_t sBT[N * QS];   // B^T
-    __shared__ __attribute__((aligned(16))) uint16_t sBR[Q * HS];   // B, token rows
-    __shared__ __attribute__((aligned(16))) uint16_t sHh[P * HS];   // state entering the chunk, hi
-    __shared__ __attribute__((aligned(16))) uint16_t sHl[P * HS];   // ... lo
+    __shared__ __attribute__((aligned(16))) uint16_t sBR[Q * HS];         // B, token rows
+    __shared__ __attribute__((aligned(16))) uint16_t sXT[HPW][Q * XS];    // x, token rows
+    __shared__ __attribute__((aligned(16))) uint16_t sXh[HPW][Q * XS];    // wbar exp(S_last - S_j) x, hi
+    __shared__ __attribute__((aligned(16))) uint16_t sXl[HPW][Q * XS];    // ... lo
+    __shared__ __attribute__((aligned(16))) uint16_t sHh[HPW][P * HS];    // state entering the chunk, hi
+    __shared__ __attribute__((aligned(16))) uint16_t sHl[HPW][P * HS];    // ... lo
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hs = w >> 2, wl = w & 3;   // head slot, role within the head
     const int r16 = lane & 15, g4 = lane >> 4;
-    const int I0 = 16 * w;   // this wave's output tokens within a chunk
+    const int I0 = 16 * wl;              // this wave's output tokens within a chunk
 
     const int nb = gridDim.x, bid = blockIdx.x;
     const int qx = nb / kXcds, rx = nb % kXcds, xcd = bid % kXcds;
     const int logical = xcd * qx + min(xcd, rx) + bid / kXcds;
-    const int h = logical % p.H, b = logical / p.H;
+    const int hpb = p.H / HPW;
+    const int b = logical / hpb;
+    const int h = (logical % hpb) * HPW + hs;
     const int grp = h / p.hpg;
 
     const float a = p.A[h];
@@ -170,16 +217,21 @@ __global__ __launch_bounds__(kSsdThreads, 1) void ssd_fwd_kernel(const SsdParams
     const uint16_t *Bb = p.B + (int64_t)b * L * bs + (int64_t)grp * N;
     const uint16_t *Cb = p.C + (int64_t)b * L * bs + (int64_t)grp * N;
     const uint16_t *db = p.dt + (int64_t)b * L * p.H + h;
+    uint16_t *const XT = sXT[hs];
+    uint16_t *const Xh = sXh[hs];
+    uint16_t *const Xl = sXl[hs];
+    uint16_t *const Hh = sHh[hs];
+    uint16_t *const Hl = sHl[hs];
 
-    // Global loads of the chunk starting at c: rows past the end are clamped
-    // to the last token (their values are never used or are masked).
+    // Staging loads of the chunk starting at c, one chunk ahead: rows past
+    // the end are clamped to the last token (their values are zeroed or masked).
     auto load_stage = [&](int64_t c, Stage &st) {
         const int nv = (int)min<int64_t>(Q, L - c);
         const int64_t tl = c + min(lane, nv - 1);
         st.dt = db[tl * p.H];
 #pragma unroll
         for (int k = 0; k < Stage::XPW; ++k) {
-            const int pt = 4 * k + w;
+            const int pt = 4 * k + wl;
             if (pt < PT) {
                 const uint4 *src = reinterpret_cast<const uint4 *>(xb + tl * xs + 16 * pt);
                 st.x[k][0] = src[0];
@@ -187,29 +239,18 @@ __global__ __launch_bounds__(kSsdThreads, 1) void ssd_fwd_kernel(const SsdParams
             }
         }
 #pragma unroll
-        for (int k = 0; k < NW / 8; ++k)
-            st.b[k] = *reinterpret_cast<const uint4 *>(Bb + tl * bs + w * NW + 8 * k);
-        const int64_t ti = c + min(I0 + r16, nv - 1);
-#pragma unroll
-        for (int s = 0; s < NK; ++s)
-            st.c[s] = ssd_ld16(Cb + ti * bs + 32 * s + 8 * g4);
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            if (p.D)
-                st.xe[pt] = *reinterpret_cast<const uint2 *>(xb + ti * xs + 16 * pt + 4 * g4);
-            if (zb)
-                st.ze[pt] = *reinterpret_cast<const uint2 *>(zb + ti * xs + 16 * pt + 4 * g4);
-        }
+        for (int k = 0; k < NBW / 8; ++k)
+            st.b[k] = *reinterpret_cast<const uint4 *>(Bb + tl * bs + w * NBW + 8 * k);
     };
 
-    // State: hacc[i][pt][r] = h[p = 16 pt + r16][n = 16 (w NTW + i) + 4 g4 + r].
+    // State: hacc[i][pt][r] = h[p = 16 pt + r16][n = 16 (wl NTW + i) + 4 g4 + r].
     ssd_f32x4 hacc[NTW][PT];
     const float *h0b = p.h0 ? p.h0 + ((int64_t)b * p.H + h) * P * N : nullptr;
 #pragma unroll
     for (int i = 0; i < NTW; ++i)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            const int n = 16 * (w * NTW + i) + 4 * g4;
+            const int n = 16 * (wl * NTW + i) + 4 * g4;
             hacc[i][pt] = h0b ? *reinterpret_cast<const ssd_f32x4 *>(h0b + (16 * pt + r16) * N + n)
                               : ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
@@ -217,8 +258,35 @@ __global__ __launch_bounds__(kSsdThreads, 1) void ssd_fwd_kernel(const SsdParams
     Stage st;
     if (L > 0)
         load_stage(0, st);
+    // nothing of the prologue stays in flight into the loop (the loop's wait
+    // counts then only see its own loads)
+    __builtin_amdgcn_s_waitcnt(0);
 
     for (int64_t c0 = 0; c0 < L; c0 += Q) {
+        const int nv = (int)min<int64_t>(Q, L - c0);   // valid tokens in this chunk
+        const bool valid = lane < nv;
+
+        // this wave's C rows (operands of the readout and the scores) and the
+        // skip and gate inputs of its outputs; issued before the next chunk's
+        // staging loads (which are unconditional), so that waiting for them
+        // never waits for those
+        const int64_t ti = c0 + min(I0 + r16, nv - 1);
+        ssd_bf16x8 cop[NK];
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+            cop[s] = ssd_ld16(Cb + ti * bs + 32 * s + 8 * g4);
+        uint2 xe[PT], ze[PT];
+        if (p.D) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                xe[pt] = *reinterpret_cast<const uint2 *>(xb + ti * xs + 16 * pt + 4 * g4);
+        }
+        if (zb) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                ze[pt] = *reinterpret_cast<const uint2 *>(zb + ti * xs + 16 * pt + 4 * g4);
+        }
+
         // the state entering this chunk, as hi + lo bf16 (every wave has
         // finished reading the previous one: barrier at the end of the last chunk)
 #pragma unroll
@@ -228,15 +296,12 @@ __global__ __launch_bounds__(kSsdThreads, 1) void ssd_fwd_kernel(const SsdParams
                 uint2 hi, lo;
                 ssd_split2(hacc[i][pt][0], hacc[i][pt][1], hi.x, lo.x);
                 ssd_split2(hacc[i][pt][2], hacc[i][pt][3], hi.y, lo.y);
-                const int o = (16 * pt + r16) * HS + 16 * (w * NTW + i) + 4 * g4;
-                *reinterpret_cast<uint2 *>(&sHh[o]) = hi;
-                *reinterpret_cast<uint2 *>(&sHl[o]) = lo;
+                const int o = (16 * pt + r16) * HS + 16 * (wl * NTW + i) + 4 * g4;
+                *reinterpret_cast<uint2 *>(&Hh[o]) = hi;
+                *reinterpret_cast<uint2 *>(&Hl[o]) = lo;
             }
 
-        const int nv = (int)min<int64_t>(Q, L - c0);   // valid tokens in this chunk
-        const bool valid = lane < nv;
-
-        // step, decay and input weight of token `lane` (every wave computes all 64)
+        // step, decay and input weight of token `lane` (every wave of a head computes all 64)
         float step = 0.0f;
         if (valid) {
             step = ssd_bf(st.dt) + bias;
@@ -247,176 +312,174 @@ __global__ __launch_bounds__(kSsdThreads, 1) void ssd_fwd_kernel(const SsdParams
         float wbar = step;
         if (ZOH)
             wbar = step * expm1_over_x(step * a, __builtin_amdgcn_exp2f(la));
-        float S = la;                               // inclusive prefix sum over the chunk
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float v = __shfl_up(S, o);
-            if (lane >= o)
-                S += v;
-        }
-        const float Slast = __shfl(S, 63);
+        const float S = ssd_prefix_sum(la, lane);    // inclusive prefix sum over the chunk
+        const float Slast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), 63));
         const float fd = wbar * __builtin_amdgcn_exp2f(Slast - S);
 
-        // stage x (raw, and weighted for the state update as hi + lo) and B
-        // (transposed and as token rows); lane = token, tokens past the end zero
+        // stage x (raw, and weighted for the state update as hi + lo) and B as
+        // token rows; lane = token, tokens past the end zero. Products over
+        // tokens read these rows with transposing LDS reads.
 #pragma unroll
         for (int k = 0; k < Stage::XPW; ++k) {
-            const int pt = 4 * k + w;
+            const int pt = 4 * k + wl;
             if (pt < PT) {
-                const uint4 v0 = st.x[k][0], v1 = st.x[k][1];
+                const uint4 v0 = valid ? st.x[k][0] : uint4{0u, 0u, 0u, 0u};
+                const uint4 v1 = valid ? st.x[k][1] : uint4{0u, 0u, 0u, 0u};
                 const uint32_t wd[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                uint32_t hw[8], lw[8];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const uint32_t bits = valid ? (e & 1 ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu) : 0u;
-                    __bf16 hi, lo;
-                    ssd_split(ssd_bf(bits) * fd, hi, lo);
-                    const int o = (16 * pt + e) * QS + lane;
-                    sXT[o] = (uint16_t)bits;
-                    sXh[o] = __builtin_bit_cast(uint16_t, hi);
-                    sXl[o] = __builtin_bit_cast(uint16_t, lo);
-                }
+                for (int e = 0; e < 8; ++e)
+                    ssd_split2(ssd_bf(wd[e] & 0xffffu) * fd, ssd_bf(wd[e] >> 16) * fd, hw[e], lw[e]);
+                const int o = lane * XS + 16 * pt;
+                *reinterpret_cast<uint4 *>(&XT[o]) = v0;
+                *reinterpret_cast<uint4 *>(&XT[o + 8]) = v1;
+                *reinterpret_cast<uint4 *>(&Xh[o]) = uint4{hw[0], hw[1], hw[2], hw[3]};
+                *reinterpret_cast<uint4 *>(&Xh[o + 8]) = uint4{hw[4], hw[5], hw[6], hw[7]};
+                *reinterpret_cast<uint4 *>(&Xl[o]) = uint4{lw[0], lw[1], lw[2], lw[3]};
+                *reinterpret_cast<uint4 *>(&Xl[o + 8]) = uint4{lw[4], lw[5], lw[6], lw[7]};
             }
         }
 #pragma unroll
-        for (int k = 0; k < NW / 8; ++k) {
+        for (int k = 0; k < NBW / 8; ++k) {
             const uint4 v = valid ? st.b[k] : uint4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<uint4 *>(&sBR[lane * HS + w * NW + 8 * k]) = v;
-            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sBT[(w * NW + 8 * k + e) * QS + lane] = (uint16_t)(e & 1 ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu);
+            *reinterpret_cast<uint4 *>(&sBR[lane * HS + w * NBW + 8 * k]) = v;
         }
-
-        // this chunk's operands stay in registers; fetch the next chunk's
-        ssd_bf16x8 cop[NK];
-        uint2 xe[PT], ze[PT];
-#pragma unroll
-        for (int s = 0; s < NK; ++s)
-            cop[s] = st.c[s];
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            xe[pt] = st.xe[pt];
-            ze[pt] = st.ze[pt];
-        }
-        if (c0 + Q < L)
-            load_stage(c0 + Q, st);
+        // the next chunk's staging loads (the last chunk reloads itself)
+        load_stage(c0 + Q < L ? c0 + Q : c0, st);
         __syncthreads();
 
-        // ---- outputs of tokens [I0, I0 + 16): lane column i = I0 + r16
-        const float Si = __shfl(S, I0 + r16);
+        // The rest of the chunk, specialised on the wave's role so that each
+        // role is straight-line code the scheduler can interleave.
+        auto compute = [&](auto role) {
+            constexpr int WL = decltype(role)::value;
+            constexpr int IW = 16 * WL;
+            // ---- outputs of tokens [IW, IW + 16): lane column i = IW + r16
+            const float Si = __shfl(S, IW + r16);
 
-        // readout of the state entering the chunk (hi + lo)
-        ssd_f32x4 yacc[PT];
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            yacc[pt] = ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < NK; ++s) {
-                const int o = (16 * pt + r16) * HS + 32 * s + 8 * g4;
-                yacc[pt] = ssd_mfma(ssd_ld16(&sHh[o]), cop[s], yacc[pt]);
-                yacc[pt] = ssd_mfma(ssd_ld16(&sHl[o]), cop[s], yacc[pt]);
-            }
-        }
-        {
-            const float ei = __builtin_amdgcn_exp2f(Si);
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-                yacc[pt] *= ei;
-        }
-
-        // scores of key tiles J <= w, decayed, weighted, masked, as hi + lo
-        // operands: element 4 (J%2) + r of mop*[J/2] is M^T[16 J + 4 g4 + r][i]
-        ssd_bf16x8 mh[2], ml[2];
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            if (J <= w) {
-                ssd_f32x4 gt = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int s = 0; s < NK; ++s)
-                    gt = ssd_mfma(ssd_ld16(&sBR[(16 * J + r16) * HS + 32 * s + 8 * g4]), cop[s], gt);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int jj = 16 * J + 4 * g4 + r;
-                    const float Sj = __shfl(S, jj);
-                    const float wj = __shfl(wbar, jj);
-                    const bool keep = J < w || 4 * g4 + r <= r16;
-                    const float m = keep ? gt[r] * __builtin_amdgcn_exp2f(Si - Sj) * wj : 0.0f;
-                    __bf16 hi, lo;
-                    ssd_split(m, hi, lo);
-                    mh[J >> 1][4 * (J & 1) + r] = hi;
-                    ml[J >> 1][4 * (J & 1) + r] = lo;
-                }
-            } else if ((J & 1) && J - 1 <= w) {
-                // odd key tile past the diagonal, paired with a computed one: zeros
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    mh[J >> 1][4 + r] = (__bf16)0.0f;
-                    ml[J >> 1][4 + r] = (__bf16)0.0f;
-                }
-            }
-        }
-#pragma unroll
-        for (int Jp = 0; Jp < 2; ++Jp) {
-            if (2 * Jp <= w) {
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const uint16_t *row = &sXT[(16 * pt + r16) * QS + 32 * Jp + 4 * g4];
-                    const ssd_bf16x8 xo = ssd_ld8x2(row, row + 16);
-                    yacc[pt] = ssd_mfma(xo, mh[Jp], yacc[pt]);
-                    yacc[pt] = ssd_mfma(xo, ml[Jp], yacc[pt]);
-                }
-            }
-        }
-
-        // skip, gate, store: yacc[pt][r] = y[i][p = 16 pt + 4 g4 + r]
-        if (I0 + r16 < nv) {
-            const int64_t off = (c0 + I0 + r16) * xs + 4 * g4;
+            // readout of the state entering the chunk (hi + lo)
+            ssd_f32x4 yacc[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                float v[4] = {yacc[pt][0], yacc[pt][1], yacc[pt][2], yacc[pt][3]};
-                if (p.D) {
-                    v[0] += dskip * ssd_bf(xe[pt].x & 0xffffu);
-                    v[1] += dskip * ssd_bf(xe[pt].x >> 16);
-                    v[2] += dskip * ssd_bf(xe[pt].y & 0xffffu);
-                    v[3] += dskip * ssd_bf(xe[pt].y >> 16);
-                }
-                if (zb) {
-                    v[0] *= silu(ssd_bf(ze[pt].x & 0xffffu));
-                    v[1] *= silu(ssd_bf(ze[pt].x >> 16));
-                    v[2] *= silu(ssd_bf(ze[pt].y & 0xffffu));
-                    v[3] *= silu(ssd_bf(ze[pt].y >> 16));
-                }
-                const uint2 o = {ssd_pack(v[0], v[1]), ssd_pack(v[2], v[3])};
-                *reinterpret_cast<uint2 *>(yb + off + 16 * pt) = o;
-            }
-        }
-
-        // ---- state update of rows [w NW, (w+1) NW)
-        {
-            const float dec = __builtin_amdgcn_exp2f(Slast);
+                yacc[pt] = ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < NTW; ++i)
+                for (int s = 0; s < NK; ++s) {
+                    const int o = (16 * pt + r16) * HS + 32 * s + 8 * g4;
+                    yacc[pt] = ssd_mfma(ssd_ld16(&Hh[o]), cop[s], yacc[pt]);
+                    yacc[pt] = ssd_mfma(ssd_ld16(&Hl[o]), cop[s], yacc[pt]);
+                }
+            }
+            {
+                const float ei = __builtin_amdgcn_exp2f(Si);
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt)
-                    hacc[i][pt] *= dec;
+                    yacc[pt] *= ei;
+            }
+
+            SSM_SSD_PHASE_FENCE_SCORES
+            // scores of key tiles J <= WL, decayed, weighted, masked, as hi + lo
+            // operands: element 4 (J%2) + r of m*[J/2] is M^T[16 J + 4 g4 + r][i]
+            ssd_bf16x8 mh[2], ml[2];
 #pragma unroll
-            for (int ks = 0; ks < Q / 32; ++ks) {
-                ssd_bf16x8 bop[NTW];
+            for (int J = 0; J < 4; ++J) {
+                if (J <= WL) {
+                    ssd_f32x4 gt = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int i = 0; i < NTW; ++i)
-                    bop[i] = ssd_ld16(&sBT[(16 * (w * NTW + i) + r16) * QS + 32 * ks + 8 * g4]);
+                    for (int s = 0; s < NK; ++s)
+                        gt = ssd_mfma(ssd_ld16(&sBR[(16 * J + r16) * HS + 32 * s + 8 * g4]), cop[s], gt);
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const int o = (16 * pt + r16) * QS + 32 * ks + 8 * g4;
-                    const ssd_bf16x8 xh = ssd_ld16(&sXh[o]);
-                    const ssd_bf16x8 xl = ssd_ld16(&sXl[o]);
+                    for (int r = 0; r < 4; ++r) {
+                        const int jj = 16 * J + 4 * g4 + r;
+                        const float Sj = __shfl(S, jj);
+                        const float wj = __shfl(wbar, jj);
+                        const bool keep = J < WL || 4 * g4 + r <= r16;
+                        const float m = keep ? gt[r] * __builtin_amdgcn_exp2f(Si - Sj) * wj : 0.0f;
+                        __bf16 hi, lo;
+                        ssd_split(m, hi, lo);
+                        mh[J >> 1][4 * (J & 1) + r] = hi;
+                        ml[J >> 1][4 * (J & 1) + r] = lo;
+                    }
+                } else if ((J & 1) && J - 1 <= WL) {
+                    // odd key tile past the diagonal, paired with a computed one: zeros
 #pragma unroll
-                    for (int i = 0; i < NTW; ++i) {
-                        hacc[i][pt] = ssd_mfma(bop[i], xh, hacc[i][pt]);
-                        hacc[i][pt] = ssd_mfma(bop[i], xl, hacc[i][pt]);
+                    for (int r = 0; r < 4; ++r) {
+                        mh[J >> 1][4 + r] = (__bf16)0.0f;
+                        ml[J >> 1][4 + r] = (__bf16)0.0f;
                     }
                 }
             }
+#pragma unroll
+            for (int Jp = 0; Jp < 2; ++Jp) {
+                if (2 * Jp <= WL) {
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        // x^T operand in the K order of mh / ml: tokens
+                        // 32 Jp + 4 g4 + e, then 32 Jp + 16 + 4 g4 + e
+                        const uint16_t *src = &XT[(32 * Jp + 4 * g4 + (r16 >> 2)) * XS + 16 * pt + 4 * (r16 & 3)];
+                        const ssd_bf16x8 xo = ssd_ld_tr2(src, src + 16 * XS);
+                        yacc[pt] = ssd_mfma(xo, mh[Jp], yacc[pt]);
+                        yacc[pt] = ssd_mfma(xo, ml[Jp], yacc[pt]);
+                    }
+                }
+            }
+
+            // skip, gate, store: yacc[pt][r] = y[i][p = 16 pt + 4 g4 + r]
+            if (IW + r16 < nv) {
+                const int64_t off = (c0 + IW + r16) * xs + 4 * g4;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    float v[4] = {yacc[pt][0], yacc[pt][1], yacc[pt][2], yacc[pt][3]};
+                    if (p.D) {
+                        v[0] += dskip * ssd_bf(xe[pt].x & 0xffffu);
+                        v[1] += dskip * ssd_bf(xe[pt].x >> 16);
+                        v[2] += dskip * ssd_bf(xe[pt].y & 0xffffu);
+                        v[3] += dskip * ssd_bf(xe[pt].y >> 16);
+                    }
+                    if (zb) {
+                        v[0] *= silu(ssd_bf(ze[pt].x & 0xffffu));
+                        v[1] *= silu(ssd_bf(ze[pt].x >> 16));
+                        v[2] *= silu(ssd_bf(ze[pt].y & 0xffffu));
+                        v[3] *= silu(ssd_bf(ze[pt].y >> 16));
+                    }
+                    const uint2 o = {ssd_pack(v[0], v[1]), ssd_pack(v[2], v[3])};
+                    *reinterpret_cast<uint2 *>(yb + off + 16 * pt) = o;
+                }
+            }
+
+            SSM_SSD_PHASE_FENCE_UPDATE
+            // ---- state update of rows [WL NW, (WL+1) NW)
+            {
+                const float dec = __builtin_amdgcn_exp2f(Slast);
+#pragma unroll
+                for (int i = 0; i < NTW; ++i)
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt)
+                        hacc[i][pt] *= dec;
+#pragma unroll
+                for (int ks = 0; ks < Q / 32; ++ks) {
+                    ssd_bf16x8 bop[NTW];
+#pragma unroll
+                    for (int i = 0; i < NTW; ++i)
+                        bop[i] = ssd_ld_tr2(&sBR[(32 * ks + 8 * g4 + (r16 >> 2)) * HS + 16 * (WL * NTW + i) + 4 * (r16 & 3)],
+                                            &sBR[(32 * ks + 8 * g4 + 4 + (r16 >> 2)) * HS + 16 * (WL * NTW + i) + 4 * (r16 & 3)]);
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const int o = (32 * ks + 8 * g4 + (r16 >> 2)) * XS + 16 * pt + 4 * (r16 & 3);
+                        const ssd_bf16x8 xh = ssd_ld_tr2(&Xh[o], &Xh[o + 4 * XS]);
+                        const ssd_bf16x8 xl = ssd_ld_tr2(&Xl[o], &Xl[o + 4 * XS]);
+#pragma unroll
+                        for (int i = 0; i < NTW; ++i) {
+                            hacc[i][pt] = ssd_mfma(bop[i], xh, hacc[i][pt]);
+                            hacc[i][pt] = ssd_mfma(bop[i], xl, hacc[i][pt]);
+                        }
+                    }
+                }
+            }
+        };
+        switch (wl) {
+        case 0: compute(std::integral_constant<int, 0>{}); break;
+        case 1: compute(std::integral_constant<int, 1>{}); break;
+        case 2: compute(std::integral_constant<int, 2>{}); break;
+        default: compute(std::integral_constant<int, 3>{}); break;
         }
         __syncthreads();
     }
@@ -427,14 +490,22 @@ __global__ __launch_bounds__(kSsdThreads, 1) void ssd_fwd_kernel(const SsdParams
         for (int i = 0; i < NTW; ++i)
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
-                *reinterpret_cast<ssd_f32x4 *>(hl + (16 * pt + r16) * N + 16 * (w * NTW + i) + 4 * g4) = hacc[i][pt];
+                *reinterpret_cast<ssd_f32x4 *>(hl + (16 * pt + r16) * N + 16 * (wl * NTW + i) + 4 * g4) = hacc[i][pt];
     }
 }
 
+// Two heads per workgroup when the LDS of two fits (head size 64) and they
+// share a group; otherwise one.
 template <int P, int N, bool ZOH>
 hipError_t launch_ssd_pn(const SsdParams &p, hipStream_t st) {
-    const int64_t blocks = (int64_t)p.batch * p.H;
-    hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH>), dim3((unsigned)blocks), dim3(kSsdThreads), 0, st, p);
+    if (P == 64 && p.hpg % 2 == 0) {
+        const int64_t blocks = (int64_t)p.batch * (p.H / 2);
+        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, (P == 64 ? 2 : 1)>), dim3((unsigned)blocks),
+                           dim3(kSsdThreads * (P == 64 ? 2 : 1)), 0, st, p);
+    } else {
+        const int64_t blocks = (int64_t)p.batch * p.H;
+        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, 1>), dim3((unsigned)blocks), dim3(kSsdThreads), 0, st, p);
+    }
     return hipGetLastError();
 }
 
