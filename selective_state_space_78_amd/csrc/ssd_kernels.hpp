@@ -71,6 +71,15 @@ typedef float ssd_f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSsdQ = 64;        // tokens per chunk
 
+// LDS row padding (elements) of the token-row tiles of x and of the
+// n-contiguous tiles (B rows, state).
+#ifndef SSM_SSD_XPAD
+#define SSM_SSD_XPAD 16
+#endif
+#ifndef SSM_SSD_HPAD
+#define SSM_SSD_HPAD 16
+#endif
+
 // Scheduling fences between the phases of a chunk: they keep the scheduler
 // from hoisting one phase's operand loads into the previous phase past the
 // register budget.
@@ -160,12 +169,16 @@ __device__ __forceinline__ void ssd_split2(float a, float b, uint32_t &hi, uint3
 // chunk ahead of their use.
 template <int P, int N, int HPW>
 struct SsdStage {
-    static constexpr int PT = P / 16;
-    static constexpr int XPW = (PT + 3) / 4;   // x tiles staged per wave
-    static constexpr int NBW = N / (4 * HPW);  // B columns staged per wave
+    // 16-byte pieces of a chunk's x rows (this head's P values per token) and
+    // B rows (N values per token), numbered token-major; consecutive lanes
+    // take consecutive pieces, so a load instruction covers whole rows.
+    static constexpr int XPR = P / 8;                        // x pieces per token row
+    static constexpr int XI = kSsdQ * XPR / (4 * 64);        // x loads per wave (four waves per head)
+    static constexpr int BPR = N / 8;                        // B pieces per token row
+    static constexpr int BI = kSsdQ * BPR / (4 * HPW * 64);  // B loads per wave (all waves)
     uint16_t dt;                 // bf16 step of token `lane` for this wave's head
-    uint4 x[XPW][2];             // x[token][16 pt .. 16 pt + 15], pt = wl, wl + 4, ...
-    uint4 b[NBW / 8];            // B[token][w NBW .. (w+1) NBW)
+    uint4 x[XI];                 // x piece wl XI 64 + 64 k + lane
+    uint4 b[BI];                 // B piece w BI 64 + 64 k + lane
 };
 
 // HPW heads of one group per workgroup, four waves per head; the heads share
@@ -177,11 +190,12 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
     constexpr int NK = N / 32;     // MFMA steps over n
     constexpr int NW = N / 4;      // state rows per wave
     constexpr int NTW = NW / 16;   // state row tiles per wave
-    constexpr int XS = P + 16;     // LDS row stride of token rows of x (conflict-free transposing reads)
-    constexpr int HS = N + 8;      // LDS row stride of n-contiguous tiles
+    constexpr int XS = P + SSM_SSD_XPAD;   // LDS row stride of token rows of x (conflict-free transposing reads)
+    constexpr int HS = N + SSM_SSD_HPAD;   // LDS row stride of n-contiguous tiles
     typedef SsdStage<P, N, HPW> Stage;
-    constexpr int NBW = Stage::NBW;
-    static_assert(P % 16 == 0 && N % 64 == 0 && NBW % 8 == 0, "tile shape");
+    static_assert(P % 32 == 0 && N % 64 == 0, "tile shape");
+    static_assert(Stage::XI * 4 * 64 == Q * Stage::XPR && Stage::BI * 4 * HPW * 64 == Q * Stage::BPR,
+                  "staging pieces cover the chunk");
 
     __shared__ __attribute__((aligned(16))) uint16_t sBR[Q * HS];         // B, token rows
     __shared__ __attribute__((aligned(16))) uint16_t sXT[HPW][Q * XS];    // x, token rows
@@ -195,6 +209,14 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
     const int hs = w >> 2, wl = w & 3;   // head slot, role within the head
     const int r16 = lane & 15, g4 = lane >> 4;
     const int I0 = 16 * wl;              // this wave's output tokens within a chunk
+    // Channels of the p tiles: row (or column) m of p tile pt is channel
+    // prow(pt, m) = PW (m / 4) + 4 pt + m % 4, in every product, so that the
+    // output accumulator rows 4 g4 .. 4 g4 + 3 of all tiles are the PW
+    // contiguous channels PW g4 .. PW g4 + PW - 1.
+    constexpr int PW = P / 4;
+    auto prow = [](int pt, int m) { return PW * (m >> 2) + 4 * pt + (m & 3); };
+    // the LDS row of channel c in the state's bf16 copy: hrow(prow(pt, m)) = 16 pt + m
+    auto hrow = [](int c) { return 16 * ((c % PW) >> 2) + 4 * (c / PW) + (c & 3); };
 
     const int nb = gridDim.x, bid = blockIdx.x;
     const int qx = nb / kXcds, rx = nb % kXcds, xcd = bid % kXcds;
@@ -225,25 +247,30 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
 
     // Staging loads of the chunk starting at c, one chunk ahead: rows past
     // the end are clamped to the last token (their values are zeroed or masked).
+    // (element offsets within a chunk fit 32 bits: the library checks that
+    // 64 token rows of x and of B do)
     auto load_stage = [&](int64_t c, Stage &st) {
         const int nv = (int)min<int64_t>(Q, L - c);
-        const int64_t tl = c + min(lane, nv - 1);
-        st.dt = db[tl * p.H];
+        const uint16_t *xc = xb + c * xs;
+        const uint16_t *bc = Bb + c * bs;
+        st.dt = db[(c + min(lane, nv - 1)) * p.H];
 #pragma unroll
-        for (int k = 0; k < Stage::XPW; ++k) {
-            const int pt = 4 * k + wl;
-            if (pt < PT) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(xb + tl * xs + 16 * pt);
-                st.x[k][0] = src[0];
-                st.x[k][1] = src[1];
-            }
+        for (int k = 0; k < Stage::XI; ++k) {
+            const int piece = (wl * Stage::XI + k) * 64 + lane;
+            const int t = min(piece / Stage::XPR, nv - 1);
+            st.x[k] = *reinterpret_cast<const uint4 *>(xc + (uint32_t)(t * (int)xs + 8 * (piece % Stage::XPR)));
         }
 #pragma unroll
-        for (int k = 0; k < NBW / 8; ++k)
-            st.b[k] = *reinterpret_cast<const uint4 *>(Bb + tl * bs + w * NBW + 8 * k);
+        for (int k = 0; k < Stage::BI; ++k) {
+            const int piece = (w * Stage::BI + k) * 64 + lane;
+            const int t = min(piece / Stage::BPR, nv - 1);
+            st.b[k] = *reinterpret_cast<const uint4 *>(bc + (uint32_t)(t * (int)bs + 8 * (piece % Stage::BPR)));
+        }
     };
 
-    // State: hacc[i][pt][r] = h[p = 16 pt + r16][n = 16 (wl NTW + i) + 4 g4 + r].
+    // State: hacc[i][pt][r] = h[p = 16 pt + r16][n = 16 (wl NTW + i) + 4 g4 + r]. Its
+    // bf16 copy in LDS holds channel prow(pt, m) in row 16 pt + m (hrow below), the
+    // order in which the readout's A operand takes its rows.
     ssd_f32x4 hacc[NTW][PT];
     const float *h0b = p.h0 ? p.h0 + ((int64_t)b * p.H + h) * P * N : nullptr;
 #pragma unroll
@@ -266,26 +293,15 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
         const int nv = (int)min<int64_t>(Q, L - c0);   // valid tokens in this chunk
         const bool valid = lane < nv;
 
-        // this wave's C rows (operands of the readout and the scores) and the
-        // skip and gate inputs of its outputs; issued before the next chunk's
-        // staging loads (which are unconditional), so that waiting for them
+        // this wave's C rows (operands of the readout and the scores), issued
+        // before the next chunk's staging loads, so that waiting for them
         // never waits for those
         const int64_t ti = c0 + min(I0 + r16, nv - 1);
         ssd_bf16x8 cop[NK];
 #pragma unroll
         for (int s = 0; s < NK; ++s)
             cop[s] = ssd_ld16(Cb + ti * bs + 32 * s + 8 * g4);
-        uint2 xe[PT], ze[PT];
-        if (p.D) {
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-                xe[pt] = *reinterpret_cast<const uint2 *>(xb + ti * xs + 16 * pt + 4 * g4);
-        }
-        if (zb) {
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-                ze[pt] = *reinterpret_cast<const uint2 *>(zb + ti * xs + 16 * pt + 4 * g4);
-        }
+
 
         // the state entering this chunk, as hi + lo bf16 (every wave has
         // finished reading the previous one: barrier at the end of the last chunk)
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
                 uint2 hi, lo;
                 ssd_split2(hacc[i][pt][0], hacc[i][pt][1], hi.x, lo.x);
                 ssd_split2(hacc[i][pt][2], hacc[i][pt][3], hi.y, lo.y);
-                const int o = (16 * pt + r16) * HS + 16 * (wl * NTW + i) + 4 * g4;
+                const int o = hrow(16 * pt + r16) * HS + 16 * (wl * NTW + i) + 4 * g4;
                 *reinterpret_cast<uint2 *>(&Hh[o]) = hi;
                 *reinterpret_cast<uint2 *>(&Hl[o]) = lo;
             }
@@ -317,32 +333,31 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
         const float fd = wbar * __builtin_amdgcn_exp2f(Slast - S);
 
         // stage x (raw, and weighted for the state update as hi + lo) and B as
-        // token rows; lane = token, tokens past the end zero. Products over
-        // tokens read these rows with transposing LDS reads.
+        // token rows, one 16-byte piece per lane and load; tokens past the end
+        // zero. Products over tokens read these rows with transposing LDS reads.
 #pragma unroll
-        for (int k = 0; k < Stage::XPW; ++k) {
-            const int pt = 4 * k + wl;
-            if (pt < PT) {
-                const uint4 v0 = valid ? st.x[k][0] : uint4{0u, 0u, 0u, 0u};
-                const uint4 v1 = valid ? st.x[k][1] : uint4{0u, 0u, 0u, 0u};
-                const uint32_t wd[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                uint32_t hw[8], lw[8];
+        for (int k = 0; k < Stage::XI; ++k) {
+            const int piece = (wl * Stage::XI + k) * 64 + lane;
+            const int t = piece / Stage::XPR;
+            const int col = 8 * (piece % Stage::XPR);
+            const float f = __shfl(fd, t);        // the piece's token's weight
+            const uint4 v = t < nv ? st.x[k] : uint4{0u, 0u, 0u, 0u};
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+            uint32_t hw[4], lw[4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    ssd_split2(ssd_bf(wd[e] & 0xffffu) * fd, ssd_bf(wd[e] >> 16) * fd, hw[e], lw[e]);
-                const int o = lane * XS + 16 * pt;
-                *reinterpret_cast<uint4 *>(&XT[o]) = v0;
-                *reinterpret_cast<uint4 *>(&XT[o + 8]) = v1;
-                *reinterpret_cast<uint4 *>(&Xh[o]) = uint4{hw[0], hw[1], hw[2], hw[3]};
-                *reinterpret_cast<uint4 *>(&Xh[o + 8]) = uint4{hw[4], hw[5], hw[6], hw[7]};
-                *reinterpret_cast<uint4 *>(&Xl[o]) = uint4{lw[0], lw[1], lw[2], lw[3]};
-                *reinterpret_cast<uint4 *>(&Xl[o + 8]) = uint4{lw[4], lw[5], lw[6], lw[7]};
-            }
+            for (int e = 0; e < 4; ++e)
+                ssd_split2(ssd_bf(wd[e] & 0xffffu) * f, ssd_bf(wd[e] >> 16) * f, hw[e], lw[e]);
+            const int o = t * XS + col;
+            *reinterpret_cast<uint4 *>(&XT[o]) = v;
+            *reinterpret_cast<uint4 *>(&Xh[o]) = uint4{hw[0], hw[1], hw[2], hw[3]};
+            *reinterpret_cast<uint4 *>(&Xl[o]) = uint4{lw[0], lw[1], lw[2], lw[3]};
         }
 #pragma unroll
-        for (int k = 0; k < NBW / 8; ++k) {
-            const uint4 v = valid ? st.b[k] : uint4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<uint4 *>(&sBR[lane * HS + w * NBW + 8 * k]) = v;
+        for (int k = 0; k < Stage::BI; ++k) {
+            const int piece = (w * Stage::BI + k) * 64 + lane;
+            const int t = piece / Stage::BPR;
+            const uint4 v = t < nv ? st.b[k] : uint4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<uint4 *>(&sBR[t * HS + 8 * (piece % Stage::BPR)]) = v;
         }
         // the next chunk's staging loads (the last chunk reloads itself)
         load_stage(c0 + Q < L ? c0 + Q : c0, st);
@@ -414,7 +429,7 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
                     for (int pt = 0; pt < PT; ++pt) {
                         // x^T operand in the K order of mh / ml: tokens
                         // 32 Jp + 4 g4 + e, then 32 Jp + 16 + 4 g4 + e
-                        const uint16_t *src = &XT[(32 * Jp + 4 * g4 + (r16 >> 2)) * XS + 16 * pt + 4 * (r16 & 3)];
+                        const uint16_t *src = &XT[(32 * Jp + 4 * g4 + (r16 >> 2)) * XS + PW * (r16 & 3) + 4 * pt];
                         const ssd_bf16x8 xo = ssd_ld_tr2(src, src + 16 * XS);
                         yacc[pt] = ssd_mfma(xo, mh[Jp], yacc[pt]);
                         yacc[pt] = ssd_mfma(xo, ml[Jp], yacc[pt]);
@@ -422,26 +437,34 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
                 }
             }
 
-            // skip, gate, store: yacc[pt][r] = y[i][p = 16 pt + 4 g4 + r]
+            SSM_SSD_PHASE_FENCE_UPDATE
+            // skip, gate, store: yacc[pt][r] = y[i][p = PW g4 + 4 pt + r], so
+            // the lane's PW outputs are contiguous and leave in 16-byte pieces
             if (IW + r16 < nv) {
-                const int64_t off = (c0 + IW + r16) * xs + 4 * g4;
+                const int64_t off = (c0 + IW + r16) * xs + PW * g4;
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    float v[4] = {yacc[pt][0], yacc[pt][1], yacc[pt][2], yacc[pt][3]};
+                for (int k = 0; k < PT / 2; ++k) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        v[e] = yacc[2 * k + (e >> 2)][e & 3];
                     if (p.D) {
-                        v[0] += dskip * ssd_bf(xe[pt].x & 0xffffu);
-                        v[1] += dskip * ssd_bf(xe[pt].x >> 16);
-                        v[2] += dskip * ssd_bf(xe[pt].y & 0xffffu);
-                        v[3] += dskip * ssd_bf(xe[pt].y >> 16);
+                        const uint4 xe = *reinterpret_cast<const uint4 *>(xb + off + 8 * k);
+                        const uint32_t xw[4] = {xe.x, xe.y, xe.z, xe.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            v[e] += dskip * ssd_bf(e & 1 ? xw[e >> 1] >> 16 : xw[e >> 1] & 0xffffu);
                     }
                     if (zb) {
-                        v[0] *= silu(ssd_bf(ze[pt].x & 0xffffu));
-                        v[1] *= silu(ssd_bf(ze[pt].x >> 16));
-                        v[2] *= silu(ssd_bf(ze[pt].y & 0xffffu));
-                        v[3] *= silu(ssd_bf(ze[pt].y >> 16));
+                        const uint4 ze = *reinterpret_cast<const uint4 *>(zb + off + 8 * k);
+                        const uint32_t zw[4] = {ze.x, ze.y, ze.z, ze.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            v[e] *= silu(ssd_bf(e & 1 ? zw[e >> 1] >> 16 : zw[e >> 1] & 0xffffu));
                     }
-                    const uint2 o = {ssd_pack(v[0], v[1]), ssd_pack(v[2], v[3])};
-                    *reinterpret_cast<uint2 *>(yb + off + 16 * pt) = o;
+                    const uint4 o = {ssd_pack(v[0], v[1]), ssd_pack(v[2], v[3]), ssd_pack(v[4], v[5]),
+                                     ssd_pack(v[6], v[7])};
+                    *reinterpret_cast<uint4 *>(yb + off + 8 * k) = o;
                 }
             }
 

@@ -782,7 +782,7 @@ extern "C" int ssm_ssd_fwd(const ssm_ssd_desc *desc, const void *x, const void *
     int64_t bl, heads, tok_elems, bc_elems, st_elems;
     if (!mul_ok(d.batch, d.seqlen, &bl) || !mul_ok(d.batch, H, &heads) || !mul_ok(bl, H * P, &tok_elems) ||
         !mul_ok(bl, G * N, &bc_elems) || !mul_ok(heads, P * N * 4, &st_elems) || tok_elems > INT64_MAX / 4 ||
-        heads > INT32_MAX)
+        heads > INT32_MAX || 64 * H * P > INT32_MAX || 64 * G * N > INT32_MAX)
         return SSM_ERR_SHAPE;
     st_elems /= 4;
     if (heads == 0) return SSM_OK;
