@@ -53,14 +53,30 @@ def valu_ops_per_token_ch(N: int, gate: bool) -> int:
     return 5 * N + 2 + (6 if gate else 0)
 
 
-def source_digest() -> str:
-    """Digest of the scan kernels' device source (the kernel template and the
-    bf16 instantiation unit): counter summaries older than it are stale."""
+def source_digest(names=("scan_kernels.hpp", "scan_bf16_euler.hip")) -> str:
+    """Digest of a kernel's device source (by default the scan kernel template
+    and its bf16 instantiation unit): counter summaries older than it are stale."""
     h = hashlib.sha256()
-    for name in ("scan_kernels.hpp", "scan_bf16_euler.hip"):
+    for name in names:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+SSD_SOURCES = ("ssd_kernels.hpp", "ssd_euler.hip")
+
+
+def measured_ssd_traffic():
+    """HBM bytes per launch of the SSD kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    try:
+        with open(os.path.join(PROFILES, "traffic_ssd_mamba2.json")) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest(SSD_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def to_dev(a, torch):
@@ -246,7 +262,7 @@ def bench_ssd(torch, ssm, steps=20, warmup=3, cpu=True, budget_s=10.0):
             "unit": "GB/s",
             "frac": gbps / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": nbytes,
-            "traffic": None,
+            "traffic": measured_ssd_traffic(),
             "mfma": {"algorithmic_flops_per_launch": flops, "achieved_TFLOPs": tflops,
                      "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                      "note": "bf16 dense peak; the kernel issues the readout, masked-product and update "
