@@ -211,7 +211,8 @@ def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
     return {
-        "workload": "backward of the same scan: gradients of u, delta, A, B, C, D, z, h0 from dy and dh_last",
+        "workload": "backward of the same scan: gradients of u (of x with the conv prologue), delta, A, B, C, D, z, "
+                    "h0 from dy and dh_last",
         "ms_per_call": ms,
         "Gtokens*ch/s": cfg.tokens_ch / (ms * 1e-3) / 1e9,
         "workspace_bytes": need,
@@ -431,7 +432,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = 1 << 30
-    if not args.no_bwd and not args.conv:
+    if not args.no_bwd:
         print("bench: backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(torch, ssm, cfg, dev, disc=args.disc, step_opts=step_opts)
     if not args.no_decode:

@@ -168,8 +168,18 @@ int ssm_scan_plan(const ssm_scan_desc *desc, ssm_scan_tuning *out);
  *   dD            (dim) fp32, written; required when D is given, unused otherwise
  *   dh0           (batch, dim, dstate) fp32, written, or NULL (not wanted)
  *   ddelta_bias   (dim) fp32, written when desc->delta_bias is given (else unused)
+ *   dconv_weight  (dim, W) fp32, written; required when desc->conv_width W > 0 (else unused)
+ *   dconv_bias    (dim) fp32, written when given and W > 0 (else unused); NULL: not wanted
  * With a delta bias or softplus in the descriptor, ddelta is the gradient of
- * the raw delta (the chain rule through the bias and softplus).
+ * the raw delta (the chain rule through the bias and softplus). With the
+ * convolution prologue (W > 0), u holds x as for ssm_scan_fwd and du receives
+ * the gradient of x: with pre_t = conv_bias + sum_k w[k] x_{t-(W-1)+k} and
+ * g_t the gradient of the scan input u_t = silu(pre_t),
+ *     dpre_t = g_t silu'(pre_t),  dx_s = sum_k w[k] dpre_{s+(W-1)-k},
+ *     dconv_weight[k] = sum_{b,t} dpre_t x_{t-(W-1)+k},  dconv_bias = sum_{b,t} dpre_t
+ * (the chain rule through youngju.dev MambaBlock.forward's x_conv =
+ * silu(conv1d(x))). The checkpoint pass forms u from x as the forward does;
+ * the reverse pass reads u and writes its gradient in fp32 in the workspace.
  *   workspace     at least ssm_scan_bwd_workspace_size(desc) bytes, 256-byte
  *                 aligned; contents on entry do not matter.
  * Results do not depend on timing: every sum over channels, batch rows or
@@ -182,7 +192,7 @@ int ssm_scan_bwd(const ssm_scan_desc *desc,
                  const void *B, const void *C, const float *D, const void *z,
                  const float *h0, const void *dy, const float *dh_last,
                  void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD,
-                 void *dz, float *dh0, float *ddelta_bias,
+                 void *dz, float *dh0, float *ddelta_bias, float *dconv_weight, float *dconv_bias,
                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
             L.ssm_scan_fwd_tuned.restype = ctypes.c_int
             L.ssm_scan_bwd_workspace_size.argtypes = [pdesc]
             L.ssm_scan_bwd_workspace_size.restype = sz
-            L.ssm_scan_bwd.argtypes = [pdesc] + [vp] * 19 + [vp, sz, vp]
+            L.ssm_scan_bwd.argtypes = [pdesc] + [vp] * 21 + [vp, sz, vp]
             L.ssm_scan_bwd.restype = ctypes.c_int
             L.ssm_state_update.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                            vp]
@@ -223,13 +223,14 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None
 
 
 def ssm_scan_bwd_workspace_size(batch, L, dim, N, dtype_code, disc="euler", delta_bias=None,
-                                delta_softplus=False) -> int:
-    desc = make_desc(batch, L, dim, N, dtype_code, disc, delta_bias, delta_softplus)
+                                delta_softplus=False, conv_weight=None, conv_bias=None) -> int:
+    desc = make_desc(batch, L, dim, N, dtype_code, disc, delta_bias, delta_softplus, conv_weight, conv_bias)
     return int(lib().ssm_scan_bwd_workspace_size(ctypes.byref(desc)))
 
 
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None, disc="euler",
-                 workspace=None, stream=None, want_dh0=True, out=None, delta_bias=None, delta_softplus=False):
+                 workspace=None, stream=None, want_dh0=True, out=None, delta_bias=None, delta_softplus=False,
+                 conv_weight=None, conv_bias=None):
     """Backward of ssm_scan_fwd on device tensors.
 
     Inputs as ssm_scan_fwd, plus dy (batch, L, dim) of the input dtype and an
@@ -237,7 +238,9 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None, d
     dz (input dtype, dz only with a gate), dA (dim, N), dB, dC (batch, L, N),
     dD (dim,) (with a skip) and dh0 (batch, dim, N) (when ``want_dh0``), all
     float32 except the per-token ones, and ddelta_bias (dim,) with a
-    ``delta_bias``. ``out`` may hold preallocated outputs.
+    ``delta_bias``. With ``conv_weight`` (dim, W) (and ``conv_bias``), ``u``
+    holds x, du is the gradient of x, and dconv_weight (dim, W), dconv_bias
+    (dim,) are added. ``out`` may hold preallocated outputs.
     """
     import torch
     batch, L, dim = u.shape
@@ -275,7 +278,13 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None, d
     dh0 = get("dh0", (batch, dim, N), f32, want_dh0)
     _check(delta_bias, "delta_bias", (dim,), f32, dev)
     ddb = get("ddelta_bias", (dim,), f32, delta_bias is not None)
-    desc = make_desc(batch, L, dim, N, code, disc, delta_bias, delta_softplus)
+    W = 0 if conv_weight is None else int(conv_weight.shape[1])
+    if conv_weight is not None:
+        _check(conv_weight, "conv_weight", (dim, W), f32, dev)
+    _check(conv_bias, "conv_bias", (dim,), f32, dev)
+    dcw = get("dconv_weight", (dim, W), f32, W > 0)
+    dcb = get("dconv_bias", (dim,), f32, W > 0)
+    desc = make_desc(batch, L, dim, N, code, disc, delta_bias, delta_softplus, conv_weight, conv_bias)
     L_ = lib()
     need = L_.ssm_scan_bwd_workspace_size(ctypes.byref(desc))
     if workspace is not None and workspace.numel() * workspace.element_size() < need:
@@ -286,11 +295,12 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None, d
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = L_.ssm_scan_bwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                          _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(du), _ptr(dde), _ptr(dA), _ptr(dB), _ptr(dC),
-                         _ptr(dD), _ptr(dz), _ptr(dh0), _ptr(ddb), _ptr(workspace), ws_bytes,
+                         _ptr(dD), _ptr(dz), _ptr(dh0), _ptr(ddb), _ptr(dcw), _ptr(dcb), _ptr(workspace), ws_bytes,
                          _stream(stream, dev))
     if rc != 0:
         raise SsmError(rc, "ssm_scan_bwd")
-    return dict(du=du, ddelta=dde, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0, ddelta_bias=ddb)
+    return dict(du=du, ddelta=dde, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0, ddelta_bias=ddb,
+                dconv_weight=dcw, dconv_bias=dcb)
 
 
 def ssm_state_update(x, delta, A, B, C, h, D=None, z=None, y=None, disc="euler", stream=None,

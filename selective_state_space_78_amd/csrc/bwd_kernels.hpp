@@ -42,6 +42,8 @@
 //    dD partials in a fixed order, so the result does not depend on timing.
 #pragma once
 
+#include <type_traits>
+
 #include "scan_kernels.hpp"
 
 namespace ssm_detail {
@@ -54,6 +56,8 @@ struct BwdParams {
     const float *Bf, *Cf;      // the checkpoint pass's regrouped B and C (same groups as here)
     const float *ckpt;         // (batch, nck, Npad, dim)
     void *du, *ddelta, *dz;
+    float *du_f32;             // if set, du is written here in fp32 instead (the convolution prologue's input)
+    int u_f32;                 // u is fp32 (the convolution prologue's output) whatever the tensors' type
     float *dh0;
     float *part_bc;            // (batch, ntiles, L, Npad, 2): per-tile sums over channels of dB, dC terms
     float *part_a;             // (batch, dim, Npad): per-row dA
@@ -139,7 +143,9 @@ template <int KV> struct BwdFloats;
 template <> struct BwdFloats<2> { typedef float2 type; };
 template <> struct BwdFloats<4> { typedef float4 type; };
 
-template <typename T, int NPW, int G, int TC, bool ZOH>
+// UF: u is read as fp32 whatever T is (the convolution prologue's output,
+// formed in fp32 like the forward forms it)
+template <typename T, int NPW, int G, int TC, bool ZOH, bool UF = false>
 struct BwdKernel {
     static constexpr int kThreads = kTile * G;
     static constexpr int kNP = NPW * G;
@@ -167,7 +173,8 @@ struct BwdKernel {
     static_assert(sizeof(Smem) <= 81920, "two workgroups per CU in 160 KiB of LDS");
 
     struct Prefetch {
-        Raw u[kPPT], dt[kPPT], z[kPPT], dy[kPPT];
+        typename std::conditional<UF, VecF, Raw>::type u[kPPT];
+        Raw dt[kPPT], z[kPPT], dy[kPPT];
     };
     struct Held {
         float dt[kPPT][kV], u[kPPT][kV], ds[kPPT][kV], gz[kPPT][kV];   // gz = dy g'(z)
@@ -254,13 +261,23 @@ struct BwdKernel {
             const int row = piece_row(j);
             if (!piece_in_chunk(j) || row >= tval || !colv) continue;
             const uint32_t off = (uint32_t)row * (uint32_t)p.dim + (uint32_t)col;
+            if constexpr (UF) {
+                const float *uf = static_cast<const float *>(p.u) + base + off;
+                if (p.vec) {
+                    pf.u[j] = *reinterpret_cast<const VecF *>(uf);
+                } else {
+                    float *pv = reinterpret_cast<float *>(&pf.u[j]);
+#pragma unroll
+                    for (int e = 0; e < kV; ++e) pv[e] = d0 + col + e < p.dim ? uf[e] : 0.0f;
+                }
+            }
             if (p.vec) {
-                pf.u[j] = *reinterpret_cast<const Raw *>(u + off);
+                if constexpr (!UF) pf.u[j] = *reinterpret_cast<const Raw *>(u + off);
                 pf.dt[j] = *reinterpret_cast<const Raw *>(dt + off);
                 pf.dy[j] = *reinterpret_cast<const Raw *>(dy + off);
                 if (gate) pf.z[j] = *reinterpret_cast<const Raw *>(z + off);
             } else {
-                pf.u[j] = gather(u + off, d0 + col, p.dim, true);
+                if constexpr (!UF) pf.u[j] = gather(u + off, d0 + col, p.dim, true);
                 pf.dt[j] = gather(dt + off, d0 + col, p.dim, true);
                 pf.dy[j] = gather(dy + off, d0 + col, p.dim, true);
                 pf.z[j] = gather(z + off, d0 + col, p.dim, gate);
@@ -282,7 +299,13 @@ struct BwdKernel {
             float dsv[kV];
             if (row < tval && colv) {
                 float u[kV], d[kV], g[kV];
-                unpack(pf.u[j], u);
+                if constexpr (UF) {
+                    const float *pv = reinterpret_cast<const float *>(&pf.u[j]);
+#pragma unroll
+                    for (int e = 0; e < kV; ++e) u[e] = pv[e];
+                } else {
+                    unpack(pf.u[j], u);
+                }
                 unpack(pf.dt[j], d);
                 unpack(pf.dy[j], g);
 #pragma unroll
@@ -562,7 +585,13 @@ struct BwdKernel {
                     dbacc[j][e] += od[e];
                 }
                 const int64_t off = (row0 + t0 + row) * p.dim + d0 + col;
-                store(static_cast<T *>(p.du) + off, ou, d0 + col, p.dim, p.vec);
+                if (p.du_f32 != nullptr) {
+#pragma unroll
+                    for (int e = 0; e < kV; ++e)
+                        if (d0 + col + e < p.dim) p.du_f32[off + e] = ou[e];
+                } else {
+                    store(static_cast<T *>(p.du) + off, ou, d0 + col, p.dim, p.vec);
+                }
                 store(static_cast<T *>(p.ddelta) + off, od, d0 + col, p.dim, p.vec);
             }
             {
@@ -621,17 +650,24 @@ struct BwdKernel {
 // the simplified rule fits 128 VGPRs: at least 4 waves per SIMD (two 8-wave
 // workgroups, or one 16-wave one, per CU); the hold rule's reverse step needs
 // more registers, and capping it at 128 spilled 80-170 of them to scratch
-template <typename T, int NPW, int G, int TC, bool ZOH>
+template <typename T, int NPW, int G, int TC, bool ZOH, bool UF>
 __global__ __launch_bounds__(kTile * G, ZOH ? 2 : 4) void bwd_kernel(const BwdParams p) {
-    BwdKernel<T, NPW, G, TC, ZOH>::run(p);
+    BwdKernel<T, NPW, G, TC, ZOH, UF>::run(p);
 }
 
 template <typename T, bool ZOH>
 hipError_t launch_bwd_shape(const BwdShape &sh, const BwdParams &p, hipStream_t st) {
     const int64_t blocks = (int64_t)p.batch * p.ntiles;
+    // fp32 u with bf16 tensors: the UF variant (fp32 tensors read u as fp32 anyway)
+    const bool uf = sizeof(T) == 2 && p.u_f32;
 #define SSM_BWD_CASE(NP, GG, TCC) \
     if (sh.npad == NP && sh.G == GG && sh.TC == TCC) { \
-        hipLaunchKernelGGL((bwd_kernel<T, NP / GG, GG, TCC, ZOH>), dim3((unsigned)blocks), dim3(kTile * GG), 0, st, p); \
+        if (uf) \
+            hipLaunchKernelGGL((bwd_kernel<T, NP / GG, GG, TCC, ZOH, sizeof(T) == 2>), dim3((unsigned)blocks), \
+                               dim3(kTile * GG), 0, st, p); \
+        else \
+            hipLaunchKernelGGL((bwd_kernel<T, NP / GG, GG, TCC, ZOH, false>), dim3((unsigned)blocks), \
+                               dim3(kTile * GG), 0, st, p); \
         return hipGetLastError(); \
     }
     SSM_BWD_CASE(4, 2, 16) SSM_BWD_CASE(8, 8, 16) SSM_BWD_CASE(16, 8, 16) SSM_BWD_CASE(32, 16, 8)

@@ -209,13 +209,14 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
     const int hs = w >> 2, wl = w & 3;   // head slot, role within the head
     const int r16 = lane & 15, g4 = lane >> 4;
     const int I0 = 16 * wl;              // this wave's output tokens within a chunk
-    // Channels of the p tiles: row (or column) m of p tile pt is channel
-    // prow(pt, m) = PW (m / 4) + 4 pt + m % 4, in every product, so that the
-    // output accumulator rows 4 g4 .. 4 g4 + 3 of all tiles are the PW
-    // contiguous channels PW g4 .. PW g4 + PW - 1.
+    // Channels of the output p tiles (the readout's and the masked product's
+    // A rows): row m of p tile pt is channel PW (m / 4) + 4 pt + m % 4, so
+    // that the output accumulator rows 4 g4 .. 4 g4 + 3 of all tiles are the
+    // PW contiguous channels PW g4 .. PW g4 + PW - 1. The state and its update
+    // keep the natural order (row m of tile pt is channel 16 pt + m); the
+    // state's bf16 copy in LDS puts channel c in row hrow(c), which is 16 pt + m
+    // for the channel of output row m of tile pt.
     constexpr int PW = P / 4;
-    auto prow = [](int pt, int m) { return PW * (m >> 2) + 4 * pt + (m & 3); };
-    // the LDS row of channel c in the state's bf16 copy: hrow(prow(pt, m)) = 16 pt + m
     auto hrow = [](int c) { return 16 * ((c % PW) >> 2) + 4 * (c / PW) + (c & 3); };
 
     const int nb = gridDim.x, bid = blockIdx.x;
@@ -268,9 +269,9 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
         }
     };
 
-    // State: hacc[i][pt][r] = h[p = 16 pt + r16][n = 16 (wl NTW + i) + 4 g4 + r]. Its
-    // bf16 copy in LDS holds channel prow(pt, m) in row 16 pt + m (hrow below), the
-    // order in which the readout's A operand takes its rows.
+    // State: hacc[i][pt][r] = h[p = 16 pt + r16][n = 16 (wl NTW + i) + 4 g4 + r]; its
+    // bf16 copy in LDS is written to rows hrow(p), the order in which the
+    // readout's A operand takes its rows.
     ssd_f32x4 hacc[NTW][PT];
     const float *h0b = p.h0 ? p.h0 + ((int64_t)b * p.H + h) * P * N : nullptr;
 #pragma unroll

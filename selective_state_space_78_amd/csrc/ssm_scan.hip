@@ -36,6 +36,154 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float *h0, float 
 }
 
 // ---------------------------------------------------------------------------
+// Backward of the convolution prologue. The backward scan runs on the
+// prologue's output u = silu(cb + sum_k w[k] x[t-(W-1)+k]) (x before t = 0
+// is zero), materialised by conv_silu_kernel; conv_bwd_kernel then turns the
+// scan's du (kept in fp32) into
+//   dpre_t  = du_t * silu'(pre_t),   silu'(p) = s (1 + p (1 - s)), s = sigmoid(p)
+//   dx_s    = sum_k w[k] dpre_{s+(W-1)-k}
+//   dw[k]  += dpre_t x_{t-(W-1)+k},  dcb += dpre_t
+// one thread per (batch row, channel, block of kConvBlock tokens), walking
+// time with a window of the last W values of x and dpre; the per-block
+// partial sums of dw and dcb are added in a fixed order by conv_reduce_kernel.
+constexpr int kConvBlock = 256;
+
+struct ConvParams {
+    const void *x;            // (batch, L, dim)
+    const float *w, *cb;      // (dim, W), (dim) or null
+    float *u;                 // conv_silu_kernel output (batch, L, dim), fp32
+    const float *du;          // gradient of u (fp32)
+    void *dx;                 // gradient of x
+    float *part_w, *part_b;   // (batch, nblk, dim, W), (batch, nblk, dim)
+    float *dw, *db;           // (dim, W), (dim) or null
+    int64_t L;
+    int batch, dim, W, nblk;
+};
+
+template <typename T>
+__device__ __forceinline__ float conv_ld(const void *p, int64_t i) {
+    if constexpr (sizeof(T) == 2)
+        return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
+    else
+        return static_cast<const float *>(p)[i];
+}
+
+template <typename T>
+__device__ __forceinline__ void conv_st(void *p, int64_t i, float v) {
+    if constexpr (sizeof(T) == 2)
+        static_cast<uint16_t *>(p)[i] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    else
+        static_cast<float *>(p)[i] = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void conv_silu_kernel(const ConvParams p) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, t, d)
+    const int64_t n = (int64_t)p.batch * p.L * p.dim;
+    if (i >= n) return;
+    const int d = (int)(i % p.dim);
+    const int64_t t = (i / p.dim) % p.L;
+    float acc = p.cb ? p.cb[d] : 0.0f;
+    for (int k = 0; k < p.W; ++k) {
+        const int64_t back = p.W - 1 - k;
+        if (t >= back) acc = fmaf(p.w[(int64_t)d * p.W + k], conv_ld<T>(p.x, i - back * p.dim), acc);
+    }
+    p.u[i] = silu(acc);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void conv_bwd_kernel(const ConvParams p) {
+    const int d = blockIdx.x * blockDim.x + threadIdx.x;
+    const int blk = blockIdx.y;
+    const int b = blockIdx.z;
+    if (d >= p.dim) return;
+    const int W = p.W;
+    float w[kConvMax];
+#pragma unroll
+    for (int k = 0; k < kConvMax; ++k) w[k] = k < W ? p.w[(int64_t)d * W + k] : 0.0f;
+    const float cb = p.cb ? p.cb[d] : 0.0f;
+    const int64_t t0 = (int64_t)blk * kConvBlock;
+    const int64_t t1 = min(p.L, t0 + kConvBlock);
+    const int64_t tend = min(p.L, t1 + W - 1);   // dx of the block's last tokens needs W-1 tokens ahead
+    const int64_t row = (int64_t)b * p.L;
+    // xs[j]: x_{t-j} for j = 0 .. W-1 (zero before the sequence); ds[j]: dpre_{t-j}
+    float xs[kConvMax], ds[kConvMax], gw[kConvMax];
+#pragma unroll
+    for (int j = 0; j < kConvMax; ++j) {
+        const int64_t s = t0 - 1 - j;        // xs after the shift at t0 holds x_{t0-1-j} in slot j+1
+        xs[j] = (j + 1 < W && s >= 0) ? conv_ld<T>(p.x, (row + s) * p.dim + d) : 0.0f;
+        ds[j] = 0.0f;
+        gw[j] = 0.0f;
+    }
+    float gb = 0.0f;
+    for (int64_t t = t0; t < tend; ++t) {
+        // shift the windows by one token
+#pragma unroll
+        for (int j = kConvMax - 1; j > 0; --j) {
+            xs[j] = xs[j - 1];
+            ds[j] = ds[j - 1];
+        }
+        const int64_t i = (row + t) * p.dim + d;
+        xs[0] = conv_ld<T>(p.x, i);
+        float pre = cb;
+#pragma unroll
+        for (int k = 0; k < kConvMax; ++k)
+            if (k < W) pre = fmaf(w[k], xs[W - 1 - k], pre);
+        const float sg = 1.0f / (1.0f + __expf(-pre));
+        ds[0] = p.du[i] * sg * (1.0f + pre * (1.0f - sg));
+        if (t < t1) {
+            gb += ds[0];
+#pragma unroll
+            for (int k = 0; k < kConvMax; ++k)
+                if (k < W) gw[k] = fmaf(ds[0], xs[W - 1 - k], gw[k]);
+        }
+        // dx of token t-(W-1), whose last contribution is dpre_t
+        const int64_t s = t - (W - 1);
+        if (s >= t0 && s < t1) {
+            float g = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kConvMax; ++k)
+                if (k < W) g = fmaf(w[k], ds[k], g);     // dpre_{s+(W-1)-k} = ds[k]
+            conv_st<T>(p.dx, (row + s) * p.dim + d, g);
+        }
+    }
+    // the block's last tokens when the sequence ends inside the window: dpre
+    // past the end is zero
+    for (int64_t s = max(t0, tend - (W - 1)); s < t1; ++s) {
+        const int64_t lag = tend - 1 - s;        // dpre_{s+m} sits in ds[lag - m] for s + m <= tend - 1
+        float g = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kConvMax; ++k) {
+            const int64_t m = (W - 1) - k;       // dpre_{s+m}
+            if (k < W && m <= lag) g = fmaf(w[k], ds[lag - m], g);
+        }
+        conv_st<T>(p.dx, (row + s) * p.dim + d, g);
+    }
+    float *pw = p.part_w + (((int64_t)b * p.nblk + blk) * p.dim + d) * W;
+#pragma unroll
+    for (int k = 0; k < kConvMax; ++k)
+        if (k < W) pw[k] = gw[k];
+    p.part_b[((int64_t)b * p.nblk + blk) * p.dim + d] = gb;
+}
+
+__global__ __launch_bounds__(256) void conv_reduce_kernel(const ConvParams p) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (d, k), then d for the bias
+    const int64_t nw = (int64_t)p.dim * p.W;
+    if (i < nw) {
+        float acc = 0.0f;
+        for (int b = 0; b < p.batch; ++b)
+            for (int k = 0; k < p.nblk; ++k) acc += p.part_w[((int64_t)b * p.nblk + k) * nw + i];
+        p.dw[i] = acc;
+    } else if (i < nw + p.dim && p.db != nullptr) {
+        const int64_t d = i - nw;
+        float acc = 0.0f;
+        for (int b = 0; b < p.batch; ++b)
+            for (int k = 0; k < p.nblk; ++k) acc += p.part_b[((int64_t)b * p.nblk + k) * p.dim + d];
+        p.db[d] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode step
 
 // Decode: one thread per (channel, 4 states), so that a wave's 16-byte state
@@ -484,8 +632,8 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
 struct BwdLayout {
     Plan pl;
     BwdShape sh;
-    int nck, ntiles;
-    size_t ckpt, part_bc, part_a, part_d, part_db, total;
+    int nck, ntiles, nblk;
+    size_t ckpt, part_bc, part_a, part_d, part_db, conv_u, conv_du, conv_pw, conv_pb, total;
 };
 
 BwdLayout bwd_layout(const ssm_scan_desc &d) {
@@ -502,7 +650,17 @@ BwdLayout bwd_layout(const ssm_scan_desc &d) {
     w.part_a = w.part_bc + align256((size_t)d.batch * w.ntiles * d.seqlen * np * 2 * 4);
     w.part_d = w.part_a + align256((size_t)d.batch * d.dim * np * 4);
     w.part_db = w.part_d + align256((size_t)d.batch * d.dim * 4);
-    w.total = w.part_db + (d.delta_bias != nullptr ? align256((size_t)d.batch * d.dim * 4) : 0);
+    w.conv_u = w.part_db + (d.delta_bias != nullptr ? align256((size_t)d.batch * d.dim * 4) : 0);
+    w.total = w.conv_u;
+    if (d.conv_width > 0) {
+        // the prologue's output u and the gradient of u, per-block sums of the tap and bias gradients
+        const size_t tok = (size_t)d.batch * d.seqlen * d.dim;
+        w.nblk = (int)((d.seqlen + kConvBlock - 1) / kConvBlock);
+        w.conv_du = w.conv_u + align256(tok * 4);
+        w.conv_pw = w.conv_du + align256(tok * 4);
+        w.conv_pb = w.conv_pw + align256((size_t)d.batch * w.nblk * d.dim * d.conv_width * 4);
+        w.total = w.conv_pb + align256((size_t)d.batch * w.nblk * d.dim * 4);
+    }
     return w;
 }
 
@@ -514,10 +672,13 @@ size_t bwd_workspace_bytes(const ssm_scan_desc &d) {
 int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A, const void *B,
              const void *C, const float *D, const void *z, const float *h0, const void *dy, const float *dh_last,
              void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz, float *dh0,
-             float *ddelta_bias, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+             float *ddelta_bias, float *dconv_weight, float *dconv_bias, void *workspace, size_t workspace_bytes,
+             hipStream_t stream) {
     if (int rc = validate_desc(desc); rc != SSM_OK) return rc;
     const ssm_scan_desc d = *desc;
-    if (d.conv_width != 0) return SSM_ERR_UNSUPPORTED;   // the backward takes u as given
+    const int cw = d.conv_width;
+    if (cw > 0 && dconv_weight == nullptr) return SSM_ERR_NULL;
+    if (cw == 0) dconv_weight = dconv_bias = nullptr;
     if (d.batch == 0 || d.dim == 0) return SSM_OK;
     const int es = d.dtype == SSM_BF16 ? 2 : 4;
     const int64_t tok = d.batch * d.seqlen * d.dim;
@@ -536,7 +697,7 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     const void *tok_ptrs[] = {u, delta, B, C, z, dy, du, ddelta, z ? dz : nullptr};
     for (const void *q : tok_ptrs)
         if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
-    const void *f32_ptrs[] = {A, D, h0, dh_last, dA, dB, dC, dD, dh0, ddelta_bias};
+    const void *f32_ptrs[] = {A, D, h0, dh_last, dA, dB, dC, dD, dh0, ddelta_bias, dconv_weight, dconv_bias};
     for (const void *q : f32_ptrs)
         if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
     if (workspace && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
@@ -551,12 +712,15 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
                           range_of(dA, adn * 4), range_of(dB, d.seqlen > 0 ? bn * 4 : 0),
                           range_of(dC, d.seqlen > 0 ? bn * 4 : 0), range_of(D ? dD : nullptr, d.dim * 4),
                           range_of(dh0, state * 4), range_of(ddelta_bias, d.dim * 4),
+                          range_of(dconv_weight, (int64_t)d.dim * cw * 4), range_of(dconv_bias, d.dim * 4),
                           range_of(workspace, (int64_t)need)};
     const Range ins[] = {range_of(u, tok * es), range_of(delta, tok * es), range_of(z, z ? tok * es : 0),
                          range_of(B, bn * es), range_of(C, bn * es), range_of(A, adn * 4),
                          range_of(D, D ? d.dim * 4 : 0), range_of(h0, h0 ? state * 4 : 0),
                          range_of(dy, tok * es), range_of(dh_last, dh_last ? state * 4 : 0),
-                         range_of(dbias, dbias ? d.dim * 4 : 0)};
+                         range_of(dbias, dbias ? d.dim * 4 : 0),
+                         range_of(d.conv_weight, (int64_t)d.dim * cw * 4),
+                         range_of(d.conv_bias, cw > 0 && d.conv_bias ? d.dim * 4 : 0)};
     const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
     for (int i = 0; i < nout; ++i) {
         for (const Range &r : ins)
@@ -578,16 +742,54 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
         if (ddelta_bias != nullptr)
             hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((d.dim + 255) / 256)), dim3(256), 0, stream,
                                nullptr, ddelta_bias, d.dim);
+        if (dconv_weight != nullptr)
+            hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((d.dim * cw + 255) / 256)), dim3(256), 0, stream,
+                               nullptr, dconv_weight, d.dim * cw);
+        if (dconv_bias != nullptr)
+            hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((d.dim + 255) / 256)), dim3(256), 0, stream,
+                               nullptr, dconv_bias, d.dim);
         return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
     }
 
     char *ws = static_cast<char *>(workspace);
+    // with the convolution prologue the scan's backward runs on its output u,
+    // materialised in the workspace, and writes the gradient of u there; the
+    // caller's u holds x and its du receives the gradient of x
+    const void *x_in = u;
+    void *dx_out = du;
+    ConvParams cp{};
+    if (cw > 0) {
+        cp.x = x_in;
+        cp.w = d.conv_weight;
+        cp.cb = d.conv_bias;
+        cp.u = reinterpret_cast<float *>(ws + wl.conv_u);
+        cp.du = reinterpret_cast<const float *>(ws + wl.conv_du);
+        cp.dx = dx_out;
+        cp.part_w = reinterpret_cast<float *>(ws + wl.conv_pw);
+        cp.part_b = reinterpret_cast<float *>(ws + wl.conv_pb);
+        cp.dw = dconv_weight;
+        cp.db = dconv_bias;
+        cp.L = d.seqlen;
+        cp.batch = (int)d.batch;
+        cp.dim = (int)d.dim;
+        cp.W = cw;
+        cp.nblk = wl.nblk;
+        const int64_t n = tok;
+        if ((n + 255) / 256 > INT32_MAX) return SSM_ERR_SHAPE;
+        if (d.dtype == SSM_BF16)
+            hipLaunchKernelGGL(conv_silu_kernel<uint16_t>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, cp);
+        else
+            hipLaunchKernelGGL(conv_silu_kernel<float>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, cp);
+        if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
+    }
     const bool vec = (d.dim % 4 == 0) && aligned(u, 4 * es) && aligned(delta, 4 * es) && (!z || aligned(z, 4 * es)) &&
                      aligned(dy, 4 * es) && aligned(du, 4 * es) && aligned(ddelta, 4 * es) &&
                      (!z || aligned(dz, 4 * es));
-    // 1. checkpoints: the forward scan in its checkpoint mode (segment-parallel)
+    // 1. checkpoints: the forward scan in its checkpoint mode (segment-parallel);
+    // with the prologue it forms u from x itself, as the forward does
     ScanParams p{};
     p.u = u; p.delta = delta; p.z = z; p.B = B; p.C = C;
+    p.conv_w = cw; p.conv_weight = d.conv_weight; p.conv_bias = d.conv_bias;
     p.delta_bias = dbias; p.delta_softplus = d.delta_softplus;
     p.A = A; p.D = D; p.h0 = h0;
     p.L = d.seqlen;
@@ -626,11 +828,15 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
 
     // 2. the reverse pass
     BwdParams bp{};
-    bp.u = u; bp.delta = delta; bp.z = z; bp.dy = dy;
+    bp.u = cw > 0 ? cp.u : u; bp.delta = delta; bp.z = z; bp.dy = dy;
+    bp.u_f32 = cw > 0;
     bp.delta_bias = dbias; bp.delta_softplus = d.delta_softplus;
     bp.A = A; bp.D = D; bp.dh_last = dh_last;
     bp.Bf = p.Bf; bp.Cf = p.Cf; bp.ckpt = p.ckpt;
     bp.du = du; bp.ddelta = ddelta; bp.dz = dz; bp.dh0 = dh0;
+    // with the prologue the gradient of u stays fp32 for the prologue's backward:
+    // dx sums W products of it, which cancel, so its bf16 rounding would show
+    bp.du_f32 = cw > 0 ? reinterpret_cast<float *>(ws + wl.conv_du) : nullptr;
     bp.part_bc = reinterpret_cast<float *>(ws + wl.part_bc);
     bp.part_a = reinterpret_cast<float *>(ws + wl.part_a);
     bp.part_d = reinterpret_cast<float *>(ws + wl.part_d);
@@ -659,7 +865,21 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     rp.npad = wl.sh.npad;
     rp.ntiles = wl.ntiles;
     e = launch_bwd_reduce(rp, stream);
-    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    if (e != hipSuccess) return SSM_ERR_HIP;
+
+    // 4. the convolution prologue: dx, and the sums of the tap and bias gradients
+    if (cw > 0) {
+        if (wl.nblk > 65535 || d.batch > 65535) return SSM_ERR_SHAPE;
+        const dim3 grid((unsigned)((d.dim + 255) / 256), (unsigned)wl.nblk, (unsigned)d.batch);
+        if (d.dtype == SSM_BF16)
+            hipLaunchKernelGGL(conv_bwd_kernel<uint16_t>, grid, dim3(256), 0, stream, cp);
+        else
+            hipLaunchKernelGGL(conv_bwd_kernel<float>, grid, dim3(256), 0, stream, cp);
+        const int64_t nr = (int64_t)d.dim * cw + d.dim;
+        hipLaunchKernelGGL(conv_reduce_kernel, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, stream, cp);
+        if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
+    }
+    return SSM_OK;
 }
 
 }  // namespace
@@ -760,10 +980,10 @@ extern "C" size_t ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc) {
 extern "C" int ssm_scan_bwd(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A,
                             const void *B, const void *C, const float *D, const void *z, const float *h0,
                             const void *dy, const float *dh_last, void *du, void *ddelta, float *dA, float *dB,
-                            float *dC, float *dD, void *dz, float *dh0, float *ddelta_bias, void *workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+                            float *dC, float *dD, void *dz, float *dh0, float *ddelta_bias, float *dconv_weight,
+                            float *dconv_bias, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return bwd_impl(desc, u, delta, A, B, C, D, z, h0, dy, dh_last, du, ddelta, dA, dB, dC, dD, dz, dh0,
-                    ddelta_bias, workspace, workspace_bytes, stream);
+                    ddelta_bias, dconv_weight, dconv_bias, workspace, workspace_bytes, stream);
 }
 
 extern "C" int ssm_ssd_fwd(const ssm_ssd_desc *desc, const void *x, const void *dt, const float *A,

@@ -180,9 +180,9 @@ def test_decode_errors(L):
 
 def bwd_call(L, dsc, u=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB, h0=0,
              dy=8 * GB, dhl=0, du=9 * GB, dde=10 * GB, dA=11 * GB, dB=12 * GB, dC=13 * GB, dD=14 * GB,
-             dz=15 * GB, dh0=0, ddb=0, ws=16 * GB, ws_bytes=1 << 30):
+             dz=15 * GB, dh0=0, ddb=0, dcw=0, dcb=0, ws=16 * GB, ws_bytes=1 << 30):
     ptrs = [fake(a) if a else None for a in (u, delta, A, B, C, D, z, h0, dy, dhl, du, dde, dA, dB, dC, dD, dz,
-                                             dh0, ddb, ws)]
+                                             dh0, ddb, dcw, dcb, ws)]
     return L.ssm_scan_bwd(ctypes.byref(dsc) if dsc is not None else None, *ptrs, ws_bytes, None)
 
 
@@ -209,7 +209,13 @@ def test_bwd_errors(L):
     assert bwd_call(L, desc(), dh0=8 * GB + 128) == EALIAS    # dh0 over dy
     assert bwd_call(L, desc(bias=17 * GB)) == ENULL           # a delta bias needs its gradient
     assert bwd_call(L, desc(bias=17 * GB), ddb=17 * GB + 4) == EALIAS
-    assert bwd_call(L, desc(conv=4, cw=17 * GB)) == EUNSUP
+    # the convolution prologue's backward needs the taps' gradient
+    assert bwd_call(L, desc(conv=4, cw=17 * GB)) == ENULL
+    assert bwd_call(L, desc(conv=4, cw=17 * GB), dcw=18 * GB + 2) == EALIGN
+    assert bwd_call(L, desc(conv=4, cw=17 * GB), dcw=17 * GB + 8) == EALIAS      # over the taps
+    assert bwd_call(L, desc(conv=4, cw=17 * GB, cb=17 * GB + 4096), dcw=18 * GB,
+                    dcb=18 * GB + 64) == EALIAS                                  # bias gradient over taps gradient
+    assert bwd_call(L, desc(conv=4, cw=17 * GB), dcw=18 * GB, ws=0, ws_bytes=0) == EWS
 
 
 def test_bwd_workspace(L):
@@ -222,6 +228,10 @@ def test_bwd_workspace(L):
     assert bwd_call(L, d, ws_bytes=need - 1) == EWS
     assert L.ssm_scan_bwd_workspace_size(ctypes.byref(desc(L=0))) == 0
     assert L.ssm_scan_bwd_workspace_size(None) == 0
+    # the prologue adds u and its gradient (fp32) and per-256-token-block tap and bias sums
+    dc = desc(b=2, L=100, d=64, N=16, conv=3, cw=17 * GB)
+    extra = L.ssm_scan_bwd_workspace_size(ctypes.byref(dc)) - need
+    assert extra >= 2 * rnd(2 * 100 * 64 * 4) + rnd(2 * 1 * 64 * 3 * 4) + rnd(2 * 1 * 64 * 4)
 
 
 def ssd_desc(b=2, L=100, H=4, P=64, G=1, N=128, dtype=ssm.SSM_BF16, disc=0, softplus=0, bias=None):

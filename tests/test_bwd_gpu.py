@@ -197,3 +197,56 @@ def test_bwd_delta_bias_softplus(env, dtype, disc):
     got = {k: to_np(v) for k, v in out.items()}
     ref = ref_bwd(x, g, disc, delta_bias=r["delta_bias"], delta_softplus=True)
     compare_all(x, got, ref, "softplus", keys=GRADS + ("ddelta_bias",))
+
+
+def run_bwd_conv(ssm, torch, x, g, disc, conv, **kw):
+    dev = {k: to_dev(v, torch) for k, v in x.items() if k != "h0"}
+    out = ssm.ssm_scan_bwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], to_dev(g["dy"], torch),
+                           D=dev.get("D"), z=dev.get("z"), h0=to_dev(x["h0"], torch) if x.get("h0") is not None else None,
+                           dh_last=to_dev(g["dh_last"], torch), disc=disc,
+                           conv_weight=to_dev(conv["conv_weight"], torch),
+                           conv_bias=to_dev(conv["conv_bias"], torch), **kw)
+    torch.cuda.synchronize()
+    return {k: to_np(v) for k, v in out.items()}
+
+
+CONV_GRADS = GRADS + ("dconv_weight", "dconv_bias")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("disc", ["euler", "zoh"])
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+def test_bwd_conv_prologue(env, dtype, disc, W):
+    """The backward with the causal conv1d + SiLU prologue: du is the gradient
+    of x, plus the taps' and bias' gradients. L 300 spans two of the prologue
+    backward's 256-token blocks; dim 70 leaves a ragged channel tile."""
+    torch, ssm = env
+    x, g = make_case("mamba130m", dtype, seed=40 + W, batch=2, seqlen=300, dim=70, dstate=16)
+    conv = si.conv_inputs(70, W, seed=W)
+    say("bwd %s %s with the width-%d conv prologue" % (dtype, disc, W))
+    got = run_bwd_conv(ssm, torch, x, g, disc, conv)
+    compare_all(x, got, ref_bwd(x, g, disc, **conv), "conv%d" % W, keys=CONV_GRADS)
+
+
+def test_bwd_conv_with_softplus_step(env):
+    torch, ssm = env
+    x, g = make_case("mamba130m", "bf16", seed=48, batch=2, seqlen=129, dim=136, dstate=16)
+    cfg = cfg_of("mamba130m", "bf16")
+    r = si.raw_delta_inputs(cfg, seed=48, batch=2, seqlen=129, dim=136)
+    x = dict(x, delta=r["delta"])
+    conv = si.conv_inputs(136, 4, seed=48)
+    say("bwd with the conv prologue and the softplus step")
+    got = run_bwd_conv(ssm, torch, x, g, "euler", conv, delta_bias=to_dev(r["delta_bias"], torch),
+                       delta_softplus=True)
+    ref = ref_bwd(x, g, "euler", delta_bias=r["delta_bias"], delta_softplus=True, **conv)
+    compare_all(x, got, ref, "conv+sp", keys=CONV_GRADS + ("ddelta_bias",))
+
+
+def test_bwd_conv_mamba130m_full(env):
+    torch, ssm = env
+    cfg = si.CONFIGS["mamba130m"]
+    x, g = si.scan_inputs(cfg, seed=1), si.grad_inputs(cfg, seed=1)
+    conv = si.conv_inputs(cfg.dim, 4, seed=1)
+    say("bwd Mamba-130M-shaped layer with the width-4 conv prologue, every gradient")
+    got = run_bwd_conv(ssm, torch, x, g, "euler", conv)
+    compare_all(x, got, ref_bwd(x, g, "euler", use_h0=False, **conv), "130m conv", keys=CONV_GRADS)

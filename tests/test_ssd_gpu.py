@@ -148,3 +148,34 @@ def test_ssd_mamba2_full_size(env):
     gh = np.stack([hl[b, h] for b, h in heads])
     check((gy, gh), (ry, rh), "mamba2-ssd sampled")
     assert np.isfinite(y).all()
+
+
+def test_ssd_zero_step_keeps_state_exactly(env):
+    """dt = 0: no decay and no input, so the state passes through bit for bit
+    and y is the readout of h0 (itwiki "Mamba의 선택 메커니즘": a small step keeps
+    the state)."""
+    torch, ssm = env
+    x = case(seed=61, L=150, H=4, G=2)
+    x["dt"] = np.zeros_like(x["dt"])
+    say("ssd dt = 0")
+    y, hl = run(ssm, torch, x)
+    assert np.array_equal(hl, x["h0"].astype(np.float64))
+    check((y, hl), oracle.ssd(**x), "dt0")
+
+
+def test_ssd_a_zero_is_masked_product(env):
+    """A = 0: the layer is the causally masked product tril(C B^T)(dt x) plus
+    the readout of h0 (closed form, computed here with numpy)."""
+    torch, ssm = env
+    x = case(seed=62, L=130, H=2, G=1, gate=False, skip=False)
+    x["A"] = np.zeros_like(x["A"])
+    say("ssd A = 0 against the masked product")
+    y, hl = run(ssm, torch, x)
+    w = lambda a: si.bf16_bits_to_f32(a).astype(np.float64)
+    B, C, dt, xx = w(x["B"])[:, :, 0], w(x["C"])[:, :, 0], w(x["dt"]), w(x["x"])
+    L = xx.shape[1]
+    ref = np.einsum("bts,bsh,bshp->bthp", np.einsum("btn,bsn->bts", C, B) * np.tril(np.ones((L, L))), dt, xx)
+    ref += np.einsum("btn,bhpn->bthp", C, x["h0"].astype(np.float64))
+    e = rel_err(y, ref)
+    say("  y err %.3e" % e)
+    assert e <= TOL_BF16
