@@ -438,7 +438,6 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
                 }
             }
 
-            SSM_SSD_PHASE_FENCE_UPDATE
             // skip, gate, store: yacc[pt][r] = y[i][p = PW g4 + 4 pt + r], so
             // the lane's PW outputs are contiguous and leave in 16-byte pieces
             if (IW + r16 < nv) {
