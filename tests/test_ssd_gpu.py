@@ -179,3 +179,35 @@ def test_ssd_a_zero_is_masked_product(env):
     e = rel_err(y, ref)
     say("  y err %.3e" % e)
     assert e <= TOL_BF16
+
+
+def _sweep_cases(n=16, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        P, N = [(64, 64), (64, 128), (96, 64), (96, 128), (128, 64), (128, 128)][rng.integers(0, 6)]
+        G = int(rng.choice([1, 2, 4]))
+        H = G * int(rng.choice([1, 2, 3]))
+        cases.append(dict(k=k, P=P, N=N, G=G, H=H, L=int(rng.integers(1, 400)), batch=int(rng.integers(1, 4)),
+                          disc=str(rng.choice(["euler", "zoh"])), gate=bool(rng.integers(0, 2)),
+                          skip=bool(rng.integers(0, 2)), h0=bool(rng.integers(0, 2)),
+                          softplus=bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("c", _sweep_cases(), ids=lambda c: "case%d" % c["k"])
+def test_ssd_sweep(env, c):
+    """Seeded mixes of head size, state size, groups, heads per group (odd
+    and even: one or two heads per workgroup), length, batch, input weight
+    and the optional parts."""
+    torch, ssm = env
+    x = case(seed=300 + c["k"], batch=c["batch"], L=c["L"], H=c["H"], P=c["P"], G=c["G"], N=c["N"],
+             gate=c["gate"], skip=c["skip"], h0=c["h0"])
+    kw = {}
+    if c["softplus"]:
+        rng = np.random.default_rng(700 + c["k"])
+        x["dt"] = si.to_bf16_bits((0.5 * rng.standard_normal(x["dt"].shape)).astype(np.float32))
+        kw = dict(dt_bias=si.delta_bias(c["k"], c["H"], "uniform").astype(np.float32), dt_softplus=True)
+    say("ssd sweep %s" % c)
+    got = run(ssm, torch, x, c["disc"], **kw)
+    check(got, oracle.ssd(**x, disc=c["disc"], **kw), "case%d" % c["k"])
