@@ -79,6 +79,14 @@ constexpr int kSsdQ = 64;        // tokens per chunk
 #ifndef SSM_SSD_HPAD
 #define SSM_SSD_HPAD 16
 #endif
+// ... of the state copy (read as 16-byte row pieces), and the mask of the
+// row bits that swizzle its 64-byte column blocks
+#ifndef SSM_SSD_SPAD
+#define SSM_SSD_SPAD 8
+#endif
+#ifndef SSM_SSD_SWZ
+#define SSM_SSD_SWZ 1
+#endif
 
 // Scheduling fences between the phases of a chunk: they keep the scheduler
 // from hoisting one phase's operand loads into the previous phase past the
@@ -149,20 +157,35 @@ __device__ __forceinline__ float ssd_prefix_sum(float v, int lane) {
     return v;
 }
 
-// A float as two bf16 values whose sum carries 16 significant bits.
-__device__ __forceinline__ void ssd_split(float v, __bf16 &hi, __bf16 &lo) {
-    hi = (__bf16)v;
-    lo = (__bf16)(v - (float)hi);
+// Two floats as the hi and lo words of packed bf16 pairs whose sums carry 16
+// significant bits: hi is the pair rounded to bf16, lo the two remainders
+// rounded to bf16.
+__device__ __forceinline__ void ssd_split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = ssd_pack(a, b);
+    const float ra = a - __uint_as_float(hi << 16);
+    const float rb = b - __uint_as_float(hi & 0xffff0000u);
+    lo = ssd_pack(ra, rb);
 }
 
-// Two floats as the hi and lo words of packed bf16 pairs.
-__device__ __forceinline__ void ssd_split2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    __bf16 ah, al, bh, bl;
-    ssd_split(a, ah, al);
-    ssd_split(b, bh, bl);
-    const ssd_bf16x2 h2 = {ah, bh}, l2 = {al, bl};
-    hi = __builtin_bit_cast(uint32_t, h2);
-    lo = __builtin_bit_cast(uint32_t, l2);
+typedef unsigned int ssd_u32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer of `bytes` bytes at `base` (dword 3: 32-bit data format, the
+// setting for untyped access on gfx9). Buffer instructions check every access
+// against that size: loads past it return zero and stores past it are
+// dropped. Rows past the end of the sequence then need no branch, and the
+// compiler's wait counts, which must assume the shortest path through a
+// branch, stay exact.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ssd_buffer(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ssd_bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const ssd_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return uint4{v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ void ssd_bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4 &v) {
+    __builtin_amdgcn_raw_buffer_store_b128(ssd_u32x4{v.x, v.y, v.z, v.w}, r, (int)off, 0, 0);
 }
 
 // One chunk's global inputs as a lane (= token) of each wave loads them, one
@@ -191,33 +214,44 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
     constexpr int NW = N / 4;      // state rows per wave
     constexpr int NTW = NW / 16;   // state row tiles per wave
     constexpr int XS = P + SSM_SSD_XPAD;   // LDS row stride of token rows of x (conflict-free transposing reads)
-    constexpr int HS = N + SSM_SSD_HPAD;   // LDS row stride of n-contiguous tiles
+    constexpr int HS = N + SSM_SSD_HPAD;   // LDS row stride of the B token rows (likewise)
+    constexpr int HSH = N + SSM_SSD_SPAD;  // LDS row stride of the state copy (16-byte row reads)
     typedef SsdStage<P, N, HPW> Stage;
     static_assert(P % 32 == 0 && N % 64 == 0, "tile shape");
     static_assert(Stage::XI * 4 * 64 == Q * Stage::XPR && Stage::BI * 4 * HPW * 64 == Q * Stage::BPR,
                   "staging pieces cover the chunk");
 
     __shared__ __attribute__((aligned(16))) uint16_t sBR[Q * HS];         // B, token rows
-    __shared__ __attribute__((aligned(16))) uint16_t sXT[HPW][Q * XS];    // x, token rows
+    __shared__ __attribute__((aligned(16))) uint16_t sXT[HPW][Q * XS];    // x, token rows, output channel order
     __shared__ __attribute__((aligned(16))) uint16_t sXh[HPW][Q * XS];    // wbar exp(S_last - S_j) x, hi
     __shared__ __attribute__((aligned(16))) uint16_t sXl[HPW][Q * XS];    // ... lo
-    __shared__ __attribute__((aligned(16))) uint16_t sHh[HPW][P * HS];    // state entering the chunk, hi
-    __shared__ __attribute__((aligned(16))) uint16_t sHl[HPW][P * HS];    // ... lo
+    __shared__ __attribute__((aligned(16))) uint16_t sHh[HPW][P * HSH];   // state entering the chunk, hi
+    __shared__ __attribute__((aligned(16))) uint16_t sHl[HPW][P * HSH];   // ... lo
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int hs = w >> 2, wl = w & 3;   // head slot, role within the head
+    const int hs = w >> 2;               // head slot
+    // role within the head: the second head takes the roles in reverse, so
+    // that the two waves sharing a SIMD (w and w + 4) pair a short and a long
+    // causal triangle
+    const int wl = hs ? 3 - (w & 3) : (w & 3);
     const int r16 = lane & 15, g4 = lane >> 4;
     const int I0 = 16 * wl;              // this wave's output tokens within a chunk
-    // Channels of the output p tiles (the readout's and the masked product's
-    // A rows): row m of p tile pt is channel PW (m / 4) + 4 pt + m % 4, so
-    // that the output accumulator rows 4 g4 .. 4 g4 + 3 of all tiles are the
-    // PW contiguous channels PW g4 .. PW g4 + PW - 1. The state and its update
-    // keep the natural order (row m of tile pt is channel 16 pt + m); the
-    // state's bf16 copy in LDS puts channel c in row hrow(c), which is 16 pt + m
-    // for the channel of output row m of tile pt.
+    // Output channel order: row m of p tile pt of the readout's and the
+    // masked product's outputs is channel PW (m / 4) + 4 pt + m % 4, so that
+    // the output accumulator rows 4 g4 .. 4 g4 + 3 of all tiles are the PW
+    // contiguous channels PW g4 .. PW g4 + PW - 1. The state and its update
+    // keep the natural order (row m of tile pt is channel 16 pt + m). The raw
+    // x rows in LDS hold channel PW a + 4 pt + r in column xcol = 16 pt + 4 a + r,
+    // and the state's bf16 copy puts channel c in row hrow(c): both are then
+    // read in the output order with natural addressing.
     constexpr int PW = P / 4;
     auto hrow = [](int c) { return 16 * ((c % PW) >> 2) + 4 * (c / PW) + (c & 3); };
+    // column swizzle of the state copy: the 64-byte column blocks of a row
+    // are permuted by bits of its row index / 16, which spreads the writes
+    // of a wave (rows 16 apart) over the banks
+    constexpr int SWZ = SSM_SSD_SWZ & (N / 32 - 1);
+    auto hcol = [](int R, int col) { return col ^ (32 * ((R >> 4) & SWZ)); };
 
     const int nb = gridDim.x, bid = blockIdx.x;
     const int qx = nb / kXcds, rx = nb % kXcds, xcd = bid % kXcds;
@@ -234,6 +268,8 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
     const int64_t L = p.L;
     const int64_t xs = (int64_t)p.H * P;   // token stride of x, z, y
     const int64_t bs = (int64_t)p.G * N;   // token stride of B, C
+    // (64 token rows of x and of B fit 32-bit element offsets: the library checks it)
+    const uint32_t xs32 = (uint32_t)xs, bs32 = (uint32_t)bs, H32 = (uint32_t)p.H;
     const uint16_t *xb = p.x + (int64_t)b * L * xs + (int64_t)h * P;
     const uint16_t *zb = p.z ? p.z + (int64_t)b * L * xs + (int64_t)h * P : nullptr;
     uint16_t *yb = p.y + (int64_t)b * L * xs + (int64_t)h * P;
@@ -246,27 +282,36 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
     uint16_t *const Hh = sHh[hs];
     uint16_t *const Hl = sHl[hs];
 
-    // Staging loads of the chunk starting at c, one chunk ahead: rows past
-    // the end are clamped to the last token (their values are zeroed or masked).
-    // (element offsets within a chunk fit 32 bits: the library checks that
-    // 64 token rows of x and of B do)
+    // byte offsets of the lane's staging pieces within a chunk; the same for
+    // every chunk, whose buffers start at its first token
+    uint32_t xoff[Stage::XI], boff[Stage::BI];
+#pragma unroll
+    for (int k = 0; k < Stage::XI; ++k) {
+        const int piece = (wl * Stage::XI + k) * 64 + lane;
+        xoff[k] = 2u * ((uint32_t)(piece / Stage::XPR) * xs32 + 8u * (piece % Stage::XPR));
+    }
+#pragma unroll
+    for (int k = 0; k < Stage::BI; ++k) {
+        const int piece = (w * Stage::BI + k) * 64 + lane;
+        boff[k] = 2u * ((uint32_t)(piece / Stage::BPR) * bs32 + 8u * (piece % Stage::BPR));
+    }
+    // Valid tokens of the chunk starting at c (0 past the end)
+    auto valid_tokens = [&](int64_t c) { return (uint32_t)max<int64_t>(0, min<int64_t>(Q, L - c)); };
+    // Staging loads of the chunk starting at c, one chunk ahead: the buffers
+    // end at the chunk's last valid token, so rows past the end read as zero
+    // and a chunk past the end loads nothing.
     auto load_stage = [&](int64_t c, Stage &st) {
-        const int nv = (int)min<int64_t>(Q, L - c);
-        const uint16_t *xc = xb + c * xs;
-        const uint16_t *bc = Bb + c * bs;
-        st.dt = db[(c + min(lane, nv - 1)) * p.H];
+        const uint32_t nv = valid_tokens(c);
+        const __amdgpu_buffer_rsrc_t rd = ssd_buffer(db + c * p.H, 2u * nv * H32);
+        const __amdgpu_buffer_rsrc_t rxb = ssd_buffer(xb + c * xs, 2u * nv * xs32);
+        const __amdgpu_buffer_rsrc_t rbb = ssd_buffer(Bb + c * bs, 2u * nv * bs32);
+        st.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)(2u * (uint32_t)lane * H32), 0, 0);
 #pragma unroll
-        for (int k = 0; k < Stage::XI; ++k) {
-            const int piece = (wl * Stage::XI + k) * 64 + lane;
-            const int t = min(piece / Stage::XPR, nv - 1);
-            st.x[k] = *reinterpret_cast<const uint4 *>(xc + (uint32_t)(t * (int)xs + 8 * (piece % Stage::XPR)));
-        }
+        for (int k = 0; k < Stage::XI; ++k)
+            st.x[k] = ssd_bload16(rxb, xoff[k]);
 #pragma unroll
-        for (int k = 0; k < Stage::BI; ++k) {
-            const int piece = (w * Stage::BI + k) * 64 + lane;
-            const int t = min(piece / Stage::BPR, nv - 1);
-            st.b[k] = *reinterpret_cast<const uint4 *>(bc + (uint32_t)(t * (int)bs + 8 * (piece % Stage::BPR)));
-        }
+        for (int k = 0; k < Stage::BI; ++k)
+            st.b[k] = ssd_bload16(rbb, boff[k]);
     };
 
     // State: hacc[i][pt][r] = h[p = 16 pt + r16][n = 16 (wl NTW + i) + 4 g4 + r]; its
@@ -284,25 +329,30 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
         }
 
     Stage st;
-    if (L > 0)
-        load_stage(0, st);
+    load_stage(0, st);
     // nothing of the prologue stays in flight into the loop (the loop's wait
     // counts then only see its own loads)
     __builtin_amdgcn_s_waitcnt(0);
 
     for (int64_t c0 = 0; c0 < L; c0 += Q) {
-        const int nv = (int)min<int64_t>(Q, L - c0);   // valid tokens in this chunk
+        const uint32_t nvu = valid_tokens(c0);
+        const int nv = (int)nvu;                         // valid tokens in this chunk
         const bool valid = lane < nv;
 
-        // this wave's C rows (operands of the readout and the scores), issued
-        // before the next chunk's staging loads, so that waiting for them
-        // never waits for those
-        const int64_t ti = c0 + min(I0 + r16, nv - 1);
+        // this wave's C rows (operands of the readout and the scores) and
+        // gate values, issued before the next chunk's staging loads, so that
+        // waiting for them never waits for those; rows past the end read zero
+        const __amdgpu_buffer_rsrc_t rc = ssd_buffer(Cb + c0 * bs, 2u * nvu * bs32);
         ssd_bf16x8 cop[NK];
 #pragma unroll
         for (int s = 0; s < NK; ++s)
-            cop[s] = ssd_ld16(Cb + ti * bs + 32 * s + 8 * g4);
-
+            cop[s] = __builtin_bit_cast(ssd_bf16x8,
+                                        ssd_bload16(rc, 2u * ((uint32_t)(I0 + r16) * bs32 + 32 * s + 8 * g4)));
+        const __amdgpu_buffer_rsrc_t rz = ssd_buffer(zb ? zb + c0 * xs : xb, zb ? 2u * nvu * xs32 : 0u);
+        uint4 zop[PT / 2];
+#pragma unroll
+        for (int k = 0; k < PT / 2; ++k)
+            zop[k] = ssd_bload16(rz, 2u * ((uint32_t)(I0 + r16) * xs32 + PW * g4 + 8 * k));
 
         // the state entering this chunk, as hi + lo bf16 (every wave has
         // finished reading the previous one: barrier at the end of the last chunk)
@@ -313,7 +363,8 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
                 uint2 hi, lo;
                 ssd_split2(hacc[i][pt][0], hacc[i][pt][1], hi.x, lo.x);
                 ssd_split2(hacc[i][pt][2], hacc[i][pt][3], hi.y, lo.y);
-                const int o = hrow(16 * pt + r16) * HS + 16 * (wl * NTW + i) + 4 * g4;
+                const int R = hrow(16 * pt + r16);
+                const int o = R * HSH + hcol(R, 16 * (wl * NTW + i) + 4 * g4);
                 *reinterpret_cast<uint2 *>(&Hh[o]) = hi;
                 *reinterpret_cast<uint2 *>(&Hl[o]) = lo;
             }
@@ -333,35 +384,37 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
         const float Slast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), 63));
         const float fd = wbar * __builtin_amdgcn_exp2f(Slast - S);
 
-        // stage x (raw, and weighted for the state update as hi + lo) and B as
-        // token rows, one 16-byte piece per lane and load; tokens past the end
-        // zero. Products over tokens read these rows with transposing LDS reads.
+        // stage x (raw, in the output channel order, and weighted for the
+        // state update as hi + lo) and B as token rows, one 16-byte piece per
+        // lane and load. Products over tokens read these rows with
+        // transposing LDS reads.
 #pragma unroll
         for (int k = 0; k < Stage::XI; ++k) {
             const int piece = (wl * Stage::XI + k) * 64 + lane;
             const int t = piece / Stage::XPR;
             const int col = 8 * (piece % Stage::XPR);
             const float f = __shfl(fd, t);        // the piece's token's weight
-            const uint4 v = t < nv ? st.x[k] : uint4{0u, 0u, 0u, 0u};
+            const uint4 v = st.x[k];
             const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 ssd_split2(ssd_bf(wd[e] & 0xffffu) * f, ssd_bf(wd[e] >> 16) * f, hw[e], lw[e]);
             const int o = t * XS + col;
-            *reinterpret_cast<uint4 *>(&XT[o]) = v;
+            // channels col .. col + 3 and col + 4 .. col + 7 of the output order
+            const int xo = t * XS + 16 * ((col % PW) >> 2) + 4 * (col / PW);
+            *reinterpret_cast<uint2 *>(&XT[xo]) = uint2{v.x, v.y};
+            *reinterpret_cast<uint2 *>(&XT[xo + 16]) = uint2{v.z, v.w};
             *reinterpret_cast<uint4 *>(&Xh[o]) = uint4{hw[0], hw[1], hw[2], hw[3]};
             *reinterpret_cast<uint4 *>(&Xl[o]) = uint4{lw[0], lw[1], lw[2], lw[3]};
         }
 #pragma unroll
         for (int k = 0; k < Stage::BI; ++k) {
             const int piece = (w * Stage::BI + k) * 64 + lane;
-            const int t = piece / Stage::BPR;
-            const uint4 v = t < nv ? st.b[k] : uint4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<uint4 *>(&sBR[t * HS + 8 * (piece % Stage::BPR)]) = v;
+            *reinterpret_cast<uint4 *>(&sBR[(piece / Stage::BPR) * HS + 8 * (piece % Stage::BPR)]) = st.b[k];
         }
-        // the next chunk's staging loads (the last chunk reloads itself)
-        load_stage(c0 + Q < L ? c0 + Q : c0, st);
+        // the next chunk's staging loads (nothing past the end)
+        load_stage(c0 + Q, st);
         __syncthreads();
 
         // The rest of the chunk, specialised on the wave's role so that each
@@ -379,7 +432,8 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
                 yacc[pt] = ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int s = 0; s < NK; ++s) {
-                    const int o = (16 * pt + r16) * HS + 32 * s + 8 * g4;
+                    const int R = 16 * pt + r16;
+                    const int o = R * HSH + hcol(R, 32 * s + 8 * g4);
                     yacc[pt] = ssd_mfma(ssd_ld16(&Hh[o]), cop[s], yacc[pt]);
                     yacc[pt] = ssd_mfma(ssd_ld16(&Hl[o]), cop[s], yacc[pt]);
                 }
@@ -394,7 +448,8 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
             SSM_SSD_PHASE_FENCE_SCORES
             // scores of key tiles J <= WL, decayed, weighted, masked, as hi + lo
             // operands: element 4 (J%2) + r of m*[J/2] is M^T[16 J + 4 g4 + r][i]
-            ssd_bf16x8 mh[2], ml[2];
+            // (packed two to a word)
+            uint32_t mh[2][4], ml[2][4];
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
                 if (J <= WL) {
@@ -402,70 +457,69 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
 #pragma unroll
                     for (int s = 0; s < NK; ++s)
                         gt = ssd_mfma(ssd_ld16(&sBR[(16 * J + r16) * HS + 32 * s + 8 * g4]), cop[s], gt);
+                    float m[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int jj = 16 * J + 4 * g4 + r;
                         const float Sj = __shfl(S, jj);
                         const float wj = __shfl(wbar, jj);
                         const bool keep = J < WL || 4 * g4 + r <= r16;
-                        const float m = keep ? gt[r] * __builtin_amdgcn_exp2f(Si - Sj) * wj : 0.0f;
-                        __bf16 hi, lo;
-                        ssd_split(m, hi, lo);
-                        mh[J >> 1][4 * (J & 1) + r] = hi;
-                        ml[J >> 1][4 * (J & 1) + r] = lo;
+                        m[r] = keep ? gt[r] * __builtin_amdgcn_exp2f(Si - Sj) * wj : 0.0f;
                     }
+                    ssd_split2(m[0], m[1], mh[J >> 1][2 * (J & 1)], ml[J >> 1][2 * (J & 1)]);
+                    ssd_split2(m[2], m[3], mh[J >> 1][2 * (J & 1) + 1], ml[J >> 1][2 * (J & 1) + 1]);
                 } else if ((J & 1) && J - 1 <= WL) {
                     // odd key tile past the diagonal, paired with a computed one: zeros
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        mh[J >> 1][4 + r] = (__bf16)0.0f;
-                        ml[J >> 1][4 + r] = (__bf16)0.0f;
-                    }
+                    mh[J >> 1][2] = mh[J >> 1][3] = 0u;
+                    ml[J >> 1][2] = ml[J >> 1][3] = 0u;
                 }
             }
 #pragma unroll
             for (int Jp = 0; Jp < 2; ++Jp) {
                 if (2 * Jp <= WL) {
+                    const ssd_bf16x8 mhv = __builtin_bit_cast(ssd_bf16x8, uint4{mh[Jp][0], mh[Jp][1], mh[Jp][2], mh[Jp][3]});
+                    const ssd_bf16x8 mlv = __builtin_bit_cast(ssd_bf16x8, uint4{ml[Jp][0], ml[Jp][1], ml[Jp][2], ml[Jp][3]});
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) {
                         // x^T operand in the K order of mh / ml: tokens
                         // 32 Jp + 4 g4 + e, then 32 Jp + 16 + 4 g4 + e
-                        const uint16_t *src = &XT[(32 * Jp + 4 * g4 + (r16 >> 2)) * XS + PW * (r16 & 3) + 4 * pt];
+                        const uint16_t *src = &XT[(32 * Jp + 4 * g4 + (r16 >> 2)) * XS + 16 * pt + 4 * (r16 & 3)];
                         const ssd_bf16x8 xo = ssd_ld_tr2(src, src + 16 * XS);
-                        yacc[pt] = ssd_mfma(xo, mh[Jp], yacc[pt]);
-                        yacc[pt] = ssd_mfma(xo, ml[Jp], yacc[pt]);
+                        yacc[pt] = ssd_mfma(xo, mhv, yacc[pt]);
+                        yacc[pt] = ssd_mfma(xo, mlv, yacc[pt]);
                     }
                 }
             }
 
             // skip, gate, store: yacc[pt][r] = y[i][p = PW g4 + 4 pt + r], so
-            // the lane's PW outputs are contiguous and leave in 16-byte pieces
-            if (IW + r16 < nv) {
-                const int64_t off = (c0 + IW + r16) * xs + PW * g4;
+            // the lane's PW outputs are contiguous and leave in 16-byte
+            // pieces; rows past the end are dropped by the buffer's range
+            const __amdgpu_buffer_rsrc_t ry = ssd_buffer(yb + c0 * xs, 2u * nvu * xs32);
 #pragma unroll
-                for (int k = 0; k < PT / 2; ++k) {
-                    float v[8];
+            for (int k = 0; k < PT / 2; ++k) {
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = yacc[2 * k + (e >> 2)][e & 3];
+                if (p.D) {
+                    // x of channels PW g4 + 8 k + e from the raw rows (output order)
+                    const uint16_t *xr = &XT[(IW + r16) * XS + 32 * k + 4 * g4];
+                    const uint2 x0 = *reinterpret_cast<const uint2 *>(xr);
+                    const uint2 x1 = *reinterpret_cast<const uint2 *>(xr + 16);
+                    const uint32_t xw[4] = {x0.x, x0.y, x1.x, x1.y};
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        v[e] = yacc[2 * k + (e >> 2)][e & 3];
-                    if (p.D) {
-                        const uint4 xe = *reinterpret_cast<const uint4 *>(xb + off + 8 * k);
-                        const uint32_t xw[4] = {xe.x, xe.y, xe.z, xe.w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            v[e] += dskip * ssd_bf(e & 1 ? xw[e >> 1] >> 16 : xw[e >> 1] & 0xffffu);
-                    }
-                    if (zb) {
-                        const uint4 ze = *reinterpret_cast<const uint4 *>(zb + off + 8 * k);
-                        const uint32_t zw[4] = {ze.x, ze.y, ze.z, ze.w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            v[e] *= silu(ssd_bf(e & 1 ? zw[e >> 1] >> 16 : zw[e >> 1] & 0xffffu));
-                    }
-                    const uint4 o = {ssd_pack(v[0], v[1]), ssd_pack(v[2], v[3]), ssd_pack(v[4], v[5]),
-                                     ssd_pack(v[6], v[7])};
-                    *reinterpret_cast<uint4 *>(yb + off + 8 * k) = o;
+                        v[e] += dskip * ssd_bf(e & 1 ? xw[e >> 1] >> 16 : xw[e >> 1] & 0xffffu);
                 }
+                if (zb) {
+                    const uint32_t zw[4] = {zop[k].x, zop[k].y, zop[k].z, zop[k].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        v[e] *= silu(ssd_bf(e & 1 ? zw[e >> 1] >> 16 : zw[e >> 1] & 0xffffu));
+                }
+                const uint4 o = {ssd_pack(v[0], v[1]), ssd_pack(v[2], v[3]), ssd_pack(v[4], v[5]),
+                                 ssd_pack(v[6], v[7])};
+                ssd_bstore16(ry, 2u * ((uint32_t)(IW + r16) * xs32 + PW * g4 + 8 * k), o);
             }
 
             SSM_SSD_PHASE_FENCE_UPDATE
