@@ -108,8 +108,12 @@ namespace {
 // the values per lane (odd lanes keep c and d, then lanes 2 and 3 of a quad
 // keep the b/d sums), leave every lane with one value summed over its quad
 // (lane 0 of a quad: a, 1: c, 2: b, 3: d); row shifts by 4 and 8 add the
-// quads of a row into lanes 12..15; cross-row shuffles add the rows. The
-// sums end in lanes 60 (a), 61 (c), 62 (b) and 63 (d). Lane masks: m1 = odd
+// quads of a row into lanes 12..15; two lane swaps between copies of the
+// value (v_permlane16_swap: the odd rows of one copy with the even rows of
+// the other; v_permlane32_swap: the upper half of one with the lower half of
+// the other) add the rows without a trip through LDS. The sums end in lanes
+// 12 + 16 k (a), 13 + 16 k (c), 14 + 16 k (b) and 15 + 16 k (d) of every
+// row k. Lane masks: m1 = odd
 // lanes, m2 = lanes with bit 1 set. The s_nops give every DPP read the two
 // wait states it needs after the write it depends on.
 __device__ __forceinline__ float wave_sum4_transposed(float a, float b, float c, float d) {
@@ -134,9 +138,10 @@ __device__ __forceinline__ float wave_sum4_transposed(float a, float b, float c,
         : [r1] "=&v"(r1), [k1] "=&v"(k1), [r2] "=&v"(r2), [k2] "=&v"(k2), [p] "=&v"(p), [q] "=&v"(q),
           [s] "=&v"(s)
         : [a] "v"(a), [b] "v"(b), [c] "v"(c), [d] "v"(d), [m1] "s"(m1), [m2] "s"(m2));
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    return s;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
 }
 
 template <int KV> struct BwdFloats;
