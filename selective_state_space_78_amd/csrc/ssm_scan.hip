@@ -43,9 +43,13 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float *h0, float 
 //   dpre_t  = du_t * silu'(pre_t),   silu'(p) = s (1 + p (1 - s)), s = sigmoid(p)
 //   dx_s    = sum_k w[k] dpre_{s+(W-1)-k}
 //   dw[k]  += dpre_t x_{t-(W-1)+k},  dcb += dpre_t
-// one thread per (batch row, channel, block of kConvBlock tokens), walking
-// time with a window of the last W values of x and dpre; the per-block
-// partial sums of dw and dcb are added in a fixed order by conv_reduce_kernel.
+// Both kernels give a thread CPT consecutive channels (4 when dim % 4 == 0 and
+// the tensors are aligned: one 8- or 16-byte access per token) of one batch
+// row and walk a run of tokens with a window of the last W values in
+// registers, so every element of x, u and du moves once. With the taps taken
+// by lag j (wr[j] = w[W-1-j] multiplies x_{t-j}) every register index is a
+// compile-time constant. conv_bwd_kernel writes per-run partial sums of dw
+// and dcb, added in a fixed order by conv_reduce_kernel.
 constexpr int kConvBlock = 256;
 
 struct ConvParams {
@@ -58,6 +62,7 @@ struct ConvParams {
     float *dw, *db;           // (dim, W), (dim) or null
     int64_t L;
     int batch, dim, W, nblk;
+    int run;                  // tokens per thread of conv_silu_kernel
 };
 
 template <typename T>
@@ -68,102 +73,212 @@ __device__ __forceinline__ float conv_ld(const void *p, int64_t i) {
         return static_cast<const float *>(p)[i];
 }
 
-template <typename T>
-__device__ __forceinline__ void conv_st(void *p, int64_t i, float v) {
-    if constexpr (sizeof(T) == 2)
-        static_cast<uint16_t *>(p)[i] = __builtin_bit_cast(uint16_t, (__bf16)v);
-    else
-        static_cast<float *>(p)[i] = v;
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void conv_silu_kernel(const ConvParams p) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, t, d)
-    const int64_t n = (int64_t)p.batch * p.L * p.dim;
-    if (i >= n) return;
-    const int d = (int)(i % p.dim);
-    const int64_t t = (i / p.dim) % p.L;
-    float acc = p.cb ? p.cb[d] : 0.0f;
-    for (int k = 0; k < p.W; ++k) {
-        const int64_t back = p.W - 1 - k;
-        if (t >= back) acc = fmaf(p.w[(int64_t)d * p.W + k], conv_ld<T>(p.x, i - back * p.dim), acc);
+// CPT consecutive values of a T tensor at element offset i
+template <typename T, int CPT>
+__device__ __forceinline__ void conv_ld_piece(const void *p, int64_t i, float (&v)[CPT]) {
+    if constexpr (CPT == 1) {
+        v[0] = conv_ld<T>(p, i);
+    } else if constexpr (sizeof(T) == 2) {
+        const uint2 r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+        v[0] = __uint_as_float(r.x << 16);
+        v[1] = __uint_as_float(r.x & 0xffff0000u);
+        v[2] = __uint_as_float(r.y << 16);
+        v[3] = __uint_as_float(r.y & 0xffff0000u);
+    } else {
+        const float4 r = *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+        v[0] = r.x, v[1] = r.y, v[2] = r.z, v[3] = r.w;
     }
-    p.u[i] = silu(acc);
+}
+
+template <int CPT>
+__device__ __forceinline__ void conv_ld_f32(const float *p, int64_t i, float (&v)[CPT]) {
+    if constexpr (CPT == 1) {
+        v[0] = p[i];
+    } else {
+        const float4 r = *reinterpret_cast<const float4 *>(p + i);
+        v[0] = r.x, v[1] = r.y, v[2] = r.z, v[3] = r.w;
+    }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void conv_bwd_kernel(const ConvParams p) {
-    const int d = blockIdx.x * blockDim.x + threadIdx.x;
-    const int blk = blockIdx.y;
-    const int b = blockIdx.z;
-    if (d >= p.dim) return;
-    const int W = p.W;
-    float w[kConvMax];
+__device__ __forceinline__ uint16_t conv_bf(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+template <typename T, int CPT>
+__device__ __forceinline__ void conv_st_piece(void *p, int64_t i, const float (&v)[CPT]) {
+    if constexpr (CPT == 1) {
+        if constexpr (sizeof(T) == 2)
+            static_cast<uint16_t *>(p)[i] = conv_bf<T>(v[0]);
+        else
+            static_cast<float *>(p)[i] = v[0];
+    } else if constexpr (sizeof(T) == 2) {
+        const uint2 r = {(uint32_t)conv_bf<T>(v[0]) | ((uint32_t)conv_bf<T>(v[1]) << 16),
+                         (uint32_t)conv_bf<T>(v[2]) | ((uint32_t)conv_bf<T>(v[3]) << 16)};
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p) + i) = r;
+    } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// Taps by lag (wr[c][j] multiplies x_{t-j}; zero past W) and the bias of the
+// thread's channels
+template <int CPT>
+__device__ __forceinline__ void conv_taps(const ConvParams &p, int d0, float (&wr)[CPT][kConvMax], float (&cb)[CPT]) {
 #pragma unroll
-    for (int k = 0; k < kConvMax; ++k) w[k] = k < W ? p.w[(int64_t)d * W + k] : 0.0f;
-    const float cb = p.cb ? p.cb[d] : 0.0f;
-    const int64_t t0 = (int64_t)blk * kConvBlock;
-    const int64_t t1 = min(p.L, t0 + kConvBlock);
-    const int64_t tend = min(p.L, t1 + W - 1);   // dx of the block's last tokens needs W-1 tokens ahead
-    const int64_t row = (int64_t)b * p.L;
-    // xs[j]: x_{t-j} for j = 0 .. W-1 (zero before the sequence); ds[j]: dpre_{t-j}
-    float xs[kConvMax], ds[kConvMax], gw[kConvMax];
+    for (int c = 0; c < CPT; ++c) {
+        cb[c] = p.cb ? p.cb[d0 + c] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kConvMax; ++j)
+            wr[c][j] = j < p.W ? p.w[(int64_t)(d0 + c) * p.W + (p.W - 1 - j)] : 0.0f;
+    }
+}
+
+// pre_t = cb + sum_{j < W} wr[j] x_{t-j}, with xs[j] = x_{t-j}
+template <int CPT>
+__device__ __forceinline__ void conv_pre(const float (&wr)[CPT][kConvMax], const float (&cb)[CPT],
+                                         const float (&xs)[kConvMax][CPT], int W, float (&pre)[CPT]) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        float acc = cb[c];
+#pragma unroll
+        for (int j = 0; j < kConvMax; ++j)
+            if (j < W) acc = fmaf(wr[c][j], xs[j][c], acc);
+        pre[c] = acc;
+    }
+}
+
+template <typename T, int CPT>
+__global__ __launch_bounds__(256) void conv_silu_kernel(const ConvParams p) {
+    const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * CPT;
+    if (d0 >= p.dim) return;
+    const int64_t row = (int64_t)blockIdx.z * p.L;
+    const int64_t t0 = (int64_t)blockIdx.y * p.run;
+    if (t0 >= p.L) return;
+    const int64_t t1 = min(p.L, t0 + p.run);
+    float wr[CPT][kConvMax], cb[CPT];
+    conv_taps<CPT>(p, d0, wr, cb);
+    // xs[j] holds x_{t0-1-j} before the first shift (zero before the sequence)
+    float xs[kConvMax][CPT];
 #pragma unroll
     for (int j = 0; j < kConvMax; ++j) {
-        const int64_t s = t0 - 1 - j;        // xs after the shift at t0 holds x_{t0-1-j} in slot j+1
-        xs[j] = (j + 1 < W && s >= 0) ? conv_ld<T>(p.x, (row + s) * p.dim + d) : 0.0f;
-        ds[j] = 0.0f;
-        gw[j] = 0.0f;
-    }
-    float gb = 0.0f;
-    for (int64_t t = t0; t < tend; ++t) {
-        // shift the windows by one token
+        const int64_t s = t0 - 1 - j;
+        if (j + 1 < p.W && s >= 0) {
+            conv_ld_piece<T, CPT>(p.x, (row + s) * p.dim + d0, xs[j]);
+        } else {
 #pragma unroll
-        for (int j = kConvMax - 1; j > 0; --j) {
-            xs[j] = xs[j - 1];
-            ds[j] = ds[j - 1];
+            for (int c = 0; c < CPT; ++c) xs[j][c] = 0.0f;
         }
-        const int64_t i = (row + t) * p.dim + d;
-        xs[0] = conv_ld<T>(p.x, i);
-        float pre = cb;
+    }
+#pragma unroll 4
+    for (int64_t t = t0; t < t1; ++t) {
 #pragma unroll
-        for (int k = 0; k < kConvMax; ++k)
-            if (k < W) pre = fmaf(w[k], xs[W - 1 - k], pre);
-        const float sg = 1.0f / (1.0f + __expf(-pre));
-        ds[0] = p.du[i] * sg * (1.0f + pre * (1.0f - sg));
+        for (int j = kConvMax - 1; j > 0; --j)
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) xs[j][c] = xs[j - 1][c];
+        const int64_t i = (row + t) * p.dim + d0;
+        conv_ld_piece<T, CPT>(p.x, i, xs[0]);
+        float u[CPT];
+        conv_pre<CPT>(wr, cb, xs, p.W, u);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) u[c] = silu(u[c]);
+        conv_st_piece<float, CPT>(p.u, i, u);
+    }
+}
+
+template <typename T, int CPT>
+__global__ __launch_bounds__(256) void conv_bwd_kernel(const ConvParams p) {
+    const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * CPT;
+    if (d0 >= p.dim) return;
+    const int blk = blockIdx.y;
+    const int b = blockIdx.z;
+    const int W = p.W;
+    float wr[CPT][kConvMax], cb[CPT];
+    conv_taps<CPT>(p, d0, wr, cb);
+    const int64_t t0 = (int64_t)blk * kConvBlock;
+    const int64_t t1 = min(p.L, t0 + kConvBlock);
+    const int64_t row = (int64_t)b * p.L;
+    // xs[j]: x_{t-j}, ds[j]: dpre_{t-j} (zero outside the sequence)
+    float xs[kConvMax][CPT], ds[kConvMax][CPT], gw[CPT][kConvMax], gb[CPT];
+#pragma unroll
+    for (int j = 0; j < kConvMax; ++j) {
+        const int64_t s = t0 - 1 - j;        // slot j + 1 after the shift at t0
+        if (j + 1 < W && s >= 0) {
+            conv_ld_piece<T, CPT>(p.x, (row + s) * p.dim + d0, xs[j]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) xs[j][c] = 0.0f;
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            ds[j][c] = 0.0f;
+            gw[c][j] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) gb[c] = 0.0f;
+    // dx_s = sum_{j < W} wr[j] dpre_{s+j}: emitted at t = s + kConvMax - 1, when
+    // ds[kConvMax-1-j] holds dpre_{s+j}; the walk runs kConvMax - 1 tokens past
+    // the block, with zero x and dpre past the sequence
+    auto step = [&](int64_t t, auto load) {
+#pragma unroll
+        for (int j = kConvMax - 1; j > 0; --j)
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                xs[j][c] = xs[j - 1][c];
+                ds[j][c] = ds[j - 1][c];
+            }
+        if constexpr (decltype(load)::value) {
+            const int64_t i = (row + t) * p.dim + d0;
+            float du[CPT], pre[CPT];
+            conv_ld_piece<T, CPT>(p.x, i, xs[0]);
+            conv_ld_f32<CPT>(p.du, i, du);
+            conv_pre<CPT>(wr, cb, xs, W, pre);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const float sg = 1.0f / (1.0f + __expf(-pre[c]));
+                ds[0][c] = du[c] * sg * (1.0f + pre[c] * (1.0f - sg));
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) xs[0][c] = ds[0][c] = 0.0f;
+        }
         if (t < t1) {
-            gb += ds[0];
 #pragma unroll
-            for (int k = 0; k < kConvMax; ++k)
-                if (k < W) gw[k] = fmaf(ds[0], xs[W - 1 - k], gw[k]);
-        }
-        // dx of token t-(W-1), whose last contribution is dpre_t
-        const int64_t s = t - (W - 1);
-        if (s >= t0 && s < t1) {
-            float g = 0.0f;
+            for (int c = 0; c < CPT; ++c) {
+                gb[c] += ds[0][c];
 #pragma unroll
-            for (int k = 0; k < kConvMax; ++k)
-                if (k < W) g = fmaf(w[k], ds[k], g);     // dpre_{s+(W-1)-k} = ds[k]
-            conv_st<T>(p.dx, (row + s) * p.dim + d, g);
+                for (int j = 0; j < kConvMax; ++j)
+                    if (j < W) gw[c][j] = fmaf(ds[0][c], xs[j][c], gw[c][j]);
+            }
         }
+        const int64_t s = t - (kConvMax - 1);
+        if (s >= t0) {
+            float g[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kConvMax; ++j)
+                    if (j < W) acc = fmaf(wr[c][j], ds[kConvMax - 1 - j][c], acc);
+                g[c] = acc;
+            }
+            conv_st_piece<T, CPT>(p.dx, (row + s) * p.dim + d0, g);
+        }
+    };
+    const int64_t tw = t1 + kConvMax - 1;        // end of the walk
+    const int64_t tl = min(p.L, tw);             // end of the tokens that exist
+    int64_t t = t0;
+#pragma unroll 4
+    for (; t < tl; ++t) step(t, std::true_type{});
+    for (; t < tw; ++t) step(t, std::false_type{});
+    // per-block partials: dw[k] of the lag j = W - 1 - k
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        float *pw = p.part_w + (((int64_t)b * p.nblk + blk) * p.dim + d0 + c) * W;
+#pragma unroll
+        for (int j = 0; j < kConvMax; ++j)
+            if (j < W) pw[W - 1 - j] = gw[c][j];
+        p.part_b[((int64_t)b * p.nblk + blk) * p.dim + d0 + c] = gb[c];
     }
-    // the block's last tokens when the sequence ends inside the window: dpre
-    // past the end is zero
-    for (int64_t s = max(t0, tend - (W - 1)); s < t1; ++s) {
-        const int64_t lag = tend - 1 - s;        // dpre_{s+m} sits in ds[lag - m] for s + m <= tend - 1
-        float g = 0.0f;
-#pragma unroll
-        for (int k = 0; k < kConvMax; ++k) {
-            const int64_t m = (W - 1) - k;       // dpre_{s+m}
-            if (k < W && m <= lag) g = fmaf(w[k], ds[lag - m], g);
-        }
-        conv_st<T>(p.dx, (row + s) * p.dim + d, g);
-    }
-    float *pw = p.part_w + (((int64_t)b * p.nblk + blk) * p.dim + d) * W;
-#pragma unroll
-    for (int k = 0; k < kConvMax; ++k)
-        if (k < W) pw[k] = gw[k];
-    p.part_b[((int64_t)b * p.nblk + blk) * p.dim + d] = gb;
 }
 
 __global__ __launch_bounds__(256) void conv_reduce_kernel(const ConvParams p) {
@@ -172,12 +287,14 @@ __global__ __launch_bounds__(256) void conv_reduce_kernel(const ConvParams p) {
     if (i < nw) {
         float acc = 0.0f;
         for (int b = 0; b < p.batch; ++b)
+#pragma unroll 8
             for (int k = 0; k < p.nblk; ++k) acc += p.part_w[((int64_t)b * p.nblk + k) * nw + i];
         p.dw[i] = acc;
     } else if (i < nw + p.dim && p.db != nullptr) {
         const int64_t d = i - nw;
         float acc = 0.0f;
         for (int b = 0; b < p.batch; ++b)
+#pragma unroll 8
             for (int k = 0; k < p.nblk; ++k) acc += p.part_b[((int64_t)b * p.nblk + k) * p.dim + d];
         p.db[d] = acc;
     }
@@ -757,6 +874,9 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     // caller's u holds x and its du receives the gradient of x
     const void *x_in = u;
     void *dx_out = du;
+    // channels per thread of the convolution kernels: 4-channel pieces when
+    // they are whole and aligned (the workspace's u and du always are)
+    const int cpt = (d.dim % 4 == 0 && aligned(x_in, 4 * es) && aligned(dx_out, 4 * es)) ? 4 : 1;
     ConvParams cp{};
     if (cw > 0) {
         cp.x = x_in;
@@ -774,12 +894,22 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
         cp.dim = (int)d.dim;
         cp.W = cw;
         cp.nblk = wl.nblk;
-        const int64_t n = tok;
-        if ((n + 255) / 256 > INT32_MAX) return SSM_ERR_SHAPE;
-        if (d.dtype == SSM_BF16)
-            hipLaunchKernelGGL(conv_silu_kernel<uint16_t>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, cp);
-        else
-            hipLaunchKernelGGL(conv_silu_kernel<float>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, cp);
+        // runs of at least 64 tokens, at most 65535 of them per batch row
+        const int64_t runs = std::min<int64_t>((d.seqlen + 63) / 64, 65535);
+        cp.run = (int)((d.seqlen + runs - 1) / runs);
+        if (d.batch > 65535) return SSM_ERR_SHAPE;
+        const dim3 grid((unsigned)((d.dim / cpt + 255) / 256), (unsigned)runs, (unsigned)d.batch);
+        if (d.dtype == SSM_BF16) {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 4>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 1>), grid, dim3(256), 0, stream, cp);
+        } else {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_silu_kernel<float, 4>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_silu_kernel<float, 1>), grid, dim3(256), 0, stream, cp);
+        }
         if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
     }
     const bool vec = (d.dim % 4 == 0) && aligned(u, 4 * es) && aligned(delta, 4 * es) && (!z || aligned(z, 4 * es)) &&
@@ -870,11 +1000,18 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     // 4. the convolution prologue: dx, and the sums of the tap and bias gradients
     if (cw > 0) {
         if (wl.nblk > 65535 || d.batch > 65535) return SSM_ERR_SHAPE;
-        const dim3 grid((unsigned)((d.dim + 255) / 256), (unsigned)wl.nblk, (unsigned)d.batch);
-        if (d.dtype == SSM_BF16)
-            hipLaunchKernelGGL(conv_bwd_kernel<uint16_t>, grid, dim3(256), 0, stream, cp);
-        else
-            hipLaunchKernelGGL(conv_bwd_kernel<float>, grid, dim3(256), 0, stream, cp);
+        const dim3 grid((unsigned)((d.dim / cpt + 255) / 256), (unsigned)wl.nblk, (unsigned)d.batch);
+        if (d.dtype == SSM_BF16) {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_bwd_kernel<uint16_t, 4>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_bwd_kernel<uint16_t, 1>), grid, dim3(256), 0, stream, cp);
+        } else {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_bwd_kernel<float, 4>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_bwd_kernel<float, 1>), grid, dim3(256), 0, stream, cp);
+        }
         const int64_t nr = (int64_t)d.dim * cw + d.dim;
         hipLaunchKernelGGL(conv_reduce_kernel, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, stream, cp);
         if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;

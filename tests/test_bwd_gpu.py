@@ -228,6 +228,20 @@ def test_bwd_conv_prologue(env, dtype, disc, W):
     compare_all(x, got, ref_bwd(x, g, disc, **conv), "conv%d" % W, keys=CONV_GRADS)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("W", [2, 4])
+def test_bwd_conv_four_channel_pieces(env, dtype, W):
+    """dim 136 (a multiple of 4): the prologue kernels move 4-channel pieces;
+    L 600 gives the forward-u kernel several runs and the backward three
+    256-token blocks with a ragged last one."""
+    torch, ssm = env
+    x, g = make_case("mamba130m", dtype, seed=60 + W, batch=2, seqlen=600, dim=136, dstate=16)
+    conv = si.conv_inputs(136, W, seed=60 + W)
+    say("bwd %s with the width-%d conv prologue, 4-channel pieces" % (dtype, W))
+    got = run_bwd_conv(ssm, torch, x, g, "euler", conv)
+    compare_all(x, got, ref_bwd(x, g, "euler", **conv), "conv%d/4" % W, keys=CONV_GRADS)
+
+
 def test_bwd_conv_with_softplus_step(env):
     torch, ssm = env
     x, g = make_case("mamba130m", "bf16", seed=48, batch=2, seqlen=129, dim=136, dstate=16)
