@@ -104,44 +104,34 @@ namespace ssm_detail {
 namespace {
 
 // Sums of four values a, b, c, d over the 64 lanes of the wave, as a
-// transposing reduction: two levels of DPP quad permutes, each keeping half of
-// the values per lane (odd lanes keep c and d, then lanes 2 and 3 of a quad
-// keep the b/d sums), leave every lane with one value summed over its quad
-// (lane 0 of a quad: a, 1: c, 2: b, 3: d); row shifts by 4 and 8 add the
-// quads of a row into lanes 12..15; two lane swaps between copies of the
-// value (v_permlane16_swap: the odd rows of one copy with the even rows of
-// the other; v_permlane32_swap: the upper half of one with the lower half of
-// the other) add the rows without a trip through LDS. The sums end in lanes
-// 12 + 16 k (a), 13 + 16 k (c), 14 + 16 k (b) and 15 + 16 k (d) of every
-// row k. Lane masks: m1 = odd
-// lanes, m2 = lanes with bit 1 set. The s_nops give every DPP read the two
-// wait states it needs after the write it depends on.
+// transposing reduction in which gfx950's lane swaps do the exchanges:
+//  * v_permlane32_swap of (a, c) and of (b, d), then an add: the lower half of
+//    the wave holds a (b) summed over both halves, the upper half c (d);
+//  * v_permlane16_swap of those two, then an add: row k of the wave (16 lanes)
+//    holds value k (a, b, c, d) summed over all four rows;
+//  * an inclusive scan inside each row (DPP row shifts by 1, 2, 4, 8) leaves
+//    the row's total in its last lane.
+// The sums end in lanes 15 (a), 31 (b), 47 (c) and 63 (d): 10 VALU
+// instructions, no LDS. The s_nops give every DPP read the two wait states
+// it needs after the write it depends on.
 __device__ __forceinline__ float wave_sum4_transposed(float a, float b, float c, float d) {
-    const uint64_t m1 = 0xAAAAAAAAAAAAAAAAull, m2 = 0xCCCCCCCCCCCCCCCCull;
-    float r1, k1, r2, k2, p, q, s;
+    const auto ac = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(c), false, false);
+    const auto bd = __builtin_amdgcn_permlane32_swap(__float_as_uint(b), __float_as_uint(d), false, false);
+    const float x = __uint_as_float(ac[0]) + __uint_as_float(ac[1]);   // lower half: a, upper half: c
+    const float y = __uint_as_float(bd[0]) + __uint_as_float(bd[1]);   // lower half: b, upper half: d
+    const auto xy = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    float s = __uint_as_float(xy[0]) + __uint_as_float(xy[1]);          // row k: value k
     asm volatile(
-        "v_cndmask_b32 %[r1], %[c], %[a], %[m1]\n\t"      // r1 = odd ? a : c   (sent to the partner)
-        "v_cndmask_b32 %[k1], %[a], %[c], %[m1]\n\t"      // k1 = odd ? c : a   (kept)
-        "v_cndmask_b32 %[r2], %[d], %[b], %[m1]\n\t"
-        "v_cndmask_b32 %[k2], %[b], %[d], %[m1]\n\t"
-        "s_nop 0\n\t"
-        "v_add_f32_dpp %[p], %[r1], %[k1] quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_add_f32_dpp %[q], %[r2], %[k2] quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_cndmask_b32 %[r1], %[q], %[p], %[m2]\n\t"      // lanes 2, 3 send p, keep q
-        "v_cndmask_b32 %[k1], %[p], %[q], %[m2]\n\t"
         "s_nop 1\n\t"
-        "v_add_f32_dpp %[s], %[r1], %[k1] quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %[s], %[s], %[s] row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %[s], %[s], %[s] row_shr:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
         "s_nop 1\n\t"
         "v_add_f32_dpp %[s], %[s], %[s] row_shr:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
         "s_nop 1\n\t"
         "v_add_f32_dpp %[s], %[s], %[s] row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        : [r1] "=&v"(r1), [k1] "=&v"(k1), [r2] "=&v"(r2), [k2] "=&v"(k2), [p] "=&v"(p), [q] "=&v"(q),
-          [s] "=&v"(s)
-        : [a] "v"(a), [b] "v"(b), [c] "v"(c), [d] "v"(d), [m1] "s"(m1), [m2] "s"(m2));
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    s = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+        : [s] "+v"(s));
+    return s;
 }
 
 template <int KV> struct BwdFloats;
@@ -555,14 +545,14 @@ struct BwdKernel {
                     mu[q] = a * l;
                 }
                 // the chunk's dB, dC terms of this wave's states, summed over the 64
-                // channels: values (dB q, dC q, dB q+1, dC q+1) land in lanes 60
-                // (dB q), 61 (dB q+1), 62 (dC q), 63 (dC q+1)
+                // channels: values (dB q, dC q, dB q+1, dC q+1) land in lanes 15
+                // (dB q), 31 (dC q), 47 (dB q+1), 63 (dC q+1)
 #pragma unroll
                 for (int i = 0; i < kRed; i += 4) {
                     const float sum = wave_sum4_transposed(vr[i], vr[i + 1], vr[i + 2], vr[i + 3]);
-                    const int j = lane - (kTile - 4);
-                    const int q = i / 2 + (j & 1);
-                    if (j >= 0 && q < NPW) s.red[t][w * NPW + q][j >> 1] = sum;
+                    const int v = lane >> 4;
+                    const int q = i / 2 + (v >> 1);
+                    if ((lane & 15) == 15 && q < NPW) s.red[t][w * NPW + q][v & 1] = sum;
                 }
                 s.pl[0][w][t][lane] = pU;
                 s.pl[1][w][t][lane] = pD;
