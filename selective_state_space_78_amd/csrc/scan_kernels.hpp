@@ -133,6 +133,8 @@ struct ScanParams {
     int seg_len, nseg;
     int ntiles;
     int vec;              // u, delta, z, y move 4 channels per aligned access
+    int u_f32;            // u is fp32 whatever T is (the backward's checkpoint pass on the
+                          // convolution prologue's materialised output; one segment only)
 };
 
 struct Plan {
@@ -257,7 +259,7 @@ enum ScanMode { kModeMain = 0, kModeAggregate = 1, kModeCheckpoint = 2 };
 // FEAT: the step and input prologue (delta bias, softplus, convolution) are
 // compiled in; without it the kernel carries none of their state (their
 // uniform values alone pushed the scalar registers into spills).
-template <typename T, int NPW, int G, int TC, bool ZOH, int MODE, bool FEAT>
+template <typename T, int NPW, int G, int TC, bool ZOH, int MODE, bool FEAT, bool UF = false>
 struct ScanKernel {
     // main: y and h_last; aggregate: each segment's map h -> P h + H;
     // checkpoint: the state at the start of every chunk (for the backward)
@@ -276,6 +278,8 @@ struct ScanKernel {
     static_assert(kThreads % kRowPieces == 0, "a thread keeps the same channels in every piece");
     static_assert(TC <= kPadRows, "spare rows of the widened B and C");
     typedef typename Words<kWords>::type Raw;
+    // a piece of u: T words, or kV fp32 words when u is fp32 (UF)
+    typedef typename Words<UF ? kV : kWords>::type URaw;
     typedef typename FloatsOf<kV>::type VecF;
 
     // LDS: the staged chunk as (delta, delta*u) pairs (u instead of delta*u
@@ -290,7 +294,8 @@ struct ScanKernel {
     static_assert(sizeof(Smem) <= 81920, "two workgroups per CU in 160 KiB of LDS");
 
     struct Prefetch {
-        Raw u[kPPT], dt[kPPT], z[kPPT];
+        URaw u[kPPT];
+        Raw dt[kPPT], z[kPPT];
         Raw xh[kPPT][FEAT ? kConvMax - 1 : 1];   // with the convolution prologue: x of the rows t-1, t-2, t-3
     };
 
@@ -322,6 +327,25 @@ struct ScanKernel {
         return r;
     }
 
+    // Element-wise load of one fp32 piece of u (UF), zero past dim.
+    __device__ static URaw gather_f32(const float *src, int c0, int dim) {
+        uint32_t w[kV];
+#pragma unroll
+        for (int i = 0; i < kV; ++i) w[i] = c0 + i < dim ? __float_as_uint(src[i]) : 0u;
+        URaw r;
+        make_words(r, w);
+        return r;
+    }
+
+    __device__ static void unpack_u(const URaw &r, float (&v)[kV]) {
+        if constexpr (UF) {
+#pragma unroll
+            for (int i = 0; i < kV; ++i) v[i] = __uint_as_float(word<kV>(r, i));
+        } else {
+            unpack(r, v);
+        }
+    }
+
     __device__ static void unpack(const Raw &r, float (&v)[kV]) {
 #pragma unroll
         for (int i = 0; i < kWords; ++i) {
@@ -351,11 +375,17 @@ struct ScanKernel {
             if (!piece_in_chunk(j) || row >= tval || !colv) continue;
             const uint32_t off = (uint32_t)row * (uint32_t)p.dim + (uint32_t)col;
             if (p.vec) {
-                pf.u[j] = *reinterpret_cast<const Raw *>(u + off);
+                if constexpr (UF)
+                    pf.u[j] = *reinterpret_cast<const URaw *>(static_cast<const float *>(p.u) + base + off);
+                else
+                    pf.u[j] = *reinterpret_cast<const Raw *>(u + off);
                 pf.dt[j] = *reinterpret_cast<const Raw *>(dt + off);
                 if (gate) pf.z[j] = *reinterpret_cast<const Raw *>(z + off);
             } else {
-                pf.u[j] = gather(u + off, d0 + col, p.dim, true);
+                if constexpr (UF)
+                    pf.u[j] = gather_f32(static_cast<const float *>(p.u) + base + off, d0 + col, p.dim);
+                else
+                    pf.u[j] = gather(u + off, d0 + col, p.dim, true);
                 pf.dt[j] = gather(dt + off, d0 + col, p.dim, true);
                 pf.z[j] = gather(z + off, d0 + col, p.dim, gate);
             }
@@ -421,7 +451,7 @@ struct ScanKernel {
             float4 *dst = reinterpret_cast<float4 *>(&dx[row][col]);
             if (row < tval && colv) {
                 float u[kV], d[kV];
-                unpack(pf.u[j], u);
+                unpack_u(pf.u[j], u);
                 unpack(pf.dt[j], d);
                 if (FEAT && cw) conv_silu(pf, j, u, cw, wk, cbk);
                 if (FEAT && prep) {
@@ -747,9 +777,9 @@ struct ScanKernel {
     }
 };
 
-template <typename T, int NPW, int G, int TC, bool ZOH, int MODE, bool FEAT>
+template <typename T, int NPW, int G, int TC, bool ZOH, int MODE, bool FEAT, bool UF = false>
 __global__ __launch_bounds__(kTile * G) void scan_kernel(const ScanParams p) {
-    ScanKernel<T, NPW, G, TC, ZOH, MODE, FEAT>::run(p);
+    ScanKernel<T, NPW, G, TC, ZOH, MODE, FEAT, UF>::run(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -843,6 +873,15 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
     }
     if constexpr (CK) {
         if (p.ckpt != nullptr) {
+            if constexpr (sizeof(T) == 2) {
+                if (p.u_f32) {
+                    // fp32 u with bf16 tensors: the aggregate pass has no such variant
+                    if (nblocks_agg > 0) return hipErrorInvalidValue;
+                    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeCheckpoint, FEAT, true>), dim3(nblocks_main),
+                                       dim3(kTile * G), 0, st, p);
+                    return hipGetLastError();
+                }
+            }
             hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeCheckpoint, FEAT>), dim3(nblocks_main), dim3(kTile * G),
                                0, st, p);
             return hipGetLastError();

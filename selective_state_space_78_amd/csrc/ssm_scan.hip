@@ -915,11 +915,18 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     const bool vec = (d.dim % 4 == 0) && aligned(u, 4 * es) && aligned(delta, 4 * es) && (!z || aligned(z, 4 * es)) &&
                      aligned(dy, 4 * es) && aligned(du, 4 * es) && aligned(ddelta, 4 * es) &&
                      (!z || aligned(dz, 4 * es));
-    // 1. checkpoints: the forward scan in its checkpoint mode (segment-parallel);
-    // with the prologue it forms u from x itself, as the forward does
+    // 1. checkpoints: the forward scan in its checkpoint mode (segment-parallel).
+    // With the prologue and one segment it reads the u materialised above (fp32);
+    // with several segments it forms u from x itself, as the forward does
     ScanParams p{};
     p.u = u; p.delta = delta; p.z = z; p.B = B; p.C = C;
     p.conv_w = cw; p.conv_weight = d.conv_weight; p.conv_bias = d.conv_bias;
+    if (cw > 0 && wl.pl.S == 1) {
+        p.u = cp.u;
+        p.u_f32 = d.dtype == SSM_BF16;
+        p.conv_w = 0;
+        p.conv_weight = p.conv_bias = nullptr;
+    }
     p.delta_bias = dbias; p.delta_softplus = d.delta_softplus;
     p.A = A; p.D = D; p.h0 = h0;
     p.L = d.seqlen;
