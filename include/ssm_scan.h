@@ -178,8 +178,10 @@ int ssm_scan_plan(const ssm_scan_desc *desc, ssm_scan_tuning *out);
  *     dpre_t = g_t silu'(pre_t),  dx_s = sum_k w[k] dpre_{s+(W-1)-k},
  *     dconv_weight[k] = sum_{b,t} dpre_t x_{t-(W-1)+k},  dconv_bias = sum_{b,t} dpre_t
  * (the chain rule through youngju.dev MambaBlock.forward's x_conv =
- * silu(conv1d(x))). The checkpoint pass forms u from x as the forward does;
- * the reverse pass reads u and writes its gradient in fp32 in the workspace.
+ * silu(conv1d(x))). u is formed from x once, in fp32 in the workspace; the
+ * recomputation reads it (or, when the sequence is split into segments, forms
+ * it from x again as the forward does), and the reverse pass writes its
+ * gradient in fp32 in the workspace.
  *   workspace     at least ssm_scan_bwd_workspace_size(desc) bytes, 256-byte
  *                 aligned; contents on entry do not matter.
  * Results do not depend on timing: every sum over channels, batch rows or
