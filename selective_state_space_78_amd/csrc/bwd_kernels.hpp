@@ -244,8 +244,8 @@ struct BwdKernel {
         }
     }
 
-    __device__ static void load(const BwdParams &p, Prefetch &pf, int64_t base, int tval, int col, int d0,
-                                bool colv) {
+    template <typename PP>
+    __device__ static void load(const PP &p, Prefetch &pf, int64_t base, int tval, int col, int d0, bool colv) {
         const T *u = static_cast<const T *>(p.u) + base;
         const T *dt = static_cast<const T *>(p.delta) + base;
         const T *z = static_cast<const T *>(p.z) + base;
@@ -368,6 +368,17 @@ struct BwdKernel {
         }
     }
 
+    // The same kernel arguments through an address the compiler cannot see
+    // through: what is read from it is loaded again where it is used (one
+    // scalar load from the argument segment) instead of being held in scalar
+    // registers across the chunk loop, which would spill them.
+    typedef const __attribute__((address_space(4))) BwdParams KernArgs;
+    __device__ static KernArgs &fresh(const BwdParams &) {
+        KernArgs *q = (KernArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(q));
+        return *q;
+    }
+
     __device__ static void run(const BwdParams &p) {
         __shared__ Smem s;
         // workgroup -> (batch row, tile); the tiles of a batch row run on one XCD
@@ -421,7 +432,7 @@ struct BwdKernel {
         cword *bw0 = (cword *)(p.Bf) + ((int64_t)b * G + w) * Lp * NPW;
         cword *cw0 = (cword *)(p.Cf) + ((int64_t)b * G + w) * Lp * NPW;
         auto ckpt_at = [&](int c, int q) {
-            return p.ckpt[(((int64_t)b * nck + c) * kNP + w * NPW + q) * p.dim + dc];
+            return fresh(p).ckpt[(((int64_t)b * nck + c) * kNP + w * NPW + q) * p.dim + dc];
         };
 
         Prefetch pf;
@@ -443,7 +454,7 @@ struct BwdKernel {
 #pragma unroll
             for (int q = 0; q < NPW; ++q) hstart[q] = hnext[q];
             if (c > 0) {
-                load(p, pf, (row0 + (int64_t)(c - 1) * TC) * p.dim + d0, rows_of(c - 1), col, d0, colv);
+                load(fresh(p), pf, (row0 + (int64_t)(c - 1) * TC) * p.dim + d0, rows_of(c - 1), col, d0, colv);
 #pragma unroll
                 for (int q = 0; q < NPW; ++q) hnext[q] = ckpt_at(c - 1, q);
             }
@@ -494,7 +505,7 @@ struct BwdKernel {
                 plane_sum(s, 0, row, col, acc);
 #pragma unroll
                 for (int e = 0; e < kV; ++e) o[e] = held.gz[j][e] * (acc[e] + Dk[e] * held.u[j][e]);
-                T *dst = static_cast<T *>(p.dz) + (row0 + t0 + row) * p.dim + d0 + col;
+                T *dst = static_cast<T *>(fresh(p).dz) + (row0 + t0 + row) * p.dim + d0 + col;
                 store(dst, o, d0 + col, p.dim, p.vec);
             }
             __syncthreads();
@@ -515,8 +526,9 @@ struct BwdKernel {
                     const float cq = __uint_as_float(kPacked ? wb & 0xffff0000u : cw[t * NPW + q]);
                     const float a = kKeepA ? as[t][q] : __builtin_amdgcn_exp2f(v.x * A2[q]);
                     const float l = fmaf(cq, dsv, mu[q]);
+                    const float al = a * l;                 // the adjoint passed back to t - 1
                     const float hp = t > 0 ? hs[t - 1][q] : hstart[q];
-                    const float daa = l * hp * a;
+                    const float daa = al * hp;
                     pD = fmaf(daa, A[q], pD);
                     dA[q] = fmaf(daa, v.x, dA[q]);
                     float vb;
@@ -542,7 +554,7 @@ struct BwdKernel {
                     }
                     vr[2 * q] = vb;
                     vr[2 * q + 1] = dsv * hs[t][q];
-                    mu[q] = a * l;
+                    mu[q] = al;
                 }
                 // the chunk's dB, dC terms of this wave's states, summed over the 64
                 // channels: values (dB q, dC q, dB q+1, dC q+1) land in lanes 15
@@ -560,6 +572,7 @@ struct BwdKernel {
             __syncthreads();
 
             // 5. du, ddelta of this thread's pieces; the tile's dB, dC sums
+            KernArgs &po = fresh(p);
 #pragma unroll
             for (int j = 0; j < kPPT; ++j) {
                 const int row = piece_row(j);
@@ -580,17 +593,17 @@ struct BwdKernel {
                     dbacc[j][e] += od[e];
                 }
                 const int64_t off = (row0 + t0 + row) * p.dim + d0 + col;
-                if (p.du_f32 != nullptr) {
+                if (po.du_f32 != nullptr) {
 #pragma unroll
                     for (int e = 0; e < kV; ++e)
-                        if (d0 + col + e < p.dim) p.du_f32[off + e] = ou[e];
+                        if (d0 + col + e < p.dim) po.du_f32[off + e] = ou[e];
                 } else {
-                    store(static_cast<T *>(p.du) + off, ou, d0 + col, p.dim, p.vec);
+                    store(static_cast<T *>(po.du) + off, ou, d0 + col, p.dim, p.vec);
                 }
-                store(static_cast<T *>(p.ddelta) + off, od, d0 + col, p.dim, p.vec);
+                store(static_cast<T *>(po.ddelta) + off, od, d0 + col, p.dim, p.vec);
             }
             {
-                float *dst = p.part_bc + (((int64_t)b * p.ntiles + tile) * p.L + t0) * (kNP * 2);
+                float *dst = po.part_bc + (((int64_t)b * p.ntiles + tile) * p.L + t0) * (kNP * 2);
                 const float *src = &s.red[0][0][0];
                 for (int i = threadIdx.x; i < tval * kNP * 2; i += kThreads) dst[i] = src[i];
             }
