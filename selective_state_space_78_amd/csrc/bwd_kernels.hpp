@@ -155,6 +155,10 @@ struct BwdKernel {
     static constexpr bool kPacked = sizeof(T) == 2;
     static constexpr int kWPS = kPacked ? 1 : 2;
     static constexpr bool kKeepA = NPW == 1;
+    // the hold rule's phi(delta A) of the chunk, kept from the recomputation for
+    // the reverse step: the 8-wave hold-rule kernels run at 2 waves per SIMD
+    // and have the registers for it
+    static constexpr bool kKeepF = ZOH && G == 8;
     static constexpr int kRed = (2 * NPW + 3) / 4 * 4;             // reduced values per step, in 4s                        // keep the chunk's decays in registers
     typedef typename Words<kWords>::type Raw;
     typedef typename BwdFloats<kV>::type VecF;
@@ -465,6 +469,7 @@ struct BwdKernel {
             // 2. recompute the chunk's states of this wave; parts of s_t
             float hs[TC][NPW];
             float as[kKeepA ? TC : 1][NPW];
+            float fs[kKeepF ? TC : 1][NPW];
             {
                 float h[NPW];
 #pragma unroll
@@ -483,6 +488,7 @@ struct BwdKernel {
                             const float ph = expm1_over_x(v.x * A[q], a);
                             h[q] = fmaf(a, h[q], ph * (v.x * v.y * bq));
                             if constexpr (kKeepA) as[t][q] = a;
+                            if constexpr (kKeepF) fs[t][q] = ph;
                         } else {
                             const float a = __builtin_amdgcn_exp2f(v.x * A2[q]);
                             h[q] = fmaf(a, h[q], v.y * bq);
@@ -535,7 +541,7 @@ struct BwdKernel {
                     if constexpr (ZOH) {
                         // f = expm1(delta A)/A = delta phi(delta A)
                         const float xa = v.x * A[q];
-                        const float f = v.x * expm1_over_x(xa, a);
+                        const float f = v.x * (kKeepF ? fs[t][q] : expm1_over_x(xa, a));
                         // d f / d A = (delta a - f) / A, by its series near 0 (cancellation)
                         float dfdA;
                         if (fabsf(xa) < 0.125f)
