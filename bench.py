@@ -210,6 +210,43 @@ def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
+
+    # the training pair: a forward that keeps the checkpoints, then the
+    # backward that reads them, against the plain forward and backward
+    y = torch.empty_like(dev["u"])
+    hl = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device="cuda")
+    fws = torch.empty(max(ssm.ssm_scan_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, ssm.SSM_BF16,
+                                                      disc), 1), dtype=torch.uint8, device="cuda")
+
+    def fwd_plain():
+        ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"], y=y, h_last=hl,
+                         workspace=fws, disc=disc, **step_opts)
+
+    def fwd_save():
+        ssm.ssm_scan_fwd_save(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"], y=y,
+                              h_last=hl, workspace=ws, disc=disc, **step_opts)
+
+    def bwd_saved():
+        r = ssm.ssm_scan_bwd_saved(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dy, ws, D=dev["D"],
+                                   z=dev["z"], dh_last=dhl, out=out, disc=disc, **step_opts)
+        out.update(r)
+
+    def timed(fns):
+        for _ in range(warmup):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+        for e in evs:
+            e[0].record()
+            for f, ev in zip(fns, e[1:]):
+                f()
+                ev.record()
+        torch.cuda.synchronize()
+        return [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(len(fns))]
+
+    t_fp, t_bp = timed([fwd_plain, call])
+    t_fs, t_bs = timed([fwd_save, bwd_saved])
     return {
         "workload": "backward of the same scan: gradients of u (of x with the conv prologue), delta, A, B, C, D, z, "
                     "h0 from dy and dh_last",
@@ -217,6 +254,12 @@ def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_
         "Gtokens*ch/s": cfg.tokens_ch / (ms * 1e-3) / 1e9,
         "workspace_bytes": need,
         "calls": steps,
+        "training_step": {
+            "workload": "forward + backward of the layer: ssm_scan_fwd then ssm_scan_bwd, against "
+                        "ssm_scan_fwd_save (keeps the checkpoints) then ssm_scan_bwd_saved (reads them)",
+            "recompute_ms": {"fwd": t_fp, "bwd": t_bp, "total": t_fp + t_bp},
+            "saved_ms": {"fwd": t_fs, "bwd": t_bs, "total": t_fs + t_bs},
+        },
     }
 
 
@@ -415,6 +458,8 @@ def main():
             "frac": achieved_tops / VALU_PEAK_TOPS,
             "ops_per_token_ch": valu_ops_per_token_ch(cfg.dstate, cfg.gate),
             "mean_launch_ms": mean_launch_ms,
+            "median_launch_ms": per[len(per) // 2],
+            "min_launch_ms": per[0],
             "traffic": measured_traffic(args.workload, plan,
                                         args.disc == "euler" and not args.delta_softplus and not args.conv),
         },

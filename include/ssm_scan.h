@@ -198,6 +198,44 @@ int ssm_scan_bwd(const ssm_scan_desc *desc,
                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The forward and backward of one training step, sharing the recomputation
+ * the backward starts with. ssm_scan_fwd_save is ssm_scan_fwd (same arguments
+ * and results) run in the backward's launch shape, which also leaves in
+ * `workspace` what the backward would first recompute: the state
+ * at the start of every chunk of the sequence and the regrouped B and C (the
+ * intermediate states of doyouknow.kr "Mamba와 상태 공간 모델(SSM)의 부상 완벽
+ * 가이드" §3-3, kept at chunk granularity).
+ * ssm_scan_bwd_saved is ssm_scan_bwd without that recomputation; it reads
+ * them from the same workspace instead. Its gradients equal ssm_scan_bwd's
+ * (the checkpoints are the states the forward passes through). h_last equals
+ * ssm_scan_fwd's bit for bit; y may differ from it in the last bit where the
+ * backward's launch shape splits the states over another number of waves
+ * and so sums the readout in another order.
+ *
+ *   workspace  at least ssm_scan_bwd_workspace_size(desc) bytes, 256-byte
+ *              aligned, for both calls. ssm_scan_bwd_saved must receive the
+ *              workspace of an ssm_scan_fwd_save call with the same descriptor
+ *              and the same u, delta, A, B, C, h0 (and delta bias, convolution
+ *              taps), unmodified in between; nothing checks this, and other
+ *              contents give wrong gradients.
+ * Every other argument, condition and error is that of ssm_scan_fwd and
+ * ssm_scan_bwd. The caller owns the workspace and keeps it alive from the
+ * forward call until the backward call has completed on its stream.
+ */
+int ssm_scan_fwd_save(const ssm_scan_desc *desc,
+                      const void *u, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D, const void *z,
+                      const float *h0, void *y, float *h_last,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+int ssm_scan_bwd_saved(const ssm_scan_desc *desc,
+                       const void *u, const void *delta, const float *A,
+                       const void *B, const void *C, const float *D, const void *z,
+                       const float *h0, const void *dy, const float *dh_last,
+                       void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD,
+                       void *dz, float *dh0, float *ddelta_bias, float *dconv_weight, float *dconv_bias,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step: the recurrence for a single new token per sequence, with
  * the fixed-size state updated in place (itwiki "상태 공간 모델", "순환 형태와
  * 합성곱 형태": generation only updates h_t; ricepunchb "Mamba" §4.2: only the

@@ -26,7 +26,7 @@ _DISC = {"euler": SSM_DISC_EULER, "zoh": SSM_DISC_ZOH}
 # Every symbol include/ssm_scan.h declares.
 EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_workspace_size_tuned",
            "ssm_scan_fwd_tuned", "ssm_scan_plan", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd",
-           "ssm_state_update", "ssm_ssd_fwd", "ssm_status_string")
+           "ssm_scan_fwd_save", "ssm_scan_bwd_saved", "ssm_state_update", "ssm_ssd_fwd", "ssm_status_string")
 
 
 class ScanDesc(ctypes.Structure):
@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
             L.ssm_scan_bwd_workspace_size.argtypes = [pdesc]
             L.ssm_scan_bwd_workspace_size.restype = sz
             L.ssm_scan_bwd.argtypes = [pdesc] + [vp] * 21 + [vp, sz, vp]
+            L.ssm_scan_fwd_save.restype = ctypes.c_int
+            L.ssm_scan_fwd_save.argtypes = scan_args + [vp]
+            L.ssm_scan_bwd_saved.restype = ctypes.c_int
+            L.ssm_scan_bwd_saved.argtypes = [pdesc] + [vp] * 21 + [vp, sz, vp]
             L.ssm_scan_bwd.restype = ctypes.c_int
             L.ssm_state_update.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                            vp]
@@ -180,6 +184,24 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None
     ``conv_bias`` (dim,)), ``u`` holds x and the scan input is
     silu(causal depthwise conv1d(x) + bias), formed in the kernel.
     """
+    y, h_last, _ = _fwd(u, delta, A, B, C, D, z, h0, y, h_last, disc, workspace, tuning, stream, want_h_last,
+                        delta_bias, delta_softplus, conv_weight, conv_bias, save=False)
+    return y, h_last
+
+
+def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None,
+                      disc="euler", workspace=None, stream=None, want_h_last=True,
+                      delta_bias=None, delta_softplus=False, conv_weight=None, conv_bias=None):
+    """ssm_scan_fwd that also keeps the backward's checkpoints (the C call of
+    the same name). Returns (y, h_last, saved): ``saved`` is the workspace
+    (uint8, ssm_scan_bwd_workspace_size bytes; ``workspace`` if given) to pass
+    unchanged to ssm_scan_bwd_saved with the same inputs."""
+    return _fwd(u, delta, A, B, C, D, z, h0, y, h_last, disc, workspace, None, stream, want_h_last,
+                delta_bias, delta_softplus, conv_weight, conv_bias, save=True)
+
+
+def _fwd(u, delta, A, B, C, D, z, h0, y, h_last, disc, workspace, tuning, stream, want_h_last,
+         delta_bias, delta_softplus, conv_weight, conv_bias, save):
     import torch
     batch, L, dim = u.shape
     N = A.shape[1]
@@ -206,20 +228,29 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None
     _check(conv_bias, "conv_bias", (dim,), torch.float32, dev)
     desc = make_desc(batch, L, dim, N, code, disc, delta_bias, delta_softplus, conv_weight, conv_bias)
     L_ = lib()
-    need = (L_.ssm_scan_workspace_size(ctypes.byref(desc)) if tuning is None
-            else L_.ssm_scan_workspace_size_tuned(ctypes.byref(desc), _tuning(tuning)))
+    if save:
+        need = L_.ssm_scan_bwd_workspace_size(ctypes.byref(desc))
+    elif tuning is None:
+        need = L_.ssm_scan_workspace_size(ctypes.byref(desc))
+    else:
+        need = L_.ssm_scan_workspace_size_tuned(ctypes.byref(desc), _tuning(tuning))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(h0), _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes]
-    if tuning is None:
+    if save:
+        name = "ssm_scan_fwd_save"
+        rc = L_.ssm_scan_fwd_save(*args, _stream(stream, dev))
+    elif tuning is None:
+        name = "ssm_scan_fwd"
         rc = L_.ssm_scan_fwd(*args, _stream(stream, dev))
     else:
+        name = "ssm_scan_fwd_tuned"
         rc = L_.ssm_scan_fwd_tuned(*args, _tuning(tuning), _stream(stream, dev))
     if rc != 0:
-        raise SsmError(rc, "ssm_scan_fwd")
-    return y, h_last
+        raise SsmError(rc, name)
+    return y, h_last, workspace
 
 
 def ssm_scan_bwd_workspace_size(batch, L, dim, N, dtype_code, disc="euler", delta_bias=None,
@@ -228,9 +259,24 @@ def ssm_scan_bwd_workspace_size(batch, L, dim, N, dtype_code, disc="euler", delt
     return int(lib().ssm_scan_bwd_workspace_size(ctypes.byref(desc)))
 
 
+def ssm_scan_bwd_saved(u, delta, A, B, C, dy, saved, D=None, z=None, h0=None, dh_last=None, disc="euler",
+                       stream=None, want_dh0=True, out=None, delta_bias=None, delta_softplus=False,
+                       conv_weight=None, conv_bias=None):
+    """ssm_scan_bwd that reads the checkpoints an ssm_scan_fwd_save call with
+    the same inputs left in ``saved`` (its returned workspace) instead of
+    recomputing them (the C call of the same name). Arguments and results as
+    ssm_scan_bwd."""
+    if saved is None:
+        raise ValueError("ssm_scan_bwd_saved needs the workspace of an ssm_scan_fwd_save call")
+    return ssm_scan_bwd(u, delta, A, B, C, dy, D=D, z=z, h0=h0, dh_last=dh_last, disc=disc, workspace=saved,
+                        stream=stream, want_dh0=want_dh0, out=out, delta_bias=delta_bias,
+                        delta_softplus=delta_softplus, conv_weight=conv_weight, conv_bias=conv_bias,
+                        _saved=True)
+
+
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None, disc="euler",
                  workspace=None, stream=None, want_dh0=True, out=None, delta_bias=None, delta_softplus=False,
-                 conv_weight=None, conv_bias=None):
+                 conv_weight=None, conv_bias=None, _saved=False):
     """Backward of ssm_scan_fwd on device tensors.
 
     Inputs as ssm_scan_fwd, plus dy (batch, L, dim) of the input dtype and an
@@ -293,12 +339,13 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, h0=None, dh_last=None, d
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = L_.ssm_scan_bwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                         _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(du), _ptr(dde), _ptr(dA), _ptr(dB), _ptr(dC),
-                         _ptr(dD), _ptr(dz), _ptr(dh0), _ptr(ddb), _ptr(dcw), _ptr(dcb), _ptr(workspace), ws_bytes,
-                         _stream(stream, dev))
+    name = "ssm_scan_bwd_saved" if _saved else "ssm_scan_bwd"
+    rc = getattr(L_, name)(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                           _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(du), _ptr(dde), _ptr(dA), _ptr(dB), _ptr(dC),
+                           _ptr(dD), _ptr(dz), _ptr(dh0), _ptr(ddb), _ptr(dcw), _ptr(dcb), _ptr(workspace), ws_bytes,
+                           _stream(stream, dev))
     if rc != 0:
-        raise SsmError(rc, "ssm_scan_bwd")
+        raise SsmError(rc, name)
     return dict(du=du, ddelta=dde, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0, ddelta_bias=ddb,
                 dconv_weight=dcw, dconv_bias=dcb)
 

@@ -252,7 +252,7 @@ template <> struct FloatsOf<2> { typedef float2 type; };
 template <> struct FloatsOf<4> { typedef float4 type; };
 
 // What a pass of the scan kernel produces.
-enum ScanMode { kModeMain = 0, kModeAggregate = 1, kModeCheckpoint = 2 };
+enum ScanMode { kModeMain = 0, kModeAggregate = 1, kModeCheckpoint = 2, kModeMainCheckpoint = 3 };
 
 // FEAT: the step and input prologue (delta bias, softplus, convolution) are
 // compiled in; without it the kernel carries none of their state (their
@@ -260,8 +260,11 @@ enum ScanMode { kModeMain = 0, kModeAggregate = 1, kModeCheckpoint = 2 };
 template <typename T, int NPW, int G, int TC, bool ZOH, int MODE, bool FEAT, bool UF = false>
 struct ScanKernel {
     // main: y and h_last; aggregate: each segment's map h -> P h + H;
-    // checkpoint: the state at the start of every chunk (for the backward)
-    static constexpr bool AGG = MODE != kModeMain;            // no readout and no y
+    // checkpoint: the state at the start of every chunk (for the backward);
+    // main with checkpoints: both y, h_last and those states
+    static constexpr bool kMain = MODE == kModeMain || MODE == kModeMainCheckpoint;
+    static constexpr bool kCkpt = MODE == kModeCheckpoint || MODE == kModeMainCheckpoint;
+    static constexpr bool AGG = !kMain;                       // no readout and no y
     static constexpr bool kSum = MODE == kModeAggregate;
     static constexpr int kThreads = kTile * G;
     static constexpr int kNP = NPW * G;                       // padded state count
@@ -713,7 +716,7 @@ struct ScanKernel {
             if (k + 2 < nchunks) load_chunk(k + 2);
             const int tval = rows_of(k);
             const float2 (*dx)[kTile] = s.dx[P];
-            if constexpr (MODE == kModeCheckpoint) {
+            if constexpr (kCkpt) {
                 // the state before the chunk's first token
                 if (dval) {
                     const int64_t c = (t_begin + (int64_t)k * TC) / TC;
@@ -768,7 +771,7 @@ struct ScanKernel {
                 const int64_t o = (((int64_t)b * p.nseg + seg) * p.dim + d) * p.N + n;
                 p.agg_P[o] = __builtin_amdgcn_exp2f(l.A2[k] * l.dsum);
                 p.agg_H[o] = l.h[k];
-            } else if (MODE == kModeMain && p.h_last != nullptr && seg == p.nseg - 1) {
+            } else if (kMain && p.h_last != nullptr && seg == p.nseg - 1) {
                 p.h_last[((int64_t)b * p.dim + d) * p.N + n] = l.h[k];
             }
         }
@@ -870,6 +873,12 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if constexpr (CK) {
+        if (p.ckpt != nullptr && p.y != nullptr) {
+            // the forward that also keeps the backward's checkpoints
+            hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMainCheckpoint, FEAT>), dim3(nblocks_main),
+                               dim3(kTile * G), 0, st, p);
+            return hipGetLastError();
+        }
         if (p.ckpt != nullptr) {
             if constexpr (sizeof(T) == 2) {
                 if (p.u_f32) {

@@ -647,10 +647,18 @@ int validate_desc(const ssm_scan_desc *d) {
     return SSM_OK;
 }
 
+// What a forward that keeps the backward's checkpoints adds: the backward's
+// workspace size, and where in it the checkpoints go (the forward's own
+// workspace, regrouped B and C and segment arrays, comes first in both)
+struct SaveForBwd {
+    size_t need, ckpt;
+    int nck;
+};
+
 int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A,
               const void *B, const void *C, const float *D, const void *z, const float *h0,
               void *y, float *h_last, void *workspace, size_t workspace_bytes,
-              const ssm_scan_tuning *tuning, hipStream_t stream) {
+              const ssm_scan_tuning *tuning, hipStream_t stream, const SaveForBwd *save = nullptr) {
     if (int rc = validate_desc(desc); rc != SSM_OK) return rc;
     const ssm_scan_desc d = *desc;
     if (d.batch == 0 || d.dim == 0) return SSM_OK;
@@ -674,7 +682,7 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
         (h_last && !aligned(h_last, 4)) || (workspace && !aligned(workspace, 256)))
         return SSM_ERR_ALIGN;
 
-    const size_t need = workspace_bytes_for(d, pl);
+    const size_t need = save ? save->need : workspace_bytes_for(d, pl);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
 
     const Range r_y = range_of(y, d.seqlen > 0 ? tok * es : 0);
@@ -725,6 +733,10 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
             p.agg_P = reinterpret_cast<float *>(ws + wl.agg_p);
             p.agg_H = reinterpret_cast<float *>(ws + wl.agg_h);
             p.seg_h = reinterpret_cast<float *>(ws + wl.seg_h);
+        }
+        if (save) {
+            p.ckpt = reinterpret_cast<float *>(ws + save->ckpt);
+            p.nck = save->nck;
         }
     }
     const int64_t blocks_per_seg = (int64_t)p.ntiles * d.batch;
@@ -790,7 +802,7 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
              const void *C, const float *D, const void *z, const float *h0, const void *dy, const float *dh_last,
              void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz, float *dh0,
              float *ddelta_bias, float *dconv_weight, float *dconv_bias, void *workspace, size_t workspace_bytes,
-             hipStream_t stream) {
+             hipStream_t stream, bool saved = false) {
     if (int rc = validate_desc(desc); rc != SSM_OK) return rc;
     const ssm_scan_desc d = *desc;
     const int cw = d.conv_width;
@@ -954,14 +966,18 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     const int64_t na = wl.pl.S > 1 ? blocks_per_seg * (wl.pl.S - 1) : 0;
     if (nm > INT32_MAX) return SSM_ERR_SHAPE;
     const bool zoh = d.disc == SSM_DISC_ZOH;
-    hipError_t e;
-    if (d.dtype == SSM_BF16)
-        e = zoh ? launch_scan_bf16_zoh(wl.pl, p, (int)nm, (int)na, stream)
-                : launch_scan_bf16_euler(wl.pl, p, (int)nm, (int)na, stream);
-    else
-        e = zoh ? launch_scan_f32_zoh(wl.pl, p, (int)nm, (int)na, stream)
-                : launch_scan_f32_euler(wl.pl, p, (int)nm, (int)na, stream);
-    if (e != hipSuccess) return SSM_ERR_HIP;
+    hipError_t e = hipSuccess;
+    // (a forward that kept the checkpoints has left them, and the regrouped B
+    // and C, in this workspace)
+    if (!saved) {
+        if (d.dtype == SSM_BF16)
+            e = zoh ? launch_scan_bf16_zoh(wl.pl, p, (int)nm, (int)na, stream)
+                    : launch_scan_bf16_euler(wl.pl, p, (int)nm, (int)na, stream);
+        else
+            e = zoh ? launch_scan_f32_zoh(wl.pl, p, (int)nm, (int)na, stream)
+                    : launch_scan_f32_euler(wl.pl, p, (int)nm, (int)na, stream);
+        if (e != hipSuccess) return SSM_ERR_HIP;
+    }
 
     // 2. the reverse pass
     BwdParams bp{};
@@ -1065,6 +1081,20 @@ extern "C" int ssm_scan_fwd(const ssm_scan_desc *desc, const void *u, const void
     return scan_impl(desc, u, delta, A, B, C, D, z, h0, y, h_last, workspace, workspace_bytes, nullptr, stream);
 }
 
+extern "C" int ssm_scan_fwd_save(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A,
+                                 const void *B, const void *C, const float *D, const void *z, const float *h0,
+                                 void *y, float *h_last, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    if (int rc = validate_desc(desc); rc != SSM_OK) return rc;
+    if (desc->batch == 0 || desc->dim == 0 || desc->seqlen == 0)   // nothing for a backward to reuse
+        return scan_impl(desc, u, delta, A, B, C, D, z, h0, y, h_last, workspace, workspace_bytes, nullptr, stream);
+    // the backward's launch shape, so that its checkpoints are the ones this pass passes through
+    const BwdLayout wl = bwd_layout(*desc);
+    const ssm_scan_tuning t{wl.sh.G, 0};
+    const SaveForBwd sv{wl.total, wl.ckpt, wl.nck};
+    return scan_impl(desc, u, delta, A, B, C, D, z, h0, y, h_last, workspace, workspace_bytes, &t, stream, &sv);
+}
+
 extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t dtype, int32_t disc,
                                 const void *x, const void *delta, const float *delta_bias,
                                 int32_t delta_softplus, const float *A, const void *B,
@@ -1128,6 +1158,15 @@ extern "C" int ssm_scan_bwd(const ssm_scan_desc *desc, const void *u, const void
                             float *dconv_bias, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return bwd_impl(desc, u, delta, A, B, C, D, z, h0, dy, dh_last, du, ddelta, dA, dB, dC, dD, dz, dh0,
                     ddelta_bias, dconv_weight, dconv_bias, workspace, workspace_bytes, stream);
+}
+
+extern "C" int ssm_scan_bwd_saved(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A,
+                                  const void *B, const void *C, const float *D, const void *z, const float *h0,
+                                  const void *dy, const float *dh_last, void *du, void *ddelta, float *dA, float *dB,
+                                  float *dC, float *dD, void *dz, float *dh0, float *ddelta_bias, float *dconv_weight,
+                                  float *dconv_bias, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return bwd_impl(desc, u, delta, A, B, C, D, z, h0, dy, dh_last, du, ddelta, dA, dB, dC, dD, dz, dh0,
+                    ddelta_bias, dconv_weight, dconv_bias, workspace, workspace_bytes, stream, true);
 }
 
 extern "C" int ssm_ssd_fwd(const ssm_ssd_desc *desc, const void *x, const void *dt, const float *A,

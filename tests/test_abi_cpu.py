@@ -234,6 +234,37 @@ def test_bwd_workspace(L):
     assert extra >= 2 * rnd(2 * 100 * 64 * 4) + rnd(2 * 1 * 64 * 3 * 4) + rnd(2 * 1 * 64 * 4)
 
 
+def test_training_pair_workspace(L):
+    """ssm_scan_fwd_save needs the backward's workspace (checkpoints included),
+    not the forward's, and ssm_scan_bwd_saved the same; both reject less before
+    any launch, and share the other calls' argument checks."""
+    d = desc(b=2, L=100, d=64, N=16)
+    fwd_need = L.ssm_scan_workspace_size(ctypes.byref(d))
+    bwd_need = L.ssm_scan_bwd_workspace_size(ctypes.byref(d))
+    assert 0 < fwd_need < bwd_need
+    save = lambda **kw: _fwd_save(L, kw.pop("dsc", d), **kw)
+    assert save(ws_bytes=fwd_need) == EWS
+    assert save(ws_bytes=bwd_need - 1) == EWS
+    assert save(ws=0, ws_bytes=0) == EWS
+    assert save(dsc=None) == ENULL
+    assert save(dsc=desc(N=65)) == EUNSUP
+    assert save(y=1 * GB + 64) == EALIAS                  # y over u
+    assert save(ws=11 * GB + 64) == EALIGN
+    assert save(dsc=desc(L=0), h_last=0) == OK            # nothing to compute or keep
+    ptrs = [fake(a) if a else None for a in (1 * GB, 2 * GB, 3 * GB, 4 * GB, 5 * GB, 6 * GB, 7 * GB, 0, 8 * GB, 0,
+                                             9 * GB, 10 * GB, 11 * GB, 12 * GB, 13 * GB, 14 * GB, 15 * GB, 0, 0, 0,
+                                             0, 16 * GB)]
+    assert L.ssm_scan_bwd_saved(ctypes.byref(d), *ptrs, bwd_need - 1, None) == EWS
+    assert L.ssm_scan_bwd_saved(None, *ptrs, bwd_need, None) == ENULL
+
+
+def _fwd_save(L, dsc, u=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB, h0=0, y=8 * GB,
+              h_last=9 * GB, ws=11 * GB, ws_bytes=1 << 30):
+    args = [ctypes.byref(dsc) if dsc is not None else None]
+    args += [fake(a) if a else None for a in (u, delta, A, B, C, D, z, h0, y, h_last, ws)]
+    return L.ssm_scan_fwd_save(*args, ws_bytes, None)
+
+
 def ssd_desc(b=2, L=100, H=4, P=64, G=1, N=128, dtype=ssm.SSM_BF16, disc=0, softplus=0, bias=None):
     return ssm.SsdDesc(b, L, H, P, G, N, dtype, disc, softplus, 0, bias)
 
