@@ -216,7 +216,7 @@ def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_
     y = torch.empty_like(dev["u"])
     hl = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device="cuda")
     fws = torch.empty(max(ssm.ssm_scan_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, ssm.SSM_BF16,
-                                                      disc), 1), dtype=torch.uint8, device="cuda")
+                                                      disc, **step_opts), 1), dtype=torch.uint8, device="cuda")
 
     def fwd_plain():
         ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"], y=y, h_last=hl,
@@ -393,7 +393,7 @@ def main():
     h_last = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device="cuda")
     tuning = tuple(int(v) for v in args.tuning.split(",")) if args.tuning else None
     plan = tuning or ssm.ssm_scan_plan(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate)
-    need = ssm.ssm_scan_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, tuning=tuning)
+    need = ssm.ssm_scan_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, tuning=tuning, **step_opts)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
 
     def step():
@@ -446,12 +446,13 @@ def main():
             "global_batch": cfg.batch, "seq_len": cfg.seqlen, "dim": cfg.dim, "dstate": cfg.dstate,
             "io_dtype": "bf16", "parallelism": "none (1 GPU)",
             "disc": args.disc, "step": "softplus(delta + bias) in the kernel" if args.delta_softplus else "delta as given",
-            "prologue": "silu(causal conv1d width 4) in the kernel" if args.conv else "none",
+            "prologue": "silu(causal conv1d width 4), a pass of its own before the scan" if args.conv else "none",
             "launch": {"state_groups": plan[0], "segments": plan[1]},
         },
         "roofline": {
             "bound": "alu",
-            "kernel": "scan_kernel (main pass)" if plan[1] == 1 else "scan passes (aggregate + carry + main)",
+            "kernel": ("scan_kernel (main pass)" if plan[1] == 1 else "scan passes (aggregate + carry + main)")
+                      + (" after conv_silu_kernel" if args.conv else ""),
             "achieved": achieved_tops,
             "peak": VALU_PEAK_TOPS,
             "unit": "Top/s",

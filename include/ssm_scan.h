@@ -74,7 +74,10 @@ typedef enum { SSM_DISC_EULER = 0, SSM_DISC_ZOH = 1 } ssm_disc;
  * MambaBlock.forward, x_conv = silu(conv1d(x)), a causal depthwise convolution
  * with left padding W-1): the buffer passed as u holds x, and the scan input is
  *     u[b,t,d] = silu(conv_bias[d] + sum_{k<W} conv_weight[d,k] * x[b,t-(W-1)+k,d]),
- * x before t = 0 being zero; the D skip uses this u.
+ * x before t = 0 being zero; the D skip uses this u. The forward forms u in
+ * a pass of its own and keeps it in the tensors' type (bf16 tensors round it
+ * to bf16, as the block's x_conv would be in a bf16 model); the backward forms
+ * it in fp32.
  * Zero-initialise the struct for "delta used as given, no convolution". */
 typedef struct {
     int64_t batch;   /* b  >= 0 */
@@ -103,7 +106,9 @@ typedef struct {
 /* Bytes of device workspace ssm_scan_fwd needs for `desc`: B and C widened
  * to fp32 (about 2 * batch * seqlen * dstate * 4 bytes) plus, when the
  * sequence is split into segments, three (batch, segments, dim, dstate) fp32
- * arrays. 0 when there is nothing to compute; 0 for an invalid descriptor. */
+ * arrays, plus, with the convolution prologue, u (batch, seqlen, dim) in the
+ * tensors' type. 0 when there is nothing to compute; 0 for an invalid
+ * descriptor. */
 size_t ssm_scan_workspace_size(const ssm_scan_desc *desc);
 
 /*

@@ -152,8 +152,11 @@ def make_desc(batch, seqlen, dim, dstate, dtype, disc="euler", delta_bias=None, 
                     int(bool(delta_softplus)), W, ptr(delta_bias), ptr(conv_weight), ptr(conv_bias))
 
 
-def ssm_scan_workspace_size(batch, seqlen, dim, dstate, dtype=SSM_BF16, disc="euler", tuning=None) -> int:
-    desc = make_desc(batch, seqlen, dim, dstate, dtype, disc)
+def ssm_scan_workspace_size(batch, seqlen, dim, dstate, dtype=SSM_BF16, disc="euler", tuning=None,
+                            delta_bias=None, delta_softplus=False, conv_weight=None, conv_bias=None) -> int:
+    """Workspace bytes of ssm_scan_fwd for this shape and these options (the
+    convolution prologue adds its u)."""
+    desc = make_desc(batch, seqlen, dim, dstate, dtype, disc, delta_bias, delta_softplus, conv_weight, conv_bias)
     if tuning is None:
         return int(lib().ssm_scan_workspace_size(ctypes.byref(desc)))
     return int(lib().ssm_scan_workspace_size_tuned(ctypes.byref(desc), _tuning(tuning)))

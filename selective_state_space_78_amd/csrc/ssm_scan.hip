@@ -55,7 +55,8 @@ constexpr int kConvBlock = 256;
 struct ConvParams {
     const void *x;            // (batch, L, dim)
     const float *w, *cb;      // (dim, W), (dim) or null
-    float *u;                 // conv_silu_kernel output (batch, L, dim), fp32
+    void *u;                  // conv_silu_kernel output (batch, L, dim): fp32 for the backward, the
+                              // tensors' type for the forward
     const float *du;          // gradient of u (fp32)
     void *dx;                 // gradient of x
     float *part_w, *part_b;   // (batch, nblk, dim, W), (batch, nblk, dim)
@@ -146,7 +147,7 @@ __device__ __forceinline__ void conv_pre(const float (&wr)[CPT][kConvMax], const
     }
 }
 
-template <typename T, int CPT>
+template <typename T, int CPT, typename UT = float>
 __global__ __launch_bounds__(256) void conv_silu_kernel(const ConvParams p) {
     const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * CPT;
     if (d0 >= p.dim) return;
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const ConvParams p) {
         conv_pre<CPT>(wr, cb, xs, p.W, u);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) u[c] = silu(u[c]);
-        conv_st_piece<float, CPT>(p.u, i, u);
+        conv_st_piece<UT, CPT>(p.u, i, u);
     }
 }
 
@@ -608,9 +609,20 @@ bool plan_supported(const Plan &pl) {
     return pl.seg_len > 0 || pl.S == 1;
 }
 
+// The forward runs the convolution prologue as a pass of its own (when the
+// batch fits that pass's grid): u = silu(conv(x)) in the tensors' type, in the
+// workspace after the scan's own part. The scan is ALU-bound, so the fused
+// prologue's instructions cost it more than this pass's memory traffic.
+bool conv_pass(const ssm_scan_desc &d) { return d.conv_width > 0 && d.batch <= 65535; }
+
+size_t conv_u_bytes(const ssm_scan_desc &d) {
+    return align256((size_t)d.batch * d.seqlen * d.dim * (d.dtype == SSM_BF16 ? 2 : 4));
+}
+
 size_t workspace_bytes_for(const ssm_scan_desc &d, const Plan &pl) {
     if (d.batch == 0 || d.dim == 0 || d.seqlen == 0) return 0;
-    return workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, pl).total;
+    const size_t scan = align256(workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, pl).total);
+    return scan + (conv_pass(d) ? conv_u_bytes(d) : 0);
 }
 
 bool shape_compiled(const Plan &pl) {
@@ -653,6 +665,7 @@ int validate_desc(const ssm_scan_desc *d) {
 struct SaveForBwd {
     size_t need, ckpt;
     int nck;
+    size_t conv_u;   // where the convolution pass's u goes (the backward's fp32 u, formed again there)
 };
 
 int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A,
@@ -708,10 +721,46 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
         return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
     }
 
+    // the convolution prologue as a pass of its own; the scan then reads its u
+    const void *us = u;
+    if (conv_pass(d)) {
+        char *ws = static_cast<char *>(workspace);
+        void *uw = ws + (save ? save->conv_u : align256(workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, pl).total));
+        ConvParams cp{};
+        cp.x = u;
+        cp.w = d.conv_weight;
+        cp.cb = d.conv_bias;
+        cp.u = uw;
+        cp.L = d.seqlen;
+        cp.batch = (int)d.batch;
+        cp.dim = (int)d.dim;
+        cp.W = d.conv_width;
+        // runs of at least 64 tokens, at most 65535 of them per batch row
+        const int64_t runs = std::min<int64_t>((d.seqlen + 63) / 64, 65535);
+        cp.run = (int)((d.seqlen + runs - 1) / runs);
+        const int cpt = (d.dim % 4 == 0 && aligned(u, 4 * es)) ? 4 : 1;
+        const dim3 grid((unsigned)((d.dim / cpt + 255) / 256), (unsigned)runs, (unsigned)d.batch);
+        if (d.dtype == SSM_BF16) {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 4, uint16_t>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 1, uint16_t>), grid, dim3(256), 0, stream, cp);
+        } else {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_silu_kernel<float, 4, float>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_silu_kernel<float, 1, float>), grid, dim3(256), 0, stream, cp);
+        }
+        if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
+        us = uw;
+    }
+
     ScanParams p{};
-    p.u = u; p.delta = delta; p.z = z; p.B = B; p.C = C;
+    p.u = us; p.delta = delta; p.z = z; p.B = B; p.C = C;
     p.delta_bias = d.delta_bias; p.delta_softplus = d.delta_softplus;
-    p.conv_w = d.conv_width; p.conv_weight = d.conv_weight; p.conv_bias = d.conv_width ? d.conv_bias : nullptr;
+    if (us == u) {
+        p.conv_w = d.conv_width; p.conv_weight = d.conv_weight; p.conv_bias = d.conv_width ? d.conv_bias : nullptr;
+    }
     p.A = A; p.D = D; p.h0 = h0;
     p.y = y; p.h_last = h_last;
     p.L = d.seqlen;
@@ -722,7 +771,7 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
     p.nseg = pl.S;
     p.ntiles = (int)((d.dim + kTile - 1) / kTile);
     // 4-channel pieces move as single 8-byte (bf16) or 16-byte (fp32) accesses
-    p.vec = (d.dim % 4 == 0) && aligned(u, 4 * es) && aligned(delta, 4 * es) && (!z || aligned(z, 4 * es)) &&
+    p.vec = (d.dim % 4 == 0) && aligned(us, 4 * es) && aligned(delta, 4 * es) && (!z || aligned(z, 4 * es)) &&
             aligned(y, 4 * es);
     {
         const WorkspaceLayout wl = workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, pl);
@@ -894,7 +943,7 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
         cp.x = x_in;
         cp.w = d.conv_weight;
         cp.cb = d.conv_bias;
-        cp.u = reinterpret_cast<float *>(ws + wl.conv_u);
+        cp.u = ws + wl.conv_u;
         cp.du = reinterpret_cast<const float *>(ws + wl.conv_du);
         cp.dx = dx_out;
         cp.part_w = reinterpret_cast<float *>(ws + wl.conv_pw);
@@ -1091,7 +1140,7 @@ extern "C" int ssm_scan_fwd_save(const ssm_scan_desc *desc, const void *u, const
     // the backward's launch shape, so that its checkpoints are the ones this pass passes through
     const BwdLayout wl = bwd_layout(*desc);
     const ssm_scan_tuning t{wl.sh.G, 0};
-    const SaveForBwd sv{wl.total, wl.ckpt, wl.nck};
+    const SaveForBwd sv{wl.total, wl.ckpt, wl.nck, wl.conv_u};
     return scan_impl(desc, u, delta, A, B, C, D, z, h0, y, h_last, workspace, workspace_bytes, &t, stream, &sv);
 }
 
