@@ -258,6 +258,19 @@ def test_training_pair_workspace(L):
     assert L.ssm_scan_bwd_saved(None, *ptrs, bwd_need, None) == ENULL
 
 
+def test_conv_prologue_forward_workspace(L):
+    """The forward runs the convolution prologue as a pass of its own and keeps
+    its u, in the tensors' type, in the workspace after the scan's part; a
+    workspace sized without it is rejected before any launch."""
+    rnd = lambda v: (v + 255) // 256 * 256
+    for dtype, es in ((ssm.SSM_BF16, 2), (ssm.SSM_F32, 4)):
+        plain = L.ssm_scan_workspace_size(ctypes.byref(desc(b=2, L=100, d=64, N=16, dtype=dtype)))
+        dc = desc(b=2, L=100, d=64, N=16, dtype=dtype, conv=4, cw=17 * GB)
+        conv = L.ssm_scan_workspace_size(ctypes.byref(dc))
+        assert conv == rnd(plain) + rnd(2 * 100 * 64 * es)
+        assert scan_call(L, dc, ws_bytes=conv - 1) == EWS
+
+
 def _fwd_save(L, dsc, u=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB, h0=0, y=8 * GB,
               h_last=9 * GB, ws=11 * GB, ws_bytes=1 << 30):
     args = [ctypes.byref(dsc) if dsc is not None else None]
