@@ -140,7 +140,9 @@ template <> struct BwdFloats<4> { typedef float4 type; };
 
 // UF: u is read as fp32 whatever T is (the convolution prologue's output,
 // formed in fp32 like the forward forms it)
-template <typename T, int NPW, int G, int TC, bool ZOH, bool UF = false>
+// FEAT: the step options (delta bias, softplus) are compiled in; without it
+// the kernel carries none of their registers
+template <typename T, int NPW, int G, int TC, bool ZOH, bool UF = false, bool FEAT = true>
 struct BwdKernel {
     static constexpr int kThreads = kTile * G;
     static constexpr int kNP = NPW * G;
@@ -177,7 +179,7 @@ struct BwdKernel {
     };
     struct Held {
         float dt[kPPT][kV], u[kPPT][kV], ds[kPPT][kV], gz[kPPT][kV];   // gz = dy g'(z)
-        float sg[kPPT][kV];            // d step / d delta (sigmoid of the softplus argument, or 1)
+        float sg[FEAT ? kPPT : 1][FEAT ? kV : 1];   // d step / d delta (sigmoid of the softplus argument, or 1)
     };
 
     __device__ static int piece_row(int j) { return threadIdx.x / kRowPieces + j * kRowStep; }
@@ -309,6 +311,7 @@ struct BwdKernel {
                 unpack(pf.dy[j], g);
 #pragma unroll
                 for (int e = 0; e < kV; ++e) {
+                    if constexpr (!FEAT) continue;
                     held.sg[j][e] = 1.0f;
                     if (prep == 2) {
                         const float xs = d[e] + dbk[e];
@@ -421,9 +424,9 @@ struct BwdKernel {
 #pragma unroll
         for (int e = 0; e < kV; ++e) {
             Dk[e] = (p.D != nullptr && d0 + col + e < p.dim) ? p.D[d0 + col + e] : 0.0f;
-            dbk[e] = (p.delta_bias != nullptr && d0 + col + e < p.dim) ? p.delta_bias[d0 + col + e] : 0.0f;
+            dbk[e] = (FEAT && p.delta_bias != nullptr && d0 + col + e < p.dim) ? p.delta_bias[d0 + col + e] : 0.0f;
         }
-        const int prep = p.delta_softplus ? 2 : (p.delta_bias != nullptr ? 1 : 0);
+        const int prep = !FEAT ? 0 : p.delta_softplus ? 2 : (p.delta_bias != nullptr ? 1 : 0);
 #pragma unroll
         for (int j = 0; j < kPPT; ++j)
 #pragma unroll
@@ -595,8 +598,10 @@ struct BwdKernel {
                         ou[e] = fmaf(held.dt[j][e], su[e], Dk[e] * held.ds[j][e]);
                         od[e] = fmaf(held.u[j][e], su[e], sd[e]);
                     }
-                    od[e] *= held.sg[j][e];          // gradient of the raw delta
-                    dbacc[j][e] += od[e];
+                    if constexpr (FEAT) {
+                        od[e] *= held.sg[j][e];      // gradient of the raw delta
+                        dbacc[j][e] += od[e];
+                    }
                 }
                 const int64_t off = (row0 + t0 + row) * p.dim + d0 + col;
                 if (po.du_f32 != nullptr) {
@@ -641,7 +646,7 @@ struct BwdKernel {
             for (int r = 0; r < TC; ++r) acc += dsum[r][threadIdx.x];
             p.part_d[(int64_t)b * p.dim + d0 + threadIdx.x] = acc;
         }
-        if (p.part_db != nullptr) {
+        if (FEAT && p.part_db != nullptr) {
             // the same for the delta-bias gradient, through the second plane set
             float (*bsum)[kTile] = s.pl[1][0];
 #pragma unroll
@@ -664,9 +669,9 @@ struct BwdKernel {
 // the simplified rule fits 128 VGPRs: at least 4 waves per SIMD (two 8-wave
 // workgroups, or one 16-wave one, per CU); the hold rule's reverse step needs
 // more registers, and capping it at 128 spilled 80-170 of them to scratch
-template <typename T, int NPW, int G, int TC, bool ZOH, bool UF>
+template <typename T, int NPW, int G, int TC, bool ZOH, bool UF, bool FEAT>
 __global__ __launch_bounds__(kTile * G, ZOH ? 2 : 4) void bwd_kernel(const BwdParams p) {
-    BwdKernel<T, NPW, G, TC, ZOH, UF>::run(p);
+    BwdKernel<T, NPW, G, TC, ZOH, UF, FEAT>::run(p);
 }
 
 template <typename T, bool ZOH>
@@ -674,19 +679,23 @@ hipError_t launch_bwd_shape(const BwdShape &sh, const BwdParams &p, hipStream_t 
     const int64_t blocks = (int64_t)p.batch * p.ntiles;
     // fp32 u with bf16 tensors: the UF variant (fp32 tensors read u as fp32 anyway)
     const bool uf = sizeof(T) == 2 && p.u_f32;
+    // the step options' instance only when one is on
+    const bool feat = p.delta_bias != nullptr || p.delta_softplus;
+#define SSM_BWD_LAUNCH(NP, GG, TCC, UFV, FV) \
+    hipLaunchKernelGGL((bwd_kernel<T, NP / GG, GG, TCC, ZOH, UFV, FV>), dim3((unsigned)blocks), dim3(kTile * GG), 0, \
+                       st, p)
 #define SSM_BWD_CASE(NP, GG, TCC) \
     if (sh.npad == NP && sh.G == GG && sh.TC == TCC) { \
-        if (uf) \
-            hipLaunchKernelGGL((bwd_kernel<T, NP / GG, GG, TCC, ZOH, sizeof(T) == 2>), dim3((unsigned)blocks), \
-                               dim3(kTile * GG), 0, st, p); \
-        else \
-            hipLaunchKernelGGL((bwd_kernel<T, NP / GG, GG, TCC, ZOH, false>), dim3((unsigned)blocks), \
-                               dim3(kTile * GG), 0, st, p); \
+        if (uf && feat) SSM_BWD_LAUNCH(NP, GG, TCC, sizeof(T) == 2, true); \
+        else if (uf) SSM_BWD_LAUNCH(NP, GG, TCC, sizeof(T) == 2, false); \
+        else if (feat) SSM_BWD_LAUNCH(NP, GG, TCC, false, true); \
+        else SSM_BWD_LAUNCH(NP, GG, TCC, false, false); \
         return hipGetLastError(); \
     }
     SSM_BWD_CASE(4, 2, 16) SSM_BWD_CASE(8, 8, 16) SSM_BWD_CASE(16, 8, 16) SSM_BWD_CASE(32, 16, 8)
     SSM_BWD_CASE(64, 16, 8)
 #undef SSM_BWD_CASE
+#undef SSM_BWD_LAUNCH
     return hipErrorInvalidValue;
 }
 
