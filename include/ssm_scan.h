@@ -215,7 +215,10 @@ int ssm_scan_bwd(const ssm_scan_desc *desc,
  * (the checkpoints are the states the forward passes through). h_last equals
  * ssm_scan_fwd's bit for bit; y may differ from it in the last bit where the
  * backward's launch shape splits the states over another number of waves
- * and so sums the readout in another order.
+ * and so sums the readout in another order. With the convolution prologue,
+ * bf16 tensors and one segment, the saving forward forms u in fp32 (where the
+ * backward then reads it) instead of bf16, so y and h_last differ from
+ * ssm_scan_fwd's by that rounding of u.
  *
  *   workspace  at least ssm_scan_bwd_workspace_size(desc) bytes, 256-byte
  *              aligned, for both calls. ssm_scan_bwd_saved must receive the

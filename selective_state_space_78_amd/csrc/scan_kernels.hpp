@@ -873,7 +873,17 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
     }
     if constexpr (CK) {
         if (p.ckpt != nullptr && p.y != nullptr) {
-            // the forward that also keeps the backward's checkpoints
+            // the forward that also keeps the backward's checkpoints (with bf16
+            // tensors and the convolution pass's u in fp32: one segment only, as
+            // for the checkpoint pass)
+            if constexpr (sizeof(T) == 2) {
+                if (p.u_f32) {
+                    if (nblocks_agg > 0) return hipErrorInvalidValue;
+                    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMainCheckpoint, FEAT, true>),
+                                       dim3(nblocks_main), dim3(kTile * G), 0, st, p);
+                    return hipGetLastError();
+                }
+            }
             hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMainCheckpoint, FEAT>), dim3(nblocks_main),
                                dim3(kTile * G), 0, st, p);
             return hipGetLastError();

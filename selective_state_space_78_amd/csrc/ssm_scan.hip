@@ -721,8 +721,11 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
         return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
     }
 
-    // the convolution prologue as a pass of its own; the scan then reads its u
+    // the convolution prologue as a pass of its own; the scan then reads its u.
+    // Keeping the checkpoints over one segment, it writes u in fp32 where the
+    // backward reads it, so that the backward need not form it again
     const void *us = u;
+    const bool u32 = save && pl.S == 1 && d.dtype == SSM_BF16;
     if (conv_pass(d)) {
         char *ws = static_cast<char *>(workspace);
         void *uw = ws + (save ? save->conv_u : align256(workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, pl).total));
@@ -740,7 +743,12 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
         cp.run = (int)((d.seqlen + runs - 1) / runs);
         const int cpt = (d.dim % 4 == 0 && aligned(u, 4 * es)) ? 4 : 1;
         const dim3 grid((unsigned)((d.dim / cpt + 255) / 256), (unsigned)runs, (unsigned)d.batch);
-        if (d.dtype == SSM_BF16) {
+        if (u32) {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 4, float>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 1, float>), grid, dim3(256), 0, stream, cp);
+        } else if (d.dtype == SSM_BF16) {
             if (cpt == 4)
                 hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 4, uint16_t>), grid, dim3(256), 0, stream, cp);
             else
@@ -757,6 +765,7 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
 
     ScanParams p{};
     p.u = us; p.delta = delta; p.z = z; p.B = B; p.C = C;
+    p.u_f32 = us != u && u32;
     p.delta_bias = d.delta_bias; p.delta_softplus = d.delta_softplus;
     if (us == u) {
         p.conv_w = d.conv_width; p.conv_weight = d.conv_weight; p.conv_bias = d.conv_width ? d.conv_bias : nullptr;
@@ -939,6 +948,9 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     // they are whole and aligned (the workspace's u and du always are)
     const int cpt = (d.dim % 4 == 0 && aligned(x_in, 4 * es) && aligned(dx_out, 4 * es)) ? 4 : 1;
     ConvParams cp{};
+    // a forward that kept the checkpoints has left u in fp32 here (fp32 tensors,
+    // or bf16 ones over one segment)
+    const bool u_saved = saved && conv_pass(d) && (d.dtype == SSM_F32 || wl.pl.S == 1);
     if (cw > 0) {
         cp.x = x_in;
         cp.w = d.conv_weight;
@@ -960,7 +972,8 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
         cp.run = (int)((d.seqlen + runs - 1) / runs);
         if (d.batch > 65535) return SSM_ERR_SHAPE;
         const dim3 grid((unsigned)((d.dim / cpt + 255) / 256), (unsigned)runs, (unsigned)d.batch);
-        if (d.dtype == SSM_BF16) {
+        if (u_saved) {
+        } else if (d.dtype == SSM_BF16) {
             if (cpt == 4)
                 hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 4>), grid, dim3(256), 0, stream, cp);
             else
