@@ -184,6 +184,26 @@ def bench_decode(torch, ssm, steps=200, warmup=10, nsets=16):
     }
 
 
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy rate (bytes read + bytes written per second, in
+    GB/s) of a 1 GiB buffer on this GPU: a measured sanity denominator beside
+    the published peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_opts=None):
     """Time ssm_scan_bwd (checkpoint pass + reverse pass + reduction) on the workload."""
     g = si.grad_inputs(cfg, seed=0)
@@ -469,6 +489,7 @@ def main():
             "achieved_GBps": gbps,
             "peak_GBps": HBM_PEAK_GBPS,
             "frac": gbps / HBM_PEAK_GBPS,
+            "measured_copy_GBps": copy_bandwidth(torch),
         },
     }
     if args.calib_copy:
