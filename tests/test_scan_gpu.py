@@ -308,8 +308,9 @@ def test_delta_bias_softplus(env, dtype, disc):
 @pytest.mark.parametrize("disc", ["euler", "zoh"])
 @pytest.mark.parametrize("W", [1, 2, 3, 4])
 def test_conv_prologue(env, dtype, disc, W):
-    """silu(causal depthwise conv1d(x) + bias) formed in the kernel, across chunk
-    and segment boundaries, with and without the other options."""
+    """silu(causal depthwise conv1d(x) + bias), formed by the forward's conv
+    pass and read by the scan, across chunk and segment boundaries, with and
+    without the other options."""
     import dataclasses
     torch, ssm = env
     cfg = dataclasses.replace(si.CONFIGS["mamba130m"], dtype=dtype)
@@ -342,6 +343,27 @@ def test_conv_prologue(env, dtype, disc, W):
     ey, eh = rel_err(to_np(y), yr), rel_err(to_np(hl), hr)
     say("conv W%d %s %s, d 133, no conv bias, softplus step: y %.3e h %.3e" % (W, dtype, disc, ey, eh))
     assert ey <= tol and eh <= tol
+
+
+def test_conv_prologue_fused_for_large_batch(env):
+    """More batch rows (65536) than the conv pass's grid takes: the forward
+    forms u in the scan kernel's staging instead (the fused prologue), and
+    its workspace has no room for u."""
+    import dataclasses
+    torch, ssm = env
+    cfg = dataclasses.replace(si.CONFIGS["mamba130m"], dtype="bf16")
+    x = si.scan_inputs(cfg, seed=91, batch=65536, seqlen=5, dim=4, dstate=4)
+    c = si.conv_inputs(4, 4, seed=91)
+    assert ssm.ssm_scan_workspace_size(65536, 5, 4, 4) == ssm.ssm_scan_workspace_size(
+        65536, 5, 4, 4, conv_weight=to_dev(c["conv_weight"], torch))
+    dev = {k: to_dev(v, torch) for k, v in x.items() if k != "h0"}
+    yr, hr = oracle.load().selective_scan(**x, **c)
+    y, hl = ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                             conv_weight=to_dev(c["conv_weight"], torch), conv_bias=to_dev(c["conv_bias"], torch))
+    torch.cuda.synchronize()
+    ey, eh = rel_err(to_np(y), yr), rel_err(to_np(hl), hr)
+    say("conv W4 bf16, batch 65536 (fused prologue): y %.3e h %.3e" % (ey, eh))
+    assert ey <= tol_of(x) and eh <= tol_of(x)
 
 
 def test_conv_prologue_full_size(env):
