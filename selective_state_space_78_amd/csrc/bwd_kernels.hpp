@@ -380,7 +380,7 @@ struct BwdKernel {
     // scalar load from the argument segment) instead of being held in scalar
     // registers across the chunk loop, which would spill them.
     typedef const __attribute__((address_space(4))) BwdParams KernArgs;
-    __device__ static KernArgs &fresh(const BwdParams &) {
+    __device__ static KernArgs &fresh() {
         KernArgs *q = (KernArgs *)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(q));
         return *q;
@@ -439,7 +439,7 @@ struct BwdKernel {
         cword *bw0 = (cword *)(p.Bf) + ((int64_t)b * G + w) * Lp * NPW;
         cword *cw0 = (cword *)(p.Cf) + ((int64_t)b * G + w) * Lp * NPW;
         auto ckpt_at = [&](int c, int q) {
-            return fresh(p).ckpt[(((int64_t)b * nck + c) * kNP + w * NPW + q) * p.dim + dc];
+            return fresh().ckpt[(((int64_t)b * nck + c) * kNP + w * NPW + q) * p.dim + dc];
         };
 
         Prefetch pf;
@@ -461,7 +461,7 @@ struct BwdKernel {
 #pragma unroll
             for (int q = 0; q < NPW; ++q) hstart[q] = hnext[q];
             if (c > 0) {
-                load(fresh(p), pf, (row0 + (int64_t)(c - 1) * TC) * p.dim + d0, rows_of(c - 1), col, d0, colv);
+                load(fresh(), pf, (row0 + (int64_t)(c - 1) * TC) * p.dim + d0, rows_of(c - 1), col, d0, colv);
 #pragma unroll
                 for (int q = 0; q < NPW; ++q) hnext[q] = ckpt_at(c - 1, q);
             }
@@ -514,7 +514,7 @@ struct BwdKernel {
                 plane_sum(s, 0, row, col, acc);
 #pragma unroll
                 for (int e = 0; e < kV; ++e) o[e] = held.gz[j][e] * (acc[e] + Dk[e] * held.u[j][e]);
-                T *dst = static_cast<T *>(fresh(p).dz) + (row0 + t0 + row) * p.dim + d0 + col;
+                T *dst = static_cast<T *>(fresh().dz) + (row0 + t0 + row) * p.dim + d0 + col;
                 store(dst, o, d0 + col, p.dim, p.vec);
             }
             __syncthreads();
@@ -581,7 +581,7 @@ struct BwdKernel {
             __syncthreads();
 
             // 5. du, ddelta of this thread's pieces; the tile's dB, dC sums
-            KernArgs &po = fresh(p);
+            KernArgs &po = fresh();
 #pragma unroll
             for (int j = 0; j < kPPT; ++j) {
                 const int row = piece_row(j);
