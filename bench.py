@@ -286,6 +286,50 @@ def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+def bench_ssd_decode(torch, ssm, batch=64, steps=200, warmup=10, sets=16):
+    """The SSD decode step (ssm_ssd_state_update) for 64 batch rows of the
+    Mamba-2 layer's heads (64 x 64, N 128, one group): a 134 MB fp32 state
+    updated in place, steps cycling over `sets` per-token input sets."""
+    cfg = si.SSD_CONFIGS["mamba2-ssd"]
+    H, P, N, G = cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+    x = si.ssd_inputs(cfg, seed=0, batch=batch, seqlen=sets)
+    tok = [{n: to_dev(np.ascontiguousarray(x[n][:, k]), torch) if x[n] is not None else None
+            for n in ("x", "dt", "B", "C", "z")} for k in range(sets)]
+    A = to_dev(x["A"], torch)
+    D = to_dev(x["D"], torch) if x["D"] is not None else None
+    h = torch.zeros((batch, H, P, N), dtype=torch.float32, device="cuda")
+    y = torch.empty((batch, H, P), dtype=torch.bfloat16, device="cuda")
+
+    def step(k):
+        t = tok[k % sets]
+        ssm.ssm_ssd_state_update(t["x"], t["dt"], A, t["B"], t["C"], h, D=D, z=t["z"], y=y)
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(steps):
+        step(k)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    nbytes = (2 * batch * H * P * N * 4            # state read and written
+              + (3 if x["z"] is not None else 2) * batch * H * P * 2 + batch * H * 2   # x, (z,) y; dt
+              + 2 * batch * G * N * 2 + (2 if x["D"] is not None else 1) * H * 4)       # B, C; A, (D)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {
+        "workload": "SSD decode b%d, %d heads x %d, d_state %d, %d group%s%s: %d in-place steps cycling %d input "
+                    "sets" % (batch, H, P, N, G, ", gate" if x["z"] is not None else "",
+                              ", D skip" if x["D"] is not None else "", steps, sets),
+        "us_per_step": us,
+        "algorithmic_bytes_per_step": nbytes,
+        "GB/s": gbps,
+        "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+        "note": "the 134 MB state fits the 256 MB Infinity Cache; effective rate",
+    }
+
+
 def bench_ssd(torch, ssm, steps=20, warmup=3, cpu=True, budget_s=10.0):
     """The Mamba-2 SSD layer (ssm_ssd_fwd) on the mamba2-ssd workload, with its
     roofline position and the fp64 oracle on a bounded sample of heads."""
@@ -360,6 +404,7 @@ def bench_ssd(torch, ssm, steps=20, warmup=3, cpu=True, budget_s=10.0):
                 k, cfg.batch * cfg.nheads, cfg.seqlen, cfg.headdim, sec),
             "parity_max_rel_err_vs_gpu": rel_err(yg, yr),
         }
+    out["decode"] = bench_ssd_decode(torch, ssm)
     return out
 
 

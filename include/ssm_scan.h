@@ -316,6 +316,25 @@ int ssm_ssd_fwd(const ssm_ssd_desc *desc, const void *x, const void *dt, const f
                 void *y, float *h_last, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
+/*
+ * One decode step of the SSD layer: the recurrence above for a single new
+ * token per sequence, with each head's (headdim x dstate) state updated in
+ * place (itwiki "상태 공간 모델", "순환 형태와 합성곱 형태": generation only
+ * updates the state; the SSD layer's state as above). desc->seqlen must be 1.
+ *
+ *   x, z      (batch, nheads, headdim)   bf16; z may be NULL (no gate)
+ *   dt        (batch, nheads)            bf16 (desc->dt_bias, dt_softplus and disc as for ssm_ssd_fwd)
+ *   A, D      (nheads) fp32; D may be NULL
+ *   B, C      (batch, ngroups, dstate)   bf16, 8-byte aligned
+ *   h         (batch, nheads, headdim, dstate) fp32, 16-byte aligned, read and overwritten
+ *   y         (batch, nheads, headdim)   bf16, written; must not overlap h or an input
+ * Equal to ssm_ssd_fwd with seqlen 1, h0 = h and h_last = h, computed
+ * directly in fp32 (no matrix cores: one token is a rank-1 update).
+ */
+int ssm_ssd_state_update(const ssm_ssd_desc *desc, const void *x, const void *dt, const float *A,
+                         const void *B, const void *C, const float *D, const void *z, float *h,
+                         void *y, hipStream_t stream);
+
 const char *ssm_status_string(int status);
 
 #ifdef __cplusplus

@@ -26,7 +26,8 @@ _DISC = {"euler": SSM_DISC_EULER, "zoh": SSM_DISC_ZOH}
 # Every symbol include/ssm_scan.h declares.
 EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_workspace_size_tuned",
            "ssm_scan_fwd_tuned", "ssm_scan_plan", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd",
-           "ssm_scan_fwd_save", "ssm_scan_bwd_saved", "ssm_state_update", "ssm_ssd_fwd", "ssm_status_string")
+           "ssm_scan_fwd_save", "ssm_scan_bwd_saved", "ssm_state_update", "ssm_ssd_fwd", "ssm_ssd_state_update",
+           "ssm_status_string")
 
 
 class ScanDesc(ctypes.Structure):
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
             L.ssm_state_update.restype = ctypes.c_int
             L.ssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 11
             L.ssm_ssd_fwd.restype = ctypes.c_int
+            L.ssm_ssd_state_update.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 10
+            L.ssm_ssd_state_update.restype = ctypes.c_int
             L.ssm_status_string.argtypes = [ctypes.c_int]
             L.ssm_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -426,3 +429,34 @@ def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, h0=None, y=None, h_last=None, di
     if rc != 0:
         raise SsmError(rc, "ssm_ssd_fwd")
     return y, h_last
+
+
+def ssm_ssd_state_update(x, dt, A, B, C, h, D=None, z=None, y=None, disc="euler", dt_bias=None,
+                         dt_softplus=False, stream=None):
+    """One SSD decode step on device tensors: x, z (batch, H, P) bfloat16, dt
+    (batch, H) bfloat16, B, C (batch, G, N) bfloat16, A, D, dt_bias (H,)
+    float32; h (batch, H, P, N) float32 is updated in place. Returns y
+    (batch, H, P), allocated when not given."""
+    import torch
+    batch, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    code = _dtype_code(x)
+    _check(x, "x", device=dev)
+    _check(dt, "dt", (batch, H), x.dtype, dev)
+    _check(z, "z", (batch, H, P), x.dtype, dev)
+    _check(B, "B", (batch, G, N), x.dtype, dev)
+    _check(C, "C", (batch, G, N), x.dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(h, "h", (batch, H, P, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((batch, H, P), dtype=x.dtype, device=dev)
+    _check(y, "y", (batch, H, P), x.dtype, dev)
+    desc = make_ssd_desc(batch, 1, H, P, G, N, code, disc, dt_bias, dt_softplus)
+    rc = lib().ssm_ssd_state_update(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(z), _ptr(h), _ptr(y), _stream(stream, dev))
+    if rc != 0:
+        raise SsmError(rc, "ssm_ssd_state_update")
+    return y

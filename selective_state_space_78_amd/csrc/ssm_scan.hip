@@ -489,10 +489,70 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// One decode step of the SSD layer (ssm_ssd_fwd with one token): per batch row
+// and head, the (P x N) state is updated in place and y written for the token.
+// One thread per (batch row, head, p, 4 consecutive n): a state row of N fp32
+// values moves as N/4 16-byte pieces over N/4 consecutive lanes, which sum the
+// readout C . h over the row by lane exchanges.
+struct SsdDecodeParams {
+    const uint16_t *x, *dt, *B, *C, *z;   // bf16 bit patterns
+    const float *dt_bias, *A, *D;
+    float *h;
+    uint16_t *y;
+    int64_t rows;                         // batch * nheads * headdim
+    int H, G, hpg, P, N;
+    int dt_softplus;
+};
+
+template <bool ZOH>
+__global__ __launch_bounds__(256) void ssd_decode_kernel(const SsdDecodeParams p) {
+    const int lpr = p.N / 4;                              // lanes per state row (16 or 32)
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = tid / lpr;                        // (b, h, p)
+    const int q = (int)(tid % lpr);
+    const bool valid = row < p.rows;
+    const int64_t r = valid ? row : 0;
+    const int64_t bh = r / p.P;                           // b * H + h
+    const int hd = (int)(bh % p.H);
+    const int64_t b = bh / p.H;
+    const int g = hd / p.hpg;
+    auto bf = [](uint16_t v) { return __uint_as_float((uint32_t)v << 16); };
+
+    float part = 0.0f, xv = 0.0f;
+    if (valid) {
+        float dtv = bf(p.dt[bh]) + (p.dt_bias ? p.dt_bias[hd] : 0.0f);
+        if (p.dt_softplus) dtv = softplus_f(dtv);
+        const float Ah = p.A[hd];
+        const float a = __builtin_amdgcn_exp2f(dtv * Ah * kLog2e);
+        const float wbar = ZOH ? dtv * expm1_over_x(dtv * Ah, a) : dtv;
+        xv = bf(p.x[r]);
+        const float wx = wbar * xv;
+        const int64_t bc = (b * p.G + g) * p.N + 4 * q;
+        const uint2 bw = *reinterpret_cast<const uint2 *>(p.B + bc);
+        const uint2 cw = *reinterpret_cast<const uint2 *>(p.C + bc);
+        const float bv[4] = {bf(bw.x & 0xffffu), bf(bw.x >> 16), bf(bw.y & 0xffffu), bf(bw.y >> 16)};
+        const float cv[4] = {bf(cw.x & 0xffffu), bf(cw.x >> 16), bf(cw.y & 0xffffu), bf(cw.y >> 16)};
+        float4 *hp = reinterpret_cast<float4 *>(p.h + r * p.N + 4 * q);
+        float4 hv = *hp;
+        hv.x = fmaf(a, hv.x, wx * bv[0]);
+        hv.y = fmaf(a, hv.y, wx * bv[1]);
+        hv.z = fmaf(a, hv.z, wx * bv[2]);
+        hv.w = fmaf(a, hv.w, wx * bv[3]);
+        *hp = hv;
+        part = fmaf(cv[3], hv.w, fmaf(cv[2], hv.z, fmaf(cv[1], hv.y, cv[0] * hv.x)));
+    }
+    // the row's lanes are lpr consecutive lanes starting at a multiple of lpr
+    for (int o = lpr / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+    if (valid && q == 0) {
+        float yv = part + (p.D ? p.D[hd] * xv : 0.0f);
+        if (p.z) yv *= silu(bf(p.z[r]));
+        p.y[r] = __builtin_bit_cast(uint16_t, (__bf16)yv);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Backward: sums of the per-tile dB, dC and per-row dA, dD partials, in a fixed
 // order (tiles, then batch rows), so that the result does not depend on timing.
-
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdReduceParams p) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nbc = (int64_t)p.batch * p.L * p.N;
@@ -1298,6 +1358,71 @@ extern "C" int ssm_ssd_fwd(const ssm_ssd_desc *desc, const void *x, const void *
     const hipError_t e = d.disc == SSM_DISC_ZOH ? launch_ssd_zoh(p, (int)P, (int)N, stream)
                                                 : launch_ssd_euler(p, (int)P, (int)N, stream);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+extern "C" int ssm_ssd_state_update(const ssm_ssd_desc *desc, const void *x, const void *dt, const float *A,
+                                    const void *B, const void *C, const float *D, const void *z, float *h,
+                                    void *y, hipStream_t stream) {
+    if (desc == nullptr) return SSM_ERR_NULL;
+    const ssm_ssd_desc &d = *desc;
+    if (d.batch < 0 || d.seqlen != 1 || d.nheads < 1 || d.ngroups < 1 || d.nheads % d.ngroups != 0)
+        return SSM_ERR_SHAPE;
+    if (d.dtype != SSM_F32 && d.dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (d.dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+    if (d.disc != SSM_DISC_EULER && d.disc != SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
+    if (d.dt_softplus != 0 && d.dt_softplus != 1) return SSM_ERR_UNSUPPORTED;
+    if (!ssd_shape_supported(d.headdim, d.dstate)) return SSM_ERR_UNSUPPORTED;
+    const int64_t P = d.headdim, N = d.dstate, H = d.nheads, G = d.ngroups;
+    int64_t heads, rows, st_elems;
+    if (!mul_ok(d.batch, H, &heads) || !mul_ok(heads, P, &rows) || !mul_ok(rows, N * 4, &st_elems) ||
+        heads > INT32_MAX)
+        return SSM_ERR_SHAPE;
+    st_elems /= 4;
+    if (heads == 0) return SSM_OK;
+    if (A == nullptr || x == nullptr || dt == nullptr || B == nullptr || C == nullptr || h == nullptr ||
+        y == nullptr)
+        return SSM_ERR_NULL;
+    // states move in 16-byte pieces, B and C in 8-byte ones
+    if (!aligned(h, 16) || !aligned(B, 8) || !aligned(C, 8) || !aligned(x, 2) || (z && !aligned(z, 2)) ||
+        !aligned(y, 2) || !aligned(dt, 2) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+        (d.dt_bias && !aligned(d.dt_bias, 4)))
+        return SSM_ERR_ALIGN;
+    const int64_t bcn = d.batch * G * N;
+    const Range r_y = range_of(y, rows * 2);
+    const Range r_h = range_of(h, st_elems * 4);
+    const Range inputs[] = {range_of(x, rows * 2), range_of(z, z ? rows * 2 : 0), range_of(dt, heads * 2),
+                            range_of(B, bcn * 2), range_of(C, bcn * 2), range_of(A, H * 4),
+                            range_of(D, D ? H * 4 : 0), range_of(d.dt_bias, d.dt_bias ? H * 4 : 0)};
+    for (const Range &r : inputs)
+        if (overlaps(r_y, r) || overlaps(r_h, r)) return SSM_ERR_ALIAS;
+    if (overlaps(r_y, r_h)) return SSM_ERR_ALIAS;
+
+    SsdDecodeParams p{};
+    p.x = static_cast<const uint16_t *>(x);
+    p.dt = static_cast<const uint16_t *>(dt);
+    p.B = static_cast<const uint16_t *>(B);
+    p.C = static_cast<const uint16_t *>(C);
+    p.z = static_cast<const uint16_t *>(z);
+    p.dt_bias = d.dt_bias;
+    p.A = A;
+    p.D = D;
+    p.h = h;
+    p.y = static_cast<uint16_t *>(y);
+    p.rows = rows;
+    p.H = (int)H;
+    p.G = (int)G;
+    p.hpg = (int)(H / G);
+    p.P = (int)P;
+    p.N = (int)N;
+    p.dt_softplus = d.dt_softplus;
+    const int64_t threads = rows * (N / 4);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > INT32_MAX) return SSM_ERR_SHAPE;
+    if (d.disc == SSM_DISC_ZOH)
+        hipLaunchKernelGGL((ssd_decode_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((ssd_decode_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 extern "C" const char *ssm_status_string(int status) {

@@ -271,6 +271,26 @@ def test_conv_prologue_forward_workspace(L):
         assert scan_call(L, dc, ws_bytes=conv - 1) == EWS
 
 
+def test_ssd_decode_errors(L):
+    """ssm_ssd_state_update rejects, before any launch, what ssm_ssd_fwd would
+    and a sequence length other than one."""
+    def call(dsc, x=1 * GB, dt=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB, h=8 * GB, y=9 * GB):
+        ptrs = [fake(a) if a else None for a in (x, dt, A, B, C, D, z, h, y)]
+        return L.ssm_ssd_state_update(ctypes.byref(dsc) if dsc is not None else None, *ptrs, None)
+    assert call(None) == ENULL
+    assert call(ssd_desc(L=2)) == ESHAPE
+    assert call(ssd_desc(L=1, H=3, G=2)) == ESHAPE
+    assert call(ssd_desc(L=1, dtype=ssm.SSM_F32)) == EUNSUP
+    assert call(ssd_desc(L=1, P=80)) == EUNSUP
+    assert call(ssd_desc(L=1, b=0)) == OK
+    assert call(ssd_desc(L=1), h=0) == ENULL
+    assert call(ssd_desc(L=1), y=0) == ENULL
+    assert call(ssd_desc(L=1), h=8 * GB + 8) == EALIGN
+    assert call(ssd_desc(L=1), B=4 * GB + 4) == EALIGN
+    assert call(ssd_desc(L=1), y=8 * GB + 64) == EALIAS       # y over h
+    assert call(ssd_desc(L=1), h=1 * GB) == EALIAS            # h over x
+
+
 def _fwd_save(L, dsc, u=1 * GB, delta=2 * GB, A=3 * GB, B=4 * GB, C=5 * GB, D=6 * GB, z=7 * GB, h0=0, y=8 * GB,
               h_last=9 * GB, ws=11 * GB, ws_bytes=1 << 30):
     args = [ctypes.byref(dsc) if dsc is not None else None]
