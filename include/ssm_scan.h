@@ -315,7 +315,6 @@ int ssm_ssd_fwd(const ssm_ssd_desc *desc, const void *x, const void *dt, const f
                 const void *B, const void *C, const float *D, const void *z, const float *h0,
                 void *y, float *h_last, hipStream_t stream);
 
-/* Static, NUL-terminated description of a status code. */
 /*
  * One decode step of the SSD layer: the recurrence above for a single new
  * token per sequence, with each head's (headdim x dstate) state updated in
@@ -335,6 +334,7 @@ int ssm_ssd_state_update(const ssm_ssd_desc *desc, const void *x, const void *dt
                          const void *B, const void *C, const float *D, const void *z, float *h,
                          void *y, hipStream_t stream);
 
+/* Static, NUL-terminated description of a status code. */
 const char *ssm_status_string(int status);
 
 #ifdef __cplusplus
