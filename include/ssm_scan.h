@@ -55,7 +55,9 @@ typedef enum {
     SSM_ERR_ALIAS = -5,       /* an output overlaps an input or another output */
     SSM_ERR_WORKSPACE = -6,   /* workspace missing or smaller than ssm_scan_workspace_size() */
     SSM_ERR_HIP = -7,         /* the HIP runtime refused a launch (e.g. not a gfx950 device) */
-    SSM_ERR_ALIGN = -8        /* a pointer is not aligned to its element size */
+    SSM_ERR_ALIGN = -8,       /* a pointer is not aligned to its element size */
+    SSM_ERR_SCRATCH = -9      /* ssm_scan_fwd_noalloc: the problem needs more than
+                                 SSM_NOALLOC_SCRATCH_BYTES of scratch */
 } ssm_status;
 
 /* Element type of the per-token tensors u, delta, z, B, C and of the output y.
@@ -136,6 +138,35 @@ int ssm_scan_fwd(const ssm_scan_desc *desc,
                  const void *B, const void *C, const float *D, const void *z,
                  const float *h0, void *y, float *h_last,
                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ssm_scan_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes
+ * no workspace; the library keeps one fixed scratch buffer of
+ * SSM_NOALLOC_SCRATCH_BYTES per GPU (a static device array, held from the
+ * module's load on that GPU until the process ends) and runs the same kernels
+ * as ssm_scan_fwd on it, so its results equal ssm_scan_fwd's bit for bit.
+ *
+ *   Arguments, shapes, conditions and errors: those of ssm_scan_fwd, without
+ *   workspace and workspace_bytes.
+ *   SSM_ERR_SCRATCH when ssm_scan_workspace_size(desc) exceeds
+ *   SSM_NOALLOC_SCRATCH_BYTES (checked on the host before anything else is
+ *   done; e.g. the 1.4B-shaped layer b8 L8192 d4096 N16 needs 8.4 MB, the
+ *   131072-token d5120 layer about 33 MB, and the convolution prologue adds
+ *   b*L*d elements of u).
+ *   The buffer's device address is looked up once per GPU, on the first call
+ *   whose stream belongs to that GPU; that first call is best made outside
+ *   graph capture. The call itself allocates nothing and frees nothing.
+ *   Calls on one GPU share its buffer: calls that overlap in time on that GPU
+ *   (two streams, or two host threads) race and give wrong results. Calls
+ *   ordered on one stream are safe. Nothing in the buffer needs to start at
+ *   zero: every pass writes what the next one reads.
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ssm_scan_fwd_noalloc(const ssm_scan_desc *desc,
+                         const void *u, const void *delta, const float *A,
+                         const void *B, const void *C, const float *D, const void *z,
+                         const float *h0, void *y, float *h_last, hipStream_t stream);
 
 /* ssm_scan_workspace_size / ssm_scan_fwd with an explicit launch shape
  * (tuning == NULL is the same as the plain calls). */

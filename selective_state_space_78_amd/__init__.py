@@ -6,7 +6,7 @@ HIP stream; the library itself is a plain C ABI (include/ssm_scan.h) that
 links no torch. There is no fallback: if the library is missing, every call
 raises.
 
-Names follow the C ABI: ``ssm_scan_fwd``, ``ssm_scan_workspace_size``,
+Names follow the C ABI: ``ssm_scan_fwd``, ``ssm_scan_fwd_noalloc``, ``ssm_scan_workspace_size``,
 ``ssm_scan_plan``, ``ssm_scan_bwd``, ``ssm_state_update``, ``ssm_ssd_fwd``,
 ``ssm_status_string``.
 """
@@ -27,7 +27,10 @@ _DISC = {"euler": SSM_DISC_EULER, "zoh": SSM_DISC_ZOH}
 EXPORTS = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_workspace_size_tuned",
            "ssm_scan_fwd_tuned", "ssm_scan_plan", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd",
            "ssm_scan_fwd_save", "ssm_scan_bwd_saved", "ssm_state_update", "ssm_ssd_fwd", "ssm_ssd_state_update",
-           "ssm_status_string")
+           "ssm_scan_fwd_noalloc", "ssm_status_string")
+
+# Fixed scratch of ssm_scan_fwd_noalloc per GPU (SSM_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class ScanDesc(ctypes.Structure):
@@ -78,6 +81,8 @@ def lib() -> ctypes.CDLL:
             scan_args = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz]
             L.ssm_scan_fwd.argtypes = scan_args + [vp]
             L.ssm_scan_fwd.restype = ctypes.c_int
+            L.ssm_scan_fwd_noalloc.argtypes = scan_args[:-2] + [vp]
+            L.ssm_scan_fwd_noalloc.restype = ctypes.c_int
             L.ssm_scan_fwd_tuned.argtypes = scan_args + [ptun, vp]
             L.ssm_scan_fwd_tuned.restype = ctypes.c_int
             L.ssm_scan_bwd_workspace_size.argtypes = [pdesc]
@@ -195,6 +200,19 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None
     return y, h_last
 
 
+def ssm_scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None,
+                         disc="euler", stream=None, want_h_last=True,
+                         delta_bias=None, delta_softplus=False, conv_weight=None, conv_bias=None):
+    """ssm_scan_fwd without a workspace (the C call of the same name): the
+    library's fixed per-GPU scratch serves instead, and the call allocates no
+    device memory of its own. Pass ``y`` (and ``h_last``) to allocate nothing
+    here either. Problems needing more than NOALLOC_SCRATCH_BYTES of scratch
+    raise SsmError (SSM_ERR_SCRATCH)."""
+    y, h_last, _ = _fwd(u, delta, A, B, C, D, z, h0, y, h_last, disc, None, None, stream, want_h_last,
+                        delta_bias, delta_softplus, conv_weight, conv_bias, save=False, noalloc=True)
+    return y, h_last
+
+
 def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last=None,
                       disc="euler", workspace=None, stream=None, want_h_last=True,
                       delta_bias=None, delta_softplus=False, conv_weight=None, conv_bias=None):
@@ -207,7 +225,7 @@ def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, h0=None, y=None, h_last
 
 
 def _fwd(u, delta, A, B, C, D, z, h0, y, h_last, disc, workspace, tuning, stream, want_h_last,
-         delta_bias, delta_softplus, conv_weight, conv_bias, save):
+         delta_bias, delta_softplus, conv_weight, conv_bias, save, noalloc=False):
     import torch
     batch, L, dim = u.shape
     N = A.shape[1]
@@ -234,6 +252,12 @@ def _fwd(u, delta, A, B, C, D, z, h0, y, h_last, disc, workspace, tuning, stream
     _check(conv_bias, "conv_bias", (dim,), torch.float32, dev)
     desc = make_desc(batch, L, dim, N, code, disc, delta_bias, delta_softplus, conv_weight, conv_bias)
     L_ = lib()
+    if noalloc:
+        rc = L_.ssm_scan_fwd_noalloc(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                     _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last), _stream(stream, dev))
+        if rc != 0:
+            raise SsmError(rc, "ssm_scan_fwd_noalloc")
+        return y, h_last, None
     if save:
         need = L_.ssm_scan_bwd_workspace_size(ctypes.byref(desc))
     elif tuning is None:

@@ -12,6 +12,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "ssm_scan.h"
@@ -1164,6 +1165,40 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     return SSM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The no-allocation forward's scratch: one fixed device array, held by every
+// GPU the library's module is loaded on until the process ends. Host code never
+// passes `scratch` itself to a kernel (on the host it is only a stand-in for
+// the symbol); it passes the device address looked up once per GPU below.
+
+static __device__ __align__(256) unsigned char scratch[SSM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];
+
+// The device address of `scratch` on the GPU that owns `stream` (the current
+// device for the null stream), looked up with that GPU current on the first
+// call for it.
+int scratch_address(hipStream_t stream, void **out) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return SSM_ERR_HIP;
+    int dev = cur;
+    if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return SSM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SSM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return SSM_ERR_HIP;
+        void *addr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return SSM_ERR_HIP;
+        if (e != hipSuccess || addr == nullptr) return SSM_ERR_HIP;
+        g_scratch_addr[dev] = addr;
+    }
+    *out = g_scratch_addr[dev];
+    return SSM_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1201,6 +1236,21 @@ extern "C" int ssm_scan_fwd(const ssm_scan_desc *desc, const void *u, const void
                             void *y, float *h_last, void *workspace, size_t workspace_bytes,
                             hipStream_t stream) {
     return scan_impl(desc, u, delta, A, B, C, D, z, h0, y, h_last, workspace, workspace_bytes, nullptr, stream);
+}
+
+extern "C" int ssm_scan_fwd_noalloc(const ssm_scan_desc *desc, const void *u, const void *delta,
+                                    const float *A, const void *B, const void *C, const float *D,
+                                    const void *z, const float *h0, void *y, float *h_last, hipStream_t stream) {
+    if (int rc = validate_desc(desc); rc != SSM_OK) return rc;
+    if (desc->batch == 0 || desc->dim == 0) return SSM_OK;
+    // the size check comes before any HIP call
+    const size_t need = workspace_bytes_for(*desc, make_plan(*desc, nullptr));
+    if (need > SSM_NOALLOC_SCRATCH_BYTES) return SSM_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0)
+        if (int rc = scratch_address(stream, &ws); rc != SSM_OK) return rc;
+    return scan_impl(desc, u, delta, A, B, C, D, z, h0, y, h_last, ws, ws ? SSM_NOALLOC_SCRATCH_BYTES : 0, nullptr,
+                     stream);
 }
 
 extern "C" int ssm_scan_fwd_save(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A,
@@ -1436,6 +1486,8 @@ extern "C" const char *ssm_status_string(int status) {
     case SSM_ERR_WORKSPACE: return "workspace missing or too small";
     case SSM_ERR_HIP: return "the HIP runtime refused a kernel launch";
     case SSM_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case SSM_ERR_SCRATCH: return "the problem needs more scratch than the no-allocation forward's fixed buffer "
+                                 "(SSM_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown status";
     }
 }
