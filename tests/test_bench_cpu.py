@@ -70,3 +70,18 @@ def test_committed_traffic_records(name, workload, algorithmic):
     assert rec["fetch_bytes"] + rec["write_bytes"] == pytest.approx(rec["bytes_per_launch"])
     ratio = rec["bytes_per_launch"] / algorithmic()
     assert 0.99 < ratio < 1.05, ratio
+
+
+def test_sampled_channels_cover_the_corners():
+    """The parity samples of the extra workloads are distinct, in range, and
+    include the first and last channel of the first and last batch row."""
+    for batch, dim, k in ((4, 1536, 16), (1, 5120, 16), (256, 5120, 8)):
+        ch = bench.sample_channels(batch, dim, k)
+        assert len(ch) == len(set(ch)) == max(k, 4)
+        assert all(0 <= b < batch and 0 <= d < dim for b, d in ch)
+        assert {(0, 0), (batch - 1, dim - 1)} <= set(ch)
+
+
+def test_cpu_baseline_uses_every_core():
+    """The oracle baseline runs on every core of the affinity mask (no cap)."""
+    assert bench.host_cores() == len(os.sched_getaffinity(0))

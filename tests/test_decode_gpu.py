@@ -85,8 +85,9 @@ def test_decode_equals_scan_of_length_one(env):
 
 def test_decode_workload_1000_steps(env):
     """b256 d5120 N16: 1000 in-place steps cycling over 64 distinct per-token input
-    sets; sampled channels checked against the oracle at every step, and every
-    channel's state after the first 3 steps and after the last."""
+    sets; every channel's state checked against the oracle after each of the
+    first 3 steps; 8 sampled channels' y checked at every one of the 1000 steps
+    and their state after the last."""
     torch, ssm = env
     cfg = si.DECODE
     say("decode workload: generating inputs")
