@@ -288,7 +288,11 @@ struct ScanKernel {
     // staging threads read chunk k-1's planes and write chunk k+1's pairs,
     // so one barrier per chunk orders everything.
     struct __align__(16) Smem {
-        float2 dx[2][TC][kTile];
+        union {
+            float2 dx[2][TC][kTile];
+            // aggregate pass, after the last chunk: the staging threads' step sums
+            double dred[kSum ? kRowStep : 1][kSum ? kTile : 1];
+        };
         float y[AGG ? 1 : 2][AGG ? 1 : G][AGG ? 1 : TC][AGG ? 1 : kTile];
     };
     static_assert(sizeof(Smem) <= 81920, "two workgroups per CU in 160 KiB of LDS");
@@ -443,7 +447,8 @@ struct ScanKernel {
     // that leaves the state unchanged.
     __device__ static void commit(const Prefetch &pf, float2 (*dx)[kTile], Held &held, int tval, int col,
                                   bool colv, const float (&Dk)[kV], bool gate, const float (&dbk)[kV], int prep,
-                                  int cw, const float (&wk)[kV][kConvMax], const float (&cbk)[kV]) {
+                                  int cw, const float (&wk)[kV][kConvMax], const float (&cbk)[kV],
+                                  double (&dsum)[kV]) {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
             const int row = piece_row(j);
@@ -462,6 +467,11 @@ struct ScanKernel {
 #pragma unroll
                 for (int e = 0; e < kV; e += 2)
                     dst[e / 2] = make_float4(d[e], ZOH ? u[e] : d[e] * u[e], d[e + 1], ZOH ? u[e + 1] : d[e + 1] * u[e + 1]);
+                if constexpr (kSum) {
+                    // the segment's sum of steps, once per (token, channel), in fp64
+#pragma unroll
+                    for (int e = 0; e < kV; ++e) dsum[e] += (double)d[e];
+                }
                 if constexpr (!AGG) {
 #pragma unroll
                     for (int e = 0; e < kV; ++e) held.sk[j][e] = Dk[e] * u[e];
@@ -546,7 +556,6 @@ struct ScanKernel {
     struct Lane {
         float A2[NPW], h[NPW];
         float Az[ZOH ? NPW : 1];
-        float dsum, dcomp;   // compensated sum of delta (aggregate pass)
     };
 
     // B_t[n] and C_t[n] reach the wave as scalar words: for bf16 inputs one
@@ -591,13 +600,6 @@ struct ScanKernel {
             }
             if (!AGG) part = q == 0 ? c_of(bc[q]) * l.h[q] : fmaf(c_of(bc[q]), l.h[q], part);
         }
-        if (kSum) {
-            // Kahan summation of delta over the segment
-            const float yk = dd - l.dcomp;
-            const float tk = l.dsum + yk;
-            l.dcomp = (tk - l.dsum) - yk;
-            l.dsum = tk;
-        }
         return part;
     }
 
@@ -617,8 +619,6 @@ struct ScanKernel {
 
         // Per-lane constants and initial state of this wave's states.
         Lane l;
-        l.dsum = 0.0f;
-        l.dcomp = 0.0f;
 #pragma unroll
         for (int k = 0; k < NPW; ++k) {
             const int n = w * NPW + k;
@@ -665,12 +665,15 @@ struct ScanKernel {
         auto rows_of = [&](int k) { return (int)min((int64_t)TC, t_end - t_begin - (int64_t)k * TC); };
         Prefetch pf;
         Held held[2];                                            // by chunk parity
+        double dsum[kV];                                         // aggregate pass: this thread's staged steps
+#pragma unroll
+        for (int e = 0; e < kV; ++e) dsum[e] = 0.0;
         auto load_chunk = [&](int k) {
             load(p, pf, (row0 + (int64_t)k * TC) * p.dim + d0, rows_of(k), col, d0, colv, t_begin + (int64_t)k * TC);
         };
         if (nchunks > 0) {
             load_chunk(0);
-            commit(pf, s.dx[0], held[0], rows_of(0), col, colv, Dk, gate, dbk, prep, convw, wk, cbk);
+            commit(pf, s.dx[0], held[0], rows_of(0), col, colv, Dk, gate, dbk, prep, convw, wk, cbk, dsum);
         }
         if (nchunks > 1) load_chunk(1);
         __syncthreads();
@@ -704,7 +707,7 @@ struct ScanKernel {
             fetch(0);
             Held next;
             if (k + 1 < nchunks)
-                commit(pf, s.dx[P ^ 1], next, rows_of(k + 1), col, colv, Dk, gate, dbk, prep, convw, wk, cbk);
+                commit(pf, s.dx[P ^ 1], next, rows_of(k + 1), col, colv, Dk, gate, dbk, prep, convw, wk, cbk, dsum);
             if constexpr (!AGG) {
                 if (k > 0) {
                     finalize(p, s.y[P ^ 1], held[P ^ 1], yb, TC, col, d0);
@@ -761,6 +764,19 @@ struct ScanKernel {
             }
         }
 
+        float dtot = 0.0f;
+        if constexpr (kSum) {
+            // the staging threads' sums of this segment's steps: thread
+            // (row group r, channels col..) holds rows r, r + kRowStep, ... of
+            // every chunk; every lane adds the groups of its channel in order.
+            // (dred aliases dx, which no wave reads after the last chunk's barrier.)
+#pragma unroll
+            for (int e = 0; e < kV; ++e) s.dred[threadIdx.x / kRowPieces][col + e] = dsum[e];
+            __syncthreads();
+            double acc = 0.0;
+            for (int r = 0; r < kRowStep; ++r) acc += s.dred[r][lane];
+            dtot = (float)acc;
+        }
         if (!dval) return;
 #pragma unroll
         for (int k = 0; k < NPW; ++k) {
@@ -768,7 +784,7 @@ struct ScanKernel {
             if (n >= p.N) continue;
             if (kSum) {
                 const int64_t o = (((int64_t)b * p.nseg + seg) * p.dim + d) * p.N + n;
-                p.agg_P[o] = __builtin_amdgcn_exp2f(l.A2[k] * l.dsum);
+                p.agg_P[o] = __builtin_amdgcn_exp2f(l.A2[k] * dtot);
                 p.agg_H[o] = l.h[k];
             } else if (kMain && p.h_last != nullptr && seg == p.nseg - 1) {
                 p.h_last[((int64_t)b * p.dim + d) * p.N + n] = l.h[k];

@@ -636,22 +636,31 @@ Plan make_plan(const ssm_scan_desc &d, const ssm_scan_tuning *t) {
     // layer runs fastest with 8 waves per tile, 4096 waves)
     const int64_t want_waves = 4096;
     int G = (t && t->state_groups > 0) ? t->state_groups : 0;
+    // segments cost a second (aggregate) pass over their tokens: add them only
+    // while the waves are too few, and keep them >= 256 tokens
+    auto segments_for = [&](int g) {
+        int s = 1;
+        if (tiles * g < want_waves)
+            while (s < kMaxSegments && tiles * g * s < 2 * want_waves && d.seqlen / (2 * s) >= 256) s *= 2;
+        return s;
+    };
     if (G == 0) {
         G = pl.npad > 16 ? pl.npad / 16 : 1;     // at most 16 states per wave
         while (G < 8 && G < pl.npad && tiles * G < want_waves) G *= 2;
+        // Too few channels for 8 waves per tile and long segments: 4 waves of
+        // 4 states per tile, whose smaller workgroups fit more per CU and add
+        // 3 instead of 7 partial readouts per output (measured on L 131072 x
+        // 5120 channels, 16 states: 4 waves x 32 segments 3.80 ms against 8 x
+        // 16 4.24 ms; on L 2048 x 6144 channels the segments are short and
+        // 8 waves x 8 segments stay faster, 0.105 against 0.106 ms)
+        if (G == 8 && pl.npad == 16 && tiles * G < want_waves && (t == nullptr || t->segments == 0) &&
+            d.seqlen / segments_for(4) >= 2048)
+            G = 4;
     }
     pl.G = G;
     pl.npw = pl.npad / G;
     int S = (t && t->segments > 0) ? t->segments : 0;
-    if (S == 0) {
-        S = 1;
-        // segments cost a second (aggregate) pass over their tokens: add them
-        // only while the waves are too few, and keep them >= 256 tokens
-        // (measured: 16 segments for L 131072 x 5120 channels, 8 for
-        // L 2048 x 6144 channels)
-        if (tiles * G < want_waves)
-            while (S < kMaxSegments && tiles * G * S < 2 * want_waves && d.seqlen / (2 * S) >= 256) S *= 2;
-    }
+    if (S == 0) S = segments_for(G);
     if (d.seqlen > 0 && S > d.seqlen) S = (int)d.seqlen;
     if (S < 1) S = 1;
     pl.S = S;
