@@ -250,8 +250,7 @@ def bench_scan_workload(torch, ssm, name, steps, warmup, sets=1):
         ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev.get("D"), dev.get("z"),
                          y=y, h_last=hl, workspace=ws)
 
-    for i in range(max(warmup, sets)):
-        call(i)
+    warm = settle(torch, call, max(warmup, sets))
     torch.cuda.synchronize()
     # back-to-back calls between one pair of events (events between the calls
     # would add their own gaps to calls of ~0.1 ms)
@@ -280,6 +279,7 @@ def bench_scan_workload(torch, ssm, name, steps, warmup, sets=1):
         "launch": {"state_groups": plan[0], "segments": plan[1]},
         "ms_per_call": ms,
         "calls": steps,
+        "warmup_calls": warm,
         "timing": "one event pair around the back-to-back calls",
         "Gtokens*ch/s": tok / (ms * 1e-3) / 1e9,
         "algorithmic_bytes_per_call": nbytes,
@@ -328,9 +328,11 @@ def bench_decode(torch, ssm, nsets=64, warmup=10, copy_gbps=None):
             s = sets[k % nsets]
             ssm.ssm_state_update(s["x"], s["delta"], A, s["B"], s["C"], h, D=D, z=s["z"], y=yv[k])
 
-    for i in range(warmup):
+    def one(i):
         s = sets[i % nsets]
         ssm.ssm_state_update(s["x"], s["delta"], A, s["B"], s["C"], h, D=D, z=s["z"], y=yv[0])
+
+    warm = settle(torch, one, warmup)
     # eager: one binding call per step from Python (its host cost is part of this figure)
     h.copy_(h_init)
     torch.cuda.synchronize()
@@ -345,6 +347,7 @@ def bench_decode(torch, ssm, nsets=64, warmup=10, copy_gbps=None):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         run_steps()
+    graph.replay()                      # warm again after the capture
     h.copy_(h_init)
     ybuf.zero_()
     torch.cuda.synchronize()
@@ -378,6 +381,7 @@ def bench_decode(torch, ssm, nsets=64, warmup=10, copy_gbps=None):
         "us_per_step": us,
         "ms_per_1000_steps": us * steps / 1e3,
         "timing": "the 1000 steps replayed from one HIP graph capture",
+        "warmup_steps": warm,
         "eager_us_per_step": us_eager,
         "Gtokens*ch/s": cfg.batch * cfg.dim / (us * 1e-6) / 1e9,
         "algorithmic_bytes_per_step": nbytes,
@@ -410,8 +414,7 @@ def bench_tiny(torch, ssm, reps=20):
     def call():
         ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev.get("D"), None, y=y, h_last=hl)
 
-    for _ in range(3):
-        call()
+    settle(torch, lambda i: call(), 3, 20.0)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in evs:
@@ -427,6 +430,30 @@ def bench_tiny(torch, ssm, reps=20):
         "parity": {"max_rel_err_y": rel_err(y.cpu().numpy(), yr), "max_rel_err_h_last": rel_err(hl.cpu().numpy(), hr),
                    "tolerance": 1e-4, "checked": "every output"},
     }
+
+
+# The GPU's clocks ramp up over the first few tens of milliseconds of work
+# after an idle spell (measured: the 1.4B-shaped scan takes 1.8 ms per call in
+# its first 10 calls after a 1 s pause and settles at 1.02 ms within 30 ms).
+# Every timed section therefore warms up for at least its warm-up count and at
+# least this much GPU time, and reports what it ran.
+SETTLE_MS = 200.0
+
+
+def settle(torch, fn, min_calls, min_ms=SETTLE_MS):
+    """Call fn() at least min_calls times and until min_ms of GPU time has
+    elapsed; returns the number of calls."""
+    n = 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    while True:
+        fn(n)
+        n += 1
+        if n >= min_calls and n % 4 == 0:
+            e1.record()
+            e1.synchronize()
+            if e0.elapsed_time(e1) >= min_ms:
+                return n
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
@@ -465,8 +492,7 @@ def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_
                              dh_last=dhl, workspace=ws, out=out, disc=disc, **step_opts)
         out.update(r)
 
-    for _ in range(warmup):
-        call()
+    warm = settle(torch, lambda i: call(), warmup)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -497,9 +523,7 @@ def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_
         out.update(r)
 
     def timed(fns):
-        for _ in range(warmup):
-            for f in fns:
-                f()
+        settle(torch, lambda i: [f() for f in fns], warmup)
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
         for e in evs:
@@ -519,6 +543,7 @@ def bench_backward(torch, ssm, cfg, dev, steps=10, warmup=2, disc="euler", step_
         "Gtokens*ch/s": cfg.tokens_ch / (ms * 1e-3) / 1e9,
         "workspace_bytes": need,
         "calls": steps,
+        "warmup_calls": warm,
         "training_step": {
             "workload": "forward + backward of the layer: ssm_scan_fwd then ssm_scan_bwd, against "
                         "ssm_scan_fwd_save (keeps the checkpoints) then ssm_scan_bwd_saved (reads them)",
@@ -549,8 +574,7 @@ def bench_ssd_decode(torch, ssm, batch=64, steps=200, warmup=10, sets=16, copy_g
         t = tok[k % sets]
         ssm.ssm_ssd_state_update(t["x"], t["dt"], A, t["B"], t["C"], h, D=D, z=t["z"], y=y)
 
-    for k in range(warmup):
-        step(k)
+    settle(torch, step, warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -590,8 +614,7 @@ def bench_ssd(torch, ssm, steps=20, warmup=3, cpu=True, budget_s=10.0, copy_gbps
     def call():
         ssm.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], y=y, h_last=hl)
 
-    for _ in range(warmup):
-        call()
+    warm = settle(torch, lambda i: call(), warmup)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
@@ -609,6 +632,8 @@ def bench_ssd(torch, ssm, steps=20, warmup=3, cpu=True, budget_s=10.0, copy_gbps
                     "fp32 A and state, final state written" % (cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim,
                                                                cfg.dstate, cfg.ngroups),
         "ms_per_call": ms,
+        "calls": steps,
+        "warmup_calls": warm,
         "Gtokens*ch/s": cfg.tokens_ch / (ms * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm",
@@ -715,8 +740,7 @@ def main():
                          y=y, h_last=h_last, workspace=ws, tuning=tuning, disc=args.disc, **step_opts)
 
     print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
+    warm = settle(torch, lambda i: step(), args.warmup)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base_alloc = torch.cuda.memory_allocated()
@@ -771,6 +795,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm,
+        "warmup_note": "at least --warmup steps and at least %.0f ms of GPU work, so that the timed steps run at "
+                       "the clocks the GPU reaches under sustained load" % SETTLE_MS,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -930,10 +930,6 @@ hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg,
                 : launch_scan_tf<T, NPW, G, TC, ZOH, CK, false>(p, nblocks_main, nblocks_agg, st);
 }
 
-#ifndef SSM_TC_G8
-#define SSM_TC_G8 16
-#endif
-
 template <typename T, bool ZOH>
 hipError_t launch_scan_shape(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st) {
     // (padded states, waves per tile, chunk length): LDS stays <= 80 KiB
@@ -943,7 +939,7 @@ hipError_t launch_scan_shape(const Plan &pl, const ScanParams &p, int nm, int na
     if (pl.npad == NP && pl.G == GG) return launch_scan_t<T, NP / GG, GG, TCC, ZOH, CK>(p, nm, na, st);
     SSM_CASE(4, 1, 16, 0)  SSM_CASE(4, 2, 16, 1)  SSM_CASE(4, 4, 8, 0)
     SSM_CASE(8, 1, 16, 0)  SSM_CASE(8, 2, 16, 0)  SSM_CASE(8, 4, 8, 0)   SSM_CASE(8, 8, 16, 1)
-    SSM_CASE(16, 1, 16, 0) SSM_CASE(16, 2, 16, 0) SSM_CASE(16, 4, 8, 0)  SSM_CASE(16, 8, SSM_TC_G8, 1)
+    SSM_CASE(16, 1, 16, 0) SSM_CASE(16, 2, 16, 0) SSM_CASE(16, 4, 8, 0)  SSM_CASE(16, 8, 16, 1)
     SSM_CASE(16, 16, 8, 0)
     SSM_CASE(32, 2, 16, 0) SSM_CASE(32, 4, 8, 0)  SSM_CASE(32, 8, 16, 0) SSM_CASE(32, 16, 8, 1)
     SSM_CASE(64, 4, 8, 0)  SSM_CASE(64, 8, 16, 0) SSM_CASE(64, 16, 8, 1)

@@ -12,10 +12,12 @@
 //   H_out = exp(S_last) H + sum_j exp(S_last - S_j) wbar_j x_j B_j^T
 //
 // Kernel design:
-//  * One workgroup (4 waves) owns one (batch row, head) and walks its chunks
-//    of Q = 64 tokens in order; the fp32 state never leaves registers. Wave w
-//    holds the state rows n in [w N/4, (w+1) N/4) for every p, as MFMA
-//    accumulators (h^T tiles: lane = p column, 4 consecutive n).
+//  * Four waves own one (batch row, head) and walk its chunks of Q = 64
+//    tokens in order; the fp32 state never leaves registers. Wave w holds the
+//    state rows n in [w N/4, (w+1) N/4) for every p, as MFMA accumulators
+//    (h^T tiles: lane = p column, 4 consecutive n). A workgroup of 8 waves
+//    takes two heads of one group, which share the staged B rows, when head
+//    size 64 lets their LDS fit; otherwise a workgroup is one head, 4 waves.
 //  * Every product is a 16x16x32 bf16 MFMA with fp32 accumulation:
 //      scores  G^T[j][i] = B_j . C_i        (K = n; operands straight from L2)
 //      readout Y^T[p][i] = H[p][:] . C_i    (K = n; H from LDS as bf16)
@@ -72,31 +74,15 @@ typedef float ssd_f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSsdQ = 64;        // tokens per chunk
 
 // LDS row padding (elements) of the token-row tiles of x and of the
-// n-contiguous tiles (B rows, state).
-#ifndef SSM_SSD_XPAD
-#define SSM_SSD_XPAD 16
-#endif
-#ifndef SSM_SSD_HPAD
-#define SSM_SSD_HPAD 16
-#endif
-// ... of the state copy (read as 16-byte row pieces), and the mask of the
-// row bits that swizzle its 64-byte column blocks
-#ifndef SSM_SSD_SPAD
-#define SSM_SSD_SPAD 8
-#endif
-#ifndef SSM_SSD_SWZ
-#define SSM_SSD_SWZ 1
-#endif
+// n-contiguous tiles (B rows), and of the state copy (read as 16-byte row
+// pieces); the mask of the row bits that swizzle the state copy's 64-byte
+// column blocks. A sweep of the pads over {8, 16, 24} and of the swizzle
+// (off, one bit, two bits) found these fastest.
+constexpr int kSsdXPad = 16;
+constexpr int kSsdHPad = 16;
+constexpr int kSsdSPad = 8;
+constexpr int kSsdSwizzle = 1;
 
-// Scheduling fences between the phases of a chunk: they keep the scheduler
-// from hoisting one phase's operand loads into the previous phase past the
-// register budget.
-#ifndef SSM_SSD_PHASE_FENCE_UPDATE
-#define SSM_SSD_PHASE_FENCE_UPDATE __builtin_amdgcn_sched_barrier(0);
-#endif
-#ifndef SSM_SSD_PHASE_FENCE_SCORES
-#define SSM_SSD_PHASE_FENCE_SCORES __builtin_amdgcn_sched_barrier(0);
-#endif
 constexpr int kSsdThreads = 256; // 4 waves
 
 __device__ __forceinline__ float ssd_bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -213,9 +199,9 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
     constexpr int NK = N / 32;     // MFMA steps over n
     constexpr int NW = N / 4;      // state rows per wave
     constexpr int NTW = NW / 16;   // state row tiles per wave
-    constexpr int XS = P + SSM_SSD_XPAD;   // LDS row stride of token rows of x (conflict-free transposing reads)
-    constexpr int HS = N + SSM_SSD_HPAD;   // LDS row stride of the B token rows (likewise)
-    constexpr int HSH = N + SSM_SSD_SPAD;  // LDS row stride of the state copy (16-byte row reads)
+    constexpr int XS = P + kSsdXPad;   // LDS row stride of token rows of x (conflict-free transposing reads)
+    constexpr int HS = N + kSsdHPad;   // LDS row stride of the B token rows (likewise)
+    constexpr int HSH = N + kSsdSPad;  // LDS row stride of the state copy (16-byte row reads)
     typedef SsdStage<P, N, HPW> Stage;
     static_assert(P % 32 == 0 && N % 64 == 0, "tile shape");
     static_assert(Stage::XI * 4 * 64 == Q * Stage::XPR && Stage::BI * 4 * HPW * 64 == Q * Stage::BPR,
@@ -250,7 +236,7 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
     // column swizzle of the state copy: the 64-byte column blocks of a row
     // are permuted by bits of its row index / 16, which spreads the writes
     // of a wave (rows 16 apart) over the banks
-    constexpr int SWZ = SSM_SSD_SWZ & (N / 32 - 1);
+    constexpr int SWZ = kSsdSwizzle & (N / 32 - 1);
     auto hcol = [](int R, int col) { return col ^ (32 * ((R >> 4) & SWZ)); };
 
     const int nb = gridDim.x, bid = blockIdx.x;
@@ -445,7 +431,9 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
                     yacc[pt] *= ei;
             }
 
-            SSM_SSD_PHASE_FENCE_SCORES
+            // scheduling fence: keeps the scheduler from hoisting this phase's
+            // operand loads into the previous one past the register budget
+            __builtin_amdgcn_sched_barrier(0);
             // scores of key tiles J <= WL, decayed, weighted, masked, as hi + lo
             // operands: element 4 (J%2) + r of m*[J/2] is M^T[16 J + 4 g4 + r][i]
             // (packed two to a word)
@@ -522,7 +510,7 @@ __global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const Ssd
                 ssd_bstore16(ry, 2u * ((uint32_t)(IW + r16) * xs32 + PW * g4 + 8 * k), o);
             }
 
-            SSM_SSD_PHASE_FENCE_UPDATE
+            __builtin_amdgcn_sched_barrier(0);   // (likewise)
             // ---- state update of rows [WL NW, (WL+1) NW)
             {
                 const float dec = __builtin_amdgcn_exp2f(Slast);
