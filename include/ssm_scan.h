@@ -84,7 +84,7 @@ typedef enum { SSM_DISC_EULER = 0, SSM_DISC_ZOH = 1 } ssm_disc;
 typedef struct {
     int64_t batch;   /* b  >= 0 */
     int64_t seqlen;  /* L  >= 0 */
-    int64_t dim;     /* d  >= 0 (channels, d_inner) */
+    int64_t dim;     /* d  in 0..2^26 (channels, d_inner) */
     int64_t dstate;  /* N  in 1..64 */
     int32_t dtype;   /* ssm_dtype */
     int32_t disc;    /* ssm_disc */

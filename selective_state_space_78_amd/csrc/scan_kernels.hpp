@@ -705,16 +705,17 @@ struct ScanKernel {
         auto chunk = [&](auto parity, int k) {
             constexpr int P = decltype(parity)::value;
             fetch(0);
-            Held next;
-            if (k + 1 < nchunks)
-                commit(pf, s.dx[P ^ 1], next, rows_of(k + 1), col, colv, Dk, gate, dbk, prep, convw, wk, cbk, dsum);
             if constexpr (!AGG) {
+                // chunk k-1's outputs first: its skip and gate then make room
+                // for chunk k+1's in the same registers
                 if (k > 0) {
                     finalize(p, s.y[P ^ 1], held[P ^ 1], yb, TC, col, d0);
                     yb += (int64_t)TC * p.dim;
                 }
-                if (k + 1 < nchunks) held[P ^ 1] = next;   // chunk k-1's skip and gate are consumed
             }
+            if (k + 1 < nchunks)
+                commit(pf, s.dx[P ^ 1], held[P ^ 1], rows_of(k + 1), col, colv, Dk, gate, dbk, prep, convw, wk, cbk,
+                       dsum);
             if (k + 2 < nchunks) load_chunk(k + 2);
             const int tval = rows_of(k);
             const float2 (*dx)[kTile] = s.dx[P];

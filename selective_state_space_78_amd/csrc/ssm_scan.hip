@@ -704,6 +704,8 @@ bool shape_compiled(const Plan &pl) {
     return false;
 }
 
+constexpr int64_t kMaxDim = int64_t(1) << 26;
+
 int validate_desc(const ssm_scan_desc *d) {
     if (d == nullptr) return SSM_ERR_NULL;
     if (d->batch < 0 || d->seqlen < 0 || d->dim < 0) return SSM_ERR_SHAPE;
@@ -725,6 +727,9 @@ int validate_desc(const ssm_scan_desc *d) {
     if (!mul_ok(d->batch, d->dim, &bdn) || !mul_ok(bdn, d->dstate * 4 * kMaxSegments * 3, &bytes))
         return SSM_ERR_SHAPE;
     if (d->batch > INT32_MAX || d->dim > INT32_MAX) return SSM_ERR_SHAPE;
+    // a chunk of up to 16 token rows of fp32 channels spans less than 4 GiB,
+    // so the kernels address it with 32-bit offsets
+    if (d->dim > kMaxDim) return SSM_ERR_SHAPE;
     return SSM_OK;
 }
 

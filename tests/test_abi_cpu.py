@@ -92,6 +92,16 @@ def test_scan_descriptor_errors(L):
     assert scan_call(L, desc(bias=8 * GB + 64)) == EALIAS        # bias inside the output y
 
 
+def test_scan_dim_limit(L):
+    """dim is bounded so that 16 token rows of fp32 channels span less than
+    4 GiB (the kernels' 32-bit offsets within a chunk); beyond it the forward,
+    the backward and the workspace queries refuse the shape on the host."""
+    assert scan_call(L, desc(b=1, L=16, d=(1 << 26) + 1, N=16)) == ESHAPE
+    assert L.ssm_scan_workspace_size(ctypes.byref(desc(b=1, L=16, d=(1 << 26) + 1, N=16))) == 0
+    assert bwd_call(L, desc(b=1, L=16, d=(1 << 26) + 1, N=16)) == ESHAPE
+    assert L.ssm_scan_workspace_size(ctypes.byref(desc(b=1, L=16, d=1 << 26, N=16))) > 0
+
+
 def test_scan_empty_problem_is_ok(L):
     # nothing to compute: returns before any device work
     assert scan_call(L, desc(b=0)) == OK
