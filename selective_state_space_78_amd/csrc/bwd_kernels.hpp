@@ -668,9 +668,13 @@ struct BwdKernel {
 
 // the simplified rule fits 128 VGPRs: at least 4 waves per SIMD (two 8-wave
 // workgroups, or one 16-wave one, per CU); the hold rule's reverse step needs
-// more registers, and capping it at 128 spilled 80-170 of them to scratch
+// more registers, and capping it at 128 spilled 80-170 of them to scratch.
+// With 2 waves per workgroup (up to 4 states) the staged chunk and planes take
+// 28.5 KB of LDS per workgroup, so at most 5 workgroups (2.5 waves per SIMD)
+// fit a CU whatever the registers: the target there is 2.
+template <int G, bool ZOH> constexpr int bwd_waves_per_simd() { return (ZOH || G == 2) ? 2 : 4; }
 template <typename T, int NPW, int G, int TC, bool ZOH, bool UF, bool FEAT>
-__global__ __launch_bounds__(kTile * G, ZOH ? 2 : 4) void bwd_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kTile * G, (bwd_waves_per_simd<G, ZOH>())) void bwd_kernel(const BwdParams p) {
     BwdKernel<T, NPW, G, TC, ZOH, UF, FEAT>::run(p);
 }
 

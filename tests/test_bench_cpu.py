@@ -85,3 +85,14 @@ def test_sampled_channels_cover_the_corners():
 def test_cpu_baseline_uses_every_core():
     """The oracle baseline runs on every core of the affinity mask (no cap)."""
     assert bench.host_cores() == len(os.sched_getaffinity(0))
+
+
+def test_committed_valu_record():
+    """The scan's instruction and clock record: counted on the current kernel
+    source in the headline launch shape, issue slots = VALU + transcendentals
+    (an exp costs two), and a clock near the part's 2.4 GHz."""
+    rec = json.load(open(os.path.join(ROOT, "profiles", "valu_scan_mamba1.4b.json")))
+    assert rec["workload"] == "mamba1.4b" and list(rec["launch"]) == [8, 1]
+    assert rec["issue_slots_per_token_ch"] == pytest.approx(rec["valu_per_token_ch"] + rec["trans_per_token_ch"], abs=0.02)
+    assert bench.valu_ops_per_token_ch(16, True) <= rec["valu_per_token_ch"] <= 130
+    assert 1.5 < rec["shader_clock_GHz"] <= 2.45
