@@ -76,10 +76,10 @@ typedef enum { SSM_DISC_EULER = 0, SSM_DISC_ZOH = 1 } ssm_disc;
  * MambaBlock.forward, x_conv = silu(conv1d(x)), a causal depthwise convolution
  * with left padding W-1): the buffer passed as u holds x, and the scan input is
  *     u[b,t,d] = silu(conv_bias[d] + sum_{k<W} conv_weight[d,k] * x[b,t-(W-1)+k,d]),
- * x before t = 0 being zero; the D skip uses this u. The forward forms u in
- * a pass of its own and keeps it in the tensors' type (bf16 tensors round it
- * to bf16, as the block's x_conv would be in a bf16 model); the backward forms
- * it in fp32.
+ * x before t = 0 being zero; the D skip uses this u. Forward and backward
+ * form u in a pass of their own and keep it in fp32, whatever the tensors'
+ * type (a bf16 rounding of u can show in y far beyond one rounding of y where
+ * the scan's sums cancel).
  * Zero-initialise the struct for "delta used as given, no convolution". */
 typedef struct {
     int64_t batch;   /* b  >= 0 */
@@ -108,9 +108,8 @@ typedef struct {
 /* Bytes of device workspace ssm_scan_fwd needs for `desc`: B and C widened
  * to fp32 (about 2 * batch * seqlen * dstate * 4 bytes) plus, when the
  * sequence is split into segments, three (batch, segments, dim, dstate) fp32
- * arrays, plus, with the convolution prologue, u (batch, seqlen, dim) in the
- * tensors' type. 0 when there is nothing to compute; 0 for an invalid
- * descriptor. */
+ * arrays, plus, with the convolution prologue, u (batch, seqlen, dim) in
+ * fp32. 0 when there is nothing to compute; 0 for an invalid descriptor. */
 size_t ssm_scan_workspace_size(const ssm_scan_desc *desc);
 
 /*
@@ -153,7 +152,7 @@ int ssm_scan_fwd(const ssm_scan_desc *desc,
  *   SSM_NOALLOC_SCRATCH_BYTES (checked on the host before anything else is
  *   done; e.g. the 1.4B-shaped layer b8 L8192 d4096 N16 needs 8.4 MB, the
  *   131072-token d5120 layer about 33 MB, and the convolution prologue adds
- *   b*L*d elements of u).
+ *   4*b*L*d bytes of fp32 u).
  *   The buffer's device address is looked up once per GPU, on the first call
  *   whose stream belongs to that GPU; that first call is best made outside
  *   graph capture. The call itself allocates nothing and frees nothing.
@@ -246,10 +245,8 @@ int ssm_scan_bwd(const ssm_scan_desc *desc,
  * (the checkpoints are the states the forward passes through). h_last equals
  * ssm_scan_fwd's bit for bit; y may differ from it in the last bit where the
  * backward's launch shape splits the states over another number of waves
- * and so sums the readout in another order. With the convolution prologue,
- * bf16 tensors and one segment, the saving forward forms u in fp32 (where the
- * backward then reads it) instead of bf16, so y and h_last differ from
- * ssm_scan_fwd's by that rounding of u.
+ * and so sums the readout in another order. With the convolution prologue the
+ * saving forward leaves its fp32 u where the backward then reads it.
  *
  *   workspace  at least ssm_scan_bwd_workspace_size(desc) bytes, 256-byte
  *              aligned, for both calls. ssm_scan_bwd_saved must receive the

@@ -13,9 +13,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 # translation units: the ABI (+ decode), one scan unit and one backward unit per
-# element type and discretisation, compiled in parallel and linked into one
-# shared object
-UNITS = ("ssm_scan.hip", "scan_bf16_euler.hip", "scan_bf16_zoh.hip", "scan_f32_euler.hip", "scan_f32_zoh.hip",
+# element type and discretisation (bf16 scans also one reading u in fp32),
+# compiled in parallel and linked into one shared object
+UNITS = ("ssm_scan.hip", "scan_bf16_euler.hip", "scan_bf16_zoh.hip", "scan_bf16_euler_u32.hip",
+         "scan_bf16_zoh_u32.hip", "scan_f32_euler.hip", "scan_f32_zoh.hip",
          "bwd_bf16_euler.hip", "bwd_bf16_zoh.hip", "bwd_f32_euler.hip", "bwd_f32_zoh.hip",
          "ssd_euler.hip", "ssd_zoh.hip")
 INCLUDE = os.path.join(ROOT, "include")

@@ -115,8 +115,6 @@ struct ScanParams {
     const void *u, *delta, *z, *B, *C;
     const float *delta_bias;  // (dim) added to delta before the recurrence uses it, or null
     int delta_softplus;       // the step is softplus(delta + bias)
-    int conv_w;               // 0, or the width of the causal convolution prologue (u holds x)
-    const float *conv_weight, *conv_bias;   // (dim, conv_w), (dim) or null
     const float *A, *D, *h0;
     float *Bf, *Cf;       // (batch, G, padded_len(L), Npad/G) fp32 widened B and C (workspace)
     const float *seg_h;   // (batch, nseg, dim, N) initial state of each segment, or null
@@ -130,8 +128,8 @@ struct ScanParams {
     int seg_len, nseg;
     int ntiles;
     int vec;              // u, delta, z, y move 4 channels per aligned access
-    int u_f32;            // u is fp32 whatever T is (the backward's checkpoint pass on the
-                          // convolution prologue's materialised output; one segment only)
+    int u_f32;            // u is fp32 whatever T is (the convolution prologue's output,
+                          // materialised by its own pass): the scan_bf16_*_u32 units
 };
 
 struct Plan {
@@ -164,9 +162,12 @@ inline WorkspaceLayout workspace_layout(int64_t batch, int64_t L, int64_t dim, i
 }
 
 // Launches the prologue, aggregate, carry and main passes for one element
-// type and discretisation (defined in the scan_<type>_<disc>.hip units).
+// type and discretisation (defined in the scan_<type>_<disc>.hip units; with
+// bf16 tensors and an fp32 u, the scan_bf16_<disc>_u32.hip units).
 hipError_t launch_scan_bf16_euler(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st);
 hipError_t launch_scan_bf16_zoh(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st);
+hipError_t launch_scan_bf16_euler_u32(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st);
+hipError_t launch_scan_bf16_zoh_u32(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st);
 hipError_t launch_scan_f32_euler(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st);
 hipError_t launch_scan_f32_zoh(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st);
 
@@ -253,9 +254,9 @@ template <> struct FloatsOf<4> { typedef float4 type; };
 // What a pass of the scan kernel produces.
 enum ScanMode { kModeMain = 0, kModeAggregate = 1, kModeCheckpoint = 2, kModeMainCheckpoint = 3 };
 
-// FEAT: the step and input prologue (delta bias, softplus, convolution) are
-// compiled in; without it the kernel carries none of their state (their
-// uniform values alone pushed the scalar registers into spills).
+// FEAT: the step options (delta bias, softplus) are compiled in; without it
+// the kernel carries none of their state (their uniform values alone pushed
+// the scalar registers into spills).
 template <typename T, int NPW, int G, int TC, bool ZOH, int MODE, bool FEAT, bool UF = false>
 struct ScanKernel {
     // main: y and h_last; aggregate: each segment's map h -> P h + H;
@@ -300,7 +301,6 @@ struct ScanKernel {
     struct Prefetch {
         URaw u[kPPT];
         Raw dt[kPPT], z[kPPT];
-        Raw xh[kPPT][FEAT ? kConvMax - 1 : 1];   // with the convolution prologue: x of the rows t-1, t-2, t-3
     };
 
     // D*u and silu(z) of the thread's staged pieces, kept in registers until
@@ -365,10 +365,8 @@ struct ScanKernel {
 
     // Issue the global loads of one chunk: `base` is the element offset of
     // (the chunk's first token row, the tile's first channel); rows [0, tval).
-    // pos0: sequence position of the chunk's first row (the convolution's
-    // history rows before position 0 are zero)
     __device__ static void load(const ScanParams &p, Prefetch &pf, int64_t base, int tval, int col, int d0,
-                                bool colv, int64_t pos0) {
+                                bool colv) {
         const T *u = static_cast<const T *>(p.u) + base;
         const T *dt = static_cast<const T *>(p.delta) + base;
         const T *z = static_cast<const T *>(p.z) + base;
@@ -393,52 +391,7 @@ struct ScanKernel {
                 pf.dt[j] = gather(dt + off, d0 + col, p.dim, true);
                 pf.z[j] = gather(z + off, d0 + col, p.dim, gate);
             }
-            if (FEAT && p.conv_w > 1) {
-                if (pos0 >= kConvMax - 1 && p.vec) {
-                    // every history row exists: one uniform base per row back
-#pragma unroll
-                    for (int k = 1; k < (FEAT ? kConvMax : 1); ++k) {
-                        if (k >= p.conv_w) break;
-                        const T *uk = u - (int64_t)k * p.dim;
-                        pf.xh[j][k - 1] = *reinterpret_cast<const Raw *>(uk + off);
-                    }
-                } else {
-#pragma unroll
-                    for (int k = 1; k < (FEAT ? kConvMax : 1); ++k) {
-                        if (k >= p.conv_w) break;
-                        // rows before position 0 are zero; their address is clamped
-                        // to the current row so that every load stays inside x
-                        const bool has = pos0 + row - k >= 0;
-                        const T *src = u + (int64_t)off - (has ? (int64_t)k * p.dim : 0);
-                        Raw r = p.vec ? *reinterpret_cast<const Raw *>(src) : gather(src, d0 + col, p.dim, true);
-                        if (!has) {
-                            const uint32_t zw[4] = {0u, 0u, 0u, 0u};
-                            make_words(r, zw);
-                        }
-                        pf.xh[j][k - 1] = r;
-                    }
-                }
-            }
         }
-    }
-
-    // The convolution prologue for one piece: x (in u on entry) and its
-    // history rows become silu(bias + sum_k w[k] x[t-(W-1)+k]).
-    __device__ static void conv_silu(const Prefetch &pf, int j, float (&u)[kV], int cw,
-                                     const float (&wk)[kV][kConvMax], const float (&cbk)[kV]) {
-        float acc[kV];
-#pragma unroll
-        for (int e = 0; e < kV; ++e) acc[e] = fmaf(wk[e][cw - 1], u[e], cbk[e]);
-#pragma unroll
-        for (int k = 1; k < (FEAT ? kConvMax : 1); ++k) {
-            if (k >= cw) break;
-            float xv[kV];
-            unpack(pf.xh[j][k - 1], xv);
-#pragma unroll
-            for (int e = 0; e < kV; ++e) acc[e] = fmaf(wk[e][cw - 1 - k], xv[e], acc[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < kV; ++e) u[e] = silu(acc[e]);
     }
 
     // Stage the prefetched chunk into LDS buffer `dx`, forming the per-token
@@ -447,7 +400,6 @@ struct ScanKernel {
     // that leaves the state unchanged.
     __device__ static void commit(const Prefetch &pf, float2 (*dx)[kTile], Held &held, int tval, int col,
                                   bool colv, const float (&Dk)[kV], bool gate, const float (&dbk)[kV], int prep,
-                                  int cw, const float (&wk)[kV][kConvMax], const float (&cbk)[kV],
                                   double (&dsum)[kV]) {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
@@ -458,7 +410,6 @@ struct ScanKernel {
                 float u[kV], d[kV];
                 unpack_u(pf.u[j], u);
                 unpack(pf.dt[j], d);
-                if (FEAT && cw) conv_silu(pf, j, u, cw, wk, cbk);
                 if (FEAT && prep) {
                     // the step: delta + bias, through softplus when asked
 #pragma unroll
@@ -564,9 +515,11 @@ struct ScanKernel {
     static constexpr bool kPacked = sizeof(T) == 2;
     static constexpr int kWPS = kPacked ? 1 : 2;               // words per state and step
     // Steps whose B and C words are fetched together: at most 32 scalar
-    // registers for packed words (which leaves room for the rest of the
-    // kernel's scalars without spills; 16 with the prologue), 64 for fp32 words
-    static constexpr int kBudget = kPacked ? (FEAT ? 16 : 32) : 64;   // the prologue's state needs scalars too
+    // registers for packed words (which leaves room for most of the rest of
+    // the kernel's scalars), 64 for fp32 words. With the step options 16 would
+    // avoid a few scalar spills, but fetching twice per chunk measured slower
+    // (1.20 against 1.16 ms on the 1.4B-shaped layer with the softplus step).
+    static constexpr int kBudget = kPacked ? 32 : 64;
     static constexpr int kTBMax = kBudget / (kWPS * NPW) > 0 ? kBudget / (kWPS * NPW) : 1;
     static constexpr int kTB = kTBMax < TC ? kTBMax : TC;
     static_assert(TC % kTB == 0, "batches of steps tile the chunk");
@@ -648,17 +601,6 @@ struct ScanKernel {
         }
         // 0: delta as given; 1: plus the bias; 2: softplus of that
         const int prep = !FEAT ? 0 : p.delta_softplus ? 2 : (p.delta_bias != nullptr ? 1 : 0);
-        // convolution prologue taps and bias of this thread's channels
-        const int convw = FEAT ? p.conv_w : 0;
-        float wk[kV][kConvMax], cbk[kV];
-#pragma unroll
-        for (int e = 0; e < kV; ++e) {
-            const bool cv = convw > 0 && d0 + col + e < p.dim;
-            cbk[e] = (cv && p.conv_bias != nullptr) ? p.conv_bias[d0 + col + e] : 0.0f;
-#pragma unroll
-            for (int k = 0; k < kConvMax; ++k)
-                wk[e][k] = (cv && k < convw) ? p.conv_weight[(int64_t)(d0 + col + e) * convw + k] : 0.0f;
-        }
 
         const int nchunks = (int)((t_end - t_begin + TC - 1) / TC);
         const int64_t row0 = (int64_t)b * p.L + t_begin;        // token row of (b, t_begin)
@@ -669,11 +611,11 @@ struct ScanKernel {
 #pragma unroll
         for (int e = 0; e < kV; ++e) dsum[e] = 0.0;
         auto load_chunk = [&](int k) {
-            load(p, pf, (row0 + (int64_t)k * TC) * p.dim + d0, rows_of(k), col, d0, colv, t_begin + (int64_t)k * TC);
+            load(p, pf, (row0 + (int64_t)k * TC) * p.dim + d0, rows_of(k), col, d0, colv);
         };
         if (nchunks > 0) {
             load_chunk(0);
-            commit(pf, s.dx[0], held[0], rows_of(0), col, colv, Dk, gate, dbk, prep, convw, wk, cbk, dsum);
+            commit(pf, s.dx[0], held[0], rows_of(0), col, colv, Dk, gate, dbk, prep, dsum);
         }
         if (nchunks > 1) load_chunk(1);
         __syncthreads();
@@ -714,8 +656,7 @@ struct ScanKernel {
                 }
             }
             if (k + 1 < nchunks)
-                commit(pf, s.dx[P ^ 1], held[P ^ 1], rows_of(k + 1), col, colv, Dk, gate, dbk, prep, convw, wk, cbk,
-                       dsum);
+                commit(pf, s.dx[P ^ 1], held[P ^ 1], rows_of(k + 1), col, colv, Dk, gate, dbk, prep, dsum);
             if (k + 2 < nchunks) load_chunk(k + 2);
             const int tval = rows_of(k);
             const float2 (*dx)[kTile] = s.dx[P];
@@ -859,10 +800,12 @@ __global__ __launch_bounds__(256) __attribute__((unused)) void carry_kernel(cons
     p.seg_h[((b * p.nseg + s) * p.dim * p.N) + dn] = fmaf(P, hin, H);
 }
 
-// CK: the shape also has the checkpoint pass (the launch shapes the backward uses)
-template <typename T, int NPW, int G, int TC, bool ZOH, bool CK, bool FEAT>
+// CK: the shape also has the checkpoint pass (the launch shapes the backward
+// uses). UF: u is fp32 with bf16 tensors (every pass reads it so).
+template <typename T, int NPW, int G, int TC, bool ZOH, bool CK, bool FEAT, bool UF>
 hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg, hipStream_t st) {
     if (!CK && p.ckpt != nullptr) return hipErrorInvalidValue;
+    if ((p.u_f32 != 0) != UF) return hipErrorInvalidValue;
     {
         const int64_t total = (int64_t)p.batch * padded_len(p.L) * (NPW * G);
         hipLaunchKernelGGL(widen_bc_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
@@ -871,7 +814,8 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if (nblocks_agg > 0) {
-        hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeAggregate, FEAT>), dim3(nblocks_agg), dim3(kTile * G), 0, st, p);
+        hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeAggregate, FEAT, UF>), dim3(nblocks_agg),
+                           dim3(kTile * G), 0, st, p);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         CarryParams cp{};
         cp.P = p.agg_P;
@@ -889,55 +833,37 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if constexpr (CK) {
-        if (p.ckpt != nullptr && p.y != nullptr) {
-            // the forward that also keeps the backward's checkpoints (with bf16
-            // tensors and the convolution pass's u in fp32: one segment only, as
-            // for the checkpoint pass)
-            if constexpr (sizeof(T) == 2) {
-                if (p.u_f32) {
-                    if (nblocks_agg > 0) return hipErrorInvalidValue;
-                    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMainCheckpoint, FEAT, true>),
-                                       dim3(nblocks_main), dim3(kTile * G), 0, st, p);
-                    return hipGetLastError();
-                }
-            }
-            hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMainCheckpoint, FEAT>), dim3(nblocks_main),
-                               dim3(kTile * G), 0, st, p);
-            return hipGetLastError();
-        }
         if (p.ckpt != nullptr) {
-            if constexpr (sizeof(T) == 2) {
-                if (p.u_f32) {
-                    // fp32 u with bf16 tensors: the aggregate pass has no such variant
-                    if (nblocks_agg > 0) return hipErrorInvalidValue;
-                    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeCheckpoint, FEAT, true>), dim3(nblocks_main),
-                                       dim3(kTile * G), 0, st, p);
-                    return hipGetLastError();
-                }
-            }
-            hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeCheckpoint, FEAT>), dim3(nblocks_main), dim3(kTile * G),
-                               0, st, p);
+            // the forward that also keeps the backward's checkpoints, or the
+            // checkpoints alone
+            if (p.y != nullptr)
+                hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMainCheckpoint, FEAT, UF>),
+                                   dim3(nblocks_main), dim3(kTile * G), 0, st, p);
+            else
+                hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeCheckpoint, FEAT, UF>), dim3(nblocks_main),
+                                   dim3(kTile * G), 0, st, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMain, FEAT>), dim3(nblocks_main), dim3(kTile * G), 0, st, p);
+    hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMain, FEAT, UF>), dim3(nblocks_main), dim3(kTile * G),
+                       0, st, p);
     return hipGetLastError();
 }
 
-template <typename T, int NPW, int G, int TC, bool ZOH, bool CK>
+template <typename T, int NPW, int G, int TC, bool ZOH, bool CK, bool UF>
 hipError_t launch_scan_t(const ScanParams &p, int nblocks_main, int nblocks_agg, hipStream_t st) {
-    const bool feat = p.delta_bias != nullptr || p.delta_softplus || p.conv_w > 0;
-    return feat ? launch_scan_tf<T, NPW, G, TC, ZOH, CK, true>(p, nblocks_main, nblocks_agg, st)
-                : launch_scan_tf<T, NPW, G, TC, ZOH, CK, false>(p, nblocks_main, nblocks_agg, st);
+    const bool feat = p.delta_bias != nullptr || p.delta_softplus;
+    return feat ? launch_scan_tf<T, NPW, G, TC, ZOH, CK, true, UF>(p, nblocks_main, nblocks_agg, st)
+                : launch_scan_tf<T, NPW, G, TC, ZOH, CK, false, UF>(p, nblocks_main, nblocks_agg, st);
 }
 
-template <typename T, bool ZOH>
+template <typename T, bool ZOH, bool UF = false>
 hipError_t launch_scan_shape(const Plan &pl, const ScanParams &p, int nm, int na, hipStream_t st) {
     // (padded states, waves per tile, chunk length): LDS stays <= 80 KiB
     // (two workgroups per CU) and every thread of a workgroup of up to 8
     // waves stages a piece of each chunk
 #define SSM_CASE(NP, GG, TCC, CK) \
-    if (pl.npad == NP && pl.G == GG) return launch_scan_t<T, NP / GG, GG, TCC, ZOH, CK>(p, nm, na, st);
+    if (pl.npad == NP && pl.G == GG) return launch_scan_t<T, NP / GG, GG, TCC, ZOH, CK, UF>(p, nm, na, st);
     SSM_CASE(4, 1, 16, 0)  SSM_CASE(4, 2, 16, 1)  SSM_CASE(4, 4, 8, 0)
     SSM_CASE(8, 1, 16, 0)  SSM_CASE(8, 2, 16, 0)  SSM_CASE(8, 4, 8, 0)   SSM_CASE(8, 8, 16, 1)
     SSM_CASE(16, 1, 16, 0) SSM_CASE(16, 2, 16, 0) SSM_CASE(16, 4, 8, 0)  SSM_CASE(16, 8, 16, 1)

@@ -56,8 +56,7 @@ constexpr int kConvBlock = 256;
 struct ConvParams {
     const void *x;            // (batch, L, dim)
     const float *w, *cb;      // (dim, W), (dim) or null
-    void *u;                  // conv_silu_kernel output (batch, L, dim): fp32 for the backward, the
-                              // tensors' type for the forward
+    void *u;                  // conv_silu_kernel output (batch, L, dim), fp32
     const float *du;          // gradient of u (fp32)
     void *dx;                 // gradient of x
     float *part_w, *part_b;   // (batch, nblk, dim, W), (batch, nblk, dim)
@@ -65,6 +64,7 @@ struct ConvParams {
     int64_t L;
     int batch, dim, W, nblk;
     int run;                  // tokens per thread of conv_silu_kernel
+    int b0;                   // first batch row of this launch (grid z: at most 65535 rows)
 };
 
 template <typename T>
@@ -152,7 +152,7 @@ template <typename T, int CPT, typename UT = float>
 __global__ __launch_bounds__(256) void conv_silu_kernel(const ConvParams p) {
     const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * CPT;
     if (d0 >= p.dim) return;
-    const int64_t row = (int64_t)blockIdx.z * p.L;
+    const int64_t row = (int64_t)(p.b0 + (int)blockIdx.z) * p.L;
     const int64_t t0 = (int64_t)blockIdx.y * p.run;
     if (t0 >= p.L) return;
     const int64_t t1 = min(p.L, t0 + p.run);
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const ConvParams p) {
     const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * CPT;
     if (d0 >= p.dim) return;
     const int blk = blockIdx.y;
-    const int b = blockIdx.z;
+    const int b = p.b0 + (int)blockIdx.z;
     const int W = p.W;
     float wr[CPT][kConvMax], cb[CPT];
     conv_taps<CPT>(p, d0, wr, cb);
@@ -300,6 +300,61 @@ __global__ __launch_bounds__(256) void conv_reduce_kernel(const ConvParams p) {
             for (int k = 0; k < p.nblk; ++k) acc += p.part_b[((int64_t)b * p.nblk + k) * p.dim + d];
         p.db[d] = acc;
     }
+}
+
+// Both prologue passes run over every batch row in launches of at most 65535
+// rows, the grid's z extent.
+constexpr int64_t kMaxGridZ = 65535;
+
+// u = silu(conv(x)) in fp32. cpt: channels per thread (4 for whole, aligned
+// 4-channel pieces, else 1).
+hipError_t launch_conv_silu(ConvParams cp, bool bf16, int cpt, hipStream_t stream) {
+    // runs of at least 64 tokens, at most 65535 of them per batch row
+    const int64_t runs = std::min<int64_t>((cp.L + 63) / 64, 65535);
+    cp.run = (int)((cp.L + runs - 1) / runs);
+    for (int64_t b0 = 0; b0 < cp.batch; b0 += kMaxGridZ) {
+        cp.b0 = (int)b0;
+        const dim3 grid((unsigned)((cp.dim / cpt + 255) / 256), (unsigned)runs,
+                        (unsigned)std::min<int64_t>(kMaxGridZ, cp.batch - b0));
+        if (bf16) {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 4, float>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 1, float>), grid, dim3(256), 0, stream, cp);
+        } else {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_silu_kernel<float, 4, float>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_silu_kernel<float, 1, float>), grid, dim3(256), 0, stream, cp);
+        }
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// dx and the per-block tap and bias partials, then their fixed-order sums.
+hipError_t launch_conv_bwd(ConvParams cp, bool bf16, int cpt, hipStream_t stream) {
+    for (int64_t b0 = 0; b0 < cp.batch; b0 += kMaxGridZ) {
+        cp.b0 = (int)b0;
+        const dim3 grid((unsigned)((cp.dim / cpt + 255) / 256), (unsigned)cp.nblk,
+                        (unsigned)std::min<int64_t>(kMaxGridZ, cp.batch - b0));
+        if (bf16) {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_bwd_kernel<uint16_t, 4>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_bwd_kernel<uint16_t, 1>), grid, dim3(256), 0, stream, cp);
+        } else {
+            if (cpt == 4)
+                hipLaunchKernelGGL((conv_bwd_kernel<float, 4>), grid, dim3(256), 0, stream, cp);
+            else
+                hipLaunchKernelGGL((conv_bwd_kernel<float, 1>), grid, dim3(256), 0, stream, cp);
+        }
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    cp.b0 = 0;
+    const int64_t nr = (int64_t)cp.dim * cp.W + cp.dim;
+    hipLaunchKernelGGL(conv_reduce_kernel, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, stream, cp);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -678,20 +733,30 @@ bool plan_supported(const Plan &pl) {
     return pl.seg_len > 0 || pl.S == 1;
 }
 
-// The forward runs the convolution prologue as a pass of its own (when the
-// batch fits that pass's grid): u = silu(conv(x)) in the tensors' type, in the
-// workspace after the scan's own part. The scan is ALU-bound, so the fused
-// prologue's instructions cost it more than this pass's memory traffic.
-bool conv_pass(const ssm_scan_desc &d) { return d.conv_width > 0 && d.batch <= 65535; }
-
-size_t conv_u_bytes(const ssm_scan_desc &d) {
-    return align256((size_t)d.batch * d.seqlen * d.dim * (d.dtype == SSM_BF16 ? 2 : 4));
+// The scan's passes for the descriptor's element type and rule; bf16 tensors
+// whose u is the convolution pass's fp32 output take the units reading u so.
+hipError_t launch_scan(const ssm_scan_desc &d, const Plan &pl, const ScanParams &p, int nm, int na,
+                       hipStream_t stream) {
+    const bool zoh = d.disc == SSM_DISC_ZOH;
+    if (d.dtype == SSM_BF16 && p.u_f32)
+        return zoh ? launch_scan_bf16_zoh_u32(pl, p, nm, na, stream) : launch_scan_bf16_euler_u32(pl, p, nm, na, stream);
+    if (d.dtype == SSM_BF16)
+        return zoh ? launch_scan_bf16_zoh(pl, p, nm, na, stream) : launch_scan_bf16_euler(pl, p, nm, na, stream);
+    return zoh ? launch_scan_f32_zoh(pl, p, nm, na, stream) : launch_scan_f32_euler(pl, p, nm, na, stream);
 }
+
+// The forward runs the convolution prologue as a pass of its own: u =
+// silu(conv(x)) in fp32, in the workspace after the scan's own part. The scan
+// is ALU-bound, so the prologue's instructions inside it cost it more than this
+// pass's memory traffic. u stays fp32 for bf16 tensors too: the scan sums many
+// products of it, which can cancel, and a bf16 rounding of u then shows in y
+// well beyond one rounding of y.
+size_t conv_u_bytes(const ssm_scan_desc &d) { return align256((size_t)d.batch * d.seqlen * d.dim * 4); }
 
 size_t workspace_bytes_for(const ssm_scan_desc &d, const Plan &pl) {
     if (d.batch == 0 || d.dim == 0 || d.seqlen == 0) return 0;
     const size_t scan = align256(workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, pl).total);
-    return scan + (conv_pass(d) ? conv_u_bytes(d) : 0);
+    return scan + (d.conv_width > 0 ? conv_u_bytes(d) : 0);
 }
 
 bool shape_compiled(const Plan &pl) {
@@ -739,7 +804,7 @@ int validate_desc(const ssm_scan_desc *d) {
 struct SaveForBwd {
     size_t need, ckpt;
     int nck;
-    size_t conv_u;   // where the convolution pass's u goes (the backward's fp32 u, formed again there)
+    size_t conv_u;   // where the convolution pass's u goes (where the backward reads it)
 };
 
 int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const float *A,
@@ -795,12 +860,14 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
         return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
     }
 
-    // the convolution prologue as a pass of its own; the scan then reads its u.
-    // Keeping the checkpoints over one segment, it writes u in fp32 where the
-    // backward reads it, so that the backward need not form it again
+    // the main pass's grid (checked before anything is launched)
+    if ((d.dim + kTile - 1) / kTile * d.batch * pl.S > INT32_MAX) return SSM_ERR_SHAPE;
+
+    // the convolution prologue as a pass of its own, writing u in fp32; the scan
+    // then reads that u. Keeping the checkpoints, it writes u where the backward
+    // reads it, so that the backward need not form it again
     const void *us = u;
-    const bool u32 = save && pl.S == 1 && d.dtype == SSM_BF16;
-    if (conv_pass(d)) {
+    if (d.conv_width > 0) {
         char *ws = static_cast<char *>(workspace);
         void *uw = ws + (save ? save->conv_u : align256(workspace_layout(d.batch, d.seqlen, d.dim, d.dstate, pl).total));
         ConvParams cp{};
@@ -812,38 +879,15 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
         cp.batch = (int)d.batch;
         cp.dim = (int)d.dim;
         cp.W = d.conv_width;
-        // runs of at least 64 tokens, at most 65535 of them per batch row
-        const int64_t runs = std::min<int64_t>((d.seqlen + 63) / 64, 65535);
-        cp.run = (int)((d.seqlen + runs - 1) / runs);
         const int cpt = (d.dim % 4 == 0 && aligned(u, 4 * es)) ? 4 : 1;
-        const dim3 grid((unsigned)((d.dim / cpt + 255) / 256), (unsigned)runs, (unsigned)d.batch);
-        if (u32) {
-            if (cpt == 4)
-                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 4, float>), grid, dim3(256), 0, stream, cp);
-            else
-                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 1, float>), grid, dim3(256), 0, stream, cp);
-        } else if (d.dtype == SSM_BF16) {
-            if (cpt == 4)
-                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 4, uint16_t>), grid, dim3(256), 0, stream, cp);
-            else
-                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 1, uint16_t>), grid, dim3(256), 0, stream, cp);
-        } else {
-            if (cpt == 4)
-                hipLaunchKernelGGL((conv_silu_kernel<float, 4, float>), grid, dim3(256), 0, stream, cp);
-            else
-                hipLaunchKernelGGL((conv_silu_kernel<float, 1, float>), grid, dim3(256), 0, stream, cp);
-        }
-        if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
+        if (launch_conv_silu(cp, d.dtype == SSM_BF16, cpt, stream) != hipSuccess) return SSM_ERR_HIP;
         us = uw;
     }
 
     ScanParams p{};
     p.u = us; p.delta = delta; p.z = z; p.B = B; p.C = C;
-    p.u_f32 = us != u && u32;
+    p.u_f32 = us != u && d.dtype == SSM_BF16;
     p.delta_bias = d.delta_bias; p.delta_softplus = d.delta_softplus;
-    if (us == u) {
-        p.conv_w = d.conv_width; p.conv_weight = d.conv_weight; p.conv_bias = d.conv_width ? d.conv_bias : nullptr;
-    }
     p.A = A; p.D = D; p.h0 = h0;
     p.y = y; p.h_last = h_last;
     p.L = d.seqlen;
@@ -874,17 +918,7 @@ int scan_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const
     const int64_t blocks_per_seg = (int64_t)p.ntiles * d.batch;
     const int64_t nm = blocks_per_seg * pl.S;
     const int64_t na = pl.S > 1 ? blocks_per_seg * (pl.S - 1) : 0;
-    if (nm > INT32_MAX) return SSM_ERR_SHAPE;
-
-    hipError_t e;
-    const bool zoh = d.disc == SSM_DISC_ZOH;
-    if (d.dtype == SSM_BF16)
-        e = zoh ? launch_scan_bf16_zoh(pl, p, (int)nm, (int)na, stream)
-                : launch_scan_bf16_euler(pl, p, (int)nm, (int)na, stream);
-    else
-        e = zoh ? launch_scan_f32_zoh(pl, p, (int)nm, (int)na, stream)
-                : launch_scan_f32_euler(pl, p, (int)nm, (int)na, stream);
-    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    return launch_scan(d, pl, p, (int)nm, (int)na, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 // Backward workspace: the checkpoint pass's forward workspace (regrouped B, C
@@ -1022,9 +1056,12 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     // they are whole and aligned (the workspace's u and du always are)
     const int cpt = (d.dim % 4 == 0 && aligned(x_in, 4 * es) && aligned(dx_out, 4 * es)) ? 4 : 1;
     ConvParams cp{};
-    // a forward that kept the checkpoints has left u in fp32 here (fp32 tensors,
-    // or bf16 ones over one segment)
-    const bool u_saved = saved && conv_pass(d) && (d.dtype == SSM_F32 || wl.pl.S == 1);
+    // a forward that kept the checkpoints has left u in fp32 here
+    const bool u_saved = saved && cw > 0;
+    // grids, checked before anything is launched: the checkpoint pass's blocks,
+    // conv_bwd_kernel's 256-token blocks (grid y)
+    if ((int64_t)wl.ntiles * d.batch * wl.pl.S > INT32_MAX) return SSM_ERR_SHAPE;
+    if (cw > 0 && wl.nblk > 65535) return SSM_ERR_SHAPE;
     if (cw > 0) {
         cp.x = x_in;
         cp.w = d.conv_weight;
@@ -1041,40 +1078,16 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
         cp.dim = (int)d.dim;
         cp.W = cw;
         cp.nblk = wl.nblk;
-        // runs of at least 64 tokens, at most 65535 of them per batch row
-        const int64_t runs = std::min<int64_t>((d.seqlen + 63) / 64, 65535);
-        cp.run = (int)((d.seqlen + runs - 1) / runs);
-        if (d.batch > 65535) return SSM_ERR_SHAPE;
-        const dim3 grid((unsigned)((d.dim / cpt + 255) / 256), (unsigned)runs, (unsigned)d.batch);
-        if (u_saved) {
-        } else if (d.dtype == SSM_BF16) {
-            if (cpt == 4)
-                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 4>), grid, dim3(256), 0, stream, cp);
-            else
-                hipLaunchKernelGGL((conv_silu_kernel<uint16_t, 1>), grid, dim3(256), 0, stream, cp);
-        } else {
-            if (cpt == 4)
-                hipLaunchKernelGGL((conv_silu_kernel<float, 4>), grid, dim3(256), 0, stream, cp);
-            else
-                hipLaunchKernelGGL((conv_silu_kernel<float, 1>), grid, dim3(256), 0, stream, cp);
-        }
-        if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
+        if (!u_saved && launch_conv_silu(cp, d.dtype == SSM_BF16, cpt, stream) != hipSuccess) return SSM_ERR_HIP;
     }
     const bool vec = (d.dim % 4 == 0) && aligned(u, 4 * es) && aligned(delta, 4 * es) && (!z || aligned(z, 4 * es)) &&
                      aligned(dy, 4 * es) && aligned(du, 4 * es) && aligned(ddelta, 4 * es) &&
                      (!z || aligned(dz, 4 * es));
     // 1. checkpoints: the forward scan in its checkpoint mode (segment-parallel).
-    // With the prologue and one segment it reads the u materialised above (fp32);
-    // with several segments it forms u from x itself, as the forward does
+    // With the prologue it reads the u materialised above (fp32)
     ScanParams p{};
-    p.u = u; p.delta = delta; p.z = z; p.B = B; p.C = C;
-    p.conv_w = cw; p.conv_weight = d.conv_weight; p.conv_bias = d.conv_bias;
-    if (cw > 0 && wl.pl.S == 1) {
-        p.u = cp.u;
-        p.u_f32 = d.dtype == SSM_BF16;
-        p.conv_w = 0;
-        p.conv_weight = p.conv_bias = nullptr;
-    }
+    p.u = cw > 0 ? cp.u : u; p.delta = delta; p.z = z; p.B = B; p.C = C;
+    p.u_f32 = cw > 0 && d.dtype == SSM_BF16;
     p.delta_bias = dbias; p.delta_softplus = d.delta_softplus;
     p.A = A; p.D = D; p.h0 = h0;
     p.L = d.seqlen;
@@ -1100,20 +1113,11 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     const int64_t blocks_per_seg = (int64_t)wl.ntiles * d.batch;
     const int64_t nm = blocks_per_seg * wl.pl.S;
     const int64_t na = wl.pl.S > 1 ? blocks_per_seg * (wl.pl.S - 1) : 0;
-    if (nm > INT32_MAX) return SSM_ERR_SHAPE;
     const bool zoh = d.disc == SSM_DISC_ZOH;
     hipError_t e = hipSuccess;
     // (a forward that kept the checkpoints has left them, and the regrouped B
     // and C, in this workspace)
-    if (!saved) {
-        if (d.dtype == SSM_BF16)
-            e = zoh ? launch_scan_bf16_zoh(wl.pl, p, (int)nm, (int)na, stream)
-                    : launch_scan_bf16_euler(wl.pl, p, (int)nm, (int)na, stream);
-        else
-            e = zoh ? launch_scan_f32_zoh(wl.pl, p, (int)nm, (int)na, stream)
-                    : launch_scan_f32_euler(wl.pl, p, (int)nm, (int)na, stream);
-        if (e != hipSuccess) return SSM_ERR_HIP;
-    }
+    if (!saved && launch_scan(d, wl.pl, p, (int)nm, (int)na, stream) != hipSuccess) return SSM_ERR_HIP;
 
     // 2. the reverse pass
     BwdParams bp{};
@@ -1157,24 +1161,7 @@ int bwd_impl(const ssm_scan_desc *desc, const void *u, const void *delta, const 
     if (e != hipSuccess) return SSM_ERR_HIP;
 
     // 4. the convolution prologue: dx, and the sums of the tap and bias gradients
-    if (cw > 0) {
-        if (wl.nblk > 65535 || d.batch > 65535) return SSM_ERR_SHAPE;
-        const dim3 grid((unsigned)((d.dim / cpt + 255) / 256), (unsigned)wl.nblk, (unsigned)d.batch);
-        if (d.dtype == SSM_BF16) {
-            if (cpt == 4)
-                hipLaunchKernelGGL((conv_bwd_kernel<uint16_t, 4>), grid, dim3(256), 0, stream, cp);
-            else
-                hipLaunchKernelGGL((conv_bwd_kernel<uint16_t, 1>), grid, dim3(256), 0, stream, cp);
-        } else {
-            if (cpt == 4)
-                hipLaunchKernelGGL((conv_bwd_kernel<float, 4>), grid, dim3(256), 0, stream, cp);
-            else
-                hipLaunchKernelGGL((conv_bwd_kernel<float, 1>), grid, dim3(256), 0, stream, cp);
-        }
-        const int64_t nr = (int64_t)d.dim * cw + d.dim;
-        hipLaunchKernelGGL(conv_reduce_kernel, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, stream, cp);
-        if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
-    }
+    if (cw > 0 && launch_conv_bwd(cp, d.dtype == SSM_BF16, cpt, stream) != hipSuccess) return SSM_ERR_HIP;
     return SSM_OK;
 }
 

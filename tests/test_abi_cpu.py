@@ -301,15 +301,17 @@ def test_training_pair_workspace(L):
 
 def test_conv_prologue_forward_workspace(L):
     """The forward runs the convolution prologue as a pass of its own and keeps
-    its u, in the tensors' type, in the workspace after the scan's part; a
-    workspace sized without it is rejected before any launch."""
+    its u, in fp32 whatever the tensors' type, in the workspace after the
+    scan's part (for any batch: the pass runs in slices of rows); a workspace
+    sized without it is rejected before any launch."""
     rnd = lambda v: (v + 255) // 256 * 256
-    for dtype, es in ((ssm.SSM_BF16, 2), (ssm.SSM_F32, 4)):
-        plain = L.ssm_scan_workspace_size(ctypes.byref(desc(b=2, L=100, d=64, N=16, dtype=dtype)))
-        dc = desc(b=2, L=100, d=64, N=16, dtype=dtype, conv=4, cw=17 * GB)
-        conv = L.ssm_scan_workspace_size(ctypes.byref(dc))
-        assert conv == rnd(plain) + rnd(2 * 100 * 64 * es)
-        assert scan_call(L, dc, ws_bytes=conv - 1) == EWS
+    for dtype in (ssm.SSM_BF16, ssm.SSM_F32):
+        for b in (70000, 2):
+            plain = L.ssm_scan_workspace_size(ctypes.byref(desc(b=b, L=100, d=64, N=16, dtype=dtype)))
+            dc = desc(b=b, L=100, d=64, N=16, dtype=dtype, conv=4, cw=17 * GB)
+            conv = L.ssm_scan_workspace_size(ctypes.byref(dc))
+            assert conv == rnd(plain) + rnd(b * 100 * 64 * 4)
+        assert scan_call(L, dc, ws_bytes=conv - 1) == EWS    # b = 2
 
 
 def test_ssd_decode_errors(L):

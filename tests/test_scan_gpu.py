@@ -345,25 +345,35 @@ def test_conv_prologue(env, dtype, disc, W):
     assert ey <= tol and eh <= tol
 
 
-def test_conv_prologue_fused_for_large_batch(env):
-    """More batch rows (65536) than the conv pass's grid takes: the forward
-    forms u in the scan kernel's staging instead (the fused prologue), and
-    its workspace has no room for u."""
+def test_conv_prologue_large_batch(env):
+    """More batch rows (65536) than one launch's grid takes in z: the
+    prologue's passes run in slices of at most 65535 rows, forward and
+    backward, and the workspace holds u in fp32."""
     import dataclasses
+    from test_bwd_gpu import CONV_GRADS, compare_all, widen
     torch, ssm = env
     cfg = dataclasses.replace(si.CONFIGS["mamba130m"], dtype="bf16")
-    x = si.scan_inputs(cfg, seed=91, batch=65536, seqlen=5, dim=4, dstate=4)
-    c = si.conv_inputs(4, 4, seed=91)
-    assert ssm.ssm_scan_workspace_size(65536, 5, 4, 4) == ssm.ssm_scan_workspace_size(
-        65536, 5, 4, 4, conv_weight=to_dev(c["conv_weight"], torch))
+    b, L, d, N = 65536, 5, 4, 4
+    x = si.scan_inputs(cfg, seed=91, batch=b, seqlen=L, dim=d, dstate=N)
+    g = si.grad_inputs(cfg, seed=91, batch=b, seqlen=L, dim=d, dstate=N)
+    c = si.conv_inputs(d, 4, seed=91)
+    cw, cb = to_dev(c["conv_weight"], torch), to_dev(c["conv_bias"], torch)
+    assert ssm.ssm_scan_workspace_size(b, L, d, N, conv_weight=cw) == \
+        ssm.ssm_scan_workspace_size(b, L, d, N) + (b * L * d * 4 + 255) // 256 * 256
     dev = {k: to_dev(v, torch) for k, v in x.items() if k != "h0"}
     yr, hr = oracle.load().selective_scan(**x, **c)
     y, hl = ssm.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
-                             conv_weight=to_dev(c["conv_weight"], torch), conv_bias=to_dev(c["conv_bias"], torch))
+                             conv_weight=cw, conv_bias=cb)
     torch.cuda.synchronize()
     ey, eh = rel_err(to_np(y), yr), rel_err(to_np(hl), hr)
-    say("conv W4 bf16, batch 65536 (fused prologue): y %.3e h %.3e" % (ey, eh))
+    say("conv W4 bf16, batch 65536: y %.3e h %.3e" % (ey, eh))
     assert ey <= tol_of(x) and eh <= tol_of(x)
+    out = ssm.ssm_scan_bwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], to_dev(g["dy"], torch),
+                           D=dev["D"], z=dev["z"], dh_last=to_dev(g["dh_last"], torch), conv_weight=cw, conv_bias=cb)
+    torch.cuda.synchronize()
+    got = {k: to_np(v) for k, v in out.items()}
+    ref = oracle.load().selective_scan_bwd(**x, dy=widen(g["dy"]), dh_last=g["dh_last"], **c)
+    compare_all(x, got, ref, "conv batch 65536", keys=CONV_GRADS)
 
 
 def test_conv_prologue_full_size(env):
