@@ -73,15 +73,9 @@ typedef float ssd_f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSsdQ = 64;        // tokens per chunk
 
-// LDS row padding (elements) of the token-row tiles of x and of the
-// n-contiguous tiles (B rows), and of the state copy (read as 16-byte row
-// pieces); the mask of the row bits that swizzle the state copy's 64-byte
-// column blocks. A sweep of the pads over {8, 16, 24} and of the swizzle
-// (off, one bit, two bits) found these fastest.
-constexpr int kSsdXPad = 16;
-constexpr int kSsdHPad = 16;
-constexpr int kSsdSPad = 8;
-constexpr int kSsdSwizzle = 1;
+// LDS row padding (elements) of the token-row tiles of x and of B and C.
+constexpr int kSsdXPad = 8;
+constexpr int kSsdHPad = 8;
 
 constexpr int kSsdThreads = 256; // 4 waves
 
@@ -174,402 +168,443 @@ __device__ __forceinline__ void ssd_bstore16(__amdgpu_buffer_rsrc_t r, uint32_t 
     __builtin_amdgcn_raw_buffer_store_b128(ssd_u32x4{v.x, v.y, v.z, v.w}, r, (int)off, 0, 0);
 }
 
-// One chunk's global inputs as a lane (= token) of each wave loads them, one
-// chunk ahead of their use.
-template <int P, int N, int HPW>
-struct SsdStage {
-    // 16-byte pieces of a chunk's x rows (this head's P values per token) and
-    // B rows (N values per token), numbered token-major; consecutive lanes
-    // take consecutive pieces, so a load instruction covers whole rows.
-    static constexpr int XPR = P / 8;                        // x pieces per token row
-    static constexpr int XI = kSsdQ * XPR / (4 * 64);        // x loads per wave (four waves per head)
-    static constexpr int BPR = N / 8;                        // B pieces per token row
-    static constexpr int BI = kSsdQ * BPR / (4 * HPW * 64);  // B loads per wave (all waves)
-    uint16_t dt;                 // bf16 step of token `lane` for this wave's head
-    uint4 x[XI];                 // x piece wl XI 64 + 64 k + lane
-    uint4 b[BI];                 // B piece w BI 64 + 64 k + lane
-};
+typedef unsigned int ssd_u32x2 __attribute__((ext_vector_type(2)));
 
-// HPW heads of one group per workgroup, four waves per head; the heads share
-// the staged B tiles.
+__device__ __forceinline__ uint2 ssd_bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const ssd_u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return uint2{v.x, v.y};
+}
+
+__device__ __forceinline__ void ssd_bstore8(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint2 &v) {
+    __builtin_amdgcn_raw_buffer_store_b64(ssd_u32x2{v.x, v.y}, r, (int)off, 0, 0);
+}
+
+// The chunk's causal score tiles (output token tile T, key token tile J <= T),
+// dealt round-robin to the helper waves.
+constexpr int kSsdTiles = 10;
+constexpr int kSsdTileT[kSsdTiles] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+constexpr int kSsdTileJ[kSsdTiles] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// Slot of the masked scores of (T, key half Jp) in the exchange buffer
+__host__ __device__ constexpr int ssd_slot(int T, int Jp) { return T < 2 ? T : 2 + 2 * (T - 2) + Jp; }
+constexpr int kSsdSlots = 6;
+
+// HPW heads of one group per workgroup. Per head four compute waves hold the
+// state (wave WL: p tiles WL, WL + 4, ...; every n) and make the chunk's
+// outputs and state update; 4 HPW helper waves prepare the next chunk
+// meanwhile: they stage its x, B and C rows, its step tables and its masked
+// scores into the other half of double-buffered LDS.
 template <int P, int N, bool ZOH, int HPW>
-__global__ __launch_bounds__(kSsdThreads * HPW, 1) void ssd_fwd_kernel(const SsdParams p) {
+__global__ __launch_bounds__(2 * kSsdThreads * HPW) void ssd_fwd_kernel(const SsdParams p) {
     constexpr int Q = kSsdQ;
     constexpr int PT = P / 16;     // p tiles
+    constexpr int NT = N / 16;     // n tiles
     constexpr int NK = N / 32;     // MFMA steps over n
-    constexpr int NW = N / 4;      // state rows per wave
-    constexpr int NTW = NW / 16;   // state row tiles per wave
-    constexpr int XS = P + kSsdXPad;   // LDS row stride of token rows of x (conflict-free transposing reads)
-    constexpr int HS = N + kSsdHPad;   // LDS row stride of the B token rows (likewise)
-    constexpr int HSH = N + kSsdSPad;  // LDS row stride of the state copy (16-byte row reads)
-    typedef SsdStage<P, N, HPW> Stage;
+    constexpr int XS = P + kSsdXPad;   // LDS row stride of the x token rows
+    constexpr int HS = N + kSsdHPad;   // LDS row stride of the B and C token rows
+    constexpr int NH = kSsdThreads * HPW;   // helper threads
+    // staging: 16-byte pieces of the token rows, numbered (head,) token-major;
+    // helper thread ut takes pieces k NH + ut, so that one load instruction
+    // covers whole rows of one head
+    constexpr int XPR = P / 8, BPR = N / 8;                  // pieces per token row
+    constexpr int XI = HPW * Q * XPR / NH;                   // x loads per helper thread
+    constexpr int BI = Q * BPR / NH;                         // B (and C) loads per helper thread
     static_assert(P % 32 == 0 && N % 64 == 0, "tile shape");
-    static_assert(Stage::XI * 4 * 64 == Q * Stage::XPR && Stage::BI * 4 * HPW * 64 == Q * Stage::BPR,
-                  "staging pieces cover the chunk");
+    static_assert(XI * NH == HPW * Q * XPR && BI * NH == Q * BPR, "staging pieces cover the chunk");
+    static_assert(HPW == 1 || (Q * XPR) % NH == 0, "one head per x load instruction");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sBR[Q * HS];         // B, token rows
-    __shared__ __attribute__((aligned(16))) uint16_t sXT[HPW][Q * XS];    // x, token rows, output channel order
-    __shared__ __attribute__((aligned(16))) uint16_t sXh[HPW][Q * XS];    // wbar exp(S_last - S_j) x, hi
-    __shared__ __attribute__((aligned(16))) uint16_t sXl[HPW][Q * XS];    // ... lo
-    __shared__ __attribute__((aligned(16))) uint16_t sHh[HPW][P * HSH];   // state entering the chunk, hi
-    __shared__ __attribute__((aligned(16))) uint16_t sHl[HPW][P * HSH];   // ... lo
+    __shared__ __attribute__((aligned(16))) uint16_t sX[2][HPW][Q * XS];   // x, token rows
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][Q * HS];        // B, token rows
+    __shared__ __attribute__((aligned(16))) uint16_t sC[2][Q * HS];        // C, token rows
+    __shared__ __attribute__((aligned(16))) uint4 sM[2][HPW][kSsdSlots][2][64];   // masked scores, hi and lo
+    __shared__ __attribute__((aligned(16))) float sS[2][HPW][Q];   // S_t: prefix sums of a dt (log2)
+    __shared__ __attribute__((aligned(16))) float sW[2][HPW][Q];   // wbar_t
+    __shared__ __attribute__((aligned(16))) float sF[2][HPW][Q];   // wbar_t exp(S_last - S_t)
 
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int hs = w >> 2;               // head slot
-    // role within the head: the second head takes the roles in reverse, so
-    // that the two waves sharing a SIMD (w and w + 4) pair a short and a long
-    // causal triangle
-    const int wl = hs ? 3 - (w & 3) : (w & 3);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
-    const int I0 = 16 * wl;              // this wave's output tokens within a chunk
-    // Output channel order: row m of p tile pt of the readout's and the
-    // masked product's outputs is channel PW (m / 4) + 4 pt + m % 4, so that
-    // the output accumulator rows 4 g4 .. 4 g4 + 3 of all tiles are the PW
-    // contiguous channels PW g4 .. PW g4 + PW - 1. The state and its update
-    // keep the natural order (row m of tile pt is channel 16 pt + m). The raw
-    // x rows in LDS hold channel PW a + 4 pt + r in column xcol = 16 pt + 4 a + r,
-    // and the state's bf16 copy puts channel c in row hrow(c): both are then
-    // read in the output order with natural addressing.
-    constexpr int PW = P / 4;
-    auto hrow = [](int c) { return 16 * ((c % PW) >> 2) + 4 * (c / PW) + (c & 3); };
-    // column swizzle of the state copy: the 64-byte column blocks of a row
-    // are permuted by bits of its row index / 16, which spreads the writes
-    // of a wave (rows 16 apart) over the banks
-    constexpr int SWZ = kSsdSwizzle & (N / 32 - 1);
-    auto hcol = [](int R, int col) { return col ^ (32 * ((R >> 4) & SWZ)); };
 
     const int nb = gridDim.x, bid = blockIdx.x;
     const int qx = nb / kXcds, rx = nb % kXcds, xcd = bid % kXcds;
     const int logical = xcd * qx + min(xcd, rx) + bid / kXcds;
     const int hpb = p.H / HPW;
     const int b = logical / hpb;
-    const int h = (logical % hpb) * HPW + hs;
-    const int grp = h / p.hpg;
-
-    const float a = p.A[h];
-    const float a2 = a * kLog2e;
-    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
-    const float dskip = p.D ? p.D[h] : 0.0f;
+    const int hbase = (logical % hpb) * HPW;
+    const int grp = hbase / p.hpg;
     const int64_t L = p.L;
     const int64_t xs = (int64_t)p.H * P;   // token stride of x, z, y
     const int64_t bs = (int64_t)p.G * N;   // token stride of B, C
     // (64 token rows of x and of B fit 32-bit element offsets: the library checks it)
     const uint32_t xs32 = (uint32_t)xs, bs32 = (uint32_t)bs, H32 = (uint32_t)p.H;
-    const uint16_t *xb = p.x + (int64_t)b * L * xs + (int64_t)h * P;
-    const uint16_t *zb = p.z ? p.z + (int64_t)b * L * xs + (int64_t)h * P : nullptr;
-    uint16_t *yb = p.y + (int64_t)b * L * xs + (int64_t)h * P;
-    const uint16_t *Bb = p.B + (int64_t)b * L * bs + (int64_t)grp * N;
-    const uint16_t *Cb = p.C + (int64_t)b * L * bs + (int64_t)grp * N;
-    const uint16_t *db = p.dt + (int64_t)b * L * p.H + h;
-    uint16_t *const XT = sXT[hs];
-    uint16_t *const Xh = sXh[hs];
-    uint16_t *const Xl = sXl[hs];
-    uint16_t *const Hh = sHh[hs];
-    uint16_t *const Hl = sHl[hs];
-
-    // byte offsets of the lane's staging pieces within a chunk; the same for
-    // every chunk, whose buffers start at its first token
-    uint32_t xoff[Stage::XI], boff[Stage::BI];
-#pragma unroll
-    for (int k = 0; k < Stage::XI; ++k) {
-        const int piece = (wl * Stage::XI + k) * 64 + lane;
-        xoff[k] = 2u * ((uint32_t)(piece / Stage::XPR) * xs32 + 8u * (piece % Stage::XPR));
-    }
-#pragma unroll
-    for (int k = 0; k < Stage::BI; ++k) {
-        const int piece = (w * Stage::BI + k) * 64 + lane;
-        boff[k] = 2u * ((uint32_t)(piece / Stage::BPR) * bs32 + 8u * (piece % Stage::BPR));
-    }
-    // Valid tokens of the chunk starting at c (0 past the end)
+    const int nchunks = (int)((L + Q - 1) / Q);
     auto valid_tokens = [&](int64_t c) { return (uint32_t)max<int64_t>(0, min<int64_t>(Q, L - c)); };
-    // Staging loads of the chunk starting at c, one chunk ahead: the buffers
-    // end at the chunk's last valid token, so rows past the end read as zero
-    // and a chunk past the end loads nothing.
-    auto load_stage = [&](int64_t c, Stage &st) {
-        const uint32_t nv = valid_tokens(c);
-        const __amdgpu_buffer_rsrc_t rd = ssd_buffer(db + c * p.H, 2u * nv * H32);
-        const __amdgpu_buffer_rsrc_t rxb = ssd_buffer(xb + c * xs, 2u * nv * xs32);
-        const __amdgpu_buffer_rsrc_t rbb = ssd_buffer(Bb + c * bs, 2u * nv * bs32);
-        st.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)(2u * (uint32_t)lane * H32), 0, 0);
-#pragma unroll
-        for (int k = 0; k < Stage::XI; ++k)
-            st.x[k] = ssd_bload16(rxb, xoff[k]);
-#pragma unroll
-        for (int k = 0; k < Stage::BI; ++k)
-            st.b[k] = ssd_bload16(rbb, boff[k]);
-    };
 
-    // State: hacc[i][pt][r] = h[p = 16 pt + r16][n = 16 (wl NTW + i) + 4 g4 + r]; its
-    // bf16 copy in LDS is written to rows hrow(p), the order in which the
-    // readout's A operand takes its rows.
-    ssd_f32x4 hacc[NTW][PT];
-    const float *h0b = p.h0 ? p.h0 + ((int64_t)b * p.H + h) * P * N : nullptr;
+    if (w >= 4 * HPW) {
+        // ================= helper waves =================
+        const int ut = tid - kSsdThreads * HPW;   // 0 .. NH - 1 (after the 4 HPW compute waves)
+        const int u = w - 4 * HPW;
+        const uint16_t *Bb = p.B + (int64_t)b * L * bs + (int64_t)grp * N;
+        const uint16_t *Cb = p.C + (int64_t)b * L * bs + (int64_t)grp * N;
+        uint32_t xoff[XI], boff[BI];
 #pragma unroll
-    for (int i = 0; i < NTW; ++i)
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const int n = 16 * (wl * NTW + i) + 4 * g4;
-            hacc[i][pt] = h0b ? *reinterpret_cast<const ssd_f32x4 *>(h0b + (16 * pt + r16) * N + n)
-                              : ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k = 0; k < XI; ++k) {
+            const int rem = (k * NH + ut) % (Q * XPR);
+            xoff[k] = 2u * ((uint32_t)(rem / XPR) * xs32 + 8u * (rem % XPR));
         }
-
-    Stage st;
-    load_stage(0, st);
-    // nothing of the prologue stays in flight into the loop (the loop's wait
-    // counts then only see its own loads)
-    __builtin_amdgcn_s_waitcnt(0);
-
-    for (int64_t c0 = 0; c0 < L; c0 += Q) {
-        const uint32_t nvu = valid_tokens(c0);
-        const int nv = (int)nvu;                         // valid tokens in this chunk
-        const bool valid = lane < nv;
-
-        // this wave's C rows (operands of the readout and the scores) and
-        // gate values, issued before the next chunk's staging loads, so that
-        // waiting for them never waits for those; rows past the end read zero
-        const __amdgpu_buffer_rsrc_t rc = ssd_buffer(Cb + c0 * bs, 2u * nvu * bs32);
-        ssd_bf16x8 cop[NK];
 #pragma unroll
-        for (int s = 0; s < NK; ++s)
-            cop[s] = __builtin_bit_cast(ssd_bf16x8,
-                                        ssd_bload16(rc, 2u * ((uint32_t)(I0 + r16) * bs32 + 32 * s + 8 * g4)));
-        const __amdgpu_buffer_rsrc_t rz = ssd_buffer(zb ? zb + c0 * xs : xb, zb ? 2u * nvu * xs32 : 0u);
-        uint4 zop[PT / 2];
+        for (int k = 0; k < BI; ++k) {
+            const int piece = k * NH + ut;
+            boff[k] = 2u * ((uint32_t)(piece / BPR) * bs32 + 8u * (piece % BPR));
+        }
+        uint4 xr[XI], br[BI], cr[BI];
+        // the last HPW helpers also form the step tables, helper 4 HPW - HPW + hs
+        // those of head hs: its dt (token `lane`), and the head's constants
+        const int th = u - 3 * HPW;              // head of the tables this helper forms, or < 0
+        const int hth = hbase + (th >= 0 ? th : 0);
+        const uint16_t *dtb = p.dt + (int64_t)b * L * p.H + hth;
+        const float a = p.A[hth];
+        const float a2 = a * kLog2e;
+        const float bias = p.dt_bias ? p.dt_bias[hth] : 0.0f;
+        uint16_t dtr = 0;
+        // loads of the chunk starting at c (rows past the end read zero)
+        auto load = [&](int64_t c) {
+            const uint32_t nv = valid_tokens(c);
+            if (th >= 0)
+                dtr = __builtin_amdgcn_raw_buffer_load_b16(ssd_buffer(dtb + c * p.H, 2u * nv * H32),
+                                                           (int)(2u * (uint32_t)lane * H32), 0, 0);
 #pragma unroll
-        for (int k = 0; k < PT / 2; ++k)
-            zop[k] = ssd_bload16(rz, 2u * ((uint32_t)(I0 + r16) * xs32 + PW * g4 + 8 * k));
-
-        // the state entering this chunk, as hi + lo bf16 (every wave has
-        // finished reading the previous one: barrier at the end of the last chunk)
-#pragma unroll
-        for (int i = 0; i < NTW; ++i)
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                uint2 hi, lo;
-                ssd_split2(hacc[i][pt][0], hacc[i][pt][1], hi.x, lo.x);
-                ssd_split2(hacc[i][pt][2], hacc[i][pt][3], hi.y, lo.y);
-                const int R = hrow(16 * pt + r16);
-                const int o = R * HSH + hcol(R, 16 * (wl * NTW + i) + 4 * g4);
-                *reinterpret_cast<uint2 *>(&Hh[o]) = hi;
-                *reinterpret_cast<uint2 *>(&Hl[o]) = lo;
+            for (int k = 0; k < XI; ++k) {
+                const int hs = k * NH / (Q * XPR);
+                const uint16_t *xb = p.x + ((int64_t)b * L + c) * xs + (int64_t)(hbase + hs) * P;
+                xr[k] = ssd_bload16(ssd_buffer(xb, 2u * nv * xs32), xoff[k]);
             }
-
-        // step, decay and input weight of token `lane` (every wave of a head computes all 64)
-        float step = 0.0f;
-        if (valid) {
-            step = ssd_bf(st.dt) + bias;
-            if (p.dt_softplus)
-                step = softplus_f(step);
-        }
-        const float la = step * a2;                 // log2 of the token's decay
-        float wbar = step;
-        if (ZOH)
-            wbar = step * expm1_over_x(step * a, __builtin_amdgcn_exp2f(la));
-        const float S = ssd_prefix_sum(la, lane);    // inclusive prefix sum over the chunk
-        const float Slast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), 63));
-        const float fd = wbar * __builtin_amdgcn_exp2f(Slast - S);
-
-        // stage x (raw, in the output channel order, and weighted for the
-        // state update as hi + lo) and B as token rows, one 16-byte piece per
-        // lane and load. Products over tokens read these rows with
-        // transposing LDS reads.
+            const __amdgpu_buffer_rsrc_t rb = ssd_buffer(Bb + c * bs, 2u * nv * bs32);
+            const __amdgpu_buffer_rsrc_t rc = ssd_buffer(Cb + c * bs, 2u * nv * bs32);
 #pragma unroll
-        for (int k = 0; k < Stage::XI; ++k) {
-            const int piece = (wl * Stage::XI + k) * 64 + lane;
-            const int t = piece / Stage::XPR;
-            const int col = 8 * (piece % Stage::XPR);
-            const float f = __shfl(fd, t);        // the piece's token's weight
-            const uint4 v = st.x[k];
-            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ssd_split2(ssd_bf(wd[e] & 0xffffu) * f, ssd_bf(wd[e] >> 16) * f, hw[e], lw[e]);
-            const int o = t * XS + col;
-            // channels col .. col + 3 and col + 4 .. col + 7 of the output order
-            const int xo = t * XS + 16 * ((col % PW) >> 2) + 4 * (col / PW);
-            *reinterpret_cast<uint2 *>(&XT[xo]) = uint2{v.x, v.y};
-            *reinterpret_cast<uint2 *>(&XT[xo + 16]) = uint2{v.z, v.w};
-            *reinterpret_cast<uint4 *>(&Xh[o]) = uint4{hw[0], hw[1], hw[2], hw[3]};
-            *reinterpret_cast<uint4 *>(&Xl[o]) = uint4{lw[0], lw[1], lw[2], lw[3]};
-        }
-#pragma unroll
-        for (int k = 0; k < Stage::BI; ++k) {
-            const int piece = (w * Stage::BI + k) * 64 + lane;
-            *reinterpret_cast<uint4 *>(&sBR[(piece / Stage::BPR) * HS + 8 * (piece % Stage::BPR)]) = st.b[k];
-        }
-        // the next chunk's staging loads (nothing past the end)
-        load_stage(c0 + Q, st);
-        __syncthreads();
-
-        // The rest of the chunk, specialised on the wave's role so that each
-        // role is straight-line code the scheduler can interleave.
-        auto compute = [&](auto role) {
-            constexpr int WL = decltype(role)::value;
-            constexpr int IW = 16 * WL;
-            // ---- outputs of tokens [IW, IW + 16): lane column i = IW + r16
-            const float Si = __shfl(S, IW + r16);
-
-            // readout of the state entering the chunk (hi + lo)
-            ssd_f32x4 yacc[PT];
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                yacc[pt] = ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int s = 0; s < NK; ++s) {
-                    const int R = 16 * pt + r16;
-                    const int o = R * HSH + hcol(R, 32 * s + 8 * g4);
-                    yacc[pt] = ssd_mfma(ssd_ld16(&Hh[o]), cop[s], yacc[pt]);
-                    yacc[pt] = ssd_mfma(ssd_ld16(&Hl[o]), cop[s], yacc[pt]);
-                }
+            for (int k = 0; k < BI; ++k) {
+                br[k] = ssd_bload16(rb, boff[k]);
+                cr[k] = ssd_bload16(rc, boff[k]);
             }
-            {
-                const float ei = __builtin_amdgcn_exp2f(Si);
+        };
+        // Scores of the chunk staged in buffer `buf`, decayed, weighted and
+        // masked for each head, as hi + lo bf16: the lane of tile (T, J) holds
+        // M^T[16 J + 4 g4 + r][16 T + r16], element 4 (J % 2) + r of the same
+        // lane's operand of the compute waves' (T, J / 2) product. The tiles
+        // are dealt round-robin to the helpers; each forms its tile's scores
+        // C_i . B_j once for the workgroup's heads (they share B and C). U, the
+        // helper, is a constant, so that a helper's tiles form one
+        // straight-line block whose loads, products and exponentials overlap.
+        auto score_jobs = [&](auto uc, int buf) {
+            constexpr int U = decltype(uc)::value;
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    yacc[pt] *= ei;
-            }
-
-            // scheduling fence: keeps the scheduler from hoisting this phase's
-            // operand loads into the previous one past the register budget
-            __builtin_amdgcn_sched_barrier(0);
-            // scores of key tiles J <= WL, decayed, weighted, masked, as hi + lo
-            // operands: element 4 (J%2) + r of m*[J/2] is M^T[16 J + 4 g4 + r][i]
-            // (packed two to a word)
-            uint32_t mh[2][4], ml[2][4];
+            for (int q = 0; q < kSsdTiles; ++q) {
+                if (q % (4 * HPW) != U) continue;
+                const int T = kSsdTileT[q], J = kSsdTileJ[q];
+                ssd_f32x4 gt = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                if (J <= WL) {
-                    ssd_f32x4 gt = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int s = 0; s < NK; ++s)
+                    gt = ssd_mfma(ssd_ld16(&sB[buf][(16 * J + r16) * HS + 32 * s + 8 * g4]),
+                                  ssd_ld16(&sC[buf][(16 * T + r16) * HS + 32 * s + 8 * g4]), gt);
 #pragma unroll
-                    for (int s = 0; s < NK; ++s)
-                        gt = ssd_mfma(ssd_ld16(&sBR[(16 * J + r16) * HS + 32 * s + 8 * g4]), cop[s], gt);
+                for (int hs = 0; hs < HPW; ++hs) {
+                    const float Si = sS[buf][hs][16 * T + r16];
+                    const float4 Sj = *reinterpret_cast<const float4 *>(&sS[buf][hs][16 * J + 4 * g4]);
+                    const float4 Wj = *reinterpret_cast<const float4 *>(&sW[buf][hs][16 * J + 4 * g4]);
+                    const float sj[4] = {Sj.x, Sj.y, Sj.z, Sj.w}, wj[4] = {Wj.x, Wj.y, Wj.z, Wj.w};
                     float m[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int jj = 16 * J + 4 * g4 + r;
-                        const float Sj = __shfl(S, jj);
-                        const float wj = __shfl(wbar, jj);
-                        const bool keep = J < WL || 4 * g4 + r <= r16;
-                        m[r] = keep ? gt[r] * __builtin_amdgcn_exp2f(Si - Sj) * wj : 0.0f;
+                        const bool keep = J < T || 4 * g4 + r <= r16;
+                        m[r] = keep ? gt[r] * __builtin_amdgcn_exp2f(Si - sj[r]) * wj[r] : 0.0f;
                     }
-                    ssd_split2(m[0], m[1], mh[J >> 1][2 * (J & 1)], ml[J >> 1][2 * (J & 1)]);
-                    ssd_split2(m[2], m[3], mh[J >> 1][2 * (J & 1) + 1], ml[J >> 1][2 * (J & 1) + 1]);
-                } else if ((J & 1) && J - 1 <= WL) {
-                    // odd key tile past the diagonal, paired with a computed one: zeros
-                    mh[J >> 1][2] = mh[J >> 1][3] = 0u;
-                    ml[J >> 1][2] = ml[J >> 1][3] = 0u;
-                }
-            }
-#pragma unroll
-            for (int Jp = 0; Jp < 2; ++Jp) {
-                if (2 * Jp <= WL) {
-                    const ssd_bf16x8 mhv = __builtin_bit_cast(ssd_bf16x8, uint4{mh[Jp][0], mh[Jp][1], mh[Jp][2], mh[Jp][3]});
-                    const ssd_bf16x8 mlv = __builtin_bit_cast(ssd_bf16x8, uint4{ml[Jp][0], ml[Jp][1], ml[Jp][2], ml[Jp][3]});
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        // x^T operand in the K order of mh / ml: tokens
-                        // 32 Jp + 4 g4 + e, then 32 Jp + 16 + 4 g4 + e
-                        const uint16_t *src = &XT[(32 * Jp + 4 * g4 + (r16 >> 2)) * XS + 16 * pt + 4 * (r16 & 3)];
-                        const ssd_bf16x8 xo = ssd_ld_tr2(src, src + 16 * XS);
-                        yacc[pt] = ssd_mfma(xo, mhv, yacc[pt]);
-                        yacc[pt] = ssd_mfma(xo, mlv, yacc[pt]);
-                    }
-                }
-            }
-
-            // skip, gate, store: yacc[pt][r] = y[i][p = PW g4 + 4 pt + r], so
-            // the lane's PW outputs are contiguous and leave in 16-byte
-            // pieces; rows past the end are dropped by the buffer's range
-            const __amdgpu_buffer_rsrc_t ry = ssd_buffer(yb + c0 * xs, 2u * nvu * xs32);
-#pragma unroll
-            for (int k = 0; k < PT / 2; ++k) {
-                float v[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    v[e] = yacc[2 * k + (e >> 2)][e & 3];
-                if (p.D) {
-                    // x of channels PW g4 + 8 k + e from the raw rows (output order)
-                    const uint16_t *xr = &XT[(IW + r16) * XS + 32 * k + 4 * g4];
-                    const uint2 x0 = *reinterpret_cast<const uint2 *>(xr);
-                    const uint2 x1 = *reinterpret_cast<const uint2 *>(xr + 16);
-                    const uint32_t xw[4] = {x0.x, x0.y, x1.x, x1.y};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        v[e] += dskip * ssd_bf(e & 1 ? xw[e >> 1] >> 16 : xw[e >> 1] & 0xffffu);
-                }
-                if (zb) {
-                    const uint32_t zw[4] = {zop[k].x, zop[k].y, zop[k].z, zop[k].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        v[e] *= silu(ssd_bf(e & 1 ? zw[e >> 1] >> 16 : zw[e >> 1] & 0xffffu));
-                }
-                const uint4 o = {ssd_pack(v[0], v[1]), ssd_pack(v[2], v[3]), ssd_pack(v[4], v[5]),
-                                 ssd_pack(v[6], v[7])};
-                ssd_bstore16(ry, 2u * ((uint32_t)(IW + r16) * xs32 + PW * g4 + 8 * k), o);
-            }
-
-            __builtin_amdgcn_sched_barrier(0);   // (likewise)
-            // ---- state update of rows [WL NW, (WL+1) NW)
-            {
-                const float dec = __builtin_amdgcn_exp2f(Slast);
-#pragma unroll
-                for (int i = 0; i < NTW; ++i)
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt)
-                        hacc[i][pt] *= dec;
-#pragma unroll
-                for (int ks = 0; ks < Q / 32; ++ks) {
-                    ssd_bf16x8 bop[NTW];
-#pragma unroll
-                    for (int i = 0; i < NTW; ++i)
-                        bop[i] = ssd_ld_tr2(&sBR[(32 * ks + 8 * g4 + (r16 >> 2)) * HS + 16 * (WL * NTW + i) + 4 * (r16 & 3)],
-                                            &sBR[(32 * ks + 8 * g4 + 4 + (r16 >> 2)) * HS + 16 * (WL * NTW + i) + 4 * (r16 & 3)]);
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        const int o = (32 * ks + 8 * g4 + (r16 >> 2)) * XS + 16 * pt + 4 * (r16 & 3);
-                        const ssd_bf16x8 xh = ssd_ld_tr2(&Xh[o], &Xh[o + 4 * XS]);
-                        const ssd_bf16x8 xl = ssd_ld_tr2(&Xl[o], &Xl[o + 4 * XS]);
-#pragma unroll
-                        for (int i = 0; i < NTW; ++i) {
-                            hacc[i][pt] = ssd_mfma(bop[i], xh, hacc[i][pt]);
-                            hacc[i][pt] = ssd_mfma(bop[i], xl, hacc[i][pt]);
-                        }
+                    uint2 hi, lo;
+                    ssd_split2(m[0], m[1], hi.x, lo.x);
+                    ssd_split2(m[2], m[3], hi.y, lo.y);
+                    uint2 *mh = reinterpret_cast<uint2 *>(&sM[buf][hs][ssd_slot(T, J >> 1)][0][lane]);
+                    uint2 *ml = reinterpret_cast<uint2 *>(&sM[buf][hs][ssd_slot(T, J >> 1)][1][lane]);
+                    mh[J & 1] = hi;
+                    ml[J & 1] = lo;
+                    if (J == T && (T & 1) == 0) {
+                        // the key tile past the diagonal that shares this slot: zeros
+                        mh[1] = uint2{0u, 0u};
+                        ml[1] = uint2{0u, 0u};
                     }
                 }
             }
         };
-        switch (wl) {
-        case 0: compute(std::integral_constant<int, 0>{}); break;
-        case 1: compute(std::integral_constant<int, 1>{}); break;
-        case 2: compute(std::integral_constant<int, 2>{}); break;
-        default: compute(std::integral_constant<int, 3>{}); break;
+        load(0);
+        for (int k = -1; k < nchunks; ++k) {
+            const int buf = k & 1;   // the compute waves' buffer; this loop fills the other
+            const bool work = k + 1 < nchunks;
+            if (work) {
+                // staged rows of chunk k + 1, into the other buffer
+#pragma unroll
+                for (int q = 0; q < XI; ++q) {
+                    const int piece = q * NH + ut;
+                    const int hs = piece / (Q * XPR), rem = piece % (Q * XPR);
+                    *reinterpret_cast<uint4 *>(&sX[buf ^ 1][hs][(rem / XPR) * XS + 8 * (rem % XPR)]) = xr[q];
+                }
+#pragma unroll
+                for (int q = 0; q < BI; ++q) {
+                    const int piece = q * NH + ut;
+                    const int o = (piece / BPR) * HS + 8 * (piece % BPR);
+                    *reinterpret_cast<uint4 *>(&sB[buf ^ 1][o]) = br[q];
+                    *reinterpret_cast<uint4 *>(&sC[buf ^ 1][o]) = cr[q];
+                }
+                if (th >= 0) {
+                    // step, decay and input weight of token `lane` of chunk k + 1
+                    float step = 0.0f;
+                    if (lane < (int)valid_tokens((int64_t)(k + 1) * Q)) {
+                        step = ssd_bf(dtr) + bias;
+                        if (p.dt_softplus)
+                            step = softplus_f(step);
+                    }
+                    const float la = step * a2;
+                    float wbar = step;
+                    if (ZOH)
+                        wbar = step * expm1_over_x(step * a, __builtin_amdgcn_exp2f(la));
+                    const float S = ssd_prefix_sum(la, lane);
+                    const float Slast =
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), 63));
+                    sS[buf ^ 1][th][lane] = S;
+                    sW[buf ^ 1][th][lane] = wbar;
+                    sF[buf ^ 1][th][lane] = wbar * __builtin_amdgcn_exp2f(Slast - S);
+                }
+                if (k + 2 < nchunks) load((int64_t)(k + 2) * Q);
+            }
+            __syncthreads();
+            if (work) {
+                switch (u) {
+                case 0: score_jobs(std::integral_constant<int, 0>{}, buf ^ 1); break;
+                case 1: score_jobs(std::integral_constant<int, 1>{}, buf ^ 1); break;
+                case 2: score_jobs(std::integral_constant<int, 2>{}, buf ^ 1); break;
+                case 3: score_jobs(std::integral_constant<int, 3>{}, buf ^ 1); break;
+                case 4: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 4>{}, buf ^ 1); break;
+                case 5: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 5>{}, buf ^ 1); break;
+                case 6: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 6>{}, buf ^ 1); break;
+                default: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 7>{}, buf ^ 1); break;
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
+        return;
     }
 
-    if (p.h_last) {
-        float *hl = p.h_last + ((int64_t)b * p.H + h) * P * N;
+    // ================= compute waves =================
+    const int hs = w >> 2;
+    const int h = hbase + hs;
+    const float dskip = p.D ? p.D[h] : 0.0f;
+    const uint16_t *zb = p.z ? p.z + (int64_t)b * L * xs + (int64_t)h * P : nullptr;
+    uint16_t *yb = p.y + (int64_t)b * L * xs + (int64_t)h * P;
+    const float *h0b = p.h0 ? p.h0 + ((int64_t)b * p.H + h) * P * N : nullptr;
+    float *hlb = p.h_last ? p.h_last + ((int64_t)b * p.H + h) * P * N : nullptr;
+
+    // The role WL (p tiles WL, WL + 4, ...) is a compile-time constant, so
+    // each role's loop is straight-line code.
+    auto run = [&](auto role) {
+        constexpr int WL = decltype(role)::value;
+        constexpr int NPT = (PT - WL + 3) / 4;   // p tiles of this wave
+        // State: hacc[k][nt][r] = h[p = 16 (WL + 4 k) + r16][n = 16 nt + 4 g4 + r]
+        // (an h^T tile: lane = p column, 4 consecutive n)
+        ssd_f32x4 hacc[NPT][NT];
 #pragma unroll
-        for (int i = 0; i < NTW; ++i)
+        for (int k = 0; k < NPT; ++k)
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-                *reinterpret_cast<ssd_f32x4 *>(hl + (16 * pt + r16) * N + 16 * (wl * NTW + i) + 4 * g4) = hacc[i][pt];
+            for (int nt = 0; nt < NT; ++nt)
+                hacc[k][nt] = h0b ? *reinterpret_cast<const ssd_f32x4 *>(h0b + (16 * (WL + 4 * k) + r16) * N +
+                                                                          16 * nt + 4 * g4)
+                                  : ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        ssd_f32x4 yacc[NPT][4];
+        uint2 zop[NPT][4];
+        for (int k = -1; k < nchunks; ++k) {
+            const int buf = k & 1;
+            const int64_t c0 = (int64_t)k * Q;
+            const uint32_t nvu = k >= 0 ? valid_tokens(c0) : 0u;
+            if (k >= 0) {
+                // gate values of this wave's outputs (token 16 T + r16, channels
+                // 16 pt + 4 g4 .. + 3)
+                const __amdgpu_buffer_rsrc_t rz = ssd_buffer(zb ? zb + c0 * xs : yb, zb ? 2u * nvu * xs32 : 0u);
+#pragma unroll
+                for (int q = 0; q < NPT; ++q)
+#pragma unroll
+                    for (int T = 0; T < 4; ++T)
+                        zop[q][T] =
+                            ssd_bload8(rz, 2u * ((uint32_t)(16 * T + r16) * xs32 + 16 * (WL + 4 * q) + 4 * g4));
+
+                // ---- readout of the state entering the chunk, for every output
+                // token: Y^T[p][i] = sum_n H[p][n] C_i[n], with K running over n
+                // in the order n = 32 s + 16 (e / 4) + 4 g4 + e % 4 (e = the
+                // operand element), the order in which the lane holds its state
+#pragma unroll
+                for (int q = 0; q < NPT; ++q)
+#pragma unroll
+                    for (int T = 0; T < 4; ++T)
+                        yacc[q][T] = ssd_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < NK; ++s) {
+                    ssd_bf16x8 ah[NPT], al[NPT];
+#pragma unroll
+                    for (int q = 0; q < NPT; ++q) {
+                        uint32_t hw[4], lw[4];
+                        ssd_split2(hacc[q][2 * s][0], hacc[q][2 * s][1], hw[0], lw[0]);
+                        ssd_split2(hacc[q][2 * s][2], hacc[q][2 * s][3], hw[1], lw[1]);
+                        ssd_split2(hacc[q][2 * s + 1][0], hacc[q][2 * s + 1][1], hw[2], lw[2]);
+                        ssd_split2(hacc[q][2 * s + 1][2], hacc[q][2 * s + 1][3], hw[3], lw[3]);
+                        ah[q] = __builtin_bit_cast(ssd_bf16x8, uint4{hw[0], hw[1], hw[2], hw[3]});
+                        al[q] = __builtin_bit_cast(ssd_bf16x8, uint4{lw[0], lw[1], lw[2], lw[3]});
+                    }
+#pragma unroll
+                    for (int T = 0; T < 4; ++T) {
+                        const uint16_t *cp = &sC[buf][(16 * T + r16) * HS + 32 * s + 4 * g4];
+                        const uint2 c0v = *reinterpret_cast<const uint2 *>(cp);
+                        const uint2 c1v = *reinterpret_cast<const uint2 *>(cp + 16);
+                        const ssd_bf16x8 cop = __builtin_bit_cast(ssd_bf16x8, uint4{c0v.x, c0v.y, c1v.x, c1v.y});
+#pragma unroll
+                        for (int q = 0; q < NPT; ++q) {
+                            yacc[q][T] = ssd_mfma(ah[q], cop, yacc[q][T]);
+                            yacc[q][T] = ssd_mfma(al[q], cop, yacc[q][T]);
+                        }
+                    }
+                }
+                // decay from the chunk's start to each output token
+#pragma unroll
+                for (int T = 0; T < 4; ++T) {
+                    const float ei = __builtin_amdgcn_exp2f(sS[buf][hs][16 * T + r16]);
+#pragma unroll
+                    for (int q = 0; q < NPT; ++q)
+                        yacc[q][T] *= ei;
+                }
+            }
+            __syncthreads();
+            if (k >= 0) {
+                // ---- masked product: Y^T[p][i] += sum_j x[j][p] M^T[j][i], K over
+                // j in the order j = 32 Jp + 16 (e / 4) + 4 g4 + e % 4
+                const uint16_t *X = sX[buf][hs];
+#pragma unroll
+                for (int Jp = 0; Jp < 2; ++Jp) {
+                    ssd_bf16x8 xop[NPT];
+#pragma unroll
+                    for (int q = 0; q < NPT; ++q) {
+                        const uint16_t *src = &X[(32 * Jp + 4 * g4 + (r16 >> 2)) * XS + 16 * (WL + 4 * q) + 4 * (r16 & 3)];
+                        xop[q] = ssd_ld_tr2(src, src + 16 * XS);
+                    }
+#pragma unroll
+                    for (int T = 2 * Jp; T < 4; ++T) {
+                        const ssd_bf16x8 mh = __builtin_bit_cast(ssd_bf16x8, sM[buf][hs][ssd_slot(T, Jp)][0][lane]);
+                        const ssd_bf16x8 ml = __builtin_bit_cast(ssd_bf16x8, sM[buf][hs][ssd_slot(T, Jp)][1][lane]);
+#pragma unroll
+                        for (int q = 0; q < NPT; ++q) {
+                            yacc[q][T] = ssd_mfma(xop[q], mh, yacc[q][T]);
+                            yacc[q][T] = ssd_mfma(xop[q], ml, yacc[q][T]);
+                        }
+                    }
+                }
+
+                // ---- skip, gate, store: yacc[q][T][r] = y[i = 16 T + r16][p = 16 pt + 4 g4 + r];
+                // rows past the end are dropped by the buffer's range
+                {
+                    const __amdgpu_buffer_rsrc_t ry = ssd_buffer(yb + c0 * xs, 2u * nvu * xs32);
+#pragma unroll
+                    for (int q = 0; q < NPT; ++q)
+#pragma unroll
+                        for (int T = 0; T < 4; ++T) {
+                            const int pc = 16 * (WL + 4 * q) + 4 * g4;
+                            float v[4] = {yacc[q][T][0], yacc[q][T][1], yacc[q][T][2], yacc[q][T][3]};
+                            if (p.D) {
+                                const uint2 xw = *reinterpret_cast<const uint2 *>(&X[(16 * T + r16) * XS + pc]);
+                                v[0] += dskip * ssd_bf(xw.x & 0xffffu);
+                                v[1] += dskip * ssd_bf(xw.x >> 16);
+                                v[2] += dskip * ssd_bf(xw.y & 0xffffu);
+                                v[3] += dskip * ssd_bf(xw.y >> 16);
+                            }
+                            if (zb) {
+                                const uint2 zw = zop[q][T];
+                                v[0] *= silu(ssd_bf(zw.x & 0xffffu));
+                                v[1] *= silu(ssd_bf(zw.x >> 16));
+                                v[2] *= silu(ssd_bf(zw.y & 0xffffu));
+                                v[3] *= silu(ssd_bf(zw.y >> 16));
+                            }
+                            ssd_bstore8(ry, 2u * ((uint32_t)(16 * T + r16) * xs32 + pc),
+                                        uint2{ssd_pack(v[0], v[1]), ssd_pack(v[2], v[3])});
+                        }
+                }
+
+                // ---- state update: h^T[n][p] = exp(S_last) h^T[n][p] + sum_j B_j[n] fd_j x[j][p],
+                // K over j = 32 ks + 8 g4 + e
+                {
+                    const uint16_t *X = sX[buf][hs];
+                    const float dec = __builtin_amdgcn_exp2f(sS[buf][hs][Q - 1]);
+#pragma unroll
+                    for (int q = 0; q < NPT; ++q)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt)
+                            hacc[q][nt] *= dec;
+#pragma unroll
+                    for (int ks = 0; ks < Q / 32; ++ks) {
+                        const int j0 = 32 * ks + 8 * g4;
+                        const float4 f0 = *reinterpret_cast<const float4 *>(&sF[buf][hs][j0]);
+                        const float4 f1 = *reinterpret_cast<const float4 *>(&sF[buf][hs][j0 + 4]);
+                        const float fj[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                        ssd_bf16x8 xh[NPT], xl[NPT];
+#pragma unroll
+                        for (int q = 0; q < NPT; ++q) {
+                            const uint16_t *src = &X[(j0 + (r16 >> 2)) * XS + 16 * (WL + 4 * q) + 4 * (r16 & 3)];
+                            const uint4 xv = __builtin_bit_cast(uint4, ssd_ld_tr2(src, src + 4 * XS));
+                            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+                            uint32_t hw[4], lw[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                ssd_split2(ssd_bf(xw[e] & 0xffffu) * fj[2 * e], ssd_bf(xw[e] >> 16) * fj[2 * e + 1],
+                                           hw[e], lw[e]);
+                            xh[q] = __builtin_bit_cast(ssd_bf16x8, uint4{hw[0], hw[1], hw[2], hw[3]});
+                            xl[q] = __builtin_bit_cast(ssd_bf16x8, uint4{lw[0], lw[1], lw[2], lw[3]});
+                        }
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            const uint16_t *src = &sB[buf][(j0 + (r16 >> 2)) * HS + 16 * nt + 4 * (r16 & 3)];
+                            const ssd_bf16x8 bop = ssd_ld_tr2(src, src + 4 * HS);
+#pragma unroll
+                            for (int q = 0; q < NPT; ++q) {
+                                hacc[q][nt] = ssd_mfma(bop, xh[q], hacc[q][nt]);
+                                hacc[q][nt] = ssd_mfma(bop, xl[q], hacc[q][nt]);
+                            }
+                        }
+                    }
+                }
+
+            }
+            __syncthreads();
+        }
+
+        if (hlb) {
+#pragma unroll
+            for (int q = 0; q < NPT; ++q)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    *reinterpret_cast<ssd_f32x4 *>(hlb + (16 * (WL + 4 * q) + r16) * N + 16 * nt + 4 * g4) =
+                        hacc[q][nt];
+        }
+    };
+    switch (w & 3) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    default: run(std::integral_constant<int, 3>{}); break;
     }
 }
 
-// Two heads per workgroup when the LDS of two fits (head size 64) and they
-// share a group; otherwise one.
+// Two heads per workgroup when they share a group and their LDS fits (head
+// size 64); otherwise one.
 template <int P, int N, bool ZOH>
 hipError_t launch_ssd_pn(const SsdParams &p, hipStream_t st) {
     if (P == 64 && p.hpg % 2 == 0) {
         const int64_t blocks = (int64_t)p.batch * (p.H / 2);
         hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, (P == 64 ? 2 : 1)>), dim3((unsigned)blocks),
-                           dim3(kSsdThreads * (P == 64 ? 2 : 1)), 0, st, p);
+                           dim3(2 * kSsdThreads * (P == 64 ? 2 : 1)), 0, st, p);
     } else {
         const int64_t blocks = (int64_t)p.batch * p.H;
-        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, 1>), dim3((unsigned)blocks), dim3(kSsdThreads), 0, st, p);
+        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, 1>), dim3((unsigned)blocks), dim3(2 * kSsdThreads), 0, st, p);
     }
     return hipGetLastError();
 }
