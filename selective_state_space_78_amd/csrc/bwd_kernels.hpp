@@ -363,15 +363,15 @@ struct BwdKernel {
     }
 
     // sum over the G planes of plane set `k` at (row, col .. col + kV)
+    // (from the first plane on, not from 0.0f + the first: the compiler keeps
+    // that add, since it turns a -0.0f into +0.0f)
     __device__ static void plane_sum(const Smem &s, int k, int row, int col, float (&acc)[kV]) {
-#pragma unroll
-        for (int e = 0; e < kV; ++e) acc[e] = 0.0f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const VecF v = *reinterpret_cast<const VecF *>(&s.pl[k][g][row][col]);
             const float *pv = reinterpret_cast<const float *>(&v);
 #pragma unroll
-            for (int e = 0; e < kV; ++e) acc[e] += pv[e];
+            for (int e = 0; e < kV; ++e) acc[e] = g == 0 ? pv[e] : acc[e] + pv[e];
         }
     }
 

@@ -12,28 +12,39 @@
 //   H_out = exp(S_last) H + sum_j exp(S_last - S_j) wbar_j x_j B_j^T
 //
 // Kernel design:
-//  * Four waves own one (batch row, head) and walk its chunks of Q = 64
-//    tokens in order; the fp32 state never leaves registers. Wave w holds the
-//    state rows n in [w N/4, (w+1) N/4) for every p, as MFMA accumulators
-//    (h^T tiles: lane = p column, 4 consecutive n). A workgroup of 8 waves
-//    takes two heads of one group, which share the staged B rows, when head
-//    size 64 lets their LDS fit; otherwise a workgroup is one head, 4 waves.
-//  * Every product is a 16x16x32 bf16 MFMA with fp32 accumulation:
-//      scores  G^T[j][i] = B_j . C_i        (K = n; operands straight from L2)
-//      readout Y^T[p][i] = H[p][:] . C_i    (K = n; H from LDS as bf16)
-//      intra   Y^T[p][i] += sum_j X~[j][p] M^T[j][i]   (K = j)
-//      update  h^T[n][p] += sum_j B[j][n] X~d[j][p]    (K = j)
-//    Y^T rather than Y makes the score tile's accumulator layout (lane = i,
-//    4 consecutive j) usable as the next product's operand without a trip
-//    through LDS: the K order of that product is permuted to match, and the
-//    X~ operand is read in the same order.
-//  * Products over tokens need token-contiguous operands, so each chunk is
-//    staged into LDS transposed: X~ = wbar x, X~d = wbar exp(S_last - S_j) x
-//    (both P x Q) and B^T (N x Q); and the state as bf16 (P x N) for the
-//    readout. Waves split the staging (lane = token) and then the work: wave w
-//    computes the outputs of tokens [16w, 16w+16) and its state rows.
-//  * Tokens past the end of the sequence enter with step 0 and zero x and B,
-//    so they neither decay nor feed the state; their outputs are not stored.
+//  * A workgroup takes HPW heads of one batch row and group: two when the head
+//    size is 64 and the group's head count is even (their LDS then fits),
+//    otherwise one. Per head, four compute waves and four helper waves.
+//  * Compute wave WL of a head holds the state tiles h^T[n][p] of p tiles WL,
+//    WL + 4, ... for every n as MFMA accumulators (lane = p column, 4
+//    consecutive n); the fp32 state never leaves registers. Every product is
+//    a 16x16x32 bf16 MFMA with fp32 accumulation.
+//  * Each chunk of Q = 64 tokens takes two phases, each closed by a barrier:
+//      1. compute waves: the readout of the state entering the chunk,
+//         Y^T[p][i] = H[p][:] . C_i for every token i, whose A operand is the
+//         wave's own state split hi + lo in registers (K runs over n in the
+//         order in which the lane holds its accumulators), times exp(S_i).
+//         Helpers: they write the next chunk's x, B and C rows (loaded during
+//         the previous chunk) into the other half of double-buffered LDS,
+//         form its step tables (S_t, wbar_t, wbar_t exp(S_last - S_t)), and
+//         issue the loads of the chunk after it.
+//      2. compute waves: the masked product Y^T[p][i] += sum_j x^T[p][j]
+//         M^T[j][i] (x by transposing LDS reads, M from the exchange buffer);
+//         skip, gate, bf16 rounding and stores; then the state update
+//         h^T[n][p] = exp(S_last) h^T[n][p] + sum_j B_j[n] wbar_j
+//         exp(S_last - S_j) x_j[p] (B by transposing reads, the weighted x
+//         split hi + lo in registers).
+//         Helpers: the next chunk's score tiles G^T[j][i] = B_j . C_i (j and
+//         i blocks J <= T), formed once for the workgroup's heads, then per
+//         head decayed, weighted, masked to j <= i and split hi + lo into the
+//         exchange buffer, in the lane order of the compute waves' operand.
+//  * The computed operands (the state for its readout, the scores, the
+//    weighted x) are split into hi + lo bf16 pairs; x, B and C are exact in
+//    bf16.
+//  * Global accesses are raw buffer accesses sized to the chunk's valid rows:
+//    rows past the end of the sequence load as zero (step 0: they neither
+//    decay nor feed the state) and their outputs are dropped.
+//  * The gate is a compile-time option (GATE), the skip a run-time one.
 //  * Workgroup ids are remapped so that the heads of one batch row, which read
 //    the same B and C rows, run on the same XCD and share its L2.
 #pragma once
@@ -196,7 +207,7 @@ constexpr int kSsdSlots = 6;
 // outputs and state update; 4 HPW helper waves prepare the next chunk
 // meanwhile: they stage its x, B and C rows, its step tables and its masked
 // scores into the other half of double-buffered LDS.
-template <int P, int N, bool ZOH, int HPW>
+template <int P, int N, bool ZOH, int HPW, bool GATE>
 __global__ __launch_bounds__(2 * kSsdThreads * HPW) void ssd_fwd_kernel(const SsdParams p) {
     constexpr int Q = kSsdQ;
     constexpr int PT = P / 16;     // p tiles
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(2 * kSsdThreads * HPW) void ssd_fwd_kernel(const Ss
     const int hs = w >> 2;
     const int h = hbase + hs;
     const float dskip = p.D ? p.D[h] : 0.0f;
-    const uint16_t *zb = p.z ? p.z + (int64_t)b * L * xs + (int64_t)h * P : nullptr;
+    const uint16_t *zb = GATE ? p.z + (int64_t)b * L * xs + (int64_t)h * P : nullptr;
     uint16_t *yb = p.y + (int64_t)b * L * xs + (int64_t)h * P;
     const float *h0b = p.h0 ? p.h0 + ((int64_t)b * p.H + h) * P * N : nullptr;
     float *hlb = p.h_last ? p.h_last + ((int64_t)b * p.H + h) * P * N : nullptr;
@@ -427,13 +438,15 @@ __global__ __launch_bounds__(2 * kSsdThreads * HPW) void ssd_fwd_kernel(const Ss
             if (k >= 0) {
                 // gate values of this wave's outputs (token 16 T + r16, channels
                 // 16 pt + 4 g4 .. + 3)
-                const __amdgpu_buffer_rsrc_t rz = ssd_buffer(zb ? zb + c0 * xs : yb, zb ? 2u * nvu * xs32 : 0u);
+                if constexpr (GATE) {
+                    const __amdgpu_buffer_rsrc_t rz = ssd_buffer(zb + c0 * xs, 2u * nvu * xs32);
 #pragma unroll
-                for (int q = 0; q < NPT; ++q)
+                    for (int q = 0; q < NPT; ++q)
 #pragma unroll
-                    for (int T = 0; T < 4; ++T)
-                        zop[q][T] =
-                            ssd_bload8(rz, 2u * ((uint32_t)(16 * T + r16) * xs32 + 16 * (WL + 4 * q) + 4 * g4));
+                        for (int T = 0; T < 4; ++T)
+                            zop[q][T] =
+                                ssd_bload8(rz, 2u * ((uint32_t)(16 * T + r16) * xs32 + 16 * (WL + 4 * q) + 4 * g4));
+                }
 
                 // ---- readout of the state entering the chunk, for every output
                 // token: Y^T[p][i] = sum_n H[p][n] C_i[n], with K running over n
@@ -521,7 +534,7 @@ __global__ __launch_bounds__(2 * kSsdThreads * HPW) void ssd_fwd_kernel(const Ss
                                 v[2] += dskip * ssd_bf(xw.y & 0xffffu);
                                 v[3] += dskip * ssd_bf(xw.y >> 16);
                             }
-                            if (zb) {
+                            if constexpr (GATE) {
                                 const uint2 zw = zop[q][T];
                                 v[0] *= silu(ssd_bf(zw.x & 0xffffu));
                                 v[1] *= silu(ssd_bf(zw.x >> 16));
@@ -601,14 +614,21 @@ __global__ __launch_bounds__(2 * kSsdThreads * HPW) void ssd_fwd_kernel(const Ss
 // size 64); otherwise one.
 template <int P, int N, bool ZOH>
 hipError_t launch_ssd_pn(const SsdParams &p, hipStream_t st) {
-    if (P == 64 && p.hpg % 2 == 0) {
-        const int64_t blocks = (int64_t)p.batch * (p.H / 2);
-        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, (P == 64 ? 2 : 1)>), dim3((unsigned)blocks),
-                           dim3(2 * kSsdThreads * (P == 64 ? 2 : 1)), 0, st, p);
-    } else {
-        const int64_t blocks = (int64_t)p.batch * p.H;
-        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, 1>), dim3((unsigned)blocks), dim3(2 * kSsdThreads), 0, st, p);
-    }
+    // the gate is a compile-time option: the instance without it carries none
+    // of its loads or registers (4% faster on the Mamba-2-shaped layer). The
+    // skip stays a run-time branch: as a compile-time option it measured 3%
+    // slower than this, the compiler then scheduling the epilogue differently.
+    constexpr int kPair = P == 64 ? 2 : 1;
+    const bool pair = P == 64 && p.hpg % 2 == 0;
+    const dim3 grid((unsigned)((int64_t)p.batch * (pair ? p.H / 2 : p.H)));
+    if (pair && p.z)
+        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, kPair, true>), grid, dim3(2 * kSsdThreads * kPair), 0, st, p);
+    else if (pair)
+        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, kPair, false>), grid, dim3(2 * kSsdThreads * kPair), 0, st, p);
+    else if (p.z)
+        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, 1, true>), grid, dim3(2 * kSsdThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((ssd_fwd_kernel<P, N, ZOH, 1, false>), grid, dim3(2 * kSsdThreads), 0, st, p);
     return hipGetLastError();
 }
 
