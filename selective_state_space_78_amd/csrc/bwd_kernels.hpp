@@ -157,6 +157,11 @@ struct BwdKernel {
     static constexpr bool kPacked = sizeof(T) == 2;
     static constexpr int kWPS = kPacked ? 1 : 2;
     static constexpr bool kKeepA = NPW == 1;
+    // Otherwise the first state's decay of each token goes through the wave's
+    // own slot of the second plane set, which holds nothing from the
+    // recomputation until the reverse step overwrites it, token by token,
+    // with that token's delta-gradient part (after reading the decay there).
+    static constexpr bool kPlaneA = !kKeepA;
     // the hold rule's phi(delta A) of the chunk, kept from the recomputation for
     // the reverse step: the 8-wave hold-rule kernels run at 2 waves per SIMD
     // and have the registers for it
@@ -491,11 +496,13 @@ struct BwdKernel {
                             const float ph = expm1_over_x(v.x * A[q], a);
                             h[q] = fmaf(a, h[q], ph * (v.x * v.y * bq));
                             if constexpr (kKeepA) as[t][q] = a;
+                            if constexpr (kPlaneA) if (q == 0) s.pl[1][w][t][lane] = a;
                             if constexpr (kKeepF) fs[t][q] = ph;
                         } else {
                             const float a = __builtin_amdgcn_exp2f(v.x * A2[q]);
                             h[q] = fmaf(a, h[q], v.y * bq);
                             if constexpr (kKeepA) as[t][q] = a;
+                            if constexpr (kPlaneA) if (q == 0) s.pl[1][w][t][lane] = a;
                         }
                         hs[t][q] = h[q];
                         part = fmaf(cq, h[q], part);
@@ -533,7 +540,9 @@ struct BwdKernel {
                     const uint32_t wb = bw[t * NPW + q];
                     const float bq = __uint_as_float(kPacked ? wb << 16 : wb);
                     const float cq = __uint_as_float(kPacked ? wb & 0xffff0000u : cw[t * NPW + q]);
-                    const float a = kKeepA ? as[t][q] : __builtin_amdgcn_exp2f(v.x * A2[q]);
+                    const float a = kKeepA                 ? as[t][q]
+                                    : (kPlaneA && q == 0) ? s.pl[1][w][t][lane]
+                                                          : __builtin_amdgcn_exp2f(v.x * A2[q]);
                     const float l = fmaf(cq, dsv, mu[q]);
                     const float al = a * l;                 // the adjoint passed back to t - 1
                     const float hp = t > 0 ? hs[t - 1][q] : hstart[q];
