@@ -61,7 +61,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTile = 64;        // channels per workgroup tile = lanes per wave
 constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies
 constexpr int kMaxSegments = 64;
-constexpr int kPadRows = 16;     // spare zero rows after the widened B and C (>= every TC)
+constexpr int kPadRows = 32;     // spare zero rows after the widened B and C (>= every TC, the aggregate pass's too)
 constexpr int kConvMax = 4;      // widest convolution prologue
 
 // ---------------------------------------------------------------------------
@@ -814,7 +814,12 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if (nblocks_agg > 0) {
-        hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeAggregate, FEAT, UF>), dim3(nblocks_agg),
+        // the aggregate pass stages no readout planes, so its chunks can be
+        // twice as long within the same LDS: half the barriers per token
+        // (with 4 waves or more; fewer would hold several times the staged
+        // pieces in registers)
+        constexpr int kAggTC = G >= 4 ? 2 * TC : TC;
+        hipLaunchKernelGGL((scan_kernel<T, NPW, G, kAggTC, ZOH, kModeAggregate, FEAT, UF>), dim3(nblocks_agg),
                            dim3(kTile * G), 0, st, p);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         CarryParams cp{};

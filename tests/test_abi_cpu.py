@@ -136,7 +136,7 @@ def test_scan_aliasing(L):
 def test_scan_workspace(L):
     d = desc(b=1, L=4096, d=64, N=16)
     rnd = lambda v: (v + 255) // 256 * 256
-    bc = rnd((1 * 4096 + 16) * 16 * 4)          # widened B (and C): rows + 16 spare, 16 states
+    bc = rnd((1 * 4096 + 32) * 16 * 4)          # widened B (and C): rows + 32 spare, 16 states
     need = L.ssm_scan_workspace_size_tuned(ctypes.byref(d), ctypes.byref(ssm.ScanTuning(4, 4)))
     assert need == 2 * bc + 3 * rnd(1 * 4 * 64 * 16 * 4)
     assert scan_call(L, d, ws=0, ws_bytes=0, tuning=(4, 4)) == EWS
@@ -144,7 +144,7 @@ def test_scan_workspace(L):
     assert scan_call(L, d, ws=11 * GB + 128, ws_bytes=need, tuning=(4, 4)) == EALIGN
     assert L.ssm_scan_workspace_size_tuned(ctypes.byref(d), ctypes.byref(ssm.ScanTuning(4, 1))) == 2 * bc
     d5 = desc(b=1, L=4096, d=64, N=5)           # padded to 8 states
-    assert L.ssm_scan_workspace_size(ctypes.byref(d5)) >= 2 * rnd((4096 + 16) * 8 * 4)
+    assert L.ssm_scan_workspace_size(ctypes.byref(d5)) >= 2 * rnd((4096 + 32) * 8 * 4)
     assert L.ssm_scan_workspace_size(ctypes.byref(desc(L=0))) == 0
     assert L.ssm_scan_workspace_size(None) == 0
 
