@@ -38,6 +38,9 @@
 //         i blocks J <= T), formed once for the workgroup's heads, then per
 //         head decayed, weighted, masked to j <= i and split hi + lo into the
 //         exchange buffer, in the lane order of the compute waves' operand.
+//         With a pair of heads, two of the ten tiles are instead scored in
+//         phase 1 of their own chunk by two helpers with no step table to
+//         form, so that each helper scores at most one tile in phase 2.
 //  * The computed operands (the state for its readout, the scores, the
 //    weighted x) are split into hi + lo bf16 pairs; x, B and C are exact in
 //    bf16.
@@ -201,6 +204,15 @@ constexpr int kSsdTileJ[kSsdTiles] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 // Slot of the masked scores of (T, key half Jp) in the exchange buffer
 __host__ __device__ constexpr int ssd_slot(int T, int Jp) { return T < 2 ? T : 2 + 2 * (T - 2) + Jp; }
 constexpr int kSsdSlots = 6;
+// With a pair of heads (8 helpers) tiles 0..7 are scored one per helper in
+// the second phase of the chunk before theirs; the last two in the first
+// phase of their own chunk, by helpers 2 and 3 (the helpers that form no step
+// table and whose staging is done by then). One head (4 helpers): every tile
+// in the second phase, dealt round-robin.
+template <int HPW> constexpr int ssd_early_tiles() { return HPW == 2 ? 8 : kSsdTiles; }
+template <int HPW> constexpr int ssd_tile_owner(int q) {
+    return q < ssd_early_tiles<HPW>() ? q % (4 * HPW) : 2 + (q - ssd_early_tiles<HPW>());
+}
 
 // HPW heads of one group per workgroup. Per head four compute waves hold the
 // state (wave WL: p tiles WL, WL + 4, ...; every n) and make the chunk's
@@ -309,11 +321,12 @@ __global__ __launch_bounds__(2 * kSsdThreads * HPW) void ssd_fwd_kernel(const Ss
         // C_i . B_j once for the workgroup's heads (they share B and C). U, the
         // helper, is a constant, so that a helper's tiles form one
         // straight-line block whose loads, products and exponentials overlap.
-        auto score_jobs = [&](auto uc, int buf) {
+        auto score_jobs = [&](auto uc, auto latec, int buf) {
             constexpr int U = decltype(uc)::value;
+            constexpr bool LATE = decltype(latec)::value;
 #pragma unroll
             for (int q = 0; q < kSsdTiles; ++q) {
-                if (q % (4 * HPW) != U) continue;
+                if (ssd_tile_owner<HPW>(q) != U || (q >= ssd_early_tiles<HPW>()) != LATE) continue;
                 const int T = kSsdTileT[q], J = kSsdTileJ[q];
                 ssd_f32x4 gt = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -387,17 +400,24 @@ __global__ __launch_bounds__(2 * kSsdThreads * HPW) void ssd_fwd_kernel(const Ss
                 }
                 if (k + 2 < nchunks) load((int64_t)(k + 2) * Q);
             }
+            if constexpr (ssd_early_tiles<HPW>() < kSsdTiles) {
+                // the late tiles of chunk k, whose rows and tables are in buffer buf
+                if (k >= 0) {
+                    if (u == 2) score_jobs(std::integral_constant<int, 2>{}, std::true_type{}, buf);
+                    if (u == 3) score_jobs(std::integral_constant<int, 3>{}, std::true_type{}, buf);
+                }
+            }
             __syncthreads();
             if (work) {
                 switch (u) {
-                case 0: score_jobs(std::integral_constant<int, 0>{}, buf ^ 1); break;
-                case 1: score_jobs(std::integral_constant<int, 1>{}, buf ^ 1); break;
-                case 2: score_jobs(std::integral_constant<int, 2>{}, buf ^ 1); break;
-                case 3: score_jobs(std::integral_constant<int, 3>{}, buf ^ 1); break;
-                case 4: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 4>{}, buf ^ 1); break;
-                case 5: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 5>{}, buf ^ 1); break;
-                case 6: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 6>{}, buf ^ 1); break;
-                default: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 7>{}, buf ^ 1); break;
+                case 0: score_jobs(std::integral_constant<int, 0>{}, std::false_type{}, buf ^ 1); break;
+                case 1: score_jobs(std::integral_constant<int, 1>{}, std::false_type{}, buf ^ 1); break;
+                case 2: score_jobs(std::integral_constant<int, 2>{}, std::false_type{}, buf ^ 1); break;
+                case 3: score_jobs(std::integral_constant<int, 3>{}, std::false_type{}, buf ^ 1); break;
+                case 4: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 4>{}, std::false_type{}, buf ^ 1); break;
+                case 5: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 5>{}, std::false_type{}, buf ^ 1); break;
+                case 6: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 6>{}, std::false_type{}, buf ^ 1); break;
+                default: if constexpr (HPW > 1) score_jobs(std::integral_constant<int, 7>{}, std::false_type{}, buf ^ 1); break;
                 }
             }
             __syncthreads();
