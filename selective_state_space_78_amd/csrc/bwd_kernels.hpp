@@ -627,8 +627,12 @@ struct BwdKernel {
                 const float *src = &s.red[0][0][0];
                 for (int i = threadIdx.x; i < tval * kNP * 2; i += kThreads) dst[i] = src[i];
             }
-            __syncthreads();
+            // No barrier here: the next chunk's staging writes only the staged
+            // pairs and ds, which this phase does not read, and its first
+            // barrier keeps the planes and sums read here from being
+            // overwritten before every wave is done with them.
         }
+        __syncthreads();   // the planes, reused below, are free once every wave is past the last chunk
 
         // dA, dD of this batch row; dh0 = a_0 lam_0
         if (dval) {
@@ -640,7 +644,7 @@ struct BwdKernel {
             }
         }
         // dD: the threads sharing a channel column hold different rows' sums;
-        // add them through LDS (the planes are free after the last barrier)
+        // add them through LDS (the planes are free after the barrier above)
         float (*dsum)[kTile] = s.pl[0][0];
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
