@@ -254,6 +254,12 @@ template <> struct FloatsOf<4> { typedef float4 type; };
 // What a pass of the scan kernel produces.
 enum ScanMode { kModeMain = 0, kModeAggregate = 1, kModeCheckpoint = 2, kModeMainCheckpoint = 3 };
 
+// The aggregate and checkpoint-only passes stage no readout planes, so their
+// chunks can be longer than the main pass's within the same LDS, for fewer
+// barriers per token: twice as long with 4 waves or more (fewer waves would
+// hold several times the staged pieces in registers).
+template <int G> constexpr int long_chunk_factor() { return G >= 4 ? 2 : 1; }
+
 // FEAT: the step options (delta bias, softplus) are compiled in; without it
 // the kernel carries none of their state (their uniform values alone pushed
 // the scalar registers into spills).
@@ -266,6 +272,10 @@ struct ScanKernel {
     static constexpr bool kCkpt = MODE == kModeCheckpoint || MODE == kModeMainCheckpoint;
     static constexpr bool AGG = !kMain;                       // no readout and no y
     static constexpr bool kSum = MODE == kModeAggregate;
+    // Checkpoint spacing in tokens: the backward's chunk, which is the main
+    // pass's; the checkpoint-only pass runs in longer chunks (see
+    // long_chunk_factor) and stores that many checkpoints per chunk.
+    static constexpr int kCkEvery = MODE == kModeCheckpoint ? TC / long_chunk_factor<G>() : TC;
     static constexpr int kThreads = kTile * G;
     static constexpr int kNP = NPW * G;                       // padded state count
     // channels per staged piece: 2 when that gives every thread of the
@@ -660,21 +670,25 @@ struct ScanKernel {
             if (k + 2 < nchunks) load_chunk(k + 2);
             const int tval = rows_of(k);
             const float2 (*dx)[kTile] = s.dx[P];
-            if constexpr (kCkpt) {
-                // the state before the chunk's first token
-                if (dval) {
-                    const int64_t c = (t_begin + (int64_t)k * TC) / TC;
+            // the state before token j of the chunk, where a checkpoint falls
+            // (j is a compile-time constant once the loops are unrolled)
+            auto checkpoint = [&](int j) {
+                if constexpr (kCkpt) {
+                    if (j % kCkEvery == 0 && dval) {
+                        const int64_t c = (t_begin + (int64_t)k * TC + j) / kCkEvery;
 #pragma unroll
-                    for (int q = 0; q < NPW; ++q)
-                        p.ckpt[(((int64_t)b * p.nck + c) * kNP + w * NPW + q) * p.dim + d] = l.h[q];
+                        for (int q = 0; q < NPW; ++q)
+                            p.ckpt[(((int64_t)b * p.nck + c) * kNP + w * NPW + q) * p.dim + d] = l.h[q];
+                    }
                 }
-            }
+            };
 #pragma unroll
             for (int t0b = 0; t0b < TC; t0b += kTB) {
                 if (t0b > 0) fetch(t0b);
                 if (tval == TC) {
 #pragma unroll
                     for (int i = 0; i < kTB; ++i) {
+                        checkpoint(t0b + i);
                         const float part = step(l, dx, t0b + i, lane, bc[i]);
                         if constexpr (!AGG) s.y[P][w][t0b + i][lane] = part;
                     }
@@ -682,6 +696,7 @@ struct ScanKernel {
 #pragma unroll
                     for (int i = 0; i < kTB; ++i) {
                         if (t0b + i < tval) {
+                            checkpoint(t0b + i);
                             const float part = step(l, dx, t0b + i, lane, bc[i]);
                             if constexpr (!AGG) s.y[P][w][t0b + i][lane] = part;
                         }
@@ -806,6 +821,7 @@ template <typename T, int NPW, int G, int TC, bool ZOH, bool CK, bool FEAT, bool
 hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg, hipStream_t st) {
     if (!CK && p.ckpt != nullptr) return hipErrorInvalidValue;
     if ((p.u_f32 != 0) != UF) return hipErrorInvalidValue;
+    constexpr int kLongTC = TC * long_chunk_factor<G>();   // aggregate and checkpoint-only passes
     {
         const int64_t total = (int64_t)p.batch * padded_len(p.L) * (NPW * G);
         hipLaunchKernelGGL(widen_bc_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
@@ -814,12 +830,7 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if (nblocks_agg > 0) {
-        // the aggregate pass stages no readout planes, so its chunks can be
-        // twice as long within the same LDS: half the barriers per token
-        // (with 4 waves or more; fewer would hold several times the staged
-        // pieces in registers)
-        constexpr int kAggTC = G >= 4 ? 2 * TC : TC;
-        hipLaunchKernelGGL((scan_kernel<T, NPW, G, kAggTC, ZOH, kModeAggregate, FEAT, UF>), dim3(nblocks_agg),
+        hipLaunchKernelGGL((scan_kernel<T, NPW, G, kLongTC, ZOH, kModeAggregate, FEAT, UF>), dim3(nblocks_agg),
                            dim3(kTile * G), 0, st, p);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         CarryParams cp{};
@@ -845,8 +856,8 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
                 hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeMainCheckpoint, FEAT, UF>),
                                    dim3(nblocks_main), dim3(kTile * G), 0, st, p);
             else
-                hipLaunchKernelGGL((scan_kernel<T, NPW, G, TC, ZOH, kModeCheckpoint, FEAT, UF>), dim3(nblocks_main),
-                                   dim3(kTile * G), 0, st, p);
+                hipLaunchKernelGGL((scan_kernel<T, NPW, G, kLongTC, ZOH, kModeCheckpoint, FEAT, UF>),
+                                   dim3(nblocks_main), dim3(kTile * G), 0, st, p);
             return hipGetLastError();
         }
     }
