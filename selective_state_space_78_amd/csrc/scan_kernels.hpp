@@ -260,6 +260,12 @@ enum ScanMode { kModeMain = 0, kModeAggregate = 1, kModeCheckpoint = 2, kModeMai
 // hold several times the staged pieces in registers).
 template <int G> constexpr int long_chunk_factor() { return G >= 4 ? 2 : 1; }
 
+// With segments (few channels, so few workgroups per segment), the main pass
+// of an 8-wave tile runs in chunks half as long: a quarter of the LDS, so four
+// workgroups fit per CU instead of two, and a segmented plan's workgroups are
+// resident at once rather than in one and a half rounds.
+template <int G, int TC> constexpr int seg_main_tc() { return G == 8 ? TC / 2 : TC; }
+
 // FEAT: the step options (delta bias, softplus) are compiled in; without it
 // the kernel carries none of their state (their uniform values alone pushed
 // the scalar registers into spills).
@@ -822,6 +828,7 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
     if (!CK && p.ckpt != nullptr) return hipErrorInvalidValue;
     if ((p.u_f32 != 0) != UF) return hipErrorInvalidValue;
     constexpr int kLongTC = TC * long_chunk_factor<G>();   // aggregate and checkpoint-only passes
+    constexpr int kSegTC = seg_main_tc<G, TC>();            // main pass of a plan with segments
     {
         const int64_t total = (int64_t)p.batch * padded_len(p.L) * (NPW * G);
         hipLaunchKernelGGL(widen_bc_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
@@ -858,6 +865,13 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
             else
                 hipLaunchKernelGGL((scan_kernel<T, NPW, G, kLongTC, ZOH, kModeCheckpoint, FEAT, UF>),
                                    dim3(nblocks_main), dim3(kTile * G), 0, st, p);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (kSegTC != TC) {
+        if (nblocks_agg > 0) {
+            hipLaunchKernelGGL((scan_kernel<T, NPW, G, kSegTC, ZOH, kModeMain, FEAT, UF>), dim3(nblocks_main),
+                               dim3(kTile * G), 0, st, p);
             return hipGetLastError();
         }
     }

@@ -717,6 +717,7 @@ Plan make_plan(const ssm_scan_desc &d, const ssm_scan_tuning *t) {
             while (s < kMaxSegments && tiles * g * s < 2 * want_waves && d.seqlen / (2 * s) >= 256) s *= 2;
         return s;
     };
+    bool long_ctx = false;
     if (G == 0) {
         G = pl.npad > 16 ? pl.npad / 16 : 1;     // at most 16 states per wave
         while (G < 8 && G < pl.npad && tiles * G < want_waves) G *= 2;
@@ -727,13 +728,22 @@ Plan make_plan(const ssm_scan_desc &d, const ssm_scan_tuning *t) {
         // 16 4.24 ms; on L 2048 x 6144 channels the segments are short and
         // 8 waves x 8 segments stay faster, 0.105 against 0.106 ms)
         if (G == 8 && pl.npad == 16 && tiles * G < want_waves && (t == nullptr || t->segments == 0) &&
-            d.seqlen / segments_for(4) >= 2048)
+            d.seqlen / segments_for(4) >= 2048) {
             G = 4;
+            long_ctx = true;
+        }
     }
     pl.G = G;
     pl.npw = pl.npad / G;
     int S = (t && t->segments > 0) ? t->segments : 0;
-    if (S == 0) S = segments_for(G);
+    if (S == 0) {
+        S = segments_for(G);
+        // Long context at 4 waves per tile: half as many segments again
+        // (measured on L 131072 x 5120 channels, 16 states: 48 segments 3.55
+        // and 3.65 ms on two boxes, against 3.65 and 3.80 for 32 and 3.81
+        // for 64)
+        if (long_ctx) S = std::min(kMaxSegments, S + S / 2);
+    }
     if (d.seqlen > 0 && S > d.seqlen) S = (int)d.seqlen;
     if (S < 1) S = 1;
     pl.S = S;
