@@ -764,17 +764,27 @@ __global__ __launch_bounds__(kTile * G) void scan_kernel(const ScanParams p) {
 // ---------------------------------------------------------------------------
 // Carry pass: for each (b, d, n), the initial state of segment s is the
 // composition of the maps of segments 0..s-1 applied to h0. Lanes hold
-// consecutive segments of one (b, d, n) in groups of SP lanes (SP = segments
-// rounded up to a power of two, <= 64). An inclusive Kogge-Stone scan over the
-// affine pairs runs with DPP: row shifts by 1, 2, 4, 8 inside 16-lane rows,
-// then row broadcasts of lanes 15 and 31 to cross rows.
+// consecutive segments of one (b, d, n) item in groups of SP lanes (SP =
+// segments rounded up to a power of two, <= 64), and an inclusive
+// Kogge-Stone scan over the affine pairs runs with DPP: row shifts by 1, 2, 4,
+// 8 inside 16-lane rows, then row broadcasts of lanes 15 and 31 to cross rows.
+// With up to kCarryDirect segments every lane reads its pair from global
+// memory directly (a wave then touches runs of at least 32 bytes); with more,
+// a workgroup stages a block of kCarryItems consecutive items of one batch
+// row through LDS, so that it reads and writes every segment's rows of the
+// block as 256-byte runs.
 
 struct CarryParams {
     const float *P, *H, *h0;
     float *seg_h;
     int batch, dim, N, nseg, sp_log2;
     int64_t total;    // batch * dim * N
+    int b0;           // staged form: first batch row of this launch (grid.y covers at most 65535)
 };
+
+constexpr int kCarryDirect = 8;
+constexpr int kCarryItems = 64;      // staged form: (d, n) items per workgroup
+constexpr int kCarryThreads = 256;
 
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ void affine_step(float &P, float &H, bool take) {
@@ -791,7 +801,18 @@ __device__ __forceinline__ void affine_step(float &P, float &H, bool take) {
     }
 }
 
-__global__ __launch_bounds__(256) __attribute__((unused)) void carry_kernel(const CarryParams p) {
+// Inclusive scan of the affine pairs inside groups of sp = 2^sp_log2 lanes
+// (s: the lane's position in its group).
+__device__ __forceinline__ void affine_scan(float &P, float &H, int lane, int sp, int s) {
+    if (sp > 1)  affine_step<0x111, 0xF>(P, H, s >= 1);    // row_shr:1
+    if (sp > 2)  affine_step<0x112, 0xF>(P, H, s >= 2);    // row_shr:2
+    if (sp > 4)  affine_step<0x114, 0xF>(P, H, s >= 4);    // row_shr:4
+    if (sp > 8)  affine_step<0x118, 0xF>(P, H, s >= 8);    // row_shr:8
+    if (sp > 16) affine_step<0x142, 0xA>(P, H, (lane & 16) != 0);   // row_bcast:15 -> rows 1, 3
+    if (sp > 32) affine_step<0x143, 0xC>(P, H, (lane & 32) != 0);   // row_bcast:31 -> rows 2, 3
+}
+
+__global__ __launch_bounds__(kCarryThreads) __attribute__((unused)) void carry_direct_kernel(const CarryParams p) {
     const int lane = threadIdx.x & 63;
     const int sp = 1 << p.sp_log2;
     const int s = lane & (sp - 1);                                  // segment
@@ -809,16 +830,55 @@ __global__ __launch_bounds__(256) __attribute__((unused)) void carry_kernel(cons
         P = p.P[o];
         H = p.H[o];
     }
-    // inclusive scan inside groups of sp lanes
-    if (sp > 1)  affine_step<0x111, 0xF>(P, H, s >= 1);    // row_shr:1
-    if (sp > 2)  affine_step<0x112, 0xF>(P, H, s >= 2);    // row_shr:2
-    if (sp > 4)  affine_step<0x114, 0xF>(P, H, s >= 4);    // row_shr:4
-    if (sp > 8)  affine_step<0x118, 0xF>(P, H, s >= 8);    // row_shr:8
-    if (sp > 16) affine_step<0x142, 0xA>(P, H, (lane & 16) != 0);   // row_bcast:15 -> rows 1, 3
-    if (sp > 32) affine_step<0x143, 0xC>(P, H, (lane & 32) != 0);   // row_bcast:31 -> rows 2, 3
+    affine_scan(P, H, lane, sp, s);
     if (!valid) return;
     const float hin = p.h0 != nullptr ? p.h0[b * (int64_t)p.dim * p.N + dn] : 0.0f;
     p.seg_h[((b * p.nseg + s) * p.dim * p.N) + dn] = fmaf(P, hin, H);
+}
+
+// grid: (blocks of kCarryItems items per batch row, batch rows from b0)
+__global__ __launch_bounds__(kCarryThreads) __attribute__((unused)) void carry_staged_kernel(const CarryParams p) {
+    // one row of the block's items per segment, padded by one against bank conflicts
+    __shared__ float sP[kMaxSegments][kCarryItems + 1], sH[kMaxSegments][kCarryItems + 1];
+    const int64_t per_row = (int64_t)p.dim * p.N;
+    const int64_t b = p.b0 + (int64_t)blockIdx.y;
+    const int64_t i0 = (int64_t)blockIdx.x * kCarryItems;
+    const int items = (int)min((int64_t)kCarryItems, per_row - i0);
+    // Row s of the block holds the map of segment s-1, which feeds segment s;
+    // row 0 the identity.
+    for (int e = threadIdx.x; e < p.nseg * kCarryItems; e += kCarryThreads) {
+        const int s = e / kCarryItems, k = e % kCarryItems;
+        float P = 1.0f, H = 0.0f;
+        if (s > 0 && k < items) {
+            const int64_t o = (b * p.nseg + (s - 1)) * per_row + i0 + k;
+            P = p.P[o];
+            H = p.H[o];
+        }
+        sP[s][k] = P;
+        sH[s][k] = H;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x / 64;
+    const int sp = 1 << p.sp_log2;
+    const int s = lane & (sp - 1);               // segment
+    const int per_wave = 64 >> p.sp_log2;        // items a wave scans at once
+    for (int k0 = wave * per_wave; k0 < items; k0 += 4 * per_wave) {
+        const int k = k0 + (lane >> p.sp_log2);
+        const bool valid = k < items && s < p.nseg;
+        float P = valid ? sP[s][k] : 1.0f;
+        float H = valid ? sH[s][k] : 0.0f;
+        affine_scan(P, H, lane, sp, s);
+        if (valid) {
+            const float hin = p.h0 != nullptr ? p.h0[b * per_row + i0 + k] : 0.0f;
+            sH[s][k] = fmaf(P, hin, H);   // only this lane reads or writes (s, k)
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < p.nseg * kCarryItems; e += kCarryThreads) {
+        const int s2 = e / kCarryItems, k = e % kCarryItems;
+        if (k < items) p.seg_h[(b * p.nseg + s2) * per_row + i0 + k] = sH[s2][k];
+    }
 }
 
 // CK: the shape also has the checkpoint pass (the launch shapes the backward
@@ -851,9 +911,21 @@ hipError_t launch_scan_tf(const ScanParams &p, int nblocks_main, int nblocks_agg
         cp.nseg = p.nseg;
         cp.sp_log2 = ilog2(p.nseg);
         cp.total = (int64_t)p.batch * p.dim * p.N;
-        const int64_t threads = cp.total << cp.sp_log2;
-        hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, cp);
-        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+        if (p.nseg <= kCarryDirect) {
+            const int64_t threads = cp.total << cp.sp_log2;
+            hipLaunchKernelGGL(carry_direct_kernel, dim3((unsigned)((threads + kCarryThreads - 1) / kCarryThreads)),
+                               dim3(kCarryThreads), 0, st, cp);
+            if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+        } else {
+            const int64_t per_row = (int64_t)p.dim * p.N;
+            for (int b0 = 0; b0 < p.batch; b0 += 65535) {
+                cp.b0 = b0;
+                const dim3 grid((unsigned)((per_row + kCarryItems - 1) / kCarryItems),
+                                (unsigned)min(p.batch - b0, 65535));
+                hipLaunchKernelGGL(carry_staged_kernel, grid, dim3(kCarryThreads), 0, st, cp);
+                if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+            }
+        }
     }
     if constexpr (CK) {
         if (p.ckpt != nullptr) {

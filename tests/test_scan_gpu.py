@@ -165,6 +165,21 @@ def test_long_single_tile(env, segments):
     compare(x, y, hl, what="L5000 S%d" % segments)
 
 
+@pytest.mark.parametrize("segments", [9, 12, 20, 50])
+def test_carry_staged_segment_counts(env, segments):
+    """Segment counts past the direct carry form (the plan rounds the requests
+    to 9, 12, 19 and 47 segments of whole 16-token chunks): the carry pass
+    stages blocks of 64 (d, n) items through LDS, with one to four items per
+    wave (groups of 16, 32 or 64 lanes) and a ragged last block (dim * N =
+    360), over three batch rows, from a nonzero initial state."""
+    torch, ssm = env
+    x = reduced("mamba130m", seed=segments, batch=3, seqlen=1500, dim=72, dstate=5)
+    h0 = np.random.default_rng(segments).standard_normal((3, 72, 5)).astype(np.float32)
+    say("staged carry b3 L1500 d72 N5 G2 S%d" % segments)
+    y, hl = run_scan(ssm, torch, x, h0=h0, tuning=(2, segments))
+    compare(x, y, hl, h0=h0, what="S%d" % segments)
+
+
 def test_delta_zero_keeps_state_exactly(env):
     torch, ssm = env
     x = reduced("mamba130m", batch=2, seqlen=64, dim=128)
