@@ -644,9 +644,9 @@ struct ScanKernel {
 
         // B and C of a batch of kTB steps, fetched with a few wide scalar loads
         // and waited for once. Scalar and LDS reads share one wait counter, so
-        // the first batch of a chunk is fetched right after the barrier that
-        // opens it, ahead of the staging work, and lands before the first LDS
-        // wait.
+        // the first batch of a chunk is requested between the LDS wait and the
+        // barrier that close the chunk before it: its latency then overlaps the
+        // barrier, and it lands before the first LDS wait of its chunk.
         uint32_t bc[kTB][NPW][kWPS];
         auto fetch = [&](int t0b) {
 #pragma unroll
@@ -658,11 +658,12 @@ struct ScanKernel {
                 }
         };
 
-        // Chunk k (parity P): fetch its B and C, stage chunk k+1's inputs,
-        // store chunk k-1's outputs, scan chunk k, then one barrier.
+        // Chunk k (parity P): stage chunk k+1's inputs, store chunk k-1's
+        // outputs, scan chunk k, then one barrier (with chunk k+1's first B and
+        // C requested just before it).
+        if (nchunks > 0) fetch(0);
         auto chunk = [&](auto parity, int k) {
             constexpr int P = decltype(parity)::value;
-            fetch(0);
             if constexpr (!AGG) {
                 // chunk k-1's outputs first: its skip and gate then make room
                 // for chunk k+1's in the same registers
@@ -711,7 +712,12 @@ struct ScanKernel {
             }
             bw += TC * NPW;
             cw += TC * NPW;
-            __syncthreads();
+            // the barrier, as __syncthreads() is, with the next chunk's first
+            // fetch after the LDS writes have completed
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            if (k + 1 < nchunks) fetch(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         };
         for (int k = 0; k < nchunks; k += 2) {
             chunk(std::integral_constant<int, 0>(), k);
