@@ -166,7 +166,11 @@ struct BwdKernel {
     // the reverse step: the 8-wave hold-rule kernels run at 2 waves per SIMD
     // and have the registers for it
     static constexpr bool kKeepF = ZOH && G == 8;
-    static constexpr int kRed = (2 * NPW + 3) / 4 * 4;             // reduced values per step, in 4s                        // keep the chunk's decays in registers
+    static constexpr int kRed = (2 * NPW + 3) / 4 * 4;             // reduced values per step, in 4s
+    // bf16 B/C words of the whole chunk fit in 32 scalar registers: they are
+    // requested before the barrier that opens the chunk, so that their
+    // latency overlaps it, and held for both passes over the chunk
+    static constexpr bool kPreBC = kPacked && TC * NPW <= 32;
     typedef typename Words<kWords>::type Raw;
     typedef typename BwdFloats<kV>::type VecF;
 
@@ -472,7 +476,21 @@ struct BwdKernel {
             }
             cword *bw = bw0 + t0 * NPW;
             cword *cw = cw0 + t0 * NPW;
-            __syncthreads();
+            uint32_t bcw[kPreBC ? TC : 1][kPreBC ? NPW : 1];
+            if constexpr (kPreBC) {
+                // the barrier, as __syncthreads() is, with the chunk's B and C
+                // requested after the LDS writes have completed
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+#pragma unroll
+                for (int t = 0; t < TC; ++t)
+#pragma unroll
+                    for (int q = 0; q < NPW; ++q) bcw[t][q] = bw[t * NPW + q];
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            } else {
+                __syncthreads();
+            }
+            auto bc_word = [&](int t, int q) { return kPreBC ? bcw[kPreBC ? t : 0][kPreBC ? q : 0] : bw[t * NPW + q]; };
 
             // 2. recompute the chunk's states of this wave; parts of s_t
             float hs[TC][NPW];
@@ -488,7 +506,7 @@ struct BwdKernel {
                     float part = 0.0f;
 #pragma unroll
                     for (int q = 0; q < NPW; ++q) {
-                        const uint32_t wb = bw[t * NPW + q];
+                        const uint32_t wb = bc_word(t, q);
                         const float bq = __uint_as_float(kPacked ? wb << 16 : wb);
                         const float cq = __uint_as_float(kPacked ? wb & 0xffff0000u : cw[t * NPW + q]);
                         if constexpr (ZOH) {
@@ -537,7 +555,7 @@ struct BwdKernel {
                 for (int i = 2 * NPW; i < kRed; ++i) vr[i] = 0.0f;
 #pragma unroll
                 for (int q = 0; q < NPW; ++q) {
-                    const uint32_t wb = bw[t * NPW + q];
+                    const uint32_t wb = bc_word(t, q);
                     const float bq = __uint_as_float(kPacked ? wb << 16 : wb);
                     const float cq = __uint_as_float(kPacked ? wb & 0xffff0000u : cw[t * NPW + q]);
                     const float a = kKeepA                 ? as[t][q]
