@@ -618,9 +618,12 @@ struct ScanKernel {
         // 0: delta as given; 1: plus the bias; 2: softplus of that
         const int prep = !FEAT ? 0 : p.delta_softplus ? 2 : (p.delta_bias != nullptr ? 1 : 0);
 
-        const int nchunks = (int)((t_end - t_begin + TC - 1) / TC);
+        // the segment's tokens: at most seg_len, an int (32-bit arithmetic
+        // keeps the per-chunk row counts on the scalar unit)
+        const int seg_rows = (int)(t_end - t_begin);
+        const int nchunks = (seg_rows + TC - 1) / TC;
         const int64_t row0 = (int64_t)b * p.L + t_begin;        // token row of (b, t_begin)
-        auto rows_of = [&](int k) { return (int)min((int64_t)TC, t_end - t_begin - (int64_t)k * TC); };
+        auto rows_of = [&](int k) { return min(TC, seg_rows - k * TC); };
         Prefetch pf;
         Held held[2];                                            // by chunk parity
         double dsum[kV];                                         // aggregate pass: this thread's staged steps

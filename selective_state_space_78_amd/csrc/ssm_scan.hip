@@ -749,8 +749,11 @@ Plan make_plan(const ssm_scan_desc &d, const ssm_scan_tuning *t) {
     pl.S = S;
     // segments start on 16-token boundaries (whole chunks, aligned runs of B and C)
     const int64_t seg_len = d.seqlen > 0 ? ((d.seqlen + S - 1) / S + 15) / 16 * 16 : 0;
-    pl.seg_len = seg_len > INT32_MAX ? 0 : (int)seg_len;
-    if (d.seqlen > 0) pl.S = (int)((d.seqlen + pl.seg_len - 1) / pl.seg_len);   // drop empty segments
+    // a segment longer than an int is not supported (-1): the kernels count a
+    // segment's tokens in 32 bits
+    pl.seg_len = seg_len > INT32_MAX ? -1 : (int)seg_len;
+    if (d.seqlen > 0 && pl.seg_len > 0)
+        pl.S = (int)((d.seqlen + pl.seg_len - 1) / pl.seg_len);   // drop empty segments
     return pl;
 }
 
@@ -759,7 +762,7 @@ bool plan_supported(const Plan &pl) {
     if (pl.npad % pl.G != 0) return false;
     if (pl.npw < 1 || pl.npw > 16) return false;
     if (pl.S < 1 || pl.S > kMaxSegments) return false;
-    return pl.seg_len > 0 || pl.S == 1;
+    return pl.seg_len > 0 || (pl.seg_len == 0 && pl.S == 1);   // 0: an empty sequence
 }
 
 // The scan's passes for the descriptor's element type and rule; bf16 tensors

@@ -82,6 +82,9 @@ def test_scan_descriptor_errors(L):
     assert scan_call(L, desc(N=0)) == EUNSUP
     assert scan_call(L, desc(N=65)) == EUNSUP
     assert scan_call(L, desc(b=1 << 40, L=1 << 40)) == ESHAPE
+    # one segment longer than 2^31 tokens (forced by the tuning): the kernels
+    # count a segment's tokens in 32 bits, so the plan is refused
+    assert scan_call(L, desc(b=1, L=(1 << 31) + 16, d=64), tuning=(8, 1)) == EUNSUP
     assert scan_call(L, desc(softplus=2)) == EUNSUP
     assert scan_call(L, desc(conv=5)) == EUNSUP
     assert scan_call(L, desc(conv=-1)) == EUNSUP
