@@ -443,7 +443,10 @@ struct BwdKernel {
 
         const int nck = p.nck;                                  // chunks of this row, walked last to first
         const int64_t row0 = (int64_t)b * p.L;
-        auto rows_of = [&](int c) { return (int)min((int64_t)TC, p.L - (int64_t)c * TC); };
+        // every chunk but the last holds TC rows (a 32-bit compare on the
+        // scalar unit, not a 64-bit one per chunk on the vector unit)
+        const int last_rows = nck > 0 ? (int)(p.L - (int64_t)(nck - 1) * TC) : 0;
+        auto rows_of = [&](int c) { return c == nck - 1 ? last_rows : TC; };
         const int64_t Lp = padded_len(p.L);
         cword *bw0 = (cword *)(p.Bf) + ((int64_t)b * G + w) * Lp * NPW;
         cword *cw0 = (cword *)(p.Cf) + ((int64_t)b * G + w) * Lp * NPW;
