@@ -495,7 +495,12 @@ struct BwdKernel {
             }
             auto bc_word = [&](int t, int q) { return kPreBC ? bcw[kPreBC ? t : 0][kPreBC ? q : 0] : bw[t * NPW + q]; };
 
-            // 2. recompute the chunk's states of this wave; parts of s_t
+            // 2. recompute the chunk's states of this wave; parts of s_t. The
+            // two arithmetic phases (this and 4) run at a higher issue
+            // priority than the staging, dz and finalize phases, so that a
+            // SIMD's VALU is fed from them first when its waves are in
+            // different phases.
+            __builtin_amdgcn_s_setprio(2);
             float hs[TC][NPW];
             float as[kKeepA ? TC : 1][NPW];
             float fs[kKeepF ? TC : 1][NPW];
@@ -531,6 +536,7 @@ struct BwdKernel {
                     s.pl[0][w][t][lane] = part;
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
 
             // 3. dz of this thread's pieces
@@ -548,6 +554,7 @@ struct BwdKernel {
             __syncthreads();
 
             // 4. adjoint over the chunk in reverse
+            __builtin_amdgcn_s_setprio(2);
 #pragma unroll
             for (int t = TC - 1; t >= 0; --t) {
                 const float2 v = s.dx[t][lane];
@@ -608,6 +615,7 @@ struct BwdKernel {
                 s.pl[0][w][t][lane] = pU;
                 s.pl[1][w][t][lane] = pD;
             }
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
 
             // 5. du, ddelta of this thread's pieces; the tile's dB, dC sums

@@ -680,6 +680,12 @@ struct ScanKernel {
             if (k + 2 < nchunks) load_chunk(k + 2);
             const int tval = rows_of(k);
             const float2 (*dx)[kTile] = s.dx[P];
+            // The recurrence runs at a higher issue priority than the staging
+            // work: where a SIMD holds waves in both phases (its two
+            // workgroups are rarely in step), the arbiter then feeds the VALU
+            // from the recurrence's long dependent chains first, and the
+            // staging's loads, LDS traffic and stores fill the gaps.
+            __builtin_amdgcn_s_setprio(2);
             // the state before token j of the chunk, where a checkpoint falls
             // (j is a compile-time constant once the loops are unrolled)
             auto checkpoint = [&](int j) {
@@ -713,6 +719,7 @@ struct ScanKernel {
                     }
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
             bw += TC * NPW;
             cw += TC * NPW;
             // the barrier, as __syncthreads() is, with the next chunk's first
