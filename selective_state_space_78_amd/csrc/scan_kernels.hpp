@@ -247,6 +247,13 @@ __device__ __forceinline__ void make_words(uint32_t &r, const uint32_t *w) { r =
 __device__ __forceinline__ void make_words(uint2 &r, const uint32_t *w) { r = make_uint2(w[0], w[1]); }
 __device__ __forceinline__ void make_words(uint4 &r, const uint32_t *w) { r = make_uint4(w[0], w[1], w[2], w[3]); }
 
+// a < b for values every lane of the wave shares, compared as 32-bit scalars
+// right where the branch takes it: a boolean kept across divergent blocks
+// would be rebuilt as a lane mask with vector instructions.
+__device__ __forceinline__ bool uniform_less(int a, int b) {
+    return __builtin_amdgcn_readfirstlane(b - a) > 0;
+}
+
 template <int KV> struct FloatsOf;
 template <> struct FloatsOf<2> { typedef float2 type; };
 template <> struct FloatsOf<4> { typedef float4 type; };
@@ -385,8 +392,10 @@ struct ScanKernel {
                                 bool colv) {
         const T *u = static_cast<const T *>(p.u) + base;
         const T *dt = static_cast<const T *>(p.delta) + base;
-        const T *z = static_cast<const T *>(p.z) + base;
         const bool gate = !AGG && p.z != nullptr;
+        // without a gate the z slot reloads delta (its value is not used), so
+        // that the aligned path loads unconditionally
+        const T *z = static_cast<const T *>(gate ? p.z : p.delta) + base;
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
             const int row = piece_row(j);
@@ -398,7 +407,7 @@ struct ScanKernel {
                 else
                     pf.u[j] = *reinterpret_cast<const Raw *>(u + off);
                 pf.dt[j] = *reinterpret_cast<const Raw *>(dt + off);
-                if (gate) pf.z[j] = *reinterpret_cast<const Raw *>(z + off);
+                pf.z[j] = *reinterpret_cast<const Raw *>(z + off);
             } else {
                 if constexpr (UF)
                     pf.u[j] = gather_f32(static_cast<const float *>(p.u) + base + off, d0 + col, p.dim);
@@ -675,9 +684,9 @@ struct ScanKernel {
                     yb += (int64_t)TC * p.dim;
                 }
             }
-            if (k + 1 < nchunks)
+            if (uniform_less(k + 1, nchunks))
                 commit(pf, s.dx[P ^ 1], held[P ^ 1], rows_of(k + 1), col, colv, Dk, gate, dbk, prep, dsum);
-            if (k + 2 < nchunks) load_chunk(k + 2);
+            if (uniform_less(k + 2, nchunks)) load_chunk(k + 2);
             const int tval = rows_of(k);
             const float2 (*dx)[kTile] = s.dx[P];
             // The recurrence runs at a higher issue priority than the staging
@@ -725,7 +734,7 @@ struct ScanKernel {
             // the barrier, as __syncthreads() is, with the next chunk's first
             // fetch after the LDS writes have completed
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            if (k + 1 < nchunks) fetch(0);
+            if (uniform_less(k + 1, nchunks)) fetch(0);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         };
